@@ -1,0 +1,413 @@
+"""Pins for the CPU oracle: each check reaches the expected result by a route
+independent of the oracle's own code (a library routine, a closed form, an
+invariant or brute-force enumeration).  Every check raises AssertionError on
+failure, so the same checks run against the real oracle (tests/test_oracle_pins.py)
+and against copies of the oracle with a planted mistake (tests/test_oracle_mutants.py).
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import torch
+
+import oracle
+from speculative_decoding_verification_attn_amd.workloads import (
+    bf16_bits_to_f32, f32_to_bf16_bits, make_custom)
+
+P = 16
+
+
+# ----------------------------------------------------------------------------
+# helpers (test-side definitions, written without the oracle's code)
+# ----------------------------------------------------------------------------
+def visible_sets(parent):
+    """For each node j: the set of nodes whose KV node j sees (itself and its
+    ancestors), found top-down by a DFS over child lists."""
+    n = len(parent)
+    children = [[] for _ in range(n)]
+    for j in range(1, n):
+        children[parent[j]].append(j)
+    vis = [set() for _ in range(n)]
+
+    def dfs(node, stack):
+        stack.append(node)
+        vis[node] = set(stack)
+        for c in children[node]:
+            dfs(c, stack)
+        stack.pop()
+
+    if n:
+        dfs(0, [])
+    return vis
+
+
+def chain_parent(q):
+    return np.arange(-1, q - 1, dtype=np.int32)
+
+
+def dense_request_kv(case, i):
+    """Dense [Hkv, L+q, D] fp64 K and V of request i for a case whose pages were
+    laid out contiguously in request order (permute_pages=False)."""
+    n_pages = [(int(L) + int(q) + P - 1) // P for L, q in zip(case.context_lens, case.q_lens)]
+    first = sum(n_pages[:i])
+    nk = int(case.context_lens[i] + case.q_lens[i])
+    out = []
+    for cache in (case.k_cache, case.v_cache):
+        blk = bf16_bits_to_f32(cache[first:first + n_pages[i]]).astype(np.float64)  # [n, Hkv, P, D]
+        dense = blk.transpose(1, 0, 2, 3).reshape(case.num_kv_heads, -1, case.head_dim)[:, :nk]
+        out.append(dense)
+    return out
+
+
+def run_oracle_attn(case, **kw):
+    return oracle.verify_attn(case.q, case.k_cache, case.v_cache, case.block_tables,
+                              case.context_lens, case.cu_q, case.tree_parent,
+                              num_q_heads=case.num_q_heads, num_kv_heads=case.num_kv_heads,
+                              head_dim=case.head_dim, page_size=case.page_size,
+                              num_pages=case.num_pages, **kw)
+
+
+def request_parents(case, i):
+    o, q = int(case.cu_q[i]), int(case.q_lens[i])
+    return chain_parent(q) if case.tree_parent is None else case.tree_parent[o:o + q]
+
+
+SMALL_TREES = [
+    np.array([-1, 0, 0, 1, 1, 2, 4], dtype=np.int32),
+    np.array([-1, 0, 1, 2, 0, 4, 0, 6, 7], dtype=np.int32),
+]
+
+
+def small_cases():
+    """A handful of ragged chain and tree cases (contiguous pages)."""
+    return [
+        make_custom(11, context_lens=[0, 5, 37], q_lens=[3, 1, 6], hq=4, hkv=2, d=16,
+                    permute_pages=False),
+        make_custom(12, context_lens=[17, 0], tree_parents=SMALL_TREES, hq=6, hkv=3, d=32,
+                    permute_pages=False),
+    ]
+
+
+# ----------------------------------------------------------------------------
+# attention pins
+# ----------------------------------------------------------------------------
+def check_attn_vs_sdpa():
+    """Library special case: torch SDPA (fp64, boolean mask, dense layout)."""
+    for case in small_cases():
+        out = run_oracle_attn(case)
+        G = case.group
+        for i in range(case.batch):
+            o, q = int(case.cu_q[i]), int(case.q_lens[i])
+            L = int(case.context_lens[i])
+            kd, vd = dense_request_kv(case, i)
+            vis = visible_sets(request_parents(case, i))
+            mask = np.zeros((q, L + q), dtype=bool)
+            mask[:, :L] = True
+            for j in range(q):
+                for k in vis[j]:
+                    mask[j, L + k] = True
+            qf = bf16_bits_to_f32(case.q[o:o + q]).astype(np.float64)      # [q, Hq, D]
+            for h in range(case.num_q_heads):
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    torch.from_numpy(qf[:, h][None]), torch.from_numpy(kd[h // G][None]),
+                    torch.from_numpy(vd[h // G][None]), attn_mask=torch.from_numpy(mask)[None],
+                    scale=1.0 / np.sqrt(case.head_dim))[0].numpy()
+                got = out[o:o + q, h]
+                assert np.max(np.abs(got - ref)) < 1e-10, (i, h, np.max(np.abs(got - ref)))
+
+
+def check_attn_closed_forms():
+    """V constant -> output is that constant; all keys equal -> mean of the
+    visible values; a dominant key -> its value; L=0 chain root -> v_0."""
+    base = make_custom(21, context_lens=[9, 0, 30], q_lens=[4, 3, 2], hq=4, hkv=2, d=16,
+                       permute_pages=False)
+    # (1) constant V
+    c = base
+    v_saved = c.v_cache.copy()
+    c.v_cache[...] = f32_to_bf16_bits(np.full(c.v_cache.shape, 0.625, np.float32))
+    out = run_oracle_attn(c)
+    assert np.max(np.abs(out - 0.625)) < 1e-12
+    c.v_cache[...] = v_saved
+    # (2) all keys equal -> uniform weights over the visible keys
+    k_saved = c.k_cache.copy()
+    vec = f32_to_bf16_bits(np.random.default_rng(0).standard_normal(c.head_dim).astype(np.float32))
+    c.k_cache[...] = vec
+    out = run_oracle_attn(c)
+    for i in range(c.batch):
+        o, q, L = int(c.cu_q[i]), int(c.q_lens[i]), int(c.context_lens[i])
+        _, vd = dense_request_kv(c, i)
+        vis = visible_sets(request_parents(c, i))
+        for j in range(q):
+            keys = list(range(L)) + [L + k for k in sorted(vis[j])]
+            for h in range(c.num_q_heads):
+                ref = vd[h // c.group][keys].mean(axis=0)
+                assert np.max(np.abs(out[o + j, h] - ref)) < 1e-12, (i, j, h)
+    c.k_cache[...] = k_saved
+    # (3) one dominant key: key p* = 2.0 everywhere, query = 8.0 everywhere
+    i, pstar = 2, 13
+    o = int(c.cu_q[i])
+    pg, sl = int(c.block_tables[i, pstar // P]), pstar % P
+    c.k_cache[pg, :, sl, :] = f32_to_bf16_bits(np.full((c.num_kv_heads, c.head_dim), 2.0, np.float32))
+    c.q[o] = f32_to_bf16_bits(np.full((c.num_q_heads, c.head_dim), 8.0, np.float32))
+    _, vd = dense_request_kv(c, i)
+    out = run_oracle_attn(c)
+    for h in range(c.num_q_heads):
+        assert np.max(np.abs(out[o, h] - vd[h // c.group][pstar])) < 1e-9
+    # (4) L = 0 chain: the root sees only its own key
+    i = 1
+    o = int(c.cu_q[i])
+    _, vd = dense_request_kv(c, i)
+    for h in range(c.num_q_heads):
+        assert np.array_equal(out[o, h], vd[h // c.group][0])
+
+
+def check_attn_convexity():
+    """Each output coordinate lies between the min and max over visible V rows."""
+    for case in small_cases():
+        out = run_oracle_attn(case)
+        for i in range(case.batch):
+            o, q, L = int(case.cu_q[i]), int(case.q_lens[i]), int(case.context_lens[i])
+            _, vd = dense_request_kv(case, i)
+            vis = visible_sets(request_parents(case, i))
+            for j in range(q):
+                keys = list(range(L)) + [L + k for k in sorted(vis[j])]
+                for h in range(case.num_q_heads):
+                    vv = vd[h // case.group][keys]
+                    assert np.all(out[o + j, h] >= vv.min(axis=0) - 1e-12)
+                    assert np.all(out[o + j, h] <= vv.max(axis=0) + 1e-12)
+
+
+def check_attn_decode_equivalence():
+    """A chain's token j equals one-token decoding at position L+j (no mask)."""
+    case = make_custom(31, context_lens=[12, 40], q_lens=[5, 3], hq=4, hkv=1, d=32)
+    out = run_oracle_attn(case)
+    for i in range(case.batch):
+        o, q, L = int(case.cu_q[i]), int(case.q_lens[i]), int(case.context_lens[i])
+        for j in range(q):
+            for h in range(case.num_q_heads):
+                ref = oracle.decode_attn(case.q[o + j, h], case.k_cache, case.v_cache,
+                                         case.block_tables, i, h, L + j,
+                                         num_q_heads=case.num_q_heads,
+                                         num_kv_heads=case.num_kv_heads,
+                                         head_dim=case.head_dim, page_size=P)
+                assert np.max(np.abs(out[o + j, h] - ref)) < 1e-12
+
+
+def check_decode_closed_form():
+    """Decode with all keys equal = mean of V over [0, pos]."""
+    case = make_custom(32, context_lens=[20], q_lens=[2], hq=2, hkv=1, d=16, permute_pages=False)
+    case.k_cache[...] = case.k_cache[0, 0, 0]
+    _, vd = dense_request_kv(case, 0)
+    for pos in (0, 7, 21):
+        ref = vd[0][:pos + 1].mean(axis=0)
+        got = oracle.decode_attn(case.q[0, 1], case.k_cache, case.v_cache, case.block_tables, 0, 1,
+                                 pos, num_q_heads=2, num_kv_heads=1, head_dim=16, page_size=P)
+        assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def check_attn_page_permutation_and_degenerate_tree():
+    """Relaying pages through a permuted block table and stating a chain as a
+    tree (parent j-1) both leave the output bit-identical."""
+    case = make_custom(41, context_lens=[33, 3], q_lens=[4, 6], hq=4, hkv=2, d=16,
+                       permute_pages=False)
+    out = run_oracle_attn(case)
+    perm = np.random.default_rng(5).permutation(case.num_pages)
+    k2 = np.empty_like(case.k_cache)
+    v2 = np.empty_like(case.v_cache)
+    k2[perm] = case.k_cache
+    v2[perm] = case.v_cache
+    bt2 = perm[case.block_tables].astype(np.int32)
+    out2 = oracle.verify_attn(case.q, k2, v2, bt2, case.context_lens, case.cu_q, None,
+                              num_q_heads=4, num_kv_heads=2, head_dim=16, page_size=P,
+                              num_pages=case.num_pages)
+    assert np.array_equal(out, out2)
+    tp = np.concatenate([chain_parent(int(q)) for q in case.q_lens])
+    out3 = oracle.verify_attn(case.q, case.k_cache, case.v_cache, case.block_tables,
+                              case.context_lens, case.cu_q, tp, num_q_heads=4, num_kv_heads=2,
+                              head_dim=16, page_size=P, num_pages=case.num_pages)
+    assert np.array_equal(out, out3)
+
+
+# ----------------------------------------------------------------------------
+# argmax pins
+# ----------------------------------------------------------------------------
+def check_argmax():
+    rng = np.random.default_rng(7)
+    for V in (1, 2, 3, 17, 1000, 4099):
+        x = rng.standard_normal((9, V)).astype(np.float32)
+        assert np.array_equal(oracle.argmax(x), np.argmax(x, axis=1))
+    # planted ties: the earlier of two equal maxima wins
+    x = rng.standard_normal((4, 64)).astype(np.float32)
+    x[0, 10] = x[0, 40] = 9.0
+    x[1, 0] = x[1, 63] = 9.0
+    x[2, :] = 1.5
+    x[3, 5] = -0.0
+    x[3, :5] = -1.0
+    x[3, 6:] = -1.0
+    x[3, 30] = 0.0
+    got = oracle.argmax(x)
+    assert got.tolist() == [10, 0, 0, 5], got
+    # +0 before -0: still the lower index (IEEE equality)
+    y = np.full((1, 8), -2.0, np.float32)
+    y[0, 2] = 0.0
+    y[0, 6] = -0.0
+    assert oracle.argmax(y).tolist() == [2]
+    assert np.array_equal(oracle.argmax(x), np.argmax(x, axis=1))
+
+
+# ----------------------------------------------------------------------------
+# acceptance pins
+# ----------------------------------------------------------------------------
+def brute_accept(parent, draft, target):
+    """Enumerate every root path; keep those whose every edge matches; return the
+    deepest (lowest end node on ties) as the accepted path."""
+    n = len(parent)
+    best_path = [0]
+    for end in range(n):
+        path = [end]
+        while parent[path[-1]] >= 0:
+            path.append(parent[path[-1]])
+        path.reverse()
+        ok = all(draft[path[k]] == target[path[k - 1]] for k in range(1, len(path)))
+        if ok and len(path) > len(best_path):
+            best_path = path
+    return best_path
+
+
+def check_accept_chain_exhaustive():
+    """Every match pattern of chains with gamma <= 6: accept_len = 1 + index of
+    the first mismatch (all-correct -> gamma+1; wrong first -> 1)."""
+    qs, drafts, targets, expect = [], [], [], []
+    for gamma in range(0, 7):
+        for pattern in itertools.product([0, 1], repeat=gamma):
+            q = gamma + 1
+            tgt = np.arange(100, 100 + q, dtype=np.int32)
+            d = np.empty(q, np.int32)
+            d[0] = 7
+            for j in range(1, q):
+                d[j] = tgt[j - 1] if pattern[j - 1] else tgt[j - 1] + 1000
+            first_miss = next((j for j, b in enumerate(pattern) if not b), gamma)
+            qs.append(q); drafts.append(d); targets.append(tgt); expect.append(1 + first_miss)
+    cu = np.zeros(len(qs) + 1, np.int32)
+    cu[1:] = np.cumsum(qs)
+    acc, path, toks = oracle.accept(np.concatenate(drafts), np.concatenate(targets), cu, None)
+    assert acc.tolist() == expect
+    for i in range(len(qs)):
+        o = cu[i]
+        n1 = expect[i]
+        assert path[o:o + n1].tolist() == list(range(n1))
+        assert np.all(path[o + n1:cu[i + 1]] == -1)
+        assert toks[o:o + n1].tolist() == targets[i][:n1].tolist()
+        assert np.all(toks[o + n1:cu[i + 1]] == -1)
+
+
+def all_trees(n):
+    """Every parent array with parent[0] = -1 and 0 <= parent[j] < j."""
+    for rest in itertools.product(*[range(j) for j in range(1, n)]):
+        yield np.array((-1,) + rest, dtype=np.int32)
+
+
+def check_accept_tree_bruteforce(max_nodes=6):
+    """All topologically ordered trees up to max_nodes nodes x all edge-match patterns,
+    against brute-force path enumeration; plus chain == degenerate tree."""
+    parents, drafts, targets, expects = [], [], [], []
+    for n in range(1, max_nodes + 1):
+        for par in all_trees(n):
+            for pattern in itertools.product([0, 1], repeat=n - 1):
+                tgt = np.arange(10, 10 + n, dtype=np.int32) * 3
+                d = np.empty(n, np.int32)
+                d[0] = 1
+                for j in range(1, n):
+                    d[j] = tgt[par[j]] if pattern[j - 1] else tgt[par[j]] + 1
+                parents.append(par); drafts.append(d); targets.append(tgt)
+                expects.append(brute_accept(par, d, tgt))
+    cu = np.zeros(len(parents) + 1, np.int32)
+    cu[1:] = np.cumsum([len(p) for p in parents])
+    acc, path, toks = oracle.accept(np.concatenate(drafts), np.concatenate(targets), cu,
+                                    np.concatenate(parents))
+    for i, exp in enumerate(expects):
+        o = cu[i]
+        assert acc[i] == len(exp), (parents[i], drafts[i], exp, acc[i])
+        assert path[o:o + len(exp)].tolist() == exp
+        assert toks[o:o + len(exp)].tolist() == [int(targets[i][k]) for k in exp]
+    # a chain stated as a degenerate tree gives identical results
+    rng = np.random.default_rng(3)
+    q = rng.integers(1, 9, size=50).astype(np.int32)
+    cu = np.zeros(51, np.int32)
+    cu[1:] = np.cumsum(q)
+    tgt = rng.integers(0, 3, size=cu[-1]).astype(np.int32)
+    dr = rng.integers(0, 3, size=cu[-1]).astype(np.int32)
+    tp = np.concatenate([chain_parent(int(x)) for x in q])
+    a1 = oracle.accept(dr, tgt, cu, None)
+    a2 = oracle.accept(dr, tgt, cu, tp)
+    for u, v in zip(a1, a2):
+        assert np.array_equal(u, v)
+
+
+# ----------------------------------------------------------------------------
+# compaction pins
+# ----------------------------------------------------------------------------
+def _logical_rows(cache, bt_row, L_new, g):
+    return np.stack([cache[bt_row[p // P], g, p % P] for p in range(L_new)]) if L_new else None
+
+
+def check_compact():
+    """Chains leave the pool untouched; for trees the logical read-back of
+    [0, new_len) is prefix ++ accepted-path rows, every other slot keeps its
+    value, and the result equals a serial in-place copy in increasing k."""
+    case = make_custom(51, context_lens=[5, 18, 0], tree_parents=SMALL_TREES + [np.array([-1, 0, 1], np.int32)],
+                       hq=4, hkv=2, d=8)
+    paths = [[0, 2, 5], [0, 6, 7, 8], [0, 1]]
+    acc = np.array([len(p) for p in paths], np.int32)
+    ap = np.full(case.total_q, -1, np.int32)
+    for i, p in enumerate(paths):
+        ap[case.cu_q[i]:case.cu_q[i] + len(p)] = p
+    k0, v0 = case.k_cache.copy(), case.v_cache.copy()
+    k1, v1 = case.k_cache.copy(), case.v_cache.copy()
+    new = oracle.compact(k1, v1, case.block_tables, case.context_lens, case.cu_q, ap, acc,
+                         num_kv_heads=2, head_dim=8, page_size=P, num_pages=case.num_pages)
+    assert new.tolist() == (case.context_lens + acc).tolist()
+    # serial in-place copy in increasing k (safe because path[k] >= k)
+    k2, v2 = k0.copy(), v0.copy()
+    for i, p in enumerate(paths):
+        L = int(case.context_lens[i])
+        for g in range(2):
+            for k, src in enumerate(p):
+                s, d = L + src, L + k
+                for cache in (k2, v2):
+                    cache[case.block_tables[i, d // P], g, d % P] = cache[case.block_tables[i, s // P], g, s % P]
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+    # read-back and untouched slots
+    for i, p in enumerate(paths):
+        L = int(case.context_lens[i])
+        for g in range(2):
+            for c0, c1 in ((k0, k1), (v0, v1)):
+                got = _logical_rows(c1, case.block_tables[i], L + len(p), g)
+                ref_prefix = _logical_rows(c0, case.block_tables[i], L, g)
+                ref_path = np.stack([c0[case.block_tables[i, (L + s) // P], g, (L + s) % P] for s in p])
+                ref = ref_path if ref_prefix is None else np.concatenate([ref_prefix, ref_path])
+                assert np.array_equal(got, ref)
+    changed = np.argwhere(np.any(k0 != k1, axis=-1))
+    touched = set()
+    for i, p in enumerate(paths):
+        L = int(case.context_lens[i])
+        for k in range(len(p)):
+            if p[k] != k:
+                for g in range(2):
+                    touched.add((int(case.block_tables[i, (L + k) // P]), g, (L + k) % P))
+    assert {tuple(int(x) for x in r) for r in changed} <= touched
+    # chains: nothing moves
+    ch = make_custom(52, context_lens=[3, 40], q_lens=[4, 2], hq=2, hkv=1, d=8)
+    acc = np.array([3, 2], np.int32)
+    ap = np.array([0, 1, 2, -1, 0, 1], np.int32)
+    kk, vv = ch.k_cache.copy(), ch.v_cache.copy()
+    oracle.compact(kk, vv, ch.block_tables, ch.context_lens, ch.cu_q, ap, acc, num_kv_heads=1,
+                   head_dim=8, page_size=P, num_pages=ch.num_pages)
+    assert np.array_equal(kk, ch.k_cache) and np.array_equal(vv, ch.v_cache)
+
+
+ALL_CHECKS = [check_attn_vs_sdpa, check_attn_closed_forms, check_attn_convexity,
+              check_attn_decode_equivalence, check_decode_closed_form,
+              check_attn_page_permutation_and_degenerate_tree, check_argmax,
+              check_accept_chain_exhaustive, check_accept_tree_bruteforce, check_compact]
