@@ -1,0 +1,204 @@
+/*
+ * spec_verify.h -- C ABI of libspecverify.so: the target model's verification
+ * step of speculative decoding on one AMD Instinct MI355X (gfx950).
+ *
+ * Three calls make one verify step:
+ *   spec_verify_attn  attention of every request's verify tokens (a chain of
+ *                     gamma_i+1 tokens or a draft tree of up to 64 nodes) over
+ *                     its paged bf16 KV cache, with grouped-query heads;
+ *   spec_accept       greedy acceptance: the target's argmax over the whole
+ *                     vocabulary at every verify position, then the longest
+ *                     matching prefix (chain) or deepest accepted root path (tree);
+ *   kv_compact        moves the accepted path's K/V into consecutive slots of
+ *                     the request's cache, in place, for every layer.
+ *
+ * Sources (page titles; sections as the pages name them):
+ *   SwiftSpec (ASPLOS 2026), "Fused Latency-Optimized Kernels": padding-free
+ *     attention that verifies all gamma+1 draft tokens at once, and a fused
+ *     "return verification result + KV update" operation whose result is a
+ *     short message to the drafter.
+ *   SwiftSpec, "Tree-Aware KV Cache Management": each tree node owns its KV
+ *     prefix (its root path); only the accepted path's KV is kept.
+ *   DSpark, glossary "Speculative Decoding": the longest matching prefix of
+ *     the draft is accepted.
+ *   FASER, "Per-Request Length Adaptation": gamma differs per request.
+ *   SSD, engine optimisations paragraph: PagedAttention (block tables).
+ *
+ * Common conventions
+ *   - Every pointer is a DEVICE pointer unless stated otherwise.  bf16 data is
+ *     passed as void* holding 16-bit bf16 bit patterns.  `stream` is a
+ *     hipStream_t (NULL = the default stream).
+ *   - Calls are stream-ordered and asynchronous; outputs are valid once the
+ *     stream has reached the call.  The library keeps no state between calls,
+ *     allocates no memory and retains no pointer; callers own every buffer.
+ *     Two calls that share a workspace must not overlap in time.
+ *   - Request i owns verify rows [cu_q[i], cu_q[i+1]) of every [T, ...] array
+ *     (padding-free packing), 0 <= q_i = cu_q[i+1]-cu_q[i] <= 64.  Row 0 of a
+ *     request is the root (the last committed token); a chain's row j is the
+ *     j-th draft token; a tree's rows are its nodes with tree_parent[o+0] = -1
+ *     and 0 <= tree_parent[o+j] < j (local indices).
+ *   - The KV cache of one layer is [num_pages][num_kv_heads][page_size][head_dim]
+ *     bf16; request i's logical slot p is physical page
+ *     block_tables[i*max_blocks_per_seq + p/page_size], slot p % page_size.
+ *     The committed context occupies slots [0, L_i) (L_i = context_lens[i]) and
+ *     the verify tokens' K/V, written by the caller's QKV projection, occupy
+ *     slots [L_i, L_i+q_i) in row order.
+ *   - Query head h reads KV head h / (num_q_heads/num_kv_heads).
+ *
+ * Errors
+ *   Host-checkable argument errors return a nonzero sv_status before anything
+ *   is enqueued.  A failed HIP launch returns SV_ERR_HIP and sv_last_error()
+ *   describes it (thread-local).  Content errors that only the device can see
+ *   (bad cu_q, q_i > 64, a page id outside [0, num_pages), more pages than
+ *   max_blocks_per_seq, a bad parent array) never cause an out-of-bounds
+ *   access: the affected request's outputs are unspecified and a bit is set
+ *   in the workspace's device status word, read with the *_device_status
+ *   calls.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sv_status {
+    SV_OK = 0,
+    SV_ERR_NULL = 1,        /* a required pointer is NULL */
+    SV_ERR_SHAPE = 2,       /* a size argument is out of range or inconsistent */
+    SV_ERR_UNSUPPORTED = 3, /* head_dim, page_size or head grouping not supported */
+    SV_ERR_WORKSPACE = 4,   /* workspace_bytes below the *_workspace_size value */
+    SV_ERR_ALIAS = 5,       /* an output overlaps an input it must not overlap */
+    SV_ERR_HIP = 6          /* a HIP call failed; see sv_last_error() */
+} sv_status;
+
+#define SV_MAX_VERIFY_TOKENS 64 /* per request: gamma_i+1 or tree nodes (one 64-bit ancestor word) */
+#define SV_PAGE_SIZE 16         /* tokens per KV page */
+
+/* Device status bits (see *_device_status). */
+#define SV_DEV_BAD_CU_Q 0x1u        /* cu_q not non-decreasing from 0 to total_q */
+#define SV_DEV_BAD_CONTEXT 0x2u     /* context_lens[i] < 0 */
+#define SV_DEV_TOO_MANY_TOKENS 0x4u /* q_i > 64 */
+#define SV_DEV_BAD_PARENT 0x8u      /* tree_parent violates root=-1, 0<=parent[j]<j */
+#define SV_DEV_BAD_PAGE 0x10u       /* a needed block-table entry is outside [0, num_pages) */
+#define SV_DEV_TOO_MANY_PAGES 0x20u /* ceil((L_i+q_i)/page_size) > max_blocks_per_seq */
+
+/* ------------------------------------------------------------------------- */
+/* Verify attention                                                           */
+/* ------------------------------------------------------------------------- */
+
+/* Workspace bytes spec_verify_attn needs for these sizes (host function). */
+size_t spec_verify_attn_workspace_size(int batch, int total_q, int num_q_heads, int num_kv_heads,
+                                       int head_dim);
+
+/*
+ * out[t, h, :] = softmax_p(scale * q[t,h,:] . K[p,g,:] + M[t,p]) . V[p,g,:]
+ * where for row t = cu_q[i]+j, key p of request i is visible (M = 0) iff
+ * p < L_i, or p = L_i + k with k = j or k an ancestor of j (chain: k <= j);
+ * otherwise M = -inf.  Keys are the L_i+q_i slots of the request's cache.
+ *
+ *   q            bf16 [total_q, num_q_heads, head_dim]
+ *   k_cache      bf16 [num_pages, num_kv_heads, page_size, head_dim] (one layer)
+ *   v_cache      same layout as k_cache
+ *   block_tables int32 [batch, max_blocks_per_seq]
+ *   context_lens int32 [batch]  L_i (verify tokens excluded)
+ *   cu_q         int32 [batch+1] prefix sums of q_i
+ *   tree_parent  int32 [total_q] local parents, or NULL for chains
+ *   out          bf16 [total_q, num_q_heads, head_dim]; must not overlap q/k/v
+ *   softmax_scale  0 selects 1/sqrt(head_dim)
+ *   workspace    device buffer of at least spec_verify_attn_workspace_size()
+ *                bytes (contents need no initialisation; overwritten)
+ * Supported: head_dim 64 or 128, page_size 16, num_q_heads % num_kv_heads == 0
+ * with at most 64 query heads per KV head.
+ */
+int spec_verify_attn(const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *block_tables, int max_blocks_per_seq,
+                     const int32_t *context_lens, const int32_t *cu_q, const int32_t *tree_parent,
+                     void *out, int batch, int total_q, int num_q_heads, int num_kv_heads,
+                     int head_dim, int page_size, int num_pages, float softmax_scale,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Waits for `stream`, then stores the device status bits of the last
+ * spec_verify_attn that used `workspace` into *flags (host pointer). */
+int spec_verify_attn_device_status(const void *workspace, uint32_t *flags, void *stream);
+
+/* ------------------------------------------------------------------------- */
+/* Greedy acceptance                                                          */
+/* ------------------------------------------------------------------------- */
+
+/* Workspace bytes spec_accept needs (host function). */
+size_t spec_accept_workspace_size(int batch, int total_q, int vocab);
+
+/*
+ * target_argmax[t] = lowest index of the maximum of logits[t, 0:vocab]
+ *   (IEEE comparison, so -0 equals +0; logits must be finite).
+ * Chain: n_i = largest k <= q_i-1 with draft_tokens[o+j] == target_argmax[o+j-1]
+ *   for every 1 <= j <= k.
+ * Tree: node j is accepted iff draft_tokens[o+a] == target_argmax[o+parent[a]]
+ *   for every non-root node a on its root path; the accepted node of greatest
+ *   depth (lowest index on ties) is chosen and n_i is its depth.
+ * Outputs: accept_len[i] = n_i + 1 (bonus token counted; 0 when q_i = 0);
+ *   accepted_path[o+k] = k-th node of the accepted root path for k <= n_i, -1 after;
+ *   out_tokens[o+k] = target_argmax[o + accepted_path[o+k]] for k <= n_i, -1 after.
+ *
+ *   logits       fp32 [total_q, vocab]; row o+j is the target's prediction after row j
+ *   draft_tokens int32 [total_q]; the entry at each root is ignored
+ *   cu_q, tree_parent as for spec_verify_attn
+ *   target_argmax int32 [total_q] out;  accept_len int32 [batch] out;
+ *   accepted_path int32 [total_q] out;  out_tokens int32 [total_q] out
+ */
+int spec_accept(const float *logits, int vocab, const int32_t *draft_tokens, const int32_t *cu_q,
+                const int32_t *tree_parent, int batch, int total_q, int32_t *target_argmax,
+                int32_t *accept_len, int32_t *accepted_path, int32_t *out_tokens, void *workspace,
+                size_t workspace_bytes, void *stream);
+
+/* Waits for `stream`, then stores the device status bits of the last
+ * spec_accept that used `workspace` into *flags (host pointer). */
+int spec_accept_device_status(const void *workspace, uint32_t *flags, void *stream);
+
+/* ------------------------------------------------------------------------- */
+/* KV compaction                                                              */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * For every layer l < num_layers (cache base + l*layer_stride_elems elements),
+ * request i, KV head g and k = 0..accept_len[i]-1: logical slot
+ * L_i + accepted_path[o+k] is copied into logical slot L_i + k, all sources
+ * being read before any destination is written.  Chains (path[k] = k) move
+ * nothing.  new_context_lens[i] = L_i + accept_len[i].
+ * Slots past the new length are left unchanged; the caller's page allocator
+ * releases pages beyond ceil(new_len/page_size).  NOT idempotent: run once per
+ * verify step.
+ *
+ *   k_cache, v_cache  bf16 caches, modified in place
+ *   context_lens      int32 [batch] L_i before the step (not modified)
+ *   cu_q         int32 [batch+1] as for spec_verify_attn (total_q = cu_q[batch])
+ *   accepted_path, accept_len  as produced by spec_accept
+ *   new_context_lens  int32 [batch] out; must not alias context_lens.  A
+ *                     request whose path or pages break the contract is left
+ *                     untouched and gets new_context_lens[i] = -1.
+ */
+int kv_compact(void *k_cache, void *v_cache, int64_t layer_stride_elems, int num_layers,
+               const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+               const int32_t *cu_q, const int32_t *accepted_path, const int32_t *accept_len,
+               int32_t *new_context_lens, int batch, int total_q, int num_kv_heads, int head_dim,
+               int page_size, int num_pages, void *stream);
+
+/* ------------------------------------------------------------------------- */
+/* Diagnostics (host)                                                         */
+/* ------------------------------------------------------------------------- */
+
+/* Static description of a status code. */
+const char *sv_status_string(int status);
+
+/* Thread-local detail of the most recent failing call on this thread ("" if none). */
+const char *sv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

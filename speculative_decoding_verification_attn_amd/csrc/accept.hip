@@ -1,0 +1,204 @@
+// Greedy acceptance of drafted tokens on gfx950.
+//
+// What is computed (DSpark, glossary "Speculative Decoding": the longest
+// matching prefix of the draft is accepted; SwiftSpec, "Tree-Aware KV Cache
+// Management" and "Fused Latency-Optimized Kernels": for a draft tree the
+// accepted root path is kept and the result goes back as a short message):
+//   t[r]      = lowest index of the maximum of logits row r (full vocabulary)
+//   accepted  = chain: longest prefix with draft[j] == t[j-1];
+//               tree: deepest node whose every root-path edge matches
+//               (draft[a] == t[parent[a]]), lowest index among equals.
+//
+// Two launches:
+//   argmax_partial_kernel  grid (splits, rows): each workgroup streams one slice
+//                          of one logits row with 16-byte loads and reduces
+//                          (value, index) pairs with wave shuffles;
+//   accept_kernel          one workgroup per request: reduces the slice
+//                          partials of its rows, then one wave walks the
+//                          request (<= 64 tokens, one lane per token) with a
+//                          ballot of edge matches against ancestor masks.
+#include <limits.h>
+
+#include "sv_device.h"
+#include "sv_internal.h"
+
+namespace sv {
+
+namespace {
+
+struct Best {
+  float v;
+  int i;  // -1 = empty
+};
+
+// larger value wins; equal values: lower index wins (IEEE ==, so -0 == +0)
+__device__ inline Best better(Best a, Best b) {
+  if (b.i < 0) return a;
+  if (a.i < 0) return b;
+  if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
+  return a;
+}
+
+__device__ inline Best wave_best(Best x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    Best y;
+    y.v = __shfl_xor(x.v, d);
+    y.i = __shfl_xor(x.i, d);
+    x = better(x, y);
+  }
+  return x;
+}
+
+__global__ __launch_bounds__(kArgmaxThreads) void argmax_partial_kernel(AcceptArgs a) {
+  __shared__ float s_v[kArgmaxThreads / 64];
+  __shared__ int s_i[kArgmaxThreads / 64];
+  const int split = blockIdx.x;
+  const int row = blockIdx.y;
+  const int splits = a.lay.splits;
+  const int V = a.vocab;
+  if (split == 0 && row == 0 && threadIdx.x == 0)
+    reinterpret_cast<int32_t *>(a.ws + a.lay.hdr)[0] = 0;
+  if (row >= a.total_q) return;  // the grid has one row even when total_q == 0
+  // slice bounds, multiples of 4 so 16-byte loads stay aligned when V % 4 == 0
+  int per = (V + splits - 1) / splits;
+  per = (per + 3) & ~3;
+  const int lo = min(V, split * per);
+  const int hi = min(V, lo + per);
+  const float *x = a.logits + (size_t)row * V;
+  Best b{-INFINITY, -1};
+  if ((V & 3) == 0) {
+    // each thread walks its float4s in increasing index order; strict '>'
+    // keeps the lowest index among equal values within the thread
+    const int nv = (hi - lo) >> 2;
+    const float4 *x4 = reinterpret_cast<const float4 *>(x + lo);
+    constexpr int U = 4;
+    int k = threadIdx.x;
+    for (; k + (U - 1) * kArgmaxThreads < nv; k += U * kArgmaxThreads) {
+      float4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = x4[k + u * kArgmaxThreads];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int base = lo + 4 * (k + u * kArgmaxThreads);
+        if (b.i < 0 || v[u].x > b.v) { b.v = v[u].x; b.i = base; }
+        if (v[u].y > b.v) { b.v = v[u].y; b.i = base + 1; }
+        if (v[u].z > b.v) { b.v = v[u].z; b.i = base + 2; }
+        if (v[u].w > b.v) { b.v = v[u].w; b.i = base + 3; }
+      }
+    }
+    for (; k < nv; k += kArgmaxThreads) {
+      const float4 v = x4[k];
+      const int base = lo + 4 * k;
+      if (b.i < 0 || v.x > b.v) { b.v = v.x; b.i = base; }
+      if (v.y > b.v) { b.v = v.y; b.i = base + 1; }
+      if (v.z > b.v) { b.v = v.z; b.i = base + 2; }
+      if (v.w > b.v) { b.v = v.w; b.i = base + 3; }
+    }
+  } else {
+    for (int k = lo + threadIdx.x; k < hi; k += kArgmaxThreads) {
+      const float v = x[k];
+      if (b.i < 0 || v > b.v) { b.v = v; b.i = k; }
+    }
+  }
+  b = wave_best(b);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    s_v[wave] = b.v;
+    s_i[wave] = b.i;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    Best r{s_v[0], s_i[0]};
+#pragma unroll
+    for (int w = 1; w < kArgmaxThreads / 64; ++w) r = better(r, Best{s_v[w], s_i[w]});
+    float2 *part = reinterpret_cast<float2 *>(a.ws + a.lay.part);
+    part[(size_t)row * splits + split] = make_float2(r.v, __int_as_float(r.i));
+  }
+}
+
+__global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
+  __shared__ float s_pv[kMaxTokens * kArgmaxMaxSplits];
+  __shared__ int s_pi[kMaxTokens * kArgmaxMaxSplits];
+  __shared__ int s_t[kMaxTokens];
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int splits = a.lay.splits;
+  unsigned *status = reinterpret_cast<unsigned *>(a.ws + a.lay.hdr);
+  const int o = a.cu_q[i];
+  const int c1 = a.cu_q[i + 1];
+  const int q = c1 - o;
+  if (o < 0 || c1 < o || c1 > a.total_q || q > kMaxTokens) {
+    if (tid == 0) {
+      atomicOr(status, q > kMaxTokens && o >= 0 && c1 <= a.total_q ? SV_DEV_TOO_MANY_TOKENS
+                                                                   : SV_DEV_BAD_CU_Q);
+      a.accept_len[i] = 0;
+    }
+    return;
+  }
+  if (i == 0 && tid == 0 && (a.cu_q[0] != 0 || a.cu_q[a.batch] != a.total_q))
+    atomicOr(status, SV_DEV_BAD_CU_Q);
+  if (q == 0) {
+    if (tid == 0) a.accept_len[i] = 0;
+    return;
+  }
+  // 1. gather the slice partials of this request's rows
+  const float2 *part = reinterpret_cast<const float2 *>(a.ws + a.lay.part);
+  const int np = q * splits;
+  for (int k = tid; k < np; k += 256) {
+    const float2 p = part[(size_t)o * splits + k];
+    s_pv[k] = p.x;
+    s_pi[k] = __float_as_int(p.y);
+  }
+  __syncthreads();
+  // 2. one thread per row finishes the argmax (splits in index order)
+  if (tid < q) {
+    Best b{s_pv[tid * splits], s_pi[tid * splits]};
+    for (int s = 1; s < splits; ++s) b = better(b, Best{s_pv[tid * splits + s], s_pi[tid * splits + s]});
+    s_t[tid] = b.i;
+    a.target_argmax[o + tid] = b.i;
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  // 3. the walk: lane j is verify token j
+  const int j = tid;
+  bool parents_ok;
+  const uint64_t anc = ancestor_mask(a.tree_parent, o, q, j, &parents_ok);
+  if (!parents_ok && j == 0) atomicOr(status, SV_DEV_BAD_PARENT);
+  int par = -1;
+  if (j < q && j > 0) par = a.tree_parent ? a.tree_parent[o + j] : j - 1;
+  if (par < 0 || par >= j) par = -1;
+  const bool match = j < q && par >= 0 && a.draft[o + j] == s_t[par];
+  const uint64_t matched = __ballot(match) | 1ull;
+  const bool accepted = j < q && (anc & ~matched) == 0ull;
+  const int depth = __popcll(anc) - 1;
+  // key: deeper first, then lower index
+  int key = accepted ? ((depth << 6) | (63 - j)) : -1;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) key = max(key, __shfl_xor(key, d));
+  const int best = 63 - (key & 63);
+  const int n = key >> 6;
+  const uint64_t path_mask = __shfl(anc, best);
+  if (j < q) {
+    if ((path_mask >> j) & 1ull) {
+      const int rank = __popcll(path_mask & ((1ull << j) - 1ull));
+      a.accepted_path[o + rank] = j;
+      a.out_tokens[o + rank] = s_t[j];
+    }
+    if (j > n) {
+      a.accepted_path[o + j] = -1;
+      a.out_tokens[o + j] = -1;
+    }
+  }
+  if (j == 0) a.accept_len[i] = n + 1;
+}
+
+}  // namespace
+
+void launch_accept(const AcceptArgs &a, hipStream_t stream) {
+  dim3 grid(a.lay.splits, a.total_q > 0 ? a.total_q : 1);
+  argmax_partial_kernel<<<grid, kArgmaxThreads, 0, stream>>>(a);
+  accept_kernel<<<a.batch, 256, 0, stream>>>(a);
+}
+
+}  // namespace sv

@@ -1,0 +1,241 @@
+// C ABI of libspecverify: host-side argument validation, workspace layout and
+// kernel launches.  Argument errors are detected here, before any HIP call.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sv_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return SV_OK;
+}
+
+int check_launch(const char *what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
+  const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
+  return x < y + bn && y < x + an;
+}
+
+int read_status(const void *workspace, size_t offset, uint32_t *flags, void *stream) {
+  if (!workspace || !flags) return fail(SV_ERR_NULL, "workspace and flags must be non-NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, static_cast<const char *>(workspace) + offset, sizeof v,
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(SV_ERR_HIP, "device status read: %s", hipGetErrorString(e));
+  *flags = v;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sv_status_string(int status) {
+  switch (status) {
+    case SV_OK: return "ok";
+    case SV_ERR_NULL: return "a required pointer is NULL";
+    case SV_ERR_SHAPE: return "a size argument is out of range or inconsistent";
+    case SV_ERR_UNSUPPORTED: return "unsupported head_dim, page_size or head grouping";
+    case SV_ERR_WORKSPACE: return "workspace too small";
+    case SV_ERR_ALIAS: return "an output overlaps an input";
+    case SV_ERR_HIP: return "a HIP call failed";
+    default: return "unknown status";
+  }
+}
+
+const char *sv_last_error(void) { return g_last_error; }
+
+size_t spec_verify_attn_workspace_size(int batch, int total_q, int num_q_heads, int num_kv_heads,
+                                       int head_dim) {
+  if (batch < 0 || total_q < 0 || num_kv_heads <= 0 || num_q_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || head_dim <= 0)
+    return 0;
+  return sv::attn_layout(batch, total_q, num_q_heads, num_kv_heads, head_dim).total;
+}
+
+int spec_verify_attn(const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *block_tables, int max_blocks_per_seq,
+                     const int32_t *context_lens, const int32_t *cu_q, const int32_t *tree_parent,
+                     void *out, int batch, int total_q, int num_q_heads, int num_kv_heads,
+                     int head_dim, int page_size, int num_pages, float softmax_scale,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  if (batch < 0 || total_q < 0)
+    return fail(SV_ERR_SHAPE, "batch (%d) and total_q (%d) must be >= 0", batch, total_q);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(SV_ERR_SHAPE, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, num_kv_heads);
+  if (num_q_heads / num_kv_heads > 64)
+    return fail(SV_ERR_UNSUPPORTED, "more than 64 query heads per KV head");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+  if (page_size != sv::kPage)
+    return fail(SV_ERR_UNSUPPORTED, "page_size %d (supported: 16)", page_size);
+  if (total_q > (long long)batch * sv::kMaxTokens)
+    return fail(SV_ERR_SHAPE, "total_q %d exceeds batch*64", total_q);
+  if (batch == 0 || total_q == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !cu_q || !out || !workspace)
+    return fail(SV_ERR_NULL, "spec_verify_attn: a required pointer is NULL");
+  if (max_blocks_per_seq <= 0 || num_pages <= 0)
+    return fail(SV_ERR_SHAPE, "max_blocks_per_seq (%d) and num_pages (%d) must be > 0",
+                max_blocks_per_seq, num_pages);
+  if (!(softmax_scale == 0.0f || isfinite(softmax_scale)))
+    return fail(SV_ERR_SHAPE, "softmax_scale must be finite");
+  const sv::AttnLayout lay = sv::attn_layout(batch, total_q, num_q_heads, num_kv_heads, head_dim);
+  if (workspace_bytes < lay.total)
+    return fail(SV_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, lay.total);
+  const size_t qo_bytes = (size_t)total_q * num_q_heads * head_dim * 2;
+  const size_t kv_bytes = (size_t)num_pages * num_kv_heads * page_size * head_dim * 2;
+  if (overlaps(out, qo_bytes, q, qo_bytes) || overlaps(out, qo_bytes, k_cache, kv_bytes) ||
+      overlaps(out, qo_bytes, v_cache, kv_bytes) || overlaps(out, qo_bytes, workspace, lay.total))
+    return fail(SV_ERR_ALIAS, "out overlaps q, the caches or the workspace");
+
+  sv::AttnArgs a;
+  a.q = static_cast<const uint16_t *>(q);
+  a.k_cache = static_cast<const uint16_t *>(k_cache);
+  a.v_cache = static_cast<const uint16_t *>(v_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.cu_q = cu_q;
+  a.tree_parent = tree_parent;
+  a.out = static_cast<uint16_t *>(out);
+  a.ws = static_cast<char *>(workspace);
+  a.lay = lay;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_pages = num_pages;
+  const float scale = softmax_scale == 0.0f ? 1.0f / sqrtf((float)head_dim) : softmax_scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  sv::launch_verify_attn(a, head_dim, static_cast<hipStream_t>(stream));
+  return check_launch("spec_verify_attn");
+}
+
+int spec_verify_attn_device_status(const void *workspace, uint32_t *flags, void *stream) {
+  return read_status(workspace, 0, flags, stream);
+}
+
+size_t spec_accept_workspace_size(int batch, int total_q, int vocab) {
+  if (batch < 0 || total_q < 0 || vocab <= 0) return 0;
+  return sv::accept_layout(batch, total_q, vocab).total;
+}
+
+int spec_accept(const float *logits, int vocab, const int32_t *draft_tokens, const int32_t *cu_q,
+                const int32_t *tree_parent, int batch, int total_q, int32_t *target_argmax,
+                int32_t *accept_len, int32_t *accepted_path, int32_t *out_tokens, void *workspace,
+                size_t workspace_bytes, void *stream) {
+  if (batch < 0 || total_q < 0)
+    return fail(SV_ERR_SHAPE, "batch (%d) and total_q (%d) must be >= 0", batch, total_q);
+  if (vocab <= 0) return fail(SV_ERR_SHAPE, "vocab %d must be > 0", vocab);
+  if (total_q > (long long)batch * sv::kMaxTokens)
+    return fail(SV_ERR_SHAPE, "total_q %d exceeds batch*64", total_q);
+  if (batch == 0) return ok();
+  if (!cu_q || !accept_len || !workspace)
+    return fail(SV_ERR_NULL, "spec_accept: a required pointer is NULL");
+  if (total_q > 0 && (!logits || !draft_tokens || !target_argmax || !accepted_path || !out_tokens))
+    return fail(SV_ERR_NULL, "spec_accept: a required pointer is NULL");
+  const sv::AcceptLayout lay = sv::accept_layout(batch, total_q, vocab);
+  if (workspace_bytes < lay.total)
+    return fail(SV_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, lay.total);
+  const size_t tb = (size_t)total_q * 4;
+  if (overlaps(target_argmax, tb, accepted_path, tb) || overlaps(target_argmax, tb, out_tokens, tb) ||
+      overlaps(accepted_path, tb, out_tokens, tb) ||
+      overlaps(accept_len, (size_t)batch * 4, target_argmax, tb) ||
+      overlaps(accept_len, (size_t)batch * 4, accepted_path, tb) ||
+      overlaps(accept_len, (size_t)batch * 4, out_tokens, tb))
+    return fail(SV_ERR_ALIAS, "spec_accept outputs overlap");
+  sv::AcceptArgs a;
+  a.logits = logits;
+  a.draft = draft_tokens;
+  a.cu_q = cu_q;
+  a.tree_parent = tree_parent;
+  a.target_argmax = target_argmax;
+  a.accept_len = accept_len;
+  a.accepted_path = accepted_path;
+  a.out_tokens = out_tokens;
+  a.ws = static_cast<char *>(workspace);
+  a.lay = lay;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.vocab = vocab;
+  sv::launch_accept(a, static_cast<hipStream_t>(stream));
+  return check_launch("spec_accept");
+}
+
+int spec_accept_device_status(const void *workspace, uint32_t *flags, void *stream) {
+  return read_status(workspace, 0, flags, stream);
+}
+
+int kv_compact(void *k_cache, void *v_cache, int64_t layer_stride_elems, int num_layers,
+               const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+               const int32_t *cu_q, const int32_t *accepted_path, const int32_t *accept_len,
+               int32_t *new_context_lens, int batch, int total_q, int num_kv_heads, int head_dim,
+               int page_size, int num_pages, void *stream) {
+  if (batch < 0 || total_q < 0 || num_layers < 0)
+    return fail(SV_ERR_SHAPE, "batch, total_q and num_layers must be >= 0");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+  if (page_size != sv::kPage)
+    return fail(SV_ERR_UNSUPPORTED, "page_size %d (supported: 16)", page_size);
+  if (num_kv_heads <= 0) return fail(SV_ERR_SHAPE, "num_kv_heads must be > 0");
+  if (batch == 0) return ok();
+  if (!block_tables || !context_lens || !cu_q || !accept_len || !new_context_lens)
+    return fail(SV_ERR_NULL, "kv_compact: a required pointer is NULL");
+  if (num_layers > 0 && (!k_cache || !v_cache))
+    return fail(SV_ERR_NULL, "kv_compact: cache pointers are NULL");
+  if (total_q > 0 && !accepted_path) return fail(SV_ERR_NULL, "kv_compact: accepted_path is NULL");
+  if (max_blocks_per_seq <= 0 || num_pages <= 0)
+    return fail(SV_ERR_SHAPE, "max_blocks_per_seq and num_pages must be > 0");
+  const long long pool = (long long)num_pages * num_kv_heads * page_size * head_dim;
+  if (num_layers > 1 && layer_stride_elems < pool)
+    return fail(SV_ERR_SHAPE, "layer_stride_elems %lld smaller than one pool (%lld)",
+                (long long)layer_stride_elems, pool);
+  if (new_context_lens == context_lens ||
+      overlaps(new_context_lens, (size_t)batch * 4, context_lens, (size_t)batch * 4))
+    return fail(SV_ERR_ALIAS, "new_context_lens must not alias context_lens");
+  sv::CompactArgs a;
+  a.k_cache = static_cast<uint16_t *>(k_cache);
+  a.v_cache = static_cast<uint16_t *>(v_cache);
+  a.layer_stride = layer_stride_elems;
+  a.num_layers = num_layers;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.cu_q = cu_q;
+  a.accepted_path = accepted_path;
+  a.accept_len = accept_len;
+  a.new_context_lens = new_context_lens;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_pages = num_pages;
+  sv::launch_kv_compact(a, static_cast<hipStream_t>(stream));
+  return check_launch("kv_compact");
+}
+
+}  // extern "C"

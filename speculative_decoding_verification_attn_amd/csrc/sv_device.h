@@ -1,0 +1,99 @@
+// Device helpers shared by the kernels (wave64 shuffles, bf16 packing,
+// ancestor masks of draft trees).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// bf16 bits of x (round to nearest even; gfx950 converts in hardware)
+__device__ inline uint32_t bf16_bits(float x) {
+  __bf16 b = (__bf16)x;
+  return (uint32_t)__builtin_bit_cast(uint16_t, b);
+}
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+}
+
+// Ancestor-or-self bitmask of token `lane` of a request with q tokens whose
+// rows start at o: bit k is set iff token k lies on the token's root path
+// (SwiftSpec, "Tree-Aware KV Cache Management": a node's KV prefix is its root
+// path).  Chains (tree_parent == nullptr) have parent j-1.  Must be called by
+// the whole wave; lanes >= q return 0.  *ok is false if the parent array
+// breaks root = -1, 0 <= parent[j] < j.  Pointer jumping: after round r a
+// lane knows its ancestors closer than 2^r, so 6 rounds cover depth <= 63.
+__device__ inline uint64_t ancestor_mask(const int32_t *tree_parent, int o, int q, int lane,
+                                         bool *ok) {
+  if (tree_parent == nullptr) {
+    *ok = true;
+    if (lane >= q) return 0ull;
+    return lane == 63 ? ~0ull : ((2ull << lane) - 1ull);
+  }
+  int par = lane < q ? tree_parent[o + lane] : -1;
+  bool good = lane >= q || (lane == 0 ? par == -1 : (par >= 0 && par < lane));
+  if (!good) par = -1;
+  *ok = __all(good);
+  uint64_t anc = lane < q ? (1ull << lane) : 0ull;
+  int jump = par;
+#pragma unroll
+  for (int r = 0; r < 6; ++r) {
+    const int src = jump < 0 ? lane : jump;
+    const uint64_t a2 = __shfl(anc, src);
+    const int j2 = __shfl(jump, src);
+    if (jump >= 0) {
+      anc |= a2;
+      jump = j2;
+    }
+  }
+  return anc;
+}
+
+// Exclusive prefix sum over a 1024-thread block; *total receives the sum.
+// `scratch` must hold at least 16 ints of shared memory.
+__device__ inline int block_excl_scan_1024(int v, int *scratch, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < 16 ? scratch[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      int y = __shfl_up(w, d);
+      if (lane >= d) w += y;
+    }
+    if (lane < 16) scratch[lane] = w;  // inclusive wave totals
+  }
+  __syncthreads();
+  const int before = wave > 0 ? scratch[wave - 1] : 0;
+  *total = scratch[15];
+  __syncthreads();
+  return before + x - v;
+}
+
+__device__ inline long long block_sum_1024(long long v, long long *scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  if (lane == 0) scratch[wave] = v;
+  __syncthreads();
+  long long s = 0;
+  for (int w = 0; w < 16; ++w) s += scratch[w];
+  __syncthreads();
+  return s;
+}
+
+}  // namespace sv

@@ -1,0 +1,146 @@
+// Internal declarations shared by the HIP translation units of libspecverify.
+// gfx950 (CDNA4) only: wave64, MFMA bf16 32x32x16, hardware bf16 conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "spec_verify.h"
+
+namespace sv {
+
+constexpr int kPage = 16;          // tokens per KV page
+constexpr int kMaxTokens = 64;     // verify tokens per request (one u64 ancestor word)
+constexpr int kBlockKeys = 32;     // keys per MFMA block (two pages)
+constexpr int kTileRows = 32;      // query rows per MFMA tile / per attention segment
+constexpr int kAttnWaves = 4;      // waves per attention workgroup (they split the keys)
+constexpr int kTargetItems = 2048; // aim for about this many attention work items
+constexpr int kMinChunkKeys = 128; // smallest key chunk per work item (4 waves x 32 keys)
+constexpr int kPlanThreads = 1024;
+
+// ---------------------------------------------------------------------------
+// Verify-attention workspace layout (byte offsets, all 256-byte aligned).
+// ---------------------------------------------------------------------------
+struct AttnLayout {
+  size_t hdr;        // int32[8]: 0 status bits, 1 item count, 2 chunk keys, 3 segment count
+  size_t req_meta;   // int4[B]: {segment base, item base, rowgroups, chunks}
+  size_t segs;       // int4[seg_bound]: {request, rowgroup, chunks, first partial slot}
+  size_t items;      // int2[item_bound]: {segment, head<<16 | chunk}
+  size_t part_lse;   // float[item_bound][32] log2-sum-exp of each partial row
+  size_t part_o;     // float[item_bound][32][D] normalised partial outputs
+  size_t total;
+  int seg_bound;
+  int item_bound;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+__host__ __device__ inline AttnLayout attn_layout(int batch, int total_q, int num_q_heads,
+                                                  int num_kv_heads, int head_dim) {
+  AttnLayout l;
+  const int G = num_q_heads / num_kv_heads;
+  // segments: sum_i ceil(G*q_i/32) <= B + ceil(G*T/32)
+  l.seg_bound = batch + (G * total_q + kTileRows - 1) / kTileRows;
+  // items: sum over (segment, head) of ceil(keys/C) <= W/C + Hkv*S with C >= W/kTargetItems
+  l.item_bound = kTargetItems + num_kv_heads * l.seg_bound;
+  size_t off = 0;
+  l.hdr = off;       off = align256(off + 8 * sizeof(int32_t));
+  l.req_meta = off;  off = align256(off + size_t(batch) * 16);
+  l.segs = off;      off = align256(off + size_t(l.seg_bound) * 16);
+  l.items = off;     off = align256(off + size_t(l.item_bound) * 8);
+  l.part_lse = off;  off = align256(off + size_t(l.item_bound) * kTileRows * sizeof(float));
+  l.part_o = off;    off = align256(off + size_t(l.item_bound) * kTileRows * head_dim * sizeof(float));
+  l.total = off;
+  return l;
+}
+
+struct AttnArgs {
+  const uint16_t *q;
+  const uint16_t *k_cache;
+  const uint16_t *v_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  const int32_t *cu_q;
+  const int32_t *tree_parent;
+  uint16_t *out;
+  char *ws;
+  AttnLayout lay;
+  int batch, total_q, num_q_heads, num_kv_heads, group, max_blocks, num_pages;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+void launch_verify_attn(const AttnArgs &a, int head_dim, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Acceptance
+// ---------------------------------------------------------------------------
+constexpr int kArgmaxThreads = 256;
+constexpr int kArgmaxTargetGroups = 2048;
+constexpr int kArgmaxMinSlice = 4096;
+constexpr int kArgmaxMaxSplits = 64;
+
+struct AcceptLayout {
+  size_t hdr;     // int32[8]: 0 status bits
+  size_t part;    // {float value, int index}[total_q][splits]
+  size_t total;
+  int splits;
+};
+
+__host__ __device__ inline int argmax_splits(int total_q, int vocab) {
+  int s = (kArgmaxTargetGroups + (total_q > 0 ? total_q : 1) - 1) / (total_q > 0 ? total_q : 1);
+  int by_size = (vocab + kArgmaxMinSlice - 1) / kArgmaxMinSlice;
+  if (s > by_size) s = by_size;
+  if (s > kArgmaxMaxSplits) s = kArgmaxMaxSplits;
+  if (s < 1) s = 1;
+  return s;
+}
+
+__host__ __device__ inline AcceptLayout accept_layout(int batch, int total_q, int vocab) {
+  (void)batch;
+  AcceptLayout l;
+  l.splits = argmax_splits(total_q, vocab);
+  size_t off = 0;
+  l.hdr = off;   off = align256(off + 8 * sizeof(int32_t));
+  l.part = off;  off = align256(off + size_t(total_q) * l.splits * 8);
+  l.total = off;
+  return l;
+}
+
+struct AcceptArgs {
+  const float *logits;
+  const int32_t *draft;
+  const int32_t *cu_q;
+  const int32_t *tree_parent;
+  int32_t *target_argmax;
+  int32_t *accept_len;
+  int32_t *accepted_path;
+  int32_t *out_tokens;
+  char *ws;
+  AcceptLayout lay;
+  int batch, total_q, vocab;
+};
+
+void launch_accept(const AcceptArgs &a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// KV compaction
+// ---------------------------------------------------------------------------
+struct CompactArgs {
+  uint16_t *k_cache;
+  uint16_t *v_cache;
+  int64_t layer_stride;
+  int num_layers;
+  const int32_t *block_tables;
+  int max_blocks;
+  const int32_t *context_lens;
+  const int32_t *cu_q;
+  const int32_t *accepted_path;
+  const int32_t *accept_len;
+  int32_t *new_context_lens;
+  int batch, total_q, num_kv_heads, head_dim, num_pages;
+};
+
+void launch_kv_compact(const CompactArgs &a, hipStream_t stream);
+
+}  // namespace sv

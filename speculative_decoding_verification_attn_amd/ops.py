@@ -1,0 +1,217 @@
+"""Thin Python binding of libspecverify.so (ctypes).
+
+Argument marshalling only: every step of the verification path runs in the
+HIP kernels behind the C ABI declared in include/spec_verify.h.  torch is used
+for device memory and streams.  There is no fallback: if the library is
+missing or no GPU is present, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SV_OK = 0
+SV_ERR_NULL = 1
+SV_ERR_SHAPE = 2
+SV_ERR_UNSUPPORTED = 3
+SV_ERR_WORKSPACE = 4
+SV_ERR_ALIAS = 5
+SV_ERR_HIP = 6
+
+DEV_BAD_CU_Q = 0x1
+DEV_BAD_CONTEXT = 0x2
+DEV_TOO_MANY_TOKENS = 0x4
+DEV_BAD_PARENT = 0x8
+DEV_BAD_PAGE = 0x10
+DEV_TOO_MANY_PAGES = 0x20
+
+EXPORTED = ["spec_verify_attn_workspace_size", "spec_verify_attn", "spec_verify_attn_device_status",
+            "spec_accept_workspace_size", "spec_accept", "spec_accept_device_status",
+            "kv_compact", "sv_status_string", "sv_last_error"]
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"status {status}: {detail}")
+        self.status = status
+
+
+def load_library():
+    """Load libspecverify.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "or `python -m speculative_decoding_verification_attn_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, SZ, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_int64
+    lib.spec_verify_attn_workspace_size.argtypes = [I, I, I, I, I]
+    lib.spec_verify_attn_workspace_size.restype = SZ
+    lib.spec_verify_attn.argtypes = [P, P, P, P, I, P, P, P, P, I, I, I, I, I, I, I, F, P, SZ, P]
+    lib.spec_verify_attn.restype = I
+    lib.spec_verify_attn_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
+    lib.spec_verify_attn_device_status.restype = I
+    lib.spec_accept_workspace_size.argtypes = [I, I, I]
+    lib.spec_accept_workspace_size.restype = SZ
+    lib.spec_accept.argtypes = [P, I, P, P, P, I, I, P, P, P, P, P, SZ, P]
+    lib.spec_accept.restype = I
+    lib.spec_accept_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
+    lib.spec_accept_device_status.restype = I
+    lib.kv_compact.argtypes = [P, P, I64, I, P, I, P, P, P, P, P, I, I, I, I, I, I, P]
+    lib.kv_compact.restype = I
+    lib.sv_status_string.argtypes = [I]
+    lib.sv_status_string.restype = ctypes.c_char_p
+    lib.sv_last_error.argtypes = []
+    lib.sv_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != SV_OK:
+        lib = load_library()
+        raise SpecVerifyError(rc, lib.sv_last_error().decode() or lib.sv_status_string(rc).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+# ----------------------------------------------------------------------------
+def spec_verify_attn_workspace_size(batch, total_q, num_q_heads, num_kv_heads, head_dim) -> int:
+    return int(load_library().spec_verify_attn_workspace_size(batch, total_q, num_q_heads,
+                                                              num_kv_heads, head_dim))
+
+
+def spec_verify_attn(q, k_cache, v_cache, block_tables, context_lens, cu_q, tree_parent=None,
+                     out=None, softmax_scale=0.0, workspace=None, num_pages=None, stream=None):
+    """q [T,Hq,D] bf16; caches [pages,Hkv,16,D] bf16; returns out [T,Hq,D] bf16."""
+    lib = load_library()
+    _dev(q, torch.bfloat16, "q")
+    _dev(k_cache, torch.bfloat16, "k_cache")
+    _dev(v_cache, torch.bfloat16, "v_cache")
+    _dev(block_tables, torch.int32, "block_tables")
+    _dev(context_lens, torch.int32, "context_lens")
+    _dev(cu_q, torch.int32, "cu_q")
+    _dev(tree_parent, torch.int32, "tree_parent")
+    T, Hq, D = q.shape
+    pages, Hkv, P, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    B = context_lens.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, torch.bfloat16, "out")
+    if workspace is None:
+        workspace = torch.empty(spec_verify_attn_workspace_size(B, T, Hq, Hkv, D),
+                                dtype=torch.uint8, device=q.device)
+    _check(lib.spec_verify_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                block_tables.shape[1], _ptr(context_lens), _ptr(cu_q),
+                                _ptr(tree_parent), _ptr(out), B, T, Hq, Hkv, D, P,
+                                pages if num_pages is None else num_pages, float(softmax_scale),
+                                _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def spec_verify_attn_device_status(workspace, stream=None) -> int:
+    flags = ctypes.c_uint32(0)
+    _check(load_library().spec_verify_attn_device_status(_ptr(workspace), ctypes.byref(flags),
+                                                         _stream(stream)))
+    return int(flags.value)
+
+
+def spec_accept_workspace_size(batch, total_q, vocab) -> int:
+    return int(load_library().spec_accept_workspace_size(batch, total_q, vocab))
+
+
+def spec_accept(logits, draft_tokens, cu_q, tree_parent=None, *, target_argmax=None,
+                accept_len=None, accepted_path=None, out_tokens=None, workspace=None, stream=None):
+    """logits [T,V] fp32 -> (target_argmax [T], accept_len [B], accepted_path [T], out_tokens [T])."""
+    lib = load_library()
+    _dev(logits, torch.float32, "logits")
+    _dev(draft_tokens, torch.int32, "draft_tokens")
+    _dev(cu_q, torch.int32, "cu_q")
+    _dev(tree_parent, torch.int32, "tree_parent")
+    T, V = logits.shape
+    B = cu_q.shape[0] - 1
+    dev = logits.device
+    if target_argmax is None:
+        target_argmax = torch.empty(T, dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if accepted_path is None:
+        accepted_path = torch.empty(T, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty(T, dtype=torch.int32, device=dev)
+    for t, nm in ((target_argmax, "target_argmax"), (accept_len, "accept_len"),
+                  (accepted_path, "accepted_path"), (out_tokens, "out_tokens")):
+        _dev(t, torch.int32, nm)
+    if workspace is None:
+        workspace = torch.empty(spec_accept_workspace_size(B, T, V), dtype=torch.uint8, device=dev)
+    _check(lib.spec_accept(_ptr(logits), V, _ptr(draft_tokens), _ptr(cu_q), _ptr(tree_parent), B, T,
+                           _ptr(target_argmax), _ptr(accept_len), _ptr(accepted_path),
+                           _ptr(out_tokens), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return target_argmax, accept_len, accepted_path, out_tokens
+
+
+def spec_accept_device_status(workspace, stream=None) -> int:
+    flags = ctypes.c_uint32(0)
+    _check(load_library().spec_accept_device_status(_ptr(workspace), ctypes.byref(flags),
+                                                    _stream(stream)))
+    return int(flags.value)
+
+
+def kv_compact(k_cache, v_cache, block_tables, context_lens, cu_q, accepted_path, accept_len, *,
+               num_layers=1, layer_stride_elems=None, num_kv_heads=None, head_dim=None,
+               num_pages=None, new_context_lens=None, stream=None):
+    """In-place compaction of every layer.  With num_layers > 1, k_cache/v_cache are
+    [layers, pages, Hkv, 16, D] (or flat pools `layer_stride_elems` apart).
+    Returns new_context_lens [B]."""
+    lib = load_library()
+    _dev(k_cache, torch.bfloat16, "k_cache")
+    _dev(v_cache, torch.bfloat16, "v_cache")
+    for t, nm in ((block_tables, "block_tables"), (context_lens, "context_lens"), (cu_q, "cu_q"),
+                  (accepted_path, "accepted_path"), (accept_len, "accept_len")):
+        _dev(t, torch.int32, nm)
+    shp = k_cache.shape
+    if num_kv_heads is None:
+        num_kv_heads, head_dim = shp[-3], shp[-1]
+        num_pages = shp[-4]
+    if layer_stride_elems is None:
+        layer_stride_elems = num_pages * num_kv_heads * 16 * head_dim
+    B = context_lens.shape[0]
+    T = accepted_path.shape[0]
+    if new_context_lens is None:
+        new_context_lens = torch.empty(B, dtype=torch.int32, device=k_cache.device)
+    _dev(new_context_lens, torch.int32, "new_context_lens")
+    _check(lib.kv_compact(_ptr(k_cache), _ptr(v_cache), int(layer_stride_elems), int(num_layers),
+                          _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), _ptr(cu_q),
+                          _ptr(accepted_path), _ptr(accept_len), _ptr(new_context_lens), B, T,
+                          num_kv_heads, head_dim, 16, num_pages, _stream(stream)))
+    return new_context_lens

@@ -1,0 +1,118 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and rejects bad arguments with the documented status codes before
+any HIP call (so these run without a GPU; no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from speculative_decoding_verification_attn_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ops.load_library()
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ("spec_verify_attn", "spec_accept", "kv_compact", "spec_verify_attn_workspace_size",
+              "spec_accept_workspace_size", "sv_status_string", "sv_last_error"):
+        assert n in names, names
+
+
+def test_library_exports_every_declared_function(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert sorted(ops.EXPORTED) == declared_functions()
+
+
+def test_status_strings(lib):
+    for code in range(0, 7):
+        assert lib.sv_status_string(code)
+    assert lib.sv_status_string(99) == b"unknown status"
+
+
+NULL = None
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation rejects the call first
+
+
+def attn(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, mb=4, ctx=FAKE, cu=FAKE, par=NULL, out=ctypes.c_void_p(0x90000000),
+                B=2, T=8, Hq=8, Hkv=2, D=64, P=16, pages=10, scale=0.0, ws=ctypes.c_void_p(0x20000000),
+                wsb=1 << 40, stream=NULL)
+    args.update(kw)
+    return lib.spec_verify_attn(args["q"], args["k"], args["v"], args["bt"], args["mb"], args["ctx"], args["cu"],
+                                args["par"], args["out"], args["B"], args["T"], args["Hq"], args["Hkv"], args["D"],
+                                args["P"], args["pages"], args["scale"], args["ws"], args["wsb"], args["stream"])
+
+
+def test_verify_attn_validation(lib):
+    assert attn(lib, D=96) == ops.SV_ERR_UNSUPPORTED
+    assert attn(lib, P=32) == ops.SV_ERR_UNSUPPORTED
+    assert attn(lib, Hq=6, Hkv=4) == ops.SV_ERR_SHAPE
+    assert attn(lib, Hq=130, Hkv=2) == ops.SV_ERR_UNSUPPORTED
+    assert attn(lib, B=-1) == ops.SV_ERR_SHAPE
+    assert attn(lib, T=129) == ops.SV_ERR_SHAPE          # > 64 tokens per request
+    assert attn(lib, q=NULL) == ops.SV_ERR_NULL
+    assert attn(lib, ws=NULL) == ops.SV_ERR_NULL
+    assert attn(lib, mb=0) == ops.SV_ERR_SHAPE
+    assert attn(lib, wsb=16) == ops.SV_ERR_WORKSPACE
+    assert attn(lib, scale=float("inf")) == ops.SV_ERR_SHAPE
+    assert attn(lib, out=FAKE) == ops.SV_ERR_ALIAS       # out overlaps q
+    attn(lib, D=96)
+    assert b"head_dim" in lib.sv_last_error()
+    # empty work: accepted without touching any pointer
+    assert attn(lib, B=0, T=0, q=NULL, out=NULL, ws=NULL) == ops.SV_OK
+    assert attn(lib, T=0, q=NULL, out=NULL, ws=NULL) == ops.SV_OK
+
+
+def test_verify_attn_workspace_size(lib):
+    s1 = lib.spec_verify_attn_workspace_size(1, 5, 8, 2, 64)
+    s2 = lib.spec_verify_attn_workspace_size(256, 1024, 64, 8, 128)
+    assert 0 < s1 < s2
+    assert lib.spec_verify_attn_workspace_size(1, 5, 7, 2, 64) == 0
+
+
+def test_accept_validation(lib):
+    def call(**kw):
+        a = dict(logits=FAKE, V=100, dr=FAKE, cu=FAKE, par=NULL, B=2, T=8, t=ctypes.c_void_p(0x100000),
+                 acc=ctypes.c_void_p(0x200000), path=ctypes.c_void_p(0x300000), toks=ctypes.c_void_p(0x400000),
+                 ws=FAKE, wsb=1 << 30, stream=NULL)
+        a.update(kw)
+        return lib.spec_accept(a["logits"], a["V"], a["dr"], a["cu"], a["par"], a["B"], a["T"], a["t"], a["acc"],
+                               a["path"], a["toks"], a["ws"], a["wsb"], a["stream"])
+    assert call(V=0) == ops.SV_ERR_SHAPE
+    assert call(T=200) == ops.SV_ERR_SHAPE
+    assert call(logits=NULL) == ops.SV_ERR_NULL
+    assert call(wsb=8) == ops.SV_ERR_WORKSPACE
+    assert call(path=ctypes.c_void_p(0x100000)) == ops.SV_ERR_ALIAS
+    assert call(B=0, T=0) == ops.SV_OK
+    assert lib.spec_accept_workspace_size(4, 20, 128256) > 0
+
+
+def test_compact_validation(lib):
+    def call(**kw):
+        a = dict(k=FAKE, v=FAKE, stride=10 * 2 * 16 * 64, L=1, bt=FAKE, mb=4, ctx=ctypes.c_void_p(0x100000),
+                 cu=FAKE, path=FAKE, acc=FAKE, new=ctypes.c_void_p(0x200000), B=2, T=8, Hkv=2, D=64, P=16,
+                 pages=10, stream=NULL)
+        a.update(kw)
+        return lib.kv_compact(a["k"], a["v"], a["stride"], a["L"], a["bt"], a["mb"], a["ctx"], a["cu"], a["path"],
+                              a["acc"], a["new"], a["B"], a["T"], a["Hkv"], a["D"], a["P"], a["pages"], a["stream"])
+    assert call(D=80) == ops.SV_ERR_UNSUPPORTED
+    assert call(P=8) == ops.SV_ERR_UNSUPPORTED
+    assert call(new=ctypes.c_void_p(0x100000)) == ops.SV_ERR_ALIAS
+    assert call(k=NULL) == ops.SV_ERR_NULL
+    assert call(L=2, stride=5) == ops.SV_ERR_SHAPE
+    assert call(B=0) == ops.SV_OK
