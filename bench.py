@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-decoding verification step on one MI355X.
+
+One step = the whole hot path over one batch: verify attention for every
+layer of the model (K/V of distinct layers rotate through `--kv-copies`
+resident caches), then full-vocabulary greedy acceptance, then KV compaction
+over the resident caches.  Inputs are seeded synthetic tensors already in HBM
+when the timed region starts.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+Default workload: Llama-3-70B attention geometry, batch 256, gamma 3
+(the spec shape), 80 layers per step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+
+WORKLOAD_TEXT = {
+    "tiny_chain": "tiny chain verify: B=1, gamma=4, 8/2 heads, D=64, L=256, V=1024",
+    "llama31_8b_chain": "Llama-3.1-8B geometry chain verify: B=1, gamma=5, 32/8 heads, D=128, L=4096, V=128256",
+    "llama3_70b_tree": "Llama-3-70B geometry tree verify: B=1, 64-node depth-6 tree, 64/8 heads, D=128, L=8192, V=128256",
+    "qwen3_8b_ragged": "Qwen3-8B geometry ragged batch: B=64, gamma_i~U[1,8], 32/8 heads, D=128, L log-uniform [512,32768], V=151936",
+    "llama3_70b_b256": "Llama-3-70B geometry large-batch chain verify: B=256, gamma=3, 64/8 heads, D=128, L~U[2048,8192], V=128256",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="llama3_70b_b256")
+    ap.add_argument("--layers", type=int, default=None, help="attention layers per step (default: the model's)")
+    ap.add_argument("--kv-copies", type=int, default=None, help="distinct resident layer caches")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--batch", type=int, default=None, help="override the request count (batch sweeps)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-requests", type=int, default=16)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the path shards by request or KV head across GPUs, not implemented here)"}))
+        sys.exit(2)
+
+    import torch
+    from speculative_decoding_verification_attn_amd import ops
+    from speculative_decoding_verification_attn_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    ops.load_library()
+    dev = "cuda:0"
+    name = args.config
+    layers = args.layers or W.MODEL_LAYERS[name]
+    big = name in ("qwen3_8b_ragged", "llama3_70b_b256")
+    t0 = time.time()
+    case = W.make_case(name, args.seed, kv_device=dev if big else None,
+                       logits_device=dev if big else None, batch=args.batch)
+    log(f"generated {name}: B={case.batch} T={case.total_q} pages={case.num_pages} "
+        f"({time.time() - t0:.1f}s)")
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    kv_bytes = case.kv_bytes_per_layer()
+    if args.kv_copies:
+        copies = args.kv_copies
+    else:
+        # distinct caches so layers do not hit in the 256 MB last-level cache
+        copies = min(layers, max(2, int(np.ceil(1.0e9 / max(kv_bytes, 1)))))
+    k0 = case.k_cache_dev if big else bf16(case.k_cache)
+    v0 = case.v_cache_dev if big else bf16(case.v_cache)
+    K = torch.empty((copies,) + tuple(k0.shape), dtype=torch.bfloat16, device=dev)
+    V = torch.empty_like(K)
+    for c in range(copies):
+        K[c].copy_(k0)
+        V[c].copy_(v0)
+    del k0, v0
+    case.k_cache_dev = case.v_cache_dev = None
+    q = bf16(case.q)
+    bt, ctx, cu = i32(case.block_tables), i32(case.context_lens), i32(case.cu_q)
+    par = None if case.tree_parent is None else i32(case.tree_parent)
+    logits = case.logits_dev if big else torch.from_numpy(case.logits).to(dev)
+    draft = i32(case.draft_tokens)
+    out = torch.empty_like(q)
+    B, T = case.batch, case.total_q
+    ws_attn = torch.empty(ops.spec_verify_attn_workspace_size(B, T, case.num_q_heads, case.num_kv_heads,
+                                                              case.head_dim), dtype=torch.uint8, device=dev)
+    ws_acc = torch.empty(ops.spec_accept_workspace_size(B, T, case.vocab), dtype=torch.uint8, device=dev)
+    t_arg = torch.empty(T, dtype=torch.int32, device=dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    path = torch.empty(T, dtype=torch.int32, device=dev)
+    toks = torch.empty(T, dtype=torch.int32, device=dev)
+    new_len = torch.empty(B, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    log(f"resident: {copies} KV copies x {kv_bytes / 1e9:.3f} GB, logits {T * case.vocab * 4 / 1e6:.1f} MB")
+
+    timings = {"attn": [], "accept": [], "compact": []}
+
+    def mark():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def step(record):
+        for layer in range(layers):
+            c = layer % copies
+            e0 = mark() if record else None
+            ops.spec_verify_attn(q, K[c], V[c], bt, ctx, cu, par, out=out, workspace=ws_attn, stream=stream)
+            if record:
+                timings["attn"].append((e0, mark()))
+        e0 = mark() if record else None
+        ops.spec_accept(logits, draft, cu, par, target_argmax=t_arg, accept_len=acc, accepted_path=path,
+                        out_tokens=toks, workspace=ws_acc, stream=stream)
+        e1 = mark() if record else None
+        ops.kv_compact(K, V, bt, ctx, cu, path, acc, num_layers=copies, new_context_lens=new_len, stream=stream)
+        if record:
+            timings["accept"].append((e0, e1))
+            timings["compact"].append((e1, mark()))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    # timed region: exactly `steps` steps, synchronized on both sides
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        step(True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+
+    def avg_ms(pairs):
+        return float(np.mean([a.elapsed_time(b) for a, b in pairs])) if pairs else float("nan")
+
+    attn_ms = avg_ms(timings["attn"])
+    accept_ms = avg_ms(timings["accept"])
+    compact_ms = avg_ms(timings["compact"])
+    acc_np = acc.cpu().numpy()
+
+    # algorithmic bytes (what the method must move)
+    bt_bytes = int(sum(((int(L) + int(qq) + 15) // 16) * 4 for L, qq in zip(case.context_lens, case.q_lens)))
+    attn_bytes = kv_bytes + case.qo_bytes() + bt_bytes
+    logits_bytes = T * case.vocab * 4
+    step_bytes = layers * attn_bytes + logits_bytes
+    attn_gbs = attn_bytes / (attn_ms * 1e-3) / 1e9
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    verified_tok_s = float(acc_np.sum()) / (ms_per_step * 1e-3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, K[0], V[0], logits, args.cpu_sample_requests, layers)
+
+    rec = {
+        "metric": "verify-step µs/layer & KV-stream HBM GB/s (% peak), Llama-3-70B shape",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; bf16 Q/K/V, fp32 logits)",
+        "config": {"workload": WORKLOAD_TEXT.get(name, name), "name": name, "batch": B, "total_q": T,
+                   "layers_per_step": layers, "kv_copies": copies,
+                   "kv_bytes_per_layer": kv_bytes, "logits_bytes": logits_bytes},
+        "us_per_layer": round(attn_ms * 1e3, 2),
+        "kv_stream_gbs": round(attn_gbs, 1),
+        "pct_hbm_peak": round(100 * attn_gbs / PEAK_HBM_GBS, 1),
+        "accept_us": round(accept_ms * 1e3, 2),
+        "accept_gbs": round(logits_bytes / (accept_ms * 1e-3) / 1e9, 1),
+        "compact_us": round(compact_ms * 1e3, 2),
+        "verified_tokens_per_s": round(verified_tok_s, 1),
+        "mean_accept_len": round(float(acc_np.mean()), 4),
+        "roofline": {"kernel": "spec_verify_attn (plan + verify_attn_kernel + combine, per call)",
+                     "bound": "hbm", "achieved": round(attn_gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(attn_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(case, k_dev, v_dev, logits_dev, n_req, layers):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    verify attention of the first n_req requests (one layer) plus argmax and
+    acceptance of their rows, on the host cores.  Reported in GB/s of the
+    same algorithmic bytes as the GPU figure."""
+    import torch
+
+    import oracle
+    from speculative_decoding_verification_attn_amd.workloads import VerifyCase  # noqa: F401
+
+    n_req = min(n_req, case.batch)
+    reqs = list(range(n_req))
+    P = case.page_size
+    pages, rows_bt = [], []
+    for i in reqs:
+        n = (int(case.context_lens[i]) + int(case.q_lens[i]) + P - 1) // P
+        rows_bt.append(list(range(len(pages), len(pages) + n)))
+        pages.extend(int(p) for p in case.block_tables[i, :n])
+    idx = torch.tensor(pages, dtype=torch.long, device=k_dev.device)
+    k = k_dev.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+    v = v_dev.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+    mb = max(len(r) for r in rows_bt)
+    bt = np.zeros((n_req, mb), np.int32)
+    for r, row in enumerate(rows_bt):
+        bt[r, :len(row)] = row
+    ql = case.q_lens[:n_req]
+    cu = np.zeros(n_req + 1, np.int32)
+    cu[1:] = np.cumsum(ql)
+    rows = np.arange(int(case.cu_q[0]), int(case.cu_q[n_req]))
+    tp = None if case.tree_parent is None else case.tree_parent[rows]
+    lg = logits_dev[int(case.cu_q[0]):int(case.cu_q[n_req])].cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.verify_attn(case.q[rows], k, v, bt, case.context_lens[:n_req], cu, tp,
+                       num_q_heads=case.num_q_heads, num_kv_heads=case.num_kv_heads,
+                       head_dim=case.head_dim, page_size=P, num_pages=len(pages))
+    t_attn = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    tg = oracle.argmax(lg)
+    oracle.accept(case.draft_tokens[rows], tg, cu, tp)
+    t_acc = time.perf_counter() - t0
+    keys = int(np.sum(case.context_lens[:n_req].astype(np.int64) + ql))
+    attn_bytes = keys * case.num_kv_heads * case.head_dim * 4 + len(rows) * case.num_q_heads * case.head_dim * 4
+    logit_bytes = lg.size * 4
+    # one step of the sample = `layers` attention passes + one acceptance pass
+    t_step = layers * t_attn + t_acc
+    gbs = (layers * attn_bytes + logit_bytes) / t_step / 1e9
+    log(f"cpu oracle sample: {n_req} requests, attention {t_attn:.2f}s/layer, accept {t_acc:.3f}s")
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n_req} of {case.batch} requests ({len(rows)} verify rows, {keys} keys/layer): "
+                      f"one layer of fp64 verify attention timed and scaled to {layers} layers, plus "
+                      f"argmax+acceptance of those rows; single-threaded C oracle",
+            "attn_s_per_layer": round(t_attn, 3), "accept_s": round(t_acc, 4)}
+
+
+if __name__ == "__main__":
+    main()

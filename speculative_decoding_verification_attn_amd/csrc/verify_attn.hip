@@ -182,7 +182,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   const int gq = R - (R / G) * G;
   bool parents_ok;
   const uint64_t anc_all = ancestor_mask(a.tree_parent, o, qn, lane, &parents_ok);
-  const uint64_t anc = row_ok ? __shfl(anc_all, tok) : 0ull;
+  // the shuffle must run on every lane: a source lane whose own row is past
+  // the end would be inactive and read back as zero
+  const uint64_t anc_tok = __shfl(anc_all, tok);
+  const uint64_t anc = row_ok ? anc_tok : 0ull;
   if (!parents_ok && threadIdx.x == 0 && c_idx == 0 && h == 0 && sg.rowgroup == 0)
     atomicOr(reinterpret_cast<unsigned *>(a.ws + a.lay.hdr), SV_DEV_BAD_PARENT);
 
