@@ -131,6 +131,12 @@ int spec_verify_attn(const void *q, const void *k_cache, const void *v_cache,
   a.num_pages = num_pages;
   const float scale = softmax_scale == 0.0f ? 1.0f / sqrtf((float)head_dim) : softmax_scale;
   a.scale_log2 = scale * 1.4426950408889634f;
+  // one persistent attention workgroup per compute unit of the current device
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return fail(SV_ERR_HIP, "device query: %s", hipGetErrorString(e));
+  a.grid = cus < 1 ? 1 : (cus > sv::kMaxGrid ? sv::kMaxGrid : cus);
   sv::launch_verify_attn(a, head_dim, static_cast<hipStream_t>(stream));
   return check_launch("spec_verify_attn");
 }

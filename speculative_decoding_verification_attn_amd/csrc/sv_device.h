@@ -57,28 +57,29 @@ __device__ inline uint64_t ancestor_mask(const int32_t *tree_parent, int o, int 
 }
 
 // Exclusive prefix sum over a 1024-thread block; *total receives the sum.
-// `scratch` must hold at least 16 ints of shared memory.
-__device__ inline int block_excl_scan_1024(int v, int *scratch, int *total) {
+// `scratch` must hold at least 16 values of shared memory.
+template <typename T>
+__device__ inline T block_excl_scan_1024(T v, T *scratch, T *total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
+  T x = v;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    int y = __shfl_up(x, d);
+    T y = __shfl_up(x, d);
     if (lane >= d) x += y;
   }
   if (lane == 63) scratch[wave] = x;
   __syncthreads();
   if (wave == 0) {
-    int w = lane < 16 ? scratch[lane] : 0;
+    T w = lane < 16 ? scratch[lane] : T(0);
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) {
-      int y = __shfl_up(w, d);
+      T y = __shfl_up(w, d);
       if (lane >= d) w += y;
     }
     if (lane < 16) scratch[lane] = w;  // inclusive wave totals
   }
   __syncthreads();
-  const int before = wave > 0 ? scratch[wave - 1] : 0;
+  const T before = wave > 0 ? scratch[wave - 1] : T(0);
   *total = scratch[15];
   __syncthreads();
   return before + x - v;

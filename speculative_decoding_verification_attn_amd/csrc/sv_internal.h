@@ -15,23 +15,30 @@ constexpr int kMaxTokens = 64;     // verify tokens per request (one u64 ancesto
 constexpr int kBlockKeys = 32;     // keys per MFMA block (two pages)
 constexpr int kTileRows = 32;      // query rows per MFMA tile / per attention segment
 constexpr int kAttnWaves = 4;      // waves per attention workgroup (they split the keys)
-constexpr int kTargetItems = 2048; // aim for about this many attention work items
-constexpr int kMinChunkKeys = 128; // smallest key chunk per work item (4 waves x 32 keys)
+constexpr int kMaxGrid = 512;      // persistent attention workgroups (one per CU, capped)
+constexpr int kMinBlocksPerWG = 4; // keep at least one 32-key block per wave
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanLdsRequests = 4096;  // per-request plan data kept in LDS up to this batch
 
 // ---------------------------------------------------------------------------
 // Verify-attention workspace layout (byte offsets, all 256-byte aligned).
+//
+// A "unit" is one (request, KV head, 32-row query tile) triple; its keys are
+// the request's ceil((L+q)/32) blocks of 32 keys.  All units' blocks form one
+// global block sequence, cut into equal contiguous ranges, one per
+// persistent workgroup.  A unit wholly inside one range is written straight
+// to the output; a unit cut by range boundaries leaves one partial per
+// workgroup that touched it (at most two per workgroup), merged afterwards.
 // ---------------------------------------------------------------------------
 struct AttnLayout {
-  size_t hdr;        // int32[8]: 0 status bits, 1 item count, 2 chunk keys, 3 segment count
-  size_t req_meta;   // int4[B]: {segment base, item base, rowgroups, chunks}
-  size_t segs;       // int4[seg_bound]: {request, rowgroup, chunks, first partial slot}
-  size_t items;      // int2[item_bound]: {segment, head<<16 | chunk}
-  size_t part_lse;   // float[item_bound][32] log2-sum-exp of each partial row
-  size_t part_o;     // float[item_bound][32][D] normalised partial outputs
+  size_t hdr;       // int32[8]: 0 status bits, 1 active workgroups P, 2 total blocks, 3 units
+  size_t req_meta;  // int4[B]: {unit base, block base, rowgroups, blocks per unit}
+  size_t units;     // int4[unit_bound]: {request, kv head, rowgroup, first global block}
+  size_t wg_first;  // int32[kMaxGrid]: first unit of each workgroup's range
+  size_t part_lse;  // float[2*kMaxGrid][32] log2-sum-exp of partial rows
+  size_t part_o;    // float[2*kMaxGrid][32][D] normalised partial outputs
   size_t total;
-  int seg_bound;
-  int item_bound;
+  int unit_bound;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -40,17 +47,16 @@ __host__ __device__ inline AttnLayout attn_layout(int batch, int total_q, int nu
                                                   int num_kv_heads, int head_dim) {
   AttnLayout l;
   const int G = num_q_heads / num_kv_heads;
-  // segments: sum_i ceil(G*q_i/32) <= B + ceil(G*T/32)
-  l.seg_bound = batch + (G * total_q + kTileRows - 1) / kTileRows;
-  // items: sum over (segment, head) of ceil(keys/C) <= W/C + Hkv*S with C >= W/kTargetItems
-  l.item_bound = kTargetItems + num_kv_heads * l.seg_bound;
+  // row tiles: sum_i ceil(G*q_i/32) <= B + ceil(G*T/32)
+  const long long tiles = (long long)batch + ((long long)G * total_q + kTileRows - 1) / kTileRows;
+  l.unit_bound = (int)(tiles * num_kv_heads);
   size_t off = 0;
   l.hdr = off;       off = align256(off + 8 * sizeof(int32_t));
   l.req_meta = off;  off = align256(off + size_t(batch) * 16);
-  l.segs = off;      off = align256(off + size_t(l.seg_bound) * 16);
-  l.items = off;     off = align256(off + size_t(l.item_bound) * 8);
-  l.part_lse = off;  off = align256(off + size_t(l.item_bound) * kTileRows * sizeof(float));
-  l.part_o = off;    off = align256(off + size_t(l.item_bound) * kTileRows * head_dim * sizeof(float));
+  l.units = off;     off = align256(off + size_t(l.unit_bound) * 16);
+  l.wg_first = off;  off = align256(off + size_t(kMaxGrid) * sizeof(int32_t));
+  l.part_lse = off;  off = align256(off + size_t(2 * kMaxGrid) * kTileRows * sizeof(float));
+  l.part_o = off;    off = align256(off + size_t(2 * kMaxGrid) * kTileRows * head_dim * sizeof(float));
   l.total = off;
   return l;
 }
@@ -67,6 +73,7 @@ struct AttnArgs {
   char *ws;
   AttnLayout lay;
   int batch, total_q, num_q_heads, num_kv_heads, group, max_blocks, num_pages;
+  int grid;          // persistent attention workgroups launched (<= kMaxGrid)
   float scale_log2;  // softmax scale * log2(e)
 };
 

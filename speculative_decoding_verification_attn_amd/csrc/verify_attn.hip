@@ -3,25 +3,34 @@
 //
 // What is computed (SwiftSpec, "Fused Latency-Optimized Kernels" and
 // "Tree-Aware KV Cache Management"; FASER, "Per-Request Length Adaptation";
-// SSD's PagedAttention): every verify row of request i attends to the i-th
+// SSD's PagedAttention): every verify row of request i attends to the
 // request's committed context [0, L_i) and to those verify tokens that lie on
 // its own root path, all read through the request's block table.
 //
+// Work decomposition.  A unit is one (request, KV head, 32-row query tile);
+// the rows of a tile are (token, query head) pairs of that KV head's group,
+// token-major, so every K/V block a unit reads serves all its rows (GQA
+// sharing).  Every unit's keys form ceil((L+q)/32) blocks of 32 keys; all
+// units' blocks, in (request, head, tile) order, make one global sequence that
+// is cut into equal contiguous ranges, one per persistent workgroup (one per
+// CU).  Equal ranges balance ragged batches exactly; only the first and last
+// unit of a range can be cut, so at most two partial results per workgroup
+// need merging.
+//
 // Three launches:
-//   attn_plan_kernel     one workgroup: validates per-request metadata, splits
-//                        the (request, query-row tile, KV head) work into key
-//                        chunks of equal size, writes the work-item table;
-//   verify_attn_kernel   one workgroup per work item; four waves stream
-//                        disjoint 32-key blocks of the chunk straight from HBM
-//                        into MFMA operand registers (no LDS staging), keep an
-//                        fp32 online softmax per query row, and merge through
-//                        LDS at the end;
-//   attn_combine_kernel  log-sum-exp merge of the chunks of split rows.
+//   attn_plan_kernel     one workgroup: validates per-request metadata and
+//                        writes the unit table and each workgroup's first unit;
+//   verify_attn_kernel   the persistent workgroups; four waves (one per SIMD)
+//                        stream disjoint 32-key blocks straight from HBM into
+//                        MFMA operand registers, three blocks in flight per
+//                        wave, with an fp32 online softmax per query row, then
+//                        merge through LDS;
+//   attn_merge_kernel    log-sum-exp merge of the partials of cut units.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, A 32xK, B Kx32, C 32x32):
 //   S^T[key][row] = K[key][:] . Q^T[:][row]     A = K rows (one key per lane,
 //                                               8 contiguous d per lane),
-//                                               B = Q^T (loaded once)
+//                                               B = Q^T (staged once in LDS)
 //   O^T[d][row]  += V^T[d][key] . P^T[key][row] A = V^T (each lane holds 4
 //                                               contiguous d of 8 keys, so a
 //                                               V row is one 256-byte read by
@@ -36,35 +45,45 @@ namespace sv {
 
 namespace {
 
-struct SegInfo {  // mirrors the int4 written by the plan kernel
-  int req, rowgroup, nchunk, slot;
-};
+// index of the workgroup whose range [start(w), start(w+1)) holds block x,
+// where start(w) = floor(w*NB/P)
+__device__ inline int wg_of_block(long long x, long long nb, int p) {
+  return (int)(((x + 1) * p - 1) / nb);
+}
 
 // --------------------------------------------------------------------------
 // plan
 // --------------------------------------------------------------------------
+// Per-request bases live in LDS (or, for very large batches, in the
+// workspace): unit base, block base, row tiles, blocks per unit.
 __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a) {
   __shared__ int s_scan[16];
   __shared__ long long s_red[16];
+  __shared__ int s_req[4][kPlanLdsRequests];
   int32_t *hdr = reinterpret_cast<int32_t *>(a.ws + a.lay.hdr);
-  int4 *req = reinterpret_cast<int4 *>(a.ws + a.lay.req_meta);
-  int4 *segs = reinterpret_cast<int4 *>(a.ws + a.lay.segs);
-  int2 *items = reinterpret_cast<int2 *>(a.ws + a.lay.items);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int4 *units = reinterpret_cast<int4 *>(a.ws + a.lay.units);
+  int32_t *wg_first = reinterpret_cast<int32_t *>(a.ws + a.lay.wg_first);
+  const int tid = threadIdx.x;
   const int B = a.batch, G = a.group, Hkv = a.num_kv_heads;
+  const bool in_lds = B <= kPlanLdsRequests;
+  int32_t *gmeta = reinterpret_cast<int32_t *>(a.ws + a.lay.req_meta);
+  int *ubase = in_lds ? s_req[0] : gmeta;
+  int *bbase = in_lds ? s_req[1] : gmeta + B;
+  int *rgs = in_lds ? s_req[2] : gmeta + 2 * B;
+  int *nblks = in_lds ? s_req[3] : gmeta + 3 * B;
   unsigned flags = 0;
   if (tid == 0) {
     hdr[0] = 0;
     if (a.cu_q[0] != 0 || a.cu_q[B] != a.total_q) flags |= SV_DEV_BAD_CU_Q;
   }
-  __syncthreads();
 
-  // pass 1: per request rowgroups and keys; segment bases; total work
-  long long work = 0;
-  int seg_carry = 0;
+  // pass 1: per request row tiles and blocks; unit and block bases
+  int unit_carry = 0;
+  long long blk_carry = 0;
   for (int base = 0; base < B; base += kPlanThreads) {
     const int i = base + tid;
-    int rg = 0, keys = 0;
+    int rg = 0, nblk = 0;
+    long long n_blocks = 0;
     if (i < B) {
       const int c0 = a.cu_q[i], c1 = a.cu_q[i + 1];
       const int L = a.context_lens[i];
@@ -73,363 +92,254 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a) {
       if (c0 < 0 || c1 < c0 || c1 > a.total_q) { flags |= SV_DEV_BAD_CU_Q; ok = false; }
       if (ok && q > kMaxTokens) { flags |= SV_DEV_TOO_MANY_TOKENS; ok = false; }
       if (L < 0) { flags |= SV_DEV_BAD_CONTEXT; ok = false; }
-      if (ok) {
-        const long long need = ((long long)L + q + kPage - 1) / kPage;
-        if (need > a.max_blocks) { flags |= SV_DEV_TOO_MANY_PAGES; ok = false; }
+      if (ok && ((long long)L + q + kPage - 1) / kPage > a.max_blocks) {
+        flags |= SV_DEV_TOO_MANY_PAGES;
+        ok = false;
       }
       if (ok && q > 0) {
         rg = (G * q + kTileRows - 1) / kTileRows;
-        keys = L + q;
-        work += (long long)rg * keys;
+        nblk = (L + q + kBlockKeys - 1) / kBlockKeys;
+        n_blocks = (long long)rg * Hkv * nblk;
       }
-      req[i] = make_int4(0, 0, rg, keys);  // keys parked in .w until pass 2
     }
-    int tile_total;
-    const int excl = block_excl_scan_1024(rg, s_scan, &tile_total);
-    if (i < B) req[i].x = seg_carry + excl;
-    seg_carry += tile_total;
-  }
-  const long long total_work = block_sum_1024(work, s_red) * Hkv;
-  long long C = (total_work + kTargetItems - 1) / kTargetItems;
-  C = ((C + kMinChunkKeys - 1) / kMinChunkKeys) * kMinChunkKeys;
-  if (C < kMinChunkKeys) C = kMinChunkKeys;
-  const int chunk = (int)C;
-
-  // pass 2: chunks per request and item bases
-  int item_carry = 0;
-  for (int base = 0; base < B; base += kPlanThreads) {
-    const int i = base + tid;
-    int n_items = 0;
-    int4 r = make_int4(0, 0, 0, 0);
+    int tile_units;
+    const int u_excl = block_excl_scan_1024<int>(rg * Hkv, s_scan, &tile_units);
+    long long tile_blocks;
+    const long long b_excl = block_excl_scan_1024<long long>(n_blocks, s_red, &tile_blocks);
     if (i < B) {
-      r = req[i];
-      const int nchunk = r.z > 0 ? (r.w + chunk - 1) / chunk : 0;
-      r.w = nchunk;
-      n_items = r.z * Hkv * nchunk;
+      ubase[i] = unit_carry + u_excl;
+      // bases beyond 2^31-1 make the plan fail below, so clamping is harmless
+      bbase[i] = (int)min(blk_carry + b_excl, 0x7fffffffLL);
+      rgs[i] = rg;
+      nblks[i] = nblk;
     }
-    int tile_total;
-    const int excl = block_excl_scan_1024(n_items, s_scan, &tile_total);
-    if (i < B) {
-      r.y = item_carry + excl;
-      req[i] = r;
-    }
-    item_carry += tile_total;
+    unit_carry += tile_units;
+    blk_carry += tile_blocks;
   }
+  const bool fits = unit_carry <= a.lay.unit_bound && blk_carry <= 0x7fffffffLL;
+  if (!fits) flags |= SV_DEV_BAD_CU_Q;
+  const long long nb = fits ? blk_carry : 0;
+  int P = (int)min((long long)a.grid, (nb + kMinBlocksPerWG - 1) / kMinBlocksPerWG);
+  if (P < 1) P = 1;
   __syncthreads();
 
-  // Requests whose cu_q ranges overlap (an inconsistent cu_q) could push the
-  // counts past the workspace bounds; then nothing is scheduled at all.
-  const bool fits = seg_carry <= a.lay.seg_bound && item_carry <= a.lay.item_bound;
-  if (!fits) flags |= SV_DEV_BAD_CU_Q;
-
-  // pass 3: one wave per request writes its segments and work items
-  for (int i = wave; fits && i < B; i += kPlanThreads / 64) {
-    const int4 r = req[i];
-    const int per_seg = Hkv * r.w;
-    for (int s = lane; s < r.z; s += 64)
-      segs[r.x + s] = make_int4(i, s, r.w, r.y + s * per_seg);
-    const int n = r.z * per_seg;
-    for (int t = lane; t < n; t += 64) {
-      const int s = t / per_seg, rem = t - s * per_seg;
-      const int h = rem / r.w, c = rem - h * r.w;
-      items[r.y + t] = make_int2(r.x + s, (h << 16) | c);
+  if (fits) {
+    // pass 2: each request's units ...
+    for (int i = tid; i < B; i += kPlanThreads) {
+      const int rg = rgs[i], nblk = nblks[i], u0 = ubase[i], b0 = bbase[i];
+      for (int k = 0; k < rg * Hkv; ++k) {
+        const int h = k / rg, r = k - h * rg;
+        units[u0 + k] = make_int4(i, h, r, b0 + k * nblk);
+      }
+    }
+    // ... and the first unit of each workgroup range: the request whose block
+    // span holds start(w) = floor(w*nb/P), found by binary search
+    for (int w = tid; w < P && nb > 0; w += kPlanThreads) {
+      const long long st = (long long)w * nb / P;
+      int lo = 0, hi = B - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (bbase[mid] <= st) lo = mid; else hi = mid - 1;
+      }
+      wg_first[w] = ubase[lo] + (int)((st - bbase[lo]) / nblks[lo]);
     }
   }
-  // status word: OR of all threads' bits
   if (flags) atomicOr(reinterpret_cast<unsigned *>(hdr), flags);
   if (tid == 0) {
-    hdr[1] = fits ? item_carry : 0;
-    hdr[2] = chunk;
-    hdr[3] = fits ? seg_carry : 0;
+    hdr[1] = nb > 0 ? P : 0;
+    hdr[2] = (int)nb;
+    hdr[3] = fits ? unit_carry : 0;
   }
 }
 
-// --------------------------------------------------------------------------
-// attention
-// --------------------------------------------------------------------------
+// Registers of one 32-key block in flight: K rows as MFMA A operands and the
+// lane's run of DPL contiguous d from 16 V rows (two 16-key groups x slots
+// 8t+4hh+e).
 template <int D>
-__global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void verify_attn_kernel(AttnArgs a) {
-  constexpr int KK = D / 16;   // k-steps of the S^T product (16 d each)
-  constexpr int DPL = D / 32;  // contiguous d per lane of a V row; O^T tiles
-  static_assert(D == 64 || D == 128, "head_dim");
-  __shared__ float sm_o[kAttnWaves][DPL][16][64];
-  __shared__ float sm_m[kAttnWaves][32];
-  __shared__ float sm_l[kAttnWaves][32];
+struct KVBlock {
+  bf16x8 k[D / 16];
+  uint32_t v[2][2][4][D / 64];
+};
 
-  const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.lay.hdr);
-  const int n_items = hdr[1];
-  const int item = blockIdx.x;
-  if (item >= n_items) return;
-  const int chunk = hdr[2];
-  const int2 it = reinterpret_cast<const int2 *>(a.ws + a.lay.items)[item];
-  const int4 sg4 = reinterpret_cast<const int4 *>(a.ws + a.lay.segs)[it.x];
-  const SegInfo sg{sg4.x, sg4.y, sg4.z, sg4.w};
-  const int h = it.y >> 16, c_idx = it.y & 0xffff;
+typedef const __attribute__((address_space(4))) int32_t *const_i32_ptr;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 31, hh = lane >> 5;
-  const int i = sg.req;
-  const int o = a.cu_q[i];
-  const int qn = a.cu_q[i + 1] - o;
-  const int L = a.context_lens[i];
-  const int nk = L + qn;
-  const int G = a.group;
+// Physical pages of the two logical pages of block b, read with scalar loads
+// (the block index is wave-uniform).  Pages past the request's last page, and
+// ids outside [0, num_pages), are replaced by `safe` (a valid page) so every
+// load below stays in bounds; *bad records the latter.
+__device__ inline int2 block_pages(const_i32_ptr bt, int b, int npages, int num_pages, int safe,
+                                   bool *bad) {
+  const int lp = 2 * b;
+  const int i0 = min(lp, npages - 1), i1 = min(lp + 1, npages - 1);
+  int p0 = bt[i0], p1 = bt[i1];
+  const bool bad0 = p0 < 0 || p0 >= num_pages, bad1 = p1 < 0 || p1 >= num_pages;
+  *bad = *bad || (lp < npages && bad0) || (lp + 1 < npages && bad1);
+  if (lp >= npages || bad0) p0 = safe;
+  if (lp + 1 >= npages || bad1) p1 = safe;
+  return make_int2(p0, p1);
+}
 
-  // this lane's query row (token-major: row R = token * G + head-in-group)
-  const int R = sg.rowgroup * kTileRows + n;
-  const bool row_ok = R < G * qn;
-  const int tok = row_ok ? R / G : 0;
-  const int gq = R - (R / G) * G;
-  bool parents_ok;
-  const uint64_t anc_all = ancestor_mask(a.tree_parent, o, qn, lane, &parents_ok);
-  // the shuffle must run on every lane: a source lane whose own row is past
-  // the end would be inactive and read back as zero
-  const uint64_t anc_tok = __shfl(anc_all, tok);
-  const uint64_t anc = row_ok ? anc_tok : 0ull;
-  if (!parents_ok && threadIdx.x == 0 && c_idx == 0 && h == 0 && sg.rowgroup == 0)
-    atomicOr(reinterpret_cast<unsigned *>(a.ws + a.lay.hdr), SV_DEV_BAD_PARENT);
-
-  // Q^T operand: row n, d = 16*kk + 8*hh .. +7
-  bf16x8 qop[KK];
-  {
-    const uint16_t *qrow =
-        a.q + ((size_t)(o + tok) * a.num_q_heads + (size_t)h * G + gq) * D + 8 * hh;
+template <int D>
+__device__ inline void load_block(KVBlock<D> &buf, const uint16_t *kh, const uint16_t *vh,
+                                  int2 pg, int n, int hh, size_t page_stride) {
+  constexpr int KK = D / 16, DPL = D / 32;
+  const uint16_t *krow = kh + (size_t)(n < 16 ? pg.x : pg.y) * page_stride + (size_t)(n & 15) * D + 8 * hh;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (row_ok)
-        qop[kk] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * kk);
-      else
-        qop[kk] = bf16x8{};
-    }
-  }
-
-  const int kbeg = c_idx * chunk;
-  const int kend = min(nk, kbeg + chunk);
-  const int bbeg = kbeg / kBlockKeys;
-  const int bend = (kend + kBlockKeys - 1) / kBlockKeys;
-  const int32_t *bt = a.block_tables + (size_t)i * a.max_blocks;
-  const int npages = (nk + kPage - 1) / kPage;
-  const size_t head_off = (size_t)h * kPage * D;
-  const size_t page_stride = (size_t)a.num_kv_heads * kPage * D;
-
-  float m = -INFINITY, l = 0.f;
-  floatx16 acc[DPL];
+  for (int kk = 0; kk < KK; ++kk) buf.k[kk] = *reinterpret_cast<const bf16x8 *>(krow + 16 * kk);
 #pragma unroll
-  for (int c = 0; c < DPL; ++c) acc[c] = floatx16{};
-  bool bad_page = false;
-
-  for (int b = bbeg + wave; b < bend; b += kAttnWaves) {
-    const int key0 = b * kBlockKeys;
-    const int lp = key0 / kPage;
-    // pages past the request's last page are not read; a needed page id
-    // outside [0, num_pages) is reported and read as zeros
-    int pg0 = lp < npages ? bt[lp] : -1;
-    int pg1 = lp + 1 < npages ? bt[lp + 1] : -1;
-    if (lp < npages && (pg0 < 0 || pg0 >= a.num_pages)) { bad_page = true; pg0 = -1; }
-    if (lp + 1 < npages && (pg1 < 0 || pg1 >= a.num_pages)) { bad_page = true; pg1 = -1; }
-
-    // K: lane holds key key0+n, d = 16*kk + 8*hh .. +7
-    bf16x8 kop[KK];
-    {
-      const int pg = n < 16 ? pg0 : pg1;
-      const bool ok = key0 + n < nk && pg >= 0;
-      const uint16_t *krow = a.k_cache + (size_t)(ok ? pg : 0) * page_stride + head_off +
-                             (size_t)(n & 15) * D + 8 * hh;
+  for (int m2 = 0; m2 < 2; ++m2) {
+    const uint16_t *vpage = vh + (size_t)(m2 ? pg.y : pg.x) * page_stride + DPL * n;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        kop[kk] = ok ? *reinterpret_cast<const bf16x8 *>(krow + 16 * kk) : bf16x8{};
-    }
-    // V: for key group m2 (keys 16*m2..), slot 8t+4hh+e, lane holds d = DPL*n .. +DPL-1
-    uint32_t vraw[2][2][4][DPL / 2];
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2) {
-      const int pg = m2 ? pg1 : pg0;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int slot = 8 * t + 4 * hh + e;
-          const bool ok = key0 + 16 * m2 + slot < nk && pg >= 0;
-          const uint16_t *vrow = a.v_cache + (size_t)(ok ? pg : 0) * page_stride + head_off +
-                                 (size_t)slot * D + DPL * n;
-          if constexpr (DPL == 4) {
-            uint2 v = ok ? *reinterpret_cast<const uint2 *>(vrow) : make_uint2(0, 0);
-            vraw[m2][t][e][0] = v.x;
-            vraw[m2][t][e][1] = v.y;
-          } else {
-            vraw[m2][t][e][0] = ok ? *reinterpret_cast<const uint32_t *>(vrow) : 0u;
-          }
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t *vrow = vpage + (size_t)(8 * t + 4 * hh + e) * D;
+        if constexpr (DPL == 4) {
+          const uint2 x = *reinterpret_cast<const uint2 *>(vrow);
+          buf.v[m2][t][e][0] = x.x;
+          buf.v[m2][t][e][1] = x.y;
+        } else {
+          buf.v[m2][t][e][0] = *reinterpret_cast<const uint32_t *>(vrow);
         }
-    }
+      }
+  }
+}
 
-    // S^T = K . Q^T ; acc reg r <-> key key0 + 8*(r/4) + 4*hh + r%4, row n
-    floatx16 s = floatx16{};
+// One 32-key block: S^T = K.Q^T, mask, online softmax, O^T += V^T.P^T.
+template <int D>
+__device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 *qop_lds, int key0, int L, int nk,
+                                     uint64_t anc, int hh, float scale_log2, float &m, float &l,
+                                     floatx16 (&acc)[D / 32]) {
+  constexpr int KK = D / 16, DPL = D / 32;
+  floatx16 s = floatx16{};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qop[kk], s, 0, 0, 0);
+  for (int kk = 0; kk < KK; ++kk)
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf.k[kk], qop_lds[kk * 64], s, 0, 0, 0);
 
-    float sv[16];
-    const bool need_mask = key0 + kBlockKeys > L;
+  // keys of acc reg r: key0 + 8*(r/4) + 4*hh + r%4
+  const bool need_mask = key0 + kBlockKeys > L;
+  if (need_mask) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float x = s[r] * a.scale_log2;
-      if (need_mask) {
-        const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const bool vis = key < L || (key < nk && ((anc >> (unsigned)(key - L)) & 1ull));
-        x = vis ? x : -INFINITY;
-      }
-      sv[r] = x;
+      const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const bool vis = key < L || (key < nk && ((anc >> (unsigned)(key - L)) & 1ull));
+      s[r] = vis ? s[r] * scale_log2 : -INFINITY;
     }
-    float mb = sv[0];
+    if (key0 + kBlockKeys > nk) {
+      // keys past the request: their V is stale memory (maybe non-finite)
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mb = fmaxf(mb, sv[r]);
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
-    const float mnew = fmaxf(m, mb);
-    const float mref = mnew == -INFINITY ? 0.f : mnew;
+      for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int c = 0; c < DPL / 2; ++c)
+              buf.v[m2][t][e][c] = key0 + 16 * m2 + 8 * t + 4 * hh + e < nk ? buf.v[m2][t][e][c] : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] *= scale_log2;
+  }
+  float mb = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mb = fmaxf(mb, s[r]);
+  mb = fmaxf(mb, __shfl_xor(mb, 32));
+  const float mnew = fmaxf(m, mb);
+  const float mref = mnew == -INFINITY ? 0.f : mnew;
+  if (__builtin_amdgcn_ballot_w64(mnew != m) != 0ull) {  // some row's running max moved
     const float alpha = fast_exp2(m - mref);
-    float psum = 0.f;
-    uint32_t pw[8];
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = fast_exp2(sv[r] - mref);
-      const float p1 = fast_exp2(sv[r + 1] - mref);
-      psum += p0 + p1;
-      pw[r >> 1] = pack_bf16x2(p0, p1);
-    }
-    l = l * alpha + psum;
-    m = mnew;
+    l *= alpha;
 #pragma unroll
     for (int c = 0; c < DPL; ++c) acc[c] *= alpha;
-
-    // O^T += V^T . P^T over the two 16-key groups
-#pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2) {
-      bf16x8 pop;
-      {
-        uint32_t w4[4] = {pw[4 * m2], pw[4 * m2 + 1], pw[4 * m2 + 2], pw[4 * m2 + 3]};
-        pop = __builtin_bit_cast(bf16x8, w4);
-      }
-#pragma unroll
-      for (int c = 0; c < DPL; ++c) {
-        // k-slot s = 4t+e <-> key 16*m2 + 8t + 4hh + e; element c of the lane's d-run
-        uint32_t w4[4];
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-          const int s0 = 2 * pr, s1 = 2 * pr + 1;
-          const uint32_t x0 = vraw[m2][s0 >> 2][s0 & 3][c >> 1];
-          const uint32_t x1 = vraw[m2][s1 >> 2][s1 & 3][c >> 1];
-          w4[pr] = (c & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
-        }
-        const bf16x8 vop = __builtin_bit_cast(bf16x8, w4);
-        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, acc[c], 0, 0, 0);
-      }
-    }
   }
-  if (bad_page) atomicOr(reinterpret_cast<unsigned *>(a.ws + a.lay.hdr), SV_DEV_BAD_PAGE);
-
-  // both lane halves summed different keys of the same row
-  l += __shfl_xor(l, 32);
-
-  // ---- merge the waves ----------------------------------------------------
-  if (hh == 0) {
-    sm_m[wave][n] = m;
-    sm_l[wave][n] = l;
+  m = mnew;
+  float psum = 0.f;
+  uint32_t pw[8];
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const float p0 = fast_exp2(s[r] - mref);
+    const float p1 = fast_exp2(s[r + 1] - mref);
+    psum += p0 + p1;
+    pw[r >> 1] = pack_bf16x2(p0, p1);
   }
+  l += psum;
 #pragma unroll
-  for (int c = 0; c < DPL; ++c)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sm_o[wave][c][r][lane] = acc[c][r];
-  __syncthreads();
-
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm_m[w][n]);
-  const float Mref = M == -INFINITY ? 0.f : M;
-  float f[kAttnWaves];
-  float Lsum = 0.f;
-#pragma unroll
-  for (int w = 0; w < kAttnWaves; ++w) {
-    f[w] = fast_exp2(sm_m[w][n] - Mref);
-    Lsum += f[w] * sm_l[w][n];
-  }
-  // this wave finalises registers r = 4*wave .. 4*wave+3, i.e. output
-  // d = DPL*(8*wave + 4*hh) + (0 .. 4*DPL-1), contiguous
-  float ov[4 * DPL];
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr)
+  for (int m2 = 0; m2 < 2; ++m2) {
+    uint32_t w4p[4] = {pw[4 * m2], pw[4 * m2 + 1], pw[4 * m2 + 2], pw[4 * m2 + 3]};
+    const bf16x8 pop = __builtin_bit_cast(bf16x8, w4p);
 #pragma unroll
     for (int c = 0; c < DPL; ++c) {
-      float v = 0.f;
+      // k-slot 4t+e <-> key 16*m2 + 8t + 4hh + e; element c of the lane's d-run
+      uint32_t w4[4];
 #pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) v += f[w] * sm_o[w][c][4 * wave + rr][lane];
-      ov[DPL * rr + c] = v;
-    }
-  if (!row_ok) return;
-  const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
-  const int d0 = DPL * (8 * wave + 4 * hh);
-  if (sg.nchunk == 1) {
-    uint16_t *orow = a.out + ((size_t)(o + tok) * a.num_q_heads + (size_t)h * G + gq) * D + d0;
-    uint32_t pk[2 * DPL];
-#pragma unroll
-    for (int t = 0; t < 2 * DPL; ++t) pk[t] = pack_bf16x2(ov[2 * t] * inv, ov[2 * t + 1] * inv);
-#pragma unroll
-    for (int t = 0; t < DPL / 2; ++t)
-      reinterpret_cast<uint4 *>(orow)[t] = make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]);
-  } else {
-    const int slot = sg.slot + h * sg.nchunk + c_idx;
-    float *po = reinterpret_cast<float *>(a.ws + a.lay.part_o) + ((size_t)slot * kTileRows + n) * D + d0;
-#pragma unroll
-    for (int t = 0; t < DPL; ++t)
-      reinterpret_cast<float4 *>(po)[t] =
-          make_float4(ov[4 * t] * inv, ov[4 * t + 1] * inv, ov[4 * t + 2] * inv, ov[4 * t + 3] * inv);
-    if (wave == 0 && hh == 0) {
-      float *pl = reinterpret_cast<float *>(a.ws + a.lay.part_lse);
-      pl[(size_t)slot * kTileRows + n] = Lsum > 0.f ? Mref + fast_log2(Lsum) : -INFINITY;
+      for (int pr = 0; pr < 4; ++pr) {
+        const int s0 = 2 * pr, s1 = 2 * pr + 1;
+        const uint32_t x0 = buf.v[m2][s0 >> 2][s0 & 3][c >> 1];
+        const uint32_t x1 = buf.v[m2][s1 >> 2][s1 & 3][c >> 1];
+        w4[pr] = (c & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+      }
+      const bf16x8 vop = __builtin_bit_cast(bf16x8, w4);
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, acc[c], 0, 0, 0);
     }
   }
 }
 
 // --------------------------------------------------------------------------
-// combine chunks of split rows
+// merge the partials of units cut by workgroup range boundaries.  A cut unit
+// u spans ranges w0 < w1; its merge is done by workgroup w0 + 1, the first
+// range that starts inside it, so each cut unit is merged exactly once and
+// the grid is only as large as the attention grid.  256 threads: row
+// n = tid/8, a run of D/8 output columns per thread.
 // --------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  constexpr int DT = D / 8;  // d per thread
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.lay.hdr);
-  const int s_idx = blockIdx.x / a.num_kv_heads;
-  const int h = blockIdx.x - s_idx * a.num_kv_heads;
-  if (s_idx >= hdr[3]) return;
-  const int4 sg4 = reinterpret_cast<const int4 *>(a.ws + a.lay.segs)[s_idx];
-  const SegInfo sg{sg4.x, sg4.y, sg4.z, sg4.w};
-  if (sg.nchunk <= 1) return;
+  const int P = hdr[1];
+  const int wm = blockIdx.x;
+  if (wm == 0 || wm >= P) return;
+  const long long nb = hdr[2];
+  const int u = reinterpret_cast<const int32_t *>(a.ws + a.lay.wg_first)[wm];
+  if (u < 0 || u >= hdr[3]) return;
+  const int4 U = reinterpret_cast<const int4 *>(a.ws + a.lay.units)[u];
+  const int i = U.x, h = U.y, rowgroup = U.z;
+  const long long ub = U.w;
+  if (wg_of_block(ub, nb, P) != wm - 1) return;  // not cut here, or merged by another workgroup
+  const int o = a.cu_q[i];
+  const int qn = a.cu_q[i + 1] - o;
+  const int nblk = (a.context_lens[i] + qn + kBlockKeys - 1) / kBlockKeys;
+  constexpr int DT = D / 8;
+  const int w0 = wm - 1, w1 = wg_of_block(ub + nblk - 1, nb, P);
   const int n = threadIdx.x >> 3, part = threadIdx.x & 7;
-  const int o = a.cu_q[sg.req];
-  const int qn = a.cu_q[sg.req + 1] - o;
   const int G = a.group;
-  const int R = sg.rowgroup * kTileRows + n;
+  const int R = rowgroup * kTileRows + n;
   if (R >= G * qn) return;
   const int tok = R / G, gq = R - tok * G;
-  const int slot0 = sg.slot + h * sg.nchunk;
+  const int32_t *wg_first = reinterpret_cast<const int32_t *>(a.ws + a.lay.wg_first);
   const float *pl = reinterpret_cast<const float *>(a.ws + a.lay.part_lse);
   const float *po = reinterpret_cast<const float *>(a.ws + a.lay.part_o);
   float M = -INFINITY;
-  for (int c = 0; c < sg.nchunk; ++c) M = fmaxf(M, pl[(size_t)(slot0 + c) * kTileRows + n]);
+  for (int w = w0; w <= w1; ++w) {
+    const int slot = 2 * w + (wg_first[w] == u ? 0 : 1);
+    M = fmaxf(M, pl[(size_t)slot * kTileRows + n]);
+  }
   const float Mref = M == -INFINITY ? 0.f : M;
   float accv[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) accv[t] = 0.f;
   float den = 0.f;
-  for (int c = 0; c < sg.nchunk; ++c) {
-    const float w = fast_exp2(pl[(size_t)(slot0 + c) * kTileRows + n] - Mref);
-    den += w;
-    const float4 *src = reinterpret_cast<const float4 *>(po + ((size_t)(slot0 + c) * kTileRows + n) * D + part * DT);
+  for (int w = w0; w <= w1; ++w) {
+    const int slot = 2 * w + (wg_first[w] == u ? 0 : 1);
+    const float wt = fast_exp2(pl[(size_t)slot * kTileRows + n] - Mref);
+    den += wt;
+    const float4 *src = reinterpret_cast<const float4 *>(po + ((size_t)slot * kTileRows + n) * D + part * DT);
 #pragma unroll
     for (int t = 0; t < DT / 4; ++t) {
       const float4 v = src[t];
-      accv[4 * t] += w * v.x;
-      accv[4 * t + 1] += w * v.y;
-      accv[4 * t + 2] += w * v.z;
-      accv[4 * t + 3] += w * v.w;
+      accv[4 * t] += wt * v.x;
+      accv[4 * t + 1] += wt * v.y;
+      accv[4 * t + 2] += wt * v.z;
+      accv[4 * t + 3] += wt * v.w;
     }
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
@@ -443,18 +353,196 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
                    pack_bf16x2(accv[8 * t + 6] * inv, accv[8 * t + 7] * inv));
 }
 
+// --------------------------------------------------------------------------
+// attention (persistent workgroups)
+// --------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void verify_attn_kernel(AttnArgs a) {
+  constexpr int KK = D / 16;   // k-steps of the S^T product (16 d each)
+  constexpr int DPL = D / 32;  // contiguous d per lane of a V row; O^T tiles
+  static_assert(D == 64 || D == 128, "head_dim");
+  __shared__ float sm_o[kAttnWaves][DPL][16][64];
+  __shared__ float sm_m[kAttnWaves][32];
+  __shared__ float sm_l[kAttnWaves][32];
+  __shared__ bf16x8 sm_q[KK][64];  // Q^T operands, [kk][lane], shared by the waves
+
+  const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.lay.hdr);
+  const int P = hdr[1];
+  // consecutive ranges on the same XCD (workgroups are dealt round-robin to
+  // the 8 XCDs), so units that share K/V (query tiles of one head) meet in
+  // one L2
+  const int bx = blockIdx.x;
+  const int w = (a.grid % 8 == 0) ? (bx % 8) * (a.grid / 8) + bx / 8 : bx;
+  if (w >= P) return;
+  const long long nb = hdr[2];
+  long long start = (long long)w * nb / P;
+  const long long end = (long long)(w + 1) * nb / P;
+  const int4 *units = reinterpret_cast<const int4 *>(a.ws + a.lay.units);
+  int u = reinterpret_cast<const int32_t *>(a.ws + a.lay.wg_first)[w];
+  const int n_units = hdr[3];
+  if (u < 0 || u >= n_units) return;  // cannot happen for a consistent plan
+  const int first_unit = u;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, hh = lane >> 5;
+  const int G = a.group;
+  const size_t page_stride = (size_t)a.num_kv_heads * kPage * D;
+  bool bad_page = false;
+
+  while (start < end && u < n_units) {
+    const int4 U = units[u];
+    const int i = U.x, h = U.y, rowgroup = U.z;
+    const long long ub = U.w;
+    const int o = a.cu_q[i];
+    const int qn = a.cu_q[i + 1] - o;
+    const int L = a.context_lens[i];
+    const int nk = L + qn;
+    const int nblk = (nk + kBlockKeys - 1) / kBlockKeys;
+    const int lb = (int)(start - ub);
+    const int le = (int)(min(end, ub + nblk) - ub);
+    const bool whole = lb == 0 && le == nblk;
+
+    // this lane's query row (token-major: row R = token * G + head-in-group)
+    const int R = rowgroup * kTileRows + n;
+    const bool row_ok = R < G * qn;
+    const int tok = row_ok ? R / G : 0;
+    const int gq = R - (R / G) * G;
+    bool parents_ok;
+    const uint64_t anc_all = ancestor_mask(a.tree_parent, o, qn, lane, &parents_ok);
+    // the shuffle must run on every lane: a source lane whose own row is past
+    // the end would be inactive and read back as zero
+    const uint64_t anc_tok = __shfl(anc_all, tok);
+    const uint64_t anc = row_ok ? anc_tok : 0ull;
+    if (!parents_ok && threadIdx.x == 0 && lb == 0 && h == 0 && rowgroup == 0)
+      atomicOr(reinterpret_cast<unsigned *>(a.ws + a.lay.hdr), SV_DEV_BAD_PARENT);
+
+    __syncthreads();  // the previous unit is done with sm_q / sm_o
+    if (wave == 0) {
+      const uint16_t *qrow =
+          a.q + ((size_t)(o + tok) * a.num_q_heads + (size_t)h * G + gq) * D + 8 * hh;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        sm_q[kk][lane] = row_ok ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * kk) : bf16x8{};
+    }
+    const const_i32_ptr bt = (const_i32_ptr)(uintptr_t)(a.block_tables + (size_t)i * a.max_blocks);
+    const int npages = (nk + kPage - 1) / kPage;
+    const uint16_t *kh = a.k_cache + (size_t)h * kPage * D;
+    const uint16_t *vh = a.v_cache + (size_t)h * kPage * D;
+    int safe = bt[0];
+    if (safe < 0 || safe >= a.num_pages) safe = 0;
+
+    float m = -INFINITY, l = 0.f;
+    floatx16 acc[DPL];
+#pragma unroll
+    for (int c = 0; c < DPL; ++c) acc[c] = floatx16{};
+    __syncthreads();  // sm_q ready
+    const bf16x8 *qop = &sm_q[0][lane];
+
+    // this wave's blocks: b_t = lb + wave + kAttnWaves * t, t < nbw.  Three
+    // register buffers: blocks t+1 and t+2 stream in while block t is
+    // computed.  Past the last block the loads repeat the last block (cache
+    // hits, never used).  Page ids are fetched one load ahead.
+    const int nbw = lb + wave < le ? (le - 1 - lb - wave) / kAttnWaves + 1 : 0;
+    if (nbw > 0) {
+      auto blk = [&](int t) { return lb + wave + kAttnWaves * min(t, nbw - 1); };
+      auto pages = [&](int t) { return block_pages(bt, blk(t), npages, a.num_pages, safe, &bad_page); };
+      KVBlock<D> A, Bb, Cc;
+      load_block<D>(A, kh, vh, pages(0), n, hh, page_stride);
+      load_block<D>(Bb, kh, vh, pages(1), n, hh, page_stride);
+      int2 pn = pages(2);
+      for (int t = 0; t < nbw; t += 3) {
+        load_block<D>(Cc, kh, vh, pn, n, hh, page_stride);
+        pn = pages(t + 3);
+        compute_block<D>(A, qop, blk(t) * kBlockKeys, L, nk, anc, hh, a.scale_log2, m, l, acc);
+        if (t + 1 >= nbw) break;
+        load_block<D>(A, kh, vh, pn, n, hh, page_stride);
+        pn = pages(t + 4);
+        compute_block<D>(Bb, qop, blk(t + 1) * kBlockKeys, L, nk, anc, hh, a.scale_log2, m, l, acc);
+        if (t + 2 >= nbw) break;
+        load_block<D>(Bb, kh, vh, pn, n, hh, page_stride);
+        pn = pages(t + 5);
+        compute_block<D>(Cc, qop, blk(t + 2) * kBlockKeys, L, nk, anc, hh, a.scale_log2, m, l, acc);
+      }
+    }
+
+    // both lane halves summed different keys of the same row
+    l += __shfl_xor(l, 32);
+
+    // ---- merge the waves --------------------------------------------------
+    if (hh == 0) {
+      sm_m[wave][n] = m;
+      sm_l[wave][n] = l;
+    }
+#pragma unroll
+    for (int c = 0; c < DPL; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm_o[wave][c][r][lane] = acc[c][r];
+    __syncthreads();
+
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kAttnWaves; ++ww) M = fmaxf(M, sm_m[ww][n]);
+    const float Mref = M == -INFINITY ? 0.f : M;
+    float f[kAttnWaves];
+    float Lsum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kAttnWaves; ++ww) {
+      f[ww] = fast_exp2(sm_m[ww][n] - Mref);
+      Lsum += f[ww] * sm_l[ww][n];
+    }
+    // this wave finalises registers r = 4*wave .. 4*wave+3, i.e. output
+    // d = DPL*(8*wave + 4*hh) + (0 .. 4*DPL-1), contiguous
+    float ov[4 * DPL];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+      for (int c = 0; c < DPL; ++c) {
+        float v = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kAttnWaves; ++ww) v += f[ww] * sm_o[ww][c][4 * wave + rr][lane];
+        ov[DPL * rr + c] = v;
+      }
+    const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
+    const int d0 = DPL * (8 * wave + 4 * hh);
+    if (row_ok) {
+      if (whole) {
+        uint16_t *orow = a.out + ((size_t)(o + tok) * a.num_q_heads + (size_t)h * G + gq) * D + d0;
+        uint32_t pk[2 * DPL];
+#pragma unroll
+        for (int t = 0; t < 2 * DPL; ++t) pk[t] = pack_bf16x2(ov[2 * t] * inv, ov[2 * t + 1] * inv);
+#pragma unroll
+        for (int t = 0; t < DPL / 2; ++t)
+          reinterpret_cast<uint4 *>(orow)[t] = make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]);
+      } else {
+        const int slot = 2 * w + (u == first_unit ? 0 : 1);
+        float *po = reinterpret_cast<float *>(a.ws + a.lay.part_o) + ((size_t)slot * kTileRows + n) * D + d0;
+#pragma unroll
+        for (int t = 0; t < DPL; ++t)
+          reinterpret_cast<float4 *>(po)[t] =
+              make_float4(ov[4 * t] * inv, ov[4 * t + 1] * inv, ov[4 * t + 2] * inv, ov[4 * t + 3] * inv);
+        if (wave == 0 && hh == 0) {
+          float *pl = reinterpret_cast<float *>(a.ws + a.lay.part_lse);
+          pl[(size_t)slot * kTileRows + n] = Lsum > 0.f ? Mref + fast_log2(Lsum) : -INFINITY;
+        }
+      }
+    }
+    start = ub + nblk;
+    ++u;
+  }
+  if (bad_page) atomicOr(reinterpret_cast<unsigned *>(a.ws + a.lay.hdr), SV_DEV_BAD_PAGE);
+}
+
 }  // namespace
 
 void launch_verify_attn(const AttnArgs &a, int head_dim, hipStream_t stream) {
   attn_plan_kernel<<<1, kPlanThreads, 0, stream>>>(a);
-  const int groups_attn = a.lay.item_bound;
-  const int groups_comb = a.lay.seg_bound * a.num_kv_heads;
   if (head_dim == 128) {
-    verify_attn_kernel<128><<<groups_attn, 64 * kAttnWaves, 0, stream>>>(a);
-    attn_combine_kernel<128><<<groups_comb, 256, 0, stream>>>(a);
+    verify_attn_kernel<128><<<a.grid, 64 * kAttnWaves, 0, stream>>>(a);
+    attn_merge_kernel<128><<<a.grid, 256, 0, stream>>>(a);
   } else {
-    verify_attn_kernel<64><<<groups_attn, 64 * kAttnWaves, 0, stream>>>(a);
-    attn_combine_kernel<64><<<groups_comb, 256, 0, stream>>>(a);
+    verify_attn_kernel<64><<<a.grid, 64 * kAttnWaves, 0, stream>>>(a);
+    attn_merge_kernel<64><<<a.grid, 256, 0, stream>>>(a);
   }
 }
 
