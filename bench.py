@@ -51,6 +51,9 @@ def main():
     ap.add_argument("--batch", type=int, default=None, help="override the request count (batch sweeps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-requests", type=int, default=16)
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many MB "
+                         "(reference for the HBM traffic counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -172,6 +175,16 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     verified_tok_s = float(acc_np.sum()) / (ms_per_step * 1e-3)
 
+    if args.calibrate_copy_mb > 0:
+        nbytes = args.calibrate_copy_mb * (1 << 20)
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {nbytes} bytes read, {nbytes} bytes written")
+        del src, dst
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, K[0], V[0], logits, args.cpu_sample_requests, layers)
@@ -200,12 +213,33 @@ def main():
         "compact_us": round(compact_ms * 1e3, 2),
         "verified_tokens_per_s": round(verified_tok_s, 1),
         "mean_accept_len": round(float(acc_np.mean()), 4),
-        "roofline": {"kernel": "spec_verify_attn (plan + verify_attn_kernel + combine, per call)",
+        "roofline": {"kernel": "spec_verify_attn (plan + verify_attn_kernel + merge, per call)",
                      "bound": "hbm", "achieved": round(attn_gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(attn_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(attn_gbs / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes": attn_bytes, "traffic": measured_traffic(name)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def measured_traffic(name):
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on this
+    workload and on the current kernel sources; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"verify_attn_{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    return {"read_bytes": rec["read_bytes_per_launch"], "write_bytes": rec["write_bytes_per_launch"],
+            "total_bytes": rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"],
+            "source": "rocprofv3 --pmc FETCH_SIZE x%.4f, WRITE_SIZE x%.1f (plain-copy calibration)"
+                      % (rec["fetch_scale"], rec["write_scale"])}
 
 
 def cpu_baseline(case, k_dev, v_dev, logits_dev, n_req, layers):
