@@ -121,8 +121,36 @@ int spec_verify_attn(const void *q, const void *k_cache, const void *v_cache,
                      int head_dim, int page_size, int num_pages, float softmax_scale,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * The two halves of spec_verify_attn, for callers that verify many layers
+ * with the same batch: the work decomposition (the "plan") depends only on
+ * context_lens, cu_q, the head counts and the page-count limits, so one
+ * spec_verify_attn_plan per verify step serves every layer's
+ * spec_verify_attn_run.  spec_verify_attn == plan + run.
+ *
+ * spec_verify_attn_plan writes the plan into `workspace` (same size as for
+ * spec_verify_attn); max_blocks_per_seq and num_pages bound the requests'
+ * pages.  spec_verify_attn_run must be given the same batch metadata and
+ * sizes as the plan it uses (stream-ordered after it) and must not overlap
+ * another run or plan on the same workspace.  A run with metadata that
+ * differs from its plan still reads only valid memory, but its outputs are
+ * unspecified.
+ */
+int spec_verify_attn_plan(const int32_t *context_lens, const int32_t *cu_q, int max_blocks_per_seq,
+                          int batch, int total_q, int num_q_heads, int num_kv_heads, int head_dim,
+                          int num_pages, void *workspace, size_t workspace_bytes, void *stream);
+
+int spec_verify_attn_run(const void *q, const void *k_cache, const void *v_cache,
+                         const int32_t *block_tables, int max_blocks_per_seq,
+                         const int32_t *context_lens, const int32_t *cu_q,
+                         const int32_t *tree_parent, void *out, int batch, int total_q,
+                         int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                         int num_pages, float softmax_scale, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
 /* Waits for `stream`, then stores the device status bits of the last
- * spec_verify_attn that used `workspace` into *flags (host pointer). */
+ * spec_verify_attn (plan and runs) that used `workspace` into *flags (host
+ * pointer). */
 int spec_verify_attn_device_status(const void *workspace, uint32_t *flags, void *stream);
 
 /* ------------------------------------------------------------------------- */

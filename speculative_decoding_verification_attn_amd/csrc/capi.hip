@@ -75,12 +75,17 @@ size_t spec_verify_attn_workspace_size(int batch, int total_q, int num_q_heads, 
   return sv::attn_layout(batch, total_q, num_q_heads, num_kv_heads, head_dim).total;
 }
 
-int spec_verify_attn(const void *q, const void *k_cache, const void *v_cache,
-                     const int32_t *block_tables, int max_blocks_per_seq,
-                     const int32_t *context_lens, const int32_t *cu_q, const int32_t *tree_parent,
-                     void *out, int batch, int total_q, int num_q_heads, int num_kv_heads,
-                     int head_dim, int page_size, int num_pages, float softmax_scale,
-                     void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared argument checks of the verify-attention calls; on success fills the
+// kernel argument block (metadata only; data pointers are set by the caller).
+int attn_common(const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+                const int32_t *cu_q, int batch, int total_q, int num_q_heads, int num_kv_heads,
+                int head_dim, int page_size, int num_pages, void *workspace,
+                size_t workspace_bytes, bool need_tables, sv::AttnArgs *a, bool *empty) {
+  *empty = false;
   if (batch < 0 || total_q < 0)
     return fail(SV_ERR_SHAPE, "batch (%d) and total_q (%d) must be >= 0", batch, total_q);
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
@@ -94,50 +99,121 @@ int spec_verify_attn(const void *q, const void *k_cache, const void *v_cache,
     return fail(SV_ERR_UNSUPPORTED, "page_size %d (supported: 16)", page_size);
   if (total_q > (long long)batch * sv::kMaxTokens)
     return fail(SV_ERR_SHAPE, "total_q %d exceeds batch*64", total_q);
-  if (batch == 0 || total_q == 0) return ok();
-  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !cu_q || !out || !workspace)
+  if (batch == 0 || total_q == 0) {
+    *empty = true;
+    return ok();
+  }
+  if (!context_lens || !cu_q || !workspace || (need_tables && !block_tables))
     return fail(SV_ERR_NULL, "spec_verify_attn: a required pointer is NULL");
   if (max_blocks_per_seq <= 0 || num_pages <= 0)
     return fail(SV_ERR_SHAPE, "max_blocks_per_seq (%d) and num_pages (%d) must be > 0",
                 max_blocks_per_seq, num_pages);
-  if (!(softmax_scale == 0.0f || isfinite(softmax_scale)))
-    return fail(SV_ERR_SHAPE, "softmax_scale must be finite");
   const sv::AttnLayout lay = sv::attn_layout(batch, total_q, num_q_heads, num_kv_heads, head_dim);
   if (workspace_bytes < lay.total)
     return fail(SV_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, lay.total);
-  const size_t qo_bytes = (size_t)total_q * num_q_heads * head_dim * 2;
-  const size_t kv_bytes = (size_t)num_pages * num_kv_heads * page_size * head_dim * 2;
-  if (overlaps(out, qo_bytes, q, qo_bytes) || overlaps(out, qo_bytes, k_cache, kv_bytes) ||
-      overlaps(out, qo_bytes, v_cache, kv_bytes) || overlaps(out, qo_bytes, workspace, lay.total))
-    return fail(SV_ERR_ALIAS, "out overlaps q, the caches or the workspace");
+  memset(a, 0, sizeof *a);
+  a->block_tables = block_tables;
+  a->context_lens = context_lens;
+  a->cu_q = cu_q;
+  a->ws = static_cast<char *>(workspace);
+  a->lay = lay;
+  a->batch = batch;
+  a->total_q = total_q;
+  a->num_q_heads = num_q_heads;
+  a->num_kv_heads = num_kv_heads;
+  a->group = num_q_heads / num_kv_heads;
+  a->max_blocks = max_blocks_per_seq;
+  a->num_pages = num_pages;
+  return ok();
+}
 
-  sv::AttnArgs a;
-  a.q = static_cast<const uint16_t *>(q);
-  a.k_cache = static_cast<const uint16_t *>(k_cache);
-  a.v_cache = static_cast<const uint16_t *>(v_cache);
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.cu_q = cu_q;
-  a.tree_parent = tree_parent;
-  a.out = static_cast<uint16_t *>(out);
-  a.ws = static_cast<char *>(workspace);
-  a.lay = lay;
-  a.batch = batch;
-  a.total_q = total_q;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.group = num_q_heads / num_kv_heads;
-  a.max_blocks = max_blocks_per_seq;
-  a.num_pages = num_pages;
-  const float scale = softmax_scale == 0.0f ? 1.0f / sqrtf((float)head_dim) : softmax_scale;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  // one persistent attention workgroup per compute unit of the current device
+// One persistent attention workgroup per compute unit of the current device
+// (queried after every argument check, right before launching).
+int set_grid(sv::AttnArgs *a) {
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return fail(SV_ERR_HIP, "device query: %s", hipGetErrorString(e));
-  a.grid = cus < 1 ? 1 : (cus > sv::kMaxGrid ? sv::kMaxGrid : cus);
-  sv::launch_verify_attn(a, head_dim, static_cast<hipStream_t>(stream));
+  a->grid = cus < 1 ? 1 : (cus > sv::kMaxGrid ? sv::kMaxGrid : cus);
+  return ok();
+}
+
+int attn_data(const void *q, const void *k_cache, const void *v_cache, const int32_t *tree_parent,
+              void *out, int head_dim, int page_size, float softmax_scale, sv::AttnArgs *a) {
+  if (!q || !k_cache || !v_cache || !out)
+    return fail(SV_ERR_NULL, "spec_verify_attn: a required pointer is NULL");
+  if (!(softmax_scale == 0.0f || isfinite(softmax_scale)))
+    return fail(SV_ERR_SHAPE, "softmax_scale must be finite");
+  const size_t qo_bytes = (size_t)a->total_q * a->num_q_heads * head_dim * 2;
+  const size_t kv_bytes = (size_t)a->num_pages * a->num_kv_heads * page_size * head_dim * 2;
+  if (overlaps(out, qo_bytes, q, qo_bytes) || overlaps(out, qo_bytes, k_cache, kv_bytes) ||
+      overlaps(out, qo_bytes, v_cache, kv_bytes) || overlaps(out, qo_bytes, a->ws, a->lay.total))
+    return fail(SV_ERR_ALIAS, "out overlaps q, the caches or the workspace");
+  a->q = static_cast<const uint16_t *>(q);
+  a->k_cache = static_cast<const uint16_t *>(k_cache);
+  a->v_cache = static_cast<const uint16_t *>(v_cache);
+  a->tree_parent = tree_parent;
+  a->out = static_cast<uint16_t *>(out);
+  const float scale = softmax_scale == 0.0f ? 1.0f / sqrtf((float)head_dim) : softmax_scale;
+  a->scale_log2 = scale * 1.4426950408889634f;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_attn_plan(const int32_t *context_lens, const int32_t *cu_q, int max_blocks_per_seq,
+                          int batch, int total_q, int num_q_heads, int num_kv_heads, int head_dim,
+                          int num_pages, void *workspace, size_t workspace_bytes, void *stream) {
+  sv::AttnArgs a;
+  bool empty;
+  int rc = attn_common(nullptr, max_blocks_per_seq, context_lens, cu_q, batch, total_q, num_q_heads,
+                       num_kv_heads, head_dim, sv::kPage, num_pages, workspace, workspace_bytes,
+                       false, &a, &empty);
+  if (rc != SV_OK || empty) return rc;
+  if ((rc = set_grid(&a)) != SV_OK) return rc;
+  sv::launch_verify_attn_plan(a, static_cast<hipStream_t>(stream));
+  return check_launch("spec_verify_attn_plan");
+}
+
+int spec_verify_attn_run(const void *q, const void *k_cache, const void *v_cache,
+                         const int32_t *block_tables, int max_blocks_per_seq,
+                         const int32_t *context_lens, const int32_t *cu_q,
+                         const int32_t *tree_parent, void *out, int batch, int total_q,
+                         int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                         int num_pages, float softmax_scale, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  sv::AttnArgs a;
+  bool empty;
+  int rc = attn_common(block_tables, max_blocks_per_seq, context_lens, cu_q, batch, total_q,
+                       num_q_heads, num_kv_heads, head_dim, page_size, num_pages, workspace,
+                       workspace_bytes, true, &a, &empty);
+  if (rc != SV_OK || empty) return rc;
+  rc = attn_data(q, k_cache, v_cache, tree_parent, out, head_dim, page_size, softmax_scale, &a);
+  if (rc != SV_OK) return rc;
+  if ((rc = set_grid(&a)) != SV_OK) return rc;
+  sv::launch_verify_attn_run(a, head_dim, static_cast<hipStream_t>(stream));
+  return check_launch("spec_verify_attn_run");
+}
+
+int spec_verify_attn(const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *block_tables, int max_blocks_per_seq,
+                     const int32_t *context_lens, const int32_t *cu_q, const int32_t *tree_parent,
+                     void *out, int batch, int total_q, int num_q_heads, int num_kv_heads,
+                     int head_dim, int page_size, int num_pages, float softmax_scale,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  sv::AttnArgs a;
+  bool empty;
+  int rc = attn_common(block_tables, max_blocks_per_seq, context_lens, cu_q, batch, total_q,
+                       num_q_heads, num_kv_heads, head_dim, page_size, num_pages, workspace,
+                       workspace_bytes, true, &a, &empty);
+  if (rc != SV_OK || empty) return rc;
+  rc = attn_data(q, k_cache, v_cache, tree_parent, out, head_dim, page_size, softmax_scale, &a);
+  if (rc != SV_OK) return rc;
+  if ((rc = set_grid(&a)) != SV_OK) return rc;
+  sv::launch_verify_attn_plan(a, static_cast<hipStream_t>(stream));
+  sv::launch_verify_attn_run(a, head_dim, static_cast<hipStream_t>(stream));
   return check_launch("spec_verify_attn");
 }
 

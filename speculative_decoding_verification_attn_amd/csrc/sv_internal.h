@@ -30,13 +30,22 @@ constexpr int kPlanLdsRequests = 4096;  // per-request plan data kept in LDS up 
 // to the output; a unit cut by range boundaries leaves one partial per
 // workgroup that touched it (at most two per workgroup), merged afterwards.
 // ---------------------------------------------------------------------------
+// A unit record: {request, kv head, row tile, first global block} and
+// {first verify row o, verify tokens q, context L, blocks per unit}.
+struct UnitRec {
+  int4 a;
+  int4 b;
+};
+
 struct AttnLayout {
-  size_t hdr;       // int32[8]: 0 status bits, 1 active workgroups P, 2 total blocks, 3 units
-  size_t req_meta;  // int4[B]: {unit base, block base, rowgroups, blocks per unit}
-  size_t units;     // int4[unit_bound]: {request, kv head, rowgroup, first global block}
-  size_t wg_first;  // int32[kMaxGrid]: first unit of each workgroup's range
-  size_t part_lse;  // float[2*kMaxGrid][32] log2-sum-exp of partial rows
-  size_t part_o;    // float[2*kMaxGrid][32][D] normalised partial outputs
+  size_t hdr;        // int32[8]: 0 status bits, 1 active workgroups P, 2 total blocks, 3 units
+  size_t req_meta;   // int32[4][B]: unit base, block base, row tiles, blocks per unit (large batches)
+  size_t units;      // UnitRec[unit_bound]
+  size_t wg_first;   // int32[kMaxGrid]: first unit of each workgroup's range
+  size_t wg_rec;     // UnitRec[kMaxGrid]: a copy of that first unit's record
+  size_t merge_rec;  // UnitRec[kMaxGrid]: {cut unit merged here or -1, w0, w1, side of w0}, {o, q, head, tile}
+  size_t part_lse;   // float[2*kMaxGrid][32] log2-sum-exp of partial rows
+  size_t part_o;     // float[2*kMaxGrid][32][D] normalised partial outputs
   size_t total;
   int unit_bound;
 };
@@ -51,12 +60,14 @@ __host__ __device__ inline AttnLayout attn_layout(int batch, int total_q, int nu
   const long long tiles = (long long)batch + ((long long)G * total_q + kTileRows - 1) / kTileRows;
   l.unit_bound = (int)(tiles * num_kv_heads);
   size_t off = 0;
-  l.hdr = off;       off = align256(off + 8 * sizeof(int32_t));
-  l.req_meta = off;  off = align256(off + size_t(batch) * 16);
-  l.units = off;     off = align256(off + size_t(l.unit_bound) * 16);
-  l.wg_first = off;  off = align256(off + size_t(kMaxGrid) * sizeof(int32_t));
-  l.part_lse = off;  off = align256(off + size_t(2 * kMaxGrid) * kTileRows * sizeof(float));
-  l.part_o = off;    off = align256(off + size_t(2 * kMaxGrid) * kTileRows * head_dim * sizeof(float));
+  l.hdr = off;        off = align256(off + 8 * sizeof(int32_t));
+  l.req_meta = off;   off = align256(off + size_t(batch) * 16);
+  l.units = off;      off = align256(off + size_t(l.unit_bound) * sizeof(UnitRec));
+  l.wg_first = off;   off = align256(off + size_t(kMaxGrid) * sizeof(int32_t));
+  l.wg_rec = off;     off = align256(off + size_t(kMaxGrid) * sizeof(UnitRec));
+  l.merge_rec = off;  off = align256(off + size_t(kMaxGrid) * sizeof(UnitRec));
+  l.part_lse = off;   off = align256(off + size_t(2 * kMaxGrid) * kTileRows * sizeof(float));
+  l.part_o = off;     off = align256(off + size_t(2 * kMaxGrid) * kTileRows * head_dim * sizeof(float));
   l.total = off;
   return l;
 }
@@ -77,7 +88,8 @@ struct AttnArgs {
   float scale_log2;  // softmax scale * log2(e)
 };
 
-void launch_verify_attn(const AttnArgs &a, int head_dim, hipStream_t stream);
+void launch_verify_attn_plan(const AttnArgs &a, hipStream_t stream);
+void launch_verify_attn_run(const AttnArgs &a, int head_dim, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Acceptance

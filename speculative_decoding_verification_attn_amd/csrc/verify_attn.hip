@@ -61,8 +61,10 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a) {
   __shared__ long long s_red[16];
   __shared__ int s_req[4][kPlanLdsRequests];
   int32_t *hdr = reinterpret_cast<int32_t *>(a.ws + a.lay.hdr);
-  int4 *units = reinterpret_cast<int4 *>(a.ws + a.lay.units);
+  UnitRec *units = reinterpret_cast<UnitRec *>(a.ws + a.lay.units);
   int32_t *wg_first = reinterpret_cast<int32_t *>(a.ws + a.lay.wg_first);
+  UnitRec *wg_rec = reinterpret_cast<UnitRec *>(a.ws + a.lay.wg_rec);
+  UnitRec *merge_rec = reinterpret_cast<UnitRec *>(a.ws + a.lay.merge_rec);
   const int tid = threadIdx.x;
   const int B = a.batch, G = a.group, Hkv = a.num_kv_heads;
   const bool in_lds = B <= kPlanLdsRequests;
@@ -124,16 +126,20 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a) {
   __syncthreads();
 
   if (fits) {
-    // pass 2: each request's units ...
+    // pass 2: each request's unit records
     for (int i = tid; i < B; i += kPlanThreads) {
       const int rg = rgs[i], nblk = nblks[i], u0 = ubase[i], b0 = bbase[i];
+      if (rg == 0) continue;
+      const int o = a.cu_q[i], qn = a.cu_q[i + 1] - o, L = a.context_lens[i];
       for (int k = 0; k < rg * Hkv; ++k) {
         const int h = k / rg, r = k - h * rg;
-        units[u0 + k] = make_int4(i, h, r, b0 + k * nblk);
+        units[u0 + k] = UnitRec{make_int4(i, h, r, b0 + k * nblk), make_int4(o, qn, L, nblk)};
       }
     }
-    // ... and the first unit of each workgroup range: the request whose block
-    // span holds start(w) = floor(w*nb/P), found by binary search
+    // pass 3: per workgroup w, the unit holding start(w) = floor(w*nb/P) (the
+    // request whose block span holds it, by binary search) with a copy of its
+    // record, and the cut unit this workgroup merges afterwards: the unit
+    // whose first block lies in range w-1 and which continues into range w
     for (int w = tid; w < P && nb > 0; w += kPlanThreads) {
       const long long st = (long long)w * nb / P;
       int lo = 0, hi = B - 1;
@@ -141,7 +147,22 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a) {
         const int mid = (lo + hi + 1) >> 1;
         if (bbase[mid] <= st) lo = mid; else hi = mid - 1;
       }
-      wg_first[w] = ubase[lo] + (int)((st - bbase[lo]) / nblks[lo]);
+      const int nblk = nblks[lo], rg = rgs[lo];
+      const int k = (int)((st - bbase[lo]) / nblk);
+      const int u = ubase[lo] + k;
+      const int h = k / rg, r = k - h * rg;
+      const int ub = bbase[lo] + k * nblk;
+      const int o = a.cu_q[lo], qn = a.cu_q[lo + 1] - o, L = a.context_lens[lo];
+      wg_first[w] = u;
+      wg_rec[w] = UnitRec{make_int4(lo, h, r, ub), make_int4(o, qn, L, nblk)};
+      const int w0 = wg_of_block(ub, nb, P);
+      if (w >= 1 && w0 == w - 1) {
+        const int w1 = wg_of_block((long long)ub + nblk - 1, nb, P);
+        const int side0 = ((long long)w0 * nb / P == ub) ? 0 : 1;
+        merge_rec[w] = UnitRec{make_int4(u, w0, w1, side0), make_int4(o, qn, h, r)};
+      } else {
+        merge_rec[w] = UnitRec{make_int4(-1, 0, 0, 0), make_int4(0, 0, 0, 0)};
+      }
     }
   }
   if (flags) atomicOr(reinterpret_cast<unsigned *>(hdr), flags);
@@ -294,33 +315,25 @@ __device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 *qop_lds, int
 // --------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.lay.hdr);
-  const int P = hdr[1];
-  const int wm = blockIdx.x;
-  if (wm == 0 || wm >= P) return;
-  const long long nb = hdr[2];
-  const int u = reinterpret_cast<const int32_t *>(a.ws + a.lay.wg_first)[wm];
-  if (u < 0 || u >= hdr[3]) return;
-  const int4 U = reinterpret_cast<const int4 *>(a.ws + a.lay.units)[u];
-  const int i = U.x, h = U.y, rowgroup = U.z;
-  const long long ub = U.w;
-  if (wg_of_block(ub, nb, P) != wm - 1) return;  // not cut here, or merged by another workgroup
-  const int o = a.cu_q[i];
-  const int qn = a.cu_q[i + 1] - o;
-  const int nblk = (a.context_lens[i] + qn + kBlockKeys - 1) / kBlockKeys;
   constexpr int DT = D / 8;
-  const int w0 = wm - 1, w1 = wg_of_block(ub + nblk - 1, nb, P);
+  const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.lay.hdr);
+  const int wm = blockIdx.x;
+  const UnitRec mr = reinterpret_cast<const UnitRec *>(a.ws + a.lay.merge_rec)[wm];
+  if (wm >= hdr[1] || mr.a.x < 0) return;  // no cut unit to merge here
+  const int w0 = mr.a.y, w1 = mr.a.z, side0 = mr.a.w;
+  const int o = mr.b.x, qn = mr.b.y, h = mr.b.z, rowgroup = mr.b.w;
   const int n = threadIdx.x >> 3, part = threadIdx.x & 7;
   const int G = a.group;
   const int R = rowgroup * kTileRows + n;
   if (R >= G * qn) return;
   const int tok = R / G, gq = R - tok * G;
-  const int32_t *wg_first = reinterpret_cast<const int32_t *>(a.ws + a.lay.wg_first);
   const float *pl = reinterpret_cast<const float *>(a.ws + a.lay.part_lse);
   const float *po = reinterpret_cast<const float *>(a.ws + a.lay.part_o);
+  // range w0 holds the unit's first block (its first or second partial
+  // slot); every later range starts inside the unit (first slot)
   float M = -INFINITY;
   for (int w = w0; w <= w1; ++w) {
-    const int slot = 2 * w + (wg_first[w] == u ? 0 : 1);
+    const int slot = 2 * w + (w == w0 ? side0 : 0);
     M = fmaxf(M, pl[(size_t)slot * kTileRows + n]);
   }
   const float Mref = M == -INFINITY ? 0.f : M;
@@ -329,7 +342,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   for (int t = 0; t < DT; ++t) accv[t] = 0.f;
   float den = 0.f;
   for (int w = w0; w <= w1; ++w) {
-    const int slot = 2 * w + (wg_first[w] == u ? 0 : 1);
+    const int slot = 2 * w + (w == w0 ? side0 : 0);
     const float wt = fast_exp2(pl[(size_t)slot * kTileRows + n] - Mref);
     den += wt;
     const float4 *src = reinterpret_cast<const float4 *>(po + ((size_t)slot * kTileRows + n) * D + part * DT);
@@ -356,10 +369,65 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 // --------------------------------------------------------------------------
 // attention (persistent workgroups)
 // --------------------------------------------------------------------------
+// A unit piece of one workgroup's block range, placed on the workgroup's
+// sequence of rounds (in round r of a piece, wave w takes global block
+// ps + 4r + w).  Everything here is wave-uniform.
+struct Walk {
+  int u, i, h, rg, ub, o, qn, L, nblk;
+  int ps, pe;  // global blocks [ps, pe) of the unit processed by this workgroup
+  int g0, nr;  // its rounds [g0, g0 + nr)
+  bool has_next;
+  UnitRec next;  // record of unit u+1 (fetched on entry, needed at the next advance)
+};
+
+__device__ inline void walk_enter(Walk &W, int u, const UnitRec &r, int start, int end, int g0,
+                                  const UnitRec *units, int n_units) {
+  W.u = u;
+  W.i = r.a.x; W.h = r.a.y; W.rg = r.a.z; W.ub = r.a.w;
+  W.o = r.b.x; W.qn = r.b.y; W.L = r.b.z; W.nblk = r.b.w;
+  W.ps = max(W.ub, start);
+  W.pe = min(W.ub + W.nblk, end);
+  W.g0 = g0;
+  W.nr = (W.pe - W.ps + kAttnWaves - 1) / kAttnWaves;
+  W.has_next = W.pe < end && u + 1 < n_units;
+  if (W.has_next) W.next = units[u + 1];
+}
+
+// Moves the walk forward until round g lies in its piece; false if g is past
+// the workgroup's last piece (the walk then stays on the last piece).
+__device__ inline bool walk_to(Walk &W, int g, int start, int end, const UnitRec *units,
+                               int n_units) {
+  while (g >= W.g0 + W.nr) {
+    if (!W.has_next) return false;
+    const UnitRec r = W.next;
+    walk_enter(W, W.u + 1, r, start, end, W.g0 + W.nr, units, n_units);
+  }
+  return true;
+}
+
+// Q^T operand chunks this wave stages for a unit: kk = wave*KQ .. +KQ-1, for
+// every lane's query row (lane n, half hh).
+template <int D>
+__device__ inline void load_q_chunks(const AttnArgs &a, const Walk &W, int wave, int n, int hh,
+                                     bf16x8 (&qc)[D / 64]) {
+  constexpr int KQ = D / 64;
+  const int G = a.group;
+  const int R = W.rg * kTileRows + n;
+  const bool row_ok = R < G * W.qn;
+  const int tok = row_ok ? R / G : 0;
+  const int gq = R - (R / G) * G;
+  const uint16_t *qrow =
+      a.q + ((size_t)(W.o + tok) * a.num_q_heads + (size_t)W.h * G + gq) * D + 8 * hh;
+#pragma unroll
+  for (int j = 0; j < KQ; ++j)
+    qc[j] = row_ok ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * (wave * KQ + j)) : bf16x8{};
+}
+
 template <int D>
 __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void verify_attn_kernel(AttnArgs a) {
-  constexpr int KK = D / 16;   // k-steps of the S^T product (16 d each)
   constexpr int DPL = D / 32;  // contiguous d per lane of a V row; O^T tiles
+  constexpr int KK = D / 16;   // k-steps of the S^T product (16 d each)
+  constexpr int KQ = D / 64;   // Q chunks staged per wave
   static_assert(D == 64 || D == 128, "head_dim");
   __shared__ float sm_o[kAttnWaves][DPL][16][64];
   __shared__ float sm_m[kAttnWaves][32];
@@ -375,13 +443,13 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   const int w = (a.grid % 8 == 0) ? (bx % 8) * (a.grid / 8) + bx / 8 : bx;
   if (w >= P) return;
   const long long nb = hdr[2];
-  long long start = (long long)w * nb / P;
-  const long long end = (long long)(w + 1) * nb / P;
-  const int4 *units = reinterpret_cast<const int4 *>(a.ws + a.lay.units);
-  int u = reinterpret_cast<const int32_t *>(a.ws + a.lay.wg_first)[w];
+  const int start = (int)((long long)w * nb / P);
+  const int end = (int)((long long)(w + 1) * nb / P);
+  const UnitRec *units = reinterpret_cast<const UnitRec *>(a.ws + a.lay.units);
+  const int first_unit = reinterpret_cast<const int32_t *>(a.ws + a.lay.wg_first)[w];
+  const UnitRec rec0 = reinterpret_cast<const UnitRec *>(a.ws + a.lay.wg_rec)[w];
   const int n_units = hdr[3];
-  if (u < 0 || u >= n_units) return;  // cannot happen for a consistent plan
-  const int first_unit = u;
+  if (first_unit < 0 || first_unit >= n_units || start >= end) return;  // not for a consistent plan
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -390,86 +458,68 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   const size_t page_stride = (size_t)a.num_kv_heads * kPage * D;
   bool bad_page = false;
 
-  while (start < end && u < n_units) {
-    const int4 U = units[u];
-    const int i = U.x, h = U.y, rowgroup = U.z;
-    const long long ub = U.w;
-    const int o = a.cu_q[i];
-    const int qn = a.cu_q[i + 1] - o;
-    const int L = a.context_lens[i];
-    const int nk = L + qn;
-    const int nblk = (nk + kBlockKeys - 1) / kBlockKeys;
-    const int lb = (int)(start - ub);
-    const int le = (int)(min(end, ub + nblk) - ub);
-    const bool whole = lb == 0 && le == nblk;
+  // Two walks over the same pieces: the consumer at the round being
+  // computed, the producer three rounds ahead (it fetches page ids for round
+  // g+3 and issues the K/V loads of round g+2 into the buffer freed by round
+  // g-1), so K/V streaming runs on across unit boundaries.
+  Walk Wc, Wp;
+  walk_enter(Wc, first_unit, rec0, start, end, 0, units, n_units);
+  Wp = Wc;
 
-    // this lane's query row (token-major: row R = token * G + head-in-group)
-    const int R = rowgroup * kTileRows + n;
-    const bool row_ok = R < G * qn;
+  // per-unit consumer context
+  uint64_t anc = 0;
+  int nk = 0;
+  float m = -INFINITY, l = 0.f;
+  floatx16 acc[DPL];
+  bf16x8 qpf[KQ];    // Q chunks prefetched for unit qpf_u
+  int qpf_u = -1;
+
+  // enter the consumer's unit: ancestor mask of the lane's row and Q in LDS
+  auto enter_unit = [&]() {
+    const int R = Wc.rg * kTileRows + n;
+    const bool row_ok = R < G * Wc.qn;
     const int tok = row_ok ? R / G : 0;
-    const int gq = R - (R / G) * G;
     bool parents_ok;
-    const uint64_t anc_all = ancestor_mask(a.tree_parent, o, qn, lane, &parents_ok);
+    const uint64_t anc_all = ancestor_mask(a.tree_parent, Wc.o, Wc.qn, lane, &parents_ok);
     // the shuffle must run on every lane: a source lane whose own row is past
     // the end would be inactive and read back as zero
     const uint64_t anc_tok = __shfl(anc_all, tok);
-    const uint64_t anc = row_ok ? anc_tok : 0ull;
-    if (!parents_ok && threadIdx.x == 0 && lb == 0 && h == 0 && rowgroup == 0)
+    anc = row_ok ? anc_tok : 0ull;
+    if (!parents_ok && threadIdx.x == 0 && Wc.ps == Wc.ub && Wc.h == 0 && Wc.rg == 0)
       atomicOr(reinterpret_cast<unsigned *>(a.ws + a.lay.hdr), SV_DEV_BAD_PARENT);
-
-    __syncthreads();  // the previous unit is done with sm_q / sm_o
-    if (wave == 0) {
-      const uint16_t *qrow =
-          a.q + ((size_t)(o + tok) * a.num_q_heads + (size_t)h * G + gq) * D + 8 * hh;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        sm_q[kk][lane] = row_ok ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * kk) : bf16x8{};
-    }
-    const const_i32_ptr bt = (const_i32_ptr)(uintptr_t)(a.block_tables + (size_t)i * a.max_blocks);
-    const int npages = (nk + kPage - 1) / kPage;
-    const uint16_t *kh = a.k_cache + (size_t)h * kPage * D;
-    const uint16_t *vh = a.v_cache + (size_t)h * kPage * D;
-    int safe = bt[0];
-    if (safe < 0 || safe >= a.num_pages) safe = 0;
-
-    float m = -INFINITY, l = 0.f;
-    floatx16 acc[DPL];
+    nk = Wc.L + Wc.qn;
+    m = -INFINITY;
+    l = 0.f;
 #pragma unroll
     for (int c = 0; c < DPL; ++c) acc[c] = floatx16{};
-    __syncthreads();  // sm_q ready
-    const bf16x8 *qop = &sm_q[0][lane];
+    if (qpf_u != Wc.u) load_q_chunks<D>(a, Wc, wave, n, hh, qpf);
+#pragma unroll
+    for (int j = 0; j < KQ; ++j) sm_q[wave * KQ + j][lane] = qpf[j];
+    qpf_u = -1;
+  };
 
-    // this wave's blocks: b_t = lb + wave + kAttnWaves * t, t < nbw.  Three
-    // register buffers: blocks t+1 and t+2 stream in while block t is
-    // computed.  Past the last block the loads repeat the last block (cache
-    // hits, never used).  Page ids are fetched one load ahead.
-    const int nbw = lb + wave < le ? (le - 1 - lb - wave) / kAttnWaves + 1 : 0;
-    if (nbw > 0) {
-      auto blk = [&](int t) { return lb + wave + kAttnWaves * min(t, nbw - 1); };
-      auto pages = [&](int t) { return block_pages(bt, blk(t), npages, a.num_pages, safe, &bad_page); };
-      KVBlock<D> A, Bb, Cc;
-      load_block<D>(A, kh, vh, pages(0), n, hh, page_stride);
-      load_block<D>(Bb, kh, vh, pages(1), n, hh, page_stride);
-      int2 pn = pages(2);
-      for (int t = 0; t < nbw; t += 3) {
-        load_block<D>(Cc, kh, vh, pn, n, hh, page_stride);
-        pn = pages(t + 3);
-        compute_block<D>(A, qop, blk(t) * kBlockKeys, L, nk, anc, hh, a.scale_log2, m, l, acc);
-        if (t + 1 >= nbw) break;
-        load_block<D>(A, kh, vh, pn, n, hh, page_stride);
-        pn = pages(t + 4);
-        compute_block<D>(Bb, qop, blk(t + 1) * kBlockKeys, L, nk, anc, hh, a.scale_log2, m, l, acc);
-        if (t + 2 >= nbw) break;
-        load_block<D>(Bb, kh, vh, pn, n, hh, page_stride);
-        pn = pages(t + 5);
-        compute_block<D>(Cc, qop, blk(t + 2) * kBlockKeys, L, nk, anc, hh, a.scale_log2, m, l, acc);
-      }
-    }
+  // producer: page ids and head of the round it will load next
+  int2 pg_next = make_int2(0, 0);
+  int h_next = Wp.h;
+  auto fetch_pages = [&](int g) {
+    walk_to(Wp, g, start, end, units, n_units);
+    const int lbk = (Wp.ps - Wp.ub) + kAttnWaves * min(g - Wp.g0, Wp.nr - 1) + wave;
+    const int lmax = Wp.pe - Wp.ub - 1;  // a wave without a block re-reads the piece's last one
+    const const_i32_ptr bt = (const_i32_ptr)(uintptr_t)(a.block_tables + (size_t)Wp.i * a.max_blocks);
+    const int npages = (Wp.L + Wp.qn + kPage - 1) / kPage;
+    int safe = bt[0];
+    if (safe < 0 || safe >= a.num_pages) safe = 0;
+    pg_next = block_pages(bt, min(lbk, lmax), npages, a.num_pages, safe, &bad_page);
+    h_next = Wp.h;
+  };
+  auto produce = [&](KVBlock<D> &buf) {
+    load_block<D>(buf, a.k_cache + (size_t)h_next * kPage * D, a.v_cache + (size_t)h_next * kPage * D,
+                  pg_next, n, hh, page_stride);
+  };
 
-    // both lane halves summed different keys of the same row
-    l += __shfl_xor(l, 32);
-
-    // ---- merge the waves --------------------------------------------------
+  // finish the consumer's unit: merge the waves, write output or a partial
+  auto finish_unit = [&]() {
+    l += __shfl_xor(l, 32);  // both lane halves summed different keys of the same row
     if (hh == 0) {
       sm_m[wave][n] = m;
       sm_l[wave][n] = l;
@@ -479,7 +529,6 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
       for (int r = 0; r < 16; ++r) sm_o[wave][c][r][lane] = acc[c][r];
     __syncthreads();
-
     float M = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < kAttnWaves; ++ww) M = fmaxf(M, sm_m[ww][n]);
@@ -505,9 +554,12 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
       }
     const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
     const int d0 = DPL * (8 * wave + 4 * hh);
-    if (row_ok) {
+    const int R = Wc.rg * kTileRows + n;
+    if (R < G * Wc.qn) {
+      const int tok = R / G, gq = R - tok * G;
+      const bool whole = Wc.ps == Wc.ub && Wc.pe == Wc.ub + Wc.nblk;
       if (whole) {
-        uint16_t *orow = a.out + ((size_t)(o + tok) * a.num_q_heads + (size_t)h * G + gq) * D + d0;
+        uint16_t *orow = a.out + ((size_t)(Wc.o + tok) * a.num_q_heads + (size_t)Wc.h * G + gq) * D + d0;
         uint32_t pk[2 * DPL];
 #pragma unroll
         for (int t = 0; t < 2 * DPL; ++t) pk[t] = pack_bf16x2(ov[2 * t] * inv, ov[2 * t + 1] * inv);
@@ -515,7 +567,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
         for (int t = 0; t < DPL / 2; ++t)
           reinterpret_cast<uint4 *>(orow)[t] = make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]);
       } else {
-        const int slot = 2 * w + (u == first_unit ? 0 : 1);
+        const int slot = 2 * w + (Wc.u == first_unit ? 0 : 1);
         float *po = reinterpret_cast<float *>(a.ws + a.lay.part_o) + ((size_t)slot * kTileRows + n) * D + d0;
 #pragma unroll
         for (int t = 0; t < DPL; ++t)
@@ -527,16 +579,57 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
         }
       }
     }
-    start = ub + nblk;
-    ++u;
+  };
+
+  // one round g: issue the loads of round g+2 into `into` (freed by round
+  // g-1), compute round g from `cur`; true once the last unit is finished
+  auto round = [&](int g, KVBlock<D> &cur, KVBlock<D> &into) -> bool {
+    produce(into);
+    fetch_pages(g + 3);
+    // prefetch the next unit's Q once this unit is under way
+    if (Wc.has_next && qpf_u != Wc.u + 1 && g == Wc.g0 + 1) {
+      Walk Wn;
+      walk_enter(Wn, Wc.u + 1, Wc.next, start, end, 0, units, 0);
+      load_q_chunks<D>(a, Wn, wave, n, hh, qpf);
+      qpf_u = Wc.u + 1;
+    }
+    const int gb = Wc.ps + kAttnWaves * (g - Wc.g0) + wave;  // this wave's global block
+    if (gb < Wc.pe)
+      compute_block<D>(cur, &sm_q[0][lane], (gb - Wc.ub) * kBlockKeys, Wc.L, nk, anc, hh,
+                       a.scale_log2, m, l, acc);
+    if (g + 1 == Wc.g0 + Wc.nr) {
+      finish_unit();
+      if (!Wc.has_next) return true;
+      walk_to(Wc, g + 1, start, end, units, n_units);
+      enter_unit();
+      __syncthreads();  // the next unit's Q is in LDS; sm_o may be reused
+    }
+    return false;
+  };
+
+  enter_unit();
+  __syncthreads();
+  KVBlock<D> A, Bb, Cc;
+  fetch_pages(0);
+  produce(A);
+  fetch_pages(1);
+  produce(Bb);
+  fetch_pages(2);
+  for (int g = 0;; g += 3) {
+    if (round(g, A, Cc)) break;
+    if (round(g + 1, Bb, A)) break;
+    if (round(g + 2, Cc, Bb)) break;
   }
   if (bad_page) atomicOr(reinterpret_cast<unsigned *>(a.ws + a.lay.hdr), SV_DEV_BAD_PAGE);
 }
 
 }  // namespace
 
-void launch_verify_attn(const AttnArgs &a, int head_dim, hipStream_t stream) {
+void launch_verify_attn_plan(const AttnArgs &a, hipStream_t stream) {
   attn_plan_kernel<<<1, kPlanThreads, 0, stream>>>(a);
+}
+
+void launch_verify_attn_run(const AttnArgs &a, int head_dim, hipStream_t stream) {
   if (head_dim == 128) {
     verify_attn_kernel<128><<<a.grid, 64 * kAttnWaves, 0, stream>>>(a);
     attn_merge_kernel<128><<<a.grid, 256, 0, stream>>>(a);

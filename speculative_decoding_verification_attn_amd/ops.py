@@ -30,7 +30,8 @@ DEV_BAD_PARENT = 0x8
 DEV_BAD_PAGE = 0x10
 DEV_TOO_MANY_PAGES = 0x20
 
-EXPORTED = ["spec_verify_attn_workspace_size", "spec_verify_attn", "spec_verify_attn_device_status",
+EXPORTED = ["spec_verify_attn_workspace_size", "spec_verify_attn", "spec_verify_attn_plan",
+            "spec_verify_attn_run", "spec_verify_attn_device_status",
             "spec_accept_workspace_size", "spec_accept", "spec_accept_device_status",
             "kv_compact", "sv_status_string", "sv_last_error"]
 
@@ -57,6 +58,10 @@ def load_library():
     lib.spec_verify_attn_workspace_size.restype = SZ
     lib.spec_verify_attn.argtypes = [P, P, P, P, I, P, P, P, P, I, I, I, I, I, I, I, F, P, SZ, P]
     lib.spec_verify_attn.restype = I
+    lib.spec_verify_attn_run.argtypes = [P, P, P, P, I, P, P, P, P, I, I, I, I, I, I, I, F, P, SZ, P]
+    lib.spec_verify_attn_run.restype = I
+    lib.spec_verify_attn_plan.argtypes = [P, P, I, I, I, I, I, I, I, P, SZ, P]
+    lib.spec_verify_attn_plan.restype = I
     lib.spec_verify_attn_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
     lib.spec_verify_attn_device_status.restype = I
     lib.spec_accept_workspace_size.argtypes = [I, I, I]
@@ -109,9 +114,8 @@ def spec_verify_attn_workspace_size(batch, total_q, num_q_heads, num_kv_heads, h
                                                               num_kv_heads, head_dim))
 
 
-def spec_verify_attn(q, k_cache, v_cache, block_tables, context_lens, cu_q, tree_parent=None,
-                     out=None, softmax_scale=0.0, workspace=None, num_pages=None, stream=None):
-    """q [T,Hq,D] bf16; caches [pages,Hkv,16,D] bf16; returns out [T,Hq,D] bf16."""
+def _attn_call(fn, q, k_cache, v_cache, block_tables, context_lens, cu_q, tree_parent, out,
+               softmax_scale, workspace, num_pages, stream):
     lib = load_library()
     _dev(q, torch.bfloat16, "q")
     _dev(k_cache, torch.bfloat16, "k_cache")
@@ -131,12 +135,40 @@ def spec_verify_attn(q, k_cache, v_cache, block_tables, context_lens, cu_q, tree
     if workspace is None:
         workspace = torch.empty(spec_verify_attn_workspace_size(B, T, Hq, Hkv, D),
                                 dtype=torch.uint8, device=q.device)
-    _check(lib.spec_verify_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                                block_tables.shape[1], _ptr(context_lens), _ptr(cu_q),
-                                _ptr(tree_parent), _ptr(out), B, T, Hq, Hkv, D, P,
-                                pages if num_pages is None else num_pages, float(softmax_scale),
-                                _ptr(workspace), workspace.numel(), _stream(stream)))
+    _check(getattr(lib, fn)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                            block_tables.shape[1], _ptr(context_lens), _ptr(cu_q), _ptr(tree_parent),
+                            _ptr(out), B, T, Hq, Hkv, D, P, pages if num_pages is None else num_pages,
+                            float(softmax_scale), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+def spec_verify_attn(q, k_cache, v_cache, block_tables, context_lens, cu_q, tree_parent=None,
+                     out=None, softmax_scale=0.0, workspace=None, num_pages=None, stream=None):
+    """q [T,Hq,D] bf16; caches [pages,Hkv,16,D] bf16; returns out [T,Hq,D] bf16 (plan + run)."""
+    return _attn_call("spec_verify_attn", q, k_cache, v_cache, block_tables, context_lens, cu_q,
+                      tree_parent, out, softmax_scale, workspace, num_pages, stream)
+
+
+def spec_verify_attn_run(q, k_cache, v_cache, block_tables, context_lens, cu_q, tree_parent=None,
+                         out=None, softmax_scale=0.0, workspace=None, num_pages=None, stream=None):
+    """Verify attention with the plan already in `workspace` (see spec_verify_attn_plan)."""
+    if workspace is None:
+        raise ValueError("spec_verify_attn_run needs the workspace holding the plan")
+    return _attn_call("spec_verify_attn_run", q, k_cache, v_cache, block_tables, context_lens, cu_q,
+                      tree_parent, out, softmax_scale, workspace, num_pages, stream)
+
+
+def spec_verify_attn_plan(context_lens, cu_q, *, max_blocks_per_seq, num_q_heads, num_kv_heads,
+                          head_dim, num_pages, total_q, workspace, stream=None):
+    """Build the verify-attention plan for this batch into `workspace`."""
+    lib = load_library()
+    _dev(context_lens, torch.int32, "context_lens")
+    _dev(cu_q, torch.int32, "cu_q")
+    B = context_lens.shape[0]
+    _check(lib.spec_verify_attn_plan(_ptr(context_lens), _ptr(cu_q), int(max_blocks_per_seq), B,
+                                     int(total_q), int(num_q_heads), int(num_kv_heads), int(head_dim),
+                                     int(num_pages), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return workspace
 
 
 def spec_verify_attn_device_status(workspace, stream=None) -> int:

@@ -286,3 +286,24 @@ def test_empty_inputs_are_noops():
                           cu2, None)
     torch.cuda.synchronize()
     assert res[1].cpu().tolist() == [0, 0]
+
+
+def test_plan_once_run_per_layer():
+    """One plan serves several layers: each run equals the one-shot call bit for bit."""
+    case = W.make_custom(10, context_lens=[300, 5, 1200, 64], q_lens=[4, 9, 2, 6], hq=32, hkv=8, d=128)
+    dc = DevCase(case)
+    ws = torch.empty(ops.spec_verify_attn_workspace_size(case.batch, case.total_q, 32, 8, 128),
+                     dtype=torch.uint8, device=DEV)
+    ops.spec_verify_attn_plan(dc.ctx, dc.cu, max_blocks_per_seq=case.max_blocks, num_q_heads=32,
+                              num_kv_heads=8, head_dim=128, num_pages=case.num_pages,
+                              total_q=case.total_q, workspace=ws)
+    rng = np.random.default_rng(4)
+    for layer in range(3):
+        q = u16_to_bf16_dev(W.f32_to_bf16_bits(rng.standard_normal(case.q.shape).astype(np.float32)))
+        k = u16_to_bf16_dev(W.f32_to_bf16_bits(rng.standard_normal(case.k_cache.shape).astype(np.float32)))
+        v = u16_to_bf16_dev(W.f32_to_bf16_bits(rng.standard_normal(case.v_cache.shape).astype(np.float32)))
+        got = ops.spec_verify_attn_run(q, k, v, dc.bt, dc.ctx, dc.cu, None, workspace=ws)
+        ref = ops.spec_verify_attn(q, k, v, dc.bt, dc.ctx, dc.cu, None)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), layer
+    assert ops.spec_verify_attn_device_status(ws) == 0
