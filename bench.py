@@ -5,7 +5,8 @@ One step = the whole hot path over one batch: verify attention for every
 layer of the model (K/V of distinct layers rotate through `--kv-copies`
 resident caches), then full-vocabulary greedy acceptance, then KV compaction
 over the resident caches.  Inputs are seeded synthetic tensors already in HBM
-when the timed region starts.
+when the timed region starts.  Each phase is captured once as a HIP graph and
+replayed every step (--eager launches every kernel from the host instead).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 Default workload: Llama-3-70B attention geometry, batch 256, gamma 3
@@ -50,6 +51,8 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--batch", type=int, default=None, help="override the request count (batch sweeps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every kernel from the host each step instead of replaying HIP graphs")
     ap.add_argument("--cpu-sample-requests", type=int, default=16)
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MB "
@@ -124,34 +127,84 @@ def main():
         e.record(stream)
         return e
 
-    def step(record):
+    # the four phases of a step; `st` None = the current stream (a capturing
+    # stream inside graph capture)
+    def phase_plan(st):
         # one plan per step serves every layer (it depends only on the batch metadata)
-        e0 = mark() if record else None
         ops.spec_verify_attn_plan(ctx, cu, max_blocks_per_seq=bt.shape[1], num_q_heads=case.num_q_heads,
                                   num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
-                                  num_pages=case.num_pages, total_q=T, workspace=ws_attn, stream=stream)
+                                  num_pages=case.num_pages, total_q=T, workspace=ws_attn, stream=st)
+
+    def phase_layer(layer, st):
+        c = layer % copies
+        ops.spec_verify_attn_run(q, K[c], V[c], bt, ctx, cu, par, out=out, workspace=ws_attn, stream=st)
+
+    def phase_accept(st):
+        ops.spec_accept(logits, draft, cu, par, target_argmax=t_arg, accept_len=acc, accepted_path=path,
+                        out_tokens=toks, workspace=ws_acc, stream=st)
+
+    def phase_compact(st):
+        ops.kv_compact(K, V, bt, ctx, cu, path, acc, num_layers=copies, new_context_lens=new_len, stream=st)
+
+    def step_eager(record):
+        e0 = mark() if record else None
+        phase_plan(stream)
         if record:
             timings["plan"].append((e0, mark()))
         for layer in range(layers):
-            c = layer % copies
             e0 = mark() if record else None
-            ops.spec_verify_attn_run(q, K[c], V[c], bt, ctx, cu, par, out=out, workspace=ws_attn,
-                                     stream=stream)
+            phase_layer(layer, stream)
             if record:
                 timings["attn"].append((e0, mark()))
         e0 = mark() if record else None
-        ops.spec_accept(logits, draft, cu, par, target_argmax=t_arg, accept_len=acc, accepted_path=path,
-                        out_tokens=toks, workspace=ws_acc, stream=stream)
+        phase_accept(stream)
         e1 = mark() if record else None
-        ops.kv_compact(K, V, bt, ctx, cu, path, acc, num_layers=copies, new_context_lens=new_len, stream=stream)
+        phase_compact(stream)
         if record:
             timings["accept"].append((e0, e1))
             timings["compact"].append((e1, mark()))
 
     for _ in range(args.warmup):
-        step(False)
+        step_eager(False)
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
+
+    graphs = None
+    if not args.eager:
+        # One HIP graph per phase: a step replays them back to back, with
+        # timing events between the replays (outside the graphs).  Batch-1
+        # kernels run for a few microseconds, less than a host-side launch,
+        # so eager launches would leave the GPU idle between layers.
+        graphs = {k: torch.cuda.CUDAGraph() for k in ("plan", "attn", "accept", "compact")}
+        with torch.cuda.graph(graphs["plan"]):
+            phase_plan(None)
+        with torch.cuda.graph(graphs["attn"]):
+            for layer in range(layers):
+                phase_layer(layer, None)
+        with torch.cuda.graph(graphs["accept"]):
+            phase_accept(None)
+        with torch.cuda.graph(graphs["compact"]):
+            phase_compact(None)
+        for _ in range(2):
+            for k in ("plan", "attn", "accept", "compact"):
+                graphs[k].replay()
+        torch.cuda.synchronize()
+        log("captured one graph per phase")
+
+    def step_graph():
+        e0 = mark()
+        graphs["plan"].replay()
+        e1 = mark()
+        graphs["attn"].replay()
+        e2 = mark()
+        graphs["accept"].replay()
+        e3 = mark()
+        graphs["compact"].replay()
+        e4 = mark()
+        timings["plan"].append((e0, e1))
+        timings["attn"].append((e1, e2))
+        timings["accept"].append((e2, e3))
+        timings["compact"].append((e3, e4))
 
     # timed region: exactly `steps` steps, synchronized on both sides
     start = torch.cuda.Event(enable_timing=True)
@@ -159,7 +212,10 @@ def main():
     torch.cuda.synchronize()
     start.record(stream)
     for s in range(args.steps):
-        step(True)
+        if graphs is None:
+            step_eager(True)
+        else:
+            step_graph()
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
@@ -170,7 +226,7 @@ def main():
         return float(np.mean([a.elapsed_time(b) for a, b in pairs])) if pairs else float("nan")
 
     plan_ms = avg_ms(timings["plan"])
-    attn_ms = avg_ms(timings["attn"])
+    attn_ms = avg_ms(timings["attn"]) / (1 if graphs is None else layers)
     accept_ms = avg_ms(timings["accept"])
     compact_ms = avg_ms(timings["compact"])
     acc_np = acc.cpu().numpy()
@@ -211,6 +267,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; bf16 Q/K/V, fp32 logits)",
+        "launch": "eager" if graphs is None else "one HIP graph per phase (plan, layers, accept, compact)",
         "config": {"workload": WORKLOAD_TEXT.get(name, name), "name": name, "batch": B, "total_q": T,
                    "layers_per_step": layers, "kv_copies": copies,
                    "kv_bytes_per_layer": kv_bytes, "logits_bytes": logits_bytes},

@@ -308,21 +308,28 @@ __device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 *qop_lds, int
 
 // --------------------------------------------------------------------------
 // merge the partials of units cut by workgroup range boundaries.  A cut unit
-// u spans ranges w0 < w1; its merge is done by workgroup w0 + 1, the first
-// range that starts inside it, so each cut unit is merged exactly once and
-// the grid is only as large as the attention grid.  256 threads: row
-// n = tid/8, a run of D/8 output columns per thread.
+// u spans ranges w0 < w1; it is merged by the workgroups of merge slot
+// w0 + 1 (the first range that starts inside it), so each cut unit is merged
+// exactly once.  Each merge slot has kTileRows / kMergeRows workgroups of
+// kMergeRows waves and each wave merges one output row: one pass over the
+// unit's partials with a running log-sum-exp, every lane holding D/64
+// consecutive columns, so a row's partials are read as 64-lane contiguous
+// runs and a unit cut into many ranges is merged by many CUs at once.
 // --------------------------------------------------------------------------
+constexpr int kMergeRows = 4;
+
 template <int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  constexpr int DT = D / 8;
+__global__ __launch_bounds__(64 * kMergeRows) void attn_merge_kernel(AttnArgs a) {
+  constexpr int DPT = D / 64;
   const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.lay.hdr);
-  const int wm = blockIdx.x;
+  constexpr int kChunks = kTileRows / kMergeRows;
+  const int wm = blockIdx.x / kChunks;
   const UnitRec mr = reinterpret_cast<const UnitRec *>(a.ws + a.lay.merge_rec)[wm];
   if (wm >= hdr[1] || mr.a.x < 0) return;  // no cut unit to merge here
   const int w0 = mr.a.y, w1 = mr.a.z, side0 = mr.a.w;
   const int o = mr.b.x, qn = mr.b.y, h = mr.b.z, rowgroup = mr.b.w;
-  const int n = threadIdx.x >> 3, part = threadIdx.x & 7;
+  const int n = (blockIdx.x - wm * kChunks) * kMergeRows + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int G = a.group;
   const int R = rowgroup * kTileRows + n;
   if (R >= G * qn) return;
@@ -331,39 +338,36 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const float *po = reinterpret_cast<const float *>(a.ws + a.lay.part_o);
   // range w0 holds the unit's first block (its first or second partial
   // slot); every later range starts inside the unit (first slot)
-  float M = -INFINITY;
-  for (int w = w0; w <= w1; ++w) {
-    const int slot = 2 * w + (w == w0 ? side0 : 0);
-    M = fmaxf(M, pl[(size_t)slot * kTileRows + n]);
-  }
-  const float Mref = M == -INFINITY ? 0.f : M;
-  float accv[DT];
+  float M = -INFINITY, den = 0.f;
+  float acc[DPT];
 #pragma unroll
-  for (int t = 0; t < DT; ++t) accv[t] = 0.f;
-  float den = 0.f;
+  for (int t = 0; t < DPT; ++t) acc[t] = 0.f;
+#pragma unroll 4
   for (int w = w0; w <= w1; ++w) {
-    const int slot = 2 * w + (w == w0 ? side0 : 0);
-    const float wt = fast_exp2(pl[(size_t)slot * kTileRows + n] - Mref);
-    den += wt;
-    const float4 *src = reinterpret_cast<const float4 *>(po + ((size_t)slot * kTileRows + n) * D + part * DT);
-#pragma unroll
-    for (int t = 0; t < DT / 4; ++t) {
-      const float4 v = src[t];
-      accv[4 * t] += wt * v.x;
-      accv[4 * t + 1] += wt * v.y;
-      accv[4 * t + 2] += wt * v.z;
-      accv[4 * t + 3] += wt * v.w;
+    const size_t slot = 2 * (size_t)w + (w == w0 ? side0 : 0);
+    const float ls = pl[slot * kTileRows + n];
+    float v[DPT];
+    if constexpr (DPT == 2) {
+      const float2 x = reinterpret_cast<const float2 *>(po + (slot * kTileRows + n) * D)[lane];
+      v[0] = x.x;
+      v[1] = x.y;
+    } else {
+      v[0] = po[(slot * kTileRows + n) * D + lane];
     }
+    const float Mn = fmaxf(M, ls);
+    const float sc = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+    const float wt = ls == -INFINITY ? 0.f : fast_exp2(ls - Mn);
+    den = den * sc + wt;
+#pragma unroll
+    for (int t = 0; t < DPT; ++t) acc[t] = acc[t] * sc + wt * v[t];
+    M = Mn;
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
-  uint16_t *orow = a.out + ((size_t)(o + tok) * a.num_q_heads + (size_t)h * G + gq) * D + part * DT;
-#pragma unroll
-  for (int t = 0; t < DT / 8; ++t)
-    reinterpret_cast<uint4 *>(orow)[t] =
-        make_uint4(pack_bf16x2(accv[8 * t] * inv, accv[8 * t + 1] * inv),
-                   pack_bf16x2(accv[8 * t + 2] * inv, accv[8 * t + 3] * inv),
-                   pack_bf16x2(accv[8 * t + 4] * inv, accv[8 * t + 5] * inv),
-                   pack_bf16x2(accv[8 * t + 6] * inv, accv[8 * t + 7] * inv));
+  uint16_t *orow = a.out + ((size_t)(o + tok) * a.num_q_heads + (size_t)h * G + gq) * D;
+  if constexpr (DPT == 2)
+    reinterpret_cast<uint32_t *>(orow)[lane] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  else
+    orow[lane] = (uint16_t)bf16_bits(acc[0] * inv);
 }
 
 // --------------------------------------------------------------------------
@@ -607,14 +611,16 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
     return false;
   };
 
-  enter_unit();
-  __syncthreads();
+  // the first K/V loads go out before the Q operands are staged, so the
+  // two memory round trips overlap
   KVBlock<D> A, Bb, Cc;
   fetch_pages(0);
   produce(A);
   fetch_pages(1);
   produce(Bb);
   fetch_pages(2);
+  enter_unit();
+  __syncthreads();
   for (int g = 0;; g += 3) {
     if (round(g, A, Cc)) break;
     if (round(g + 1, Bb, A)) break;
@@ -632,10 +638,10 @@ void launch_verify_attn_plan(const AttnArgs &a, hipStream_t stream) {
 void launch_verify_attn_run(const AttnArgs &a, int head_dim, hipStream_t stream) {
   if (head_dim == 128) {
     verify_attn_kernel<128><<<a.grid, 64 * kAttnWaves, 0, stream>>>(a);
-    attn_merge_kernel<128><<<a.grid, 256, 0, stream>>>(a);
+    attn_merge_kernel<128><<<a.grid * (kTileRows / kMergeRows), 64 * kMergeRows, 0, stream>>>(a);
   } else {
     verify_attn_kernel<64><<<a.grid, 64 * kAttnWaves, 0, stream>>>(a);
-    attn_merge_kernel<64><<<a.grid, 256, 0, stream>>>(a);
+    attn_merge_kernel<64><<<a.grid * (kTileRows / kMergeRows), 64 * kMergeRows, 0, stream>>>(a);
   }
 }
 
