@@ -13,7 +13,8 @@ namespace sv {
 constexpr int kPage = 16;          // tokens per KV page
 constexpr int kMaxTokens = 64;     // verify tokens per request (one u64 ancestor word)
 constexpr int kBlockKeys = 32;     // keys per MFMA block (two pages)
-constexpr int kTileRows = 32;      // query rows per MFMA tile / per attention segment
+constexpr int kTileRows = 32;      // query rows per MFMA tile
+constexpr int kUnitTiles = 2;      // query tiles of one (request, KV head) sharing each K/V block
 constexpr int kAttnWaves = 4;      // waves per attention workgroup (they split the keys)
 constexpr int kMaxGrid = 512;      // persistent attention workgroups (one per CU, capped)
 constexpr int kMinBlocksPerWG = 4; // keep at least one 32-key block per wave
@@ -23,14 +24,16 @@ constexpr int kPlanLdsRequests = 4096;  // per-request plan data kept in LDS up 
 // ---------------------------------------------------------------------------
 // Verify-attention workspace layout (byte offsets, all 256-byte aligned).
 //
-// A "unit" is one (request, KV head, 32-row query tile) triple; its keys are
-// the request's ceil((L+q)/32) blocks of 32 keys.  All units' blocks form one
+// A "unit" is one (request, KV head, group of up to kUnitTiles 32-row query
+// tiles) triple; its keys are the request's ceil((L+q)/32) blocks of 32 keys,
+// and every block a unit loads serves all of its tiles.  All units' blocks form one
 // global block sequence, cut into equal contiguous ranges, one per
 // persistent workgroup.  A unit wholly inside one range is written straight
 // to the output; a unit cut by range boundaries leaves one partial per
-// workgroup that touched it (at most two per workgroup), merged afterwards.
+// workgroup that touched it (at most two per workgroup, each with one partial
+// per tile), merged afterwards.
 // ---------------------------------------------------------------------------
-// A unit record: {request, kv head, row tile, first global block} and
+// A unit record: {request, kv head, tile group, first global block} and
 // {first verify row o, verify tokens q, context L, blocks per unit}.
 struct UnitRec {
   int4 a;
@@ -44,8 +47,8 @@ struct AttnLayout {
   size_t wg_first;   // int32[kMaxGrid]: first unit of each workgroup's range
   size_t wg_rec;     // UnitRec[kMaxGrid]: a copy of that first unit's record
   size_t merge_rec;  // UnitRec[kMaxGrid]: {cut unit merged here or -1, w0, w1, side of w0}, {o, q, head, tile}
-  size_t part_lse;   // float[2*kMaxGrid][32] log2-sum-exp of partial rows
-  size_t part_o;     // float[2*kMaxGrid][32][D] normalised partial outputs
+  size_t part_lse;   // float[2*kMaxGrid][kUnitTiles][32] log2-sum-exp of partial rows
+  size_t part_o;     // float[2*kMaxGrid][kUnitTiles][32][D] normalised partial outputs
   size_t total;
   int unit_bound;
 };
@@ -56,7 +59,8 @@ __host__ __device__ inline AttnLayout attn_layout(int batch, int total_q, int nu
                                                   int num_kv_heads, int head_dim) {
   AttnLayout l;
   const int G = num_q_heads / num_kv_heads;
-  // row tiles: sum_i ceil(G*q_i/32) <= B + ceil(G*T/32)
+  // units per KV head: sum_i ceil(G*q_i/(32*kUnitTiles)) <= row tiles
+  // sum_i ceil(G*q_i/32) <= B + ceil(G*T/32)
   const long long tiles = (long long)batch + ((long long)G * total_q + kTileRows - 1) / kTileRows;
   l.unit_bound = (int)(tiles * num_kv_heads);
   size_t off = 0;
@@ -66,8 +70,8 @@ __host__ __device__ inline AttnLayout attn_layout(int batch, int total_q, int nu
   l.wg_first = off;   off = align256(off + size_t(kMaxGrid) * sizeof(int32_t));
   l.wg_rec = off;     off = align256(off + size_t(kMaxGrid) * sizeof(UnitRec));
   l.merge_rec = off;  off = align256(off + size_t(kMaxGrid) * sizeof(UnitRec));
-  l.part_lse = off;   off = align256(off + size_t(2 * kMaxGrid) * kTileRows * sizeof(float));
-  l.part_o = off;     off = align256(off + size_t(2 * kMaxGrid) * kTileRows * head_dim * sizeof(float));
+  l.part_lse = off;   off = align256(off + size_t(2 * kMaxGrid) * kUnitTiles * kTileRows * sizeof(float));
+  l.part_o = off;     off = align256(off + size_t(2 * kMaxGrid) * kUnitTiles * kTileRows * head_dim * sizeof(float));
   l.total = off;
   return l;
 }

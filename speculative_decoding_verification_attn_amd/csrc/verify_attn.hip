@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a) {
         ok = false;
       }
       if (ok && q > 0) {
-        rg = (G * q + kTileRows - 1) / kTileRows;
+        rg = (G * q + kTileRows * kUnitTiles - 1) / (kTileRows * kUnitTiles);
         nblk = (L + q + kBlockKeys - 1) / kBlockKeys;
         n_blocks = (long long)rg * Hkv * nblk;
       }
@@ -226,82 +226,89 @@ __device__ inline void load_block(KVBlock<D> &buf, const uint16_t *kh, const uin
   }
 }
 
-// One 32-key block: S^T = K.Q^T, mask, online softmax, O^T += V^T.P^T.
+// One 32-key block for each of the unit's nt query tiles: S^T = K.Q_t^T,
+// mask, online softmax, O_t^T += V^T.P_t^T.  The block's K and V registers
+// serve every tile, so K/V is read once per unit whatever its row count.
 template <int D>
-__device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 *qop_lds, int key0, int L, int nk,
-                                     uint64_t anc, int hh, float scale_log2, float &m, float &l,
-                                     floatx16 (&acc)[D / 32]) {
+__device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 *qop_lds, int nt, int key0, int L,
+                                     int nk, const uint64_t (&anc)[kUnitTiles], int hh, float scale_log2,
+                                     float (&m)[kUnitTiles], float (&l)[kUnitTiles],
+                                     floatx16 (&acc)[kUnitTiles][D / 32]) {
   constexpr int KK = D / 16, DPL = D / 32;
-  floatx16 s = floatx16{};
+  if (key0 + kBlockKeys > nk) {
+    // keys past the request: their V is stale memory (maybe non-finite)
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf.k[kk], qop_lds[kk * 64], s, 0, 0, 0);
-
-  // keys of acc reg r: key0 + 8*(r/4) + 4*hh + r%4
+    for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int c = 0; c < DPL / 2; ++c)
+            buf.v[m2][t][e][c] = key0 + 16 * m2 + 8 * t + 4 * hh + e < nk ? buf.v[m2][t][e][c] : 0u;
+  }
   const bool need_mask = key0 + kBlockKeys > L;
-  if (need_mask) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      const bool vis = key < L || (key < nk && ((anc >> (unsigned)(key - L)) & 1ull));
-      s[r] = vis ? s[r] * scale_log2 : -INFINITY;
-    }
-    if (key0 + kBlockKeys > nk) {
-      // keys past the request: their V is stale memory (maybe non-finite)
+  for (int tt = 0; tt < kUnitTiles; ++tt) {
+    if (tt >= nt) break;  // wave-uniform
+    floatx16 s = floatx16{};
 #pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2)
+    for (int kk = 0; kk < KK; ++kk)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf.k[kk], qop_lds[(tt * KK + kk) * 64], s, 0, 0, 0);
+
+    // keys of acc reg r: key0 + 8*(r/4) + 4*hh + r%4
+    if (need_mask) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int c = 0; c < DPL / 2; ++c)
-              buf.v[m2][t][e][c] = key0 + 16 * m2 + 8 * t + 4 * hh + e < nk ? buf.v[m2][t][e][c] : 0u;
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] *= scale_log2;
-  }
-  float mb = s[0];
-#pragma unroll
-  for (int r = 1; r < 16; ++r) mb = fmaxf(mb, s[r]);
-  mb = fmaxf(mb, __shfl_xor(mb, 32));
-  const float mnew = fmaxf(m, mb);
-  const float mref = mnew == -INFINITY ? 0.f : mnew;
-  if (__builtin_amdgcn_ballot_w64(mnew != m) != 0ull) {  // some row's running max moved
-    const float alpha = fast_exp2(m - mref);
-    l *= alpha;
-#pragma unroll
-    for (int c = 0; c < DPL; ++c) acc[c] *= alpha;
-  }
-  m = mnew;
-  float psum = 0.f;
-  uint32_t pw[8];
-#pragma unroll
-  for (int r = 0; r < 16; r += 2) {
-    const float p0 = fast_exp2(s[r] - mref);
-    const float p1 = fast_exp2(s[r + 1] - mref);
-    psum += p0 + p1;
-    pw[r >> 1] = pack_bf16x2(p0, p1);
-  }
-  l += psum;
-#pragma unroll
-  for (int m2 = 0; m2 < 2; ++m2) {
-    uint32_t w4p[4] = {pw[4 * m2], pw[4 * m2 + 1], pw[4 * m2 + 2], pw[4 * m2 + 3]};
-    const bf16x8 pop = __builtin_bit_cast(bf16x8, w4p);
-#pragma unroll
-    for (int c = 0; c < DPL; ++c) {
-      // k-slot 4t+e <-> key 16*m2 + 8t + 4hh + e; element c of the lane's d-run
-      uint32_t w4[4];
-#pragma unroll
-      for (int pr = 0; pr < 4; ++pr) {
-        const int s0 = 2 * pr, s1 = 2 * pr + 1;
-        const uint32_t x0 = buf.v[m2][s0 >> 2][s0 & 3][c >> 1];
-        const uint32_t x1 = buf.v[m2][s1 >> 2][s1 & 3][c >> 1];
-        w4[pr] = (c & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const bool vis = key < L || (key < nk && ((anc[tt] >> (unsigned)(key - L)) & 1ull));
+        s[r] = vis ? s[r] * scale_log2 : -INFINITY;
       }
-      const bf16x8 vop = __builtin_bit_cast(bf16x8, w4);
-      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, acc[c], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] *= scale_log2;
+    }
+    float mb = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mb = fmaxf(mb, s[r]);
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const float mnew = fmaxf(m[tt], mb);
+    const float mref = mnew == -INFINITY ? 0.f : mnew;
+    if (__builtin_amdgcn_ballot_w64(mnew != m[tt]) != 0ull) {  // some row's running max moved
+      const float alpha = fast_exp2(m[tt] - mref);
+      l[tt] *= alpha;
+#pragma unroll
+      for (int c = 0; c < DPL; ++c) acc[tt][c] *= alpha;
+    }
+    m[tt] = mnew;
+    float psum = 0.f;
+    uint32_t pw[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = fast_exp2(s[r] - mref);
+      const float p1 = fast_exp2(s[r + 1] - mref);
+      psum += p0 + p1;
+      pw[r >> 1] = pack_bf16x2(p0, p1);
+    }
+    l[tt] += psum;
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2) {
+      uint32_t w4p[4] = {pw[4 * m2], pw[4 * m2 + 1], pw[4 * m2 + 2], pw[4 * m2 + 3]};
+      const bf16x8 pop = __builtin_bit_cast(bf16x8, w4p);
+#pragma unroll
+      for (int c = 0; c < DPL; ++c) {
+        // k-slot 4t+e <-> key 16*m2 + 8t + 4hh + e; element c of the lane's d-run
+        uint32_t w4[4];
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+          const int s0 = 2 * pr, s1 = 2 * pr + 1;
+          const uint32_t x0 = buf.v[m2][s0 >> 2][s0 & 3][c >> 1];
+          const uint32_t x1 = buf.v[m2][s1 >> 2][s1 & 3][c >> 1];
+          w4[pr] = (c & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+        }
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, w4);
+        acc[tt][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, acc[tt][c], 0, 0, 0);
+      }
     }
   }
 }
@@ -311,10 +318,10 @@ __device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 *qop_lds, int
 // u spans ranges w0 < w1; it is merged by the workgroups of merge slot
 // w0 + 1 (the first range that starts inside it), so each cut unit is merged
 // exactly once.  Each merge slot has kTileRows / kMergeRows workgroups of
-// kMergeRows waves and each wave merges one output row: one pass over the
-// unit's partials with a running log-sum-exp, every lane holding D/64
-// consecutive columns, so a row's partials are read as 64-lane contiguous
-// runs and a unit cut into many ranges is merged by many CUs at once.
+// kMergeRows waves; a wave merges row n of each of the unit's tiles in turn:
+// one pass over the unit's partials with a running log-sum-exp, every lane
+// holding D/64 consecutive columns, so a row's partials are read as 64-lane
+// contiguous runs and a unit cut into many ranges is merged by many CUs.
 // --------------------------------------------------------------------------
 constexpr int kMergeRows = 4;
 
@@ -331,11 +338,12 @@ __global__ __launch_bounds__(64 * kMergeRows) void attn_merge_kernel(AttnArgs a)
   const int n = (blockIdx.x - wm * kChunks) * kMergeRows + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int G = a.group;
-  const int R = rowgroup * kTileRows + n;
-  if (R >= G * qn) return;
-  const int tok = R / G, gq = R - tok * G;
   const float *pl = reinterpret_cast<const float *>(a.ws + a.lay.part_lse);
   const float *po = reinterpret_cast<const float *>(a.ws + a.lay.part_o);
+  for (int tt = 0; tt < kUnitTiles; ++tt) {
+  const int R = (rowgroup * kUnitTiles + tt) * kTileRows + n;
+  if (R >= G * qn) return;
+  const int tok = R / G, gq = R - tok * G;
   // range w0 holds the unit's first block (its first or second partial
   // slot); every later range starts inside the unit (first slot)
   float M = -INFINITY, den = 0.f;
@@ -344,7 +352,7 @@ __global__ __launch_bounds__(64 * kMergeRows) void attn_merge_kernel(AttnArgs a)
   for (int t = 0; t < DPT; ++t) acc[t] = 0.f;
 #pragma unroll 4
   for (int w = w0; w <= w1; ++w) {
-    const size_t slot = 2 * (size_t)w + (w == w0 ? side0 : 0);
+    const size_t slot = (2 * (size_t)w + (w == w0 ? side0 : 0)) * kUnitTiles + tt;
     const float ls = pl[slot * kTileRows + n];
     float v[DPT];
     if constexpr (DPT == 2) {
@@ -368,6 +376,7 @@ __global__ __launch_bounds__(64 * kMergeRows) void attn_merge_kernel(AttnArgs a)
     reinterpret_cast<uint32_t *>(orow)[lane] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
   else
     orow[lane] = (uint16_t)bf16_bits(acc[0] * inv);
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -409,14 +418,14 @@ __device__ inline bool walk_to(Walk &W, int g, int start, int end, const UnitRec
   return true;
 }
 
-// Q^T operand chunks this wave stages for a unit: kk = wave*KQ .. +KQ-1, for
-// every lane's query row (lane n, half hh).
+// Q^T operand chunks this wave stages for tile tt of a unit: kk = wave*KQ ..
+// +KQ-1, for every lane's query row (lane n, half hh).
 template <int D>
-__device__ inline void load_q_chunks(const AttnArgs &a, const Walk &W, int wave, int n, int hh,
+__device__ inline void load_q_chunks(const AttnArgs &a, const Walk &W, int tt, int wave, int n, int hh,
                                      bf16x8 (&qc)[D / 64]) {
   constexpr int KQ = D / 64;
   const int G = a.group;
-  const int R = W.rg * kTileRows + n;
+  const int R = (W.rg * kUnitTiles + tt) * kTileRows + n;
   const bool row_ok = R < G * W.qn;
   const int tok = row_ok ? R / G : 0;
   const int gq = R - (R / G) * G;
@@ -436,12 +445,12 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   __shared__ float sm_o[kAttnWaves][DPL][16][64];
   __shared__ float sm_m[kAttnWaves][32];
   __shared__ float sm_l[kAttnWaves][32];
-  __shared__ bf16x8 sm_q[KK][64];  // Q^T operands, [kk][lane], shared by the waves
+  __shared__ bf16x8 sm_q[kUnitTiles][KK][64];  // Q^T operands, [tile][kk][lane], shared by the waves
 
   const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.lay.hdr);
   const int P = hdr[1];
   // consecutive ranges on the same XCD (workgroups are dealt round-robin to
-  // the 8 XCDs), so units that share K/V (query tiles of one head) meet in
+  // the 8 XCDs), so units that share K/V (tile groups of one head) meet in
   // one L2
   const int bx = blockIdx.x;
   const int w = (a.grid % 8 == 0) ? (bx % 8) * (a.grid / 8) + bx / 8 : bx;
@@ -463,43 +472,56 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   bool bad_page = false;
 
   // Two walks over the same pieces: the consumer at the round being
-  // computed, the producer three rounds ahead (it fetches page ids for round
-  // g+3 and issues the K/V loads of round g+2 into the buffer freed by round
+  // computed, the producer two rounds ahead (it fetches page ids for round
+  // g+2 and issues the K/V loads of round g+1 into the buffer freed by round
   // g-1), so K/V streaming runs on across unit boundaries.
   Walk Wc, Wp;
   walk_enter(Wc, first_unit, rec0, start, end, 0, units, n_units);
   Wp = Wc;
 
-  // per-unit consumer context
-  uint64_t anc = 0;
+  // per-unit consumer context, one entry per query tile of the unit
+  int nt = 1;  // tiles of the consumer's unit
+  uint64_t anc[kUnitTiles];
   int nk = 0;
-  float m = -INFINITY, l = 0.f;
-  floatx16 acc[DPL];
-  bf16x8 qpf[KQ];    // Q chunks prefetched for unit qpf_u
+  float m[kUnitTiles], l[kUnitTiles];
+  floatx16 acc[kUnitTiles][DPL];
+  bf16x8 qpf[KQ];    // tile-0 Q chunks prefetched for unit qpf_u
   int qpf_u = -1;
 
-  // enter the consumer's unit: ancestor mask of the lane's row and Q in LDS
+  // enter the consumer's unit: ancestor masks of the lane's rows and Q in LDS
   auto enter_unit = [&]() {
-    const int R = Wc.rg * kTileRows + n;
-    const bool row_ok = R < G * Wc.qn;
-    const int tok = row_ok ? R / G : 0;
     bool parents_ok;
     const uint64_t anc_all = ancestor_mask(a.tree_parent, Wc.o, Wc.qn, lane, &parents_ok);
-    // the shuffle must run on every lane: a source lane whose own row is past
-    // the end would be inactive and read back as zero
-    const uint64_t anc_tok = __shfl(anc_all, tok);
-    anc = row_ok ? anc_tok : 0ull;
     if (!parents_ok && threadIdx.x == 0 && Wc.ps == Wc.ub && Wc.h == 0 && Wc.rg == 0)
       atomicOr(reinterpret_cast<unsigned *>(a.ws + a.lay.hdr), SV_DEV_BAD_PARENT);
+    nt = min(kUnitTiles, (G * Wc.qn + kTileRows - 1) / kTileRows - Wc.rg * kUnitTiles);
+#pragma unroll
+    for (int tt = 0; tt < kUnitTiles; ++tt) {
+      const int R = (Wc.rg * kUnitTiles + tt) * kTileRows + n;
+      const bool row_ok = R < G * Wc.qn;
+      const int tok = row_ok ? R / G : 0;
+      // the shuffle must run on every lane: a source lane whose own row is
+      // past the end would be inactive and read back as zero
+      const uint64_t anc_tok = __shfl(anc_all, tok);
+      anc[tt] = row_ok ? anc_tok : 0ull;
+      m[tt] = -INFINITY;
+      l[tt] = 0.f;
+#pragma unroll
+      for (int c = 0; c < DPL; ++c) acc[tt][c] = floatx16{};
+    }
     nk = Wc.L + Wc.qn;
-    m = -INFINITY;
-    l = 0.f;
+    if (qpf_u != Wc.u) load_q_chunks<D>(a, Wc, 0, wave, n, hh, qpf);
 #pragma unroll
-    for (int c = 0; c < DPL; ++c) acc[c] = floatx16{};
-    if (qpf_u != Wc.u) load_q_chunks<D>(a, Wc, wave, n, hh, qpf);
-#pragma unroll
-    for (int j = 0; j < KQ; ++j) sm_q[wave * KQ + j][lane] = qpf[j];
+    for (int j = 0; j < KQ; ++j) sm_q[0][wave * KQ + j][lane] = qpf[j];
     qpf_u = -1;
+#pragma unroll
+    for (int tt = 1; tt < kUnitTiles; ++tt) {
+      if (tt >= nt) break;
+      bf16x8 qc[KQ];
+      load_q_chunks<D>(a, Wc, tt, wave, n, hh, qc);
+#pragma unroll
+      for (int j = 0; j < KQ; ++j) sm_q[tt][wave * KQ + j][lane] = qc[j];
+    }
   };
 
   // producer: page ids and head of the round it will load next
@@ -521,85 +543,92 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
                   pg_next, n, hh, page_stride);
   };
 
-  // finish the consumer's unit: merge the waves, write output or a partial
+  // finish the consumer's unit: per tile, merge the waves through LDS and
+  // write the output or a partial
   auto finish_unit = [&]() {
-    l += __shfl_xor(l, 32);  // both lane halves summed different keys of the same row
-    if (hh == 0) {
-      sm_m[wave][n] = m;
-      sm_l[wave][n] = l;
-    }
+    const bool whole = Wc.ps == Wc.ub && Wc.pe == Wc.ub + Wc.nblk;
+    const int side = Wc.u == first_unit ? 0 : 1;
 #pragma unroll
-    for (int c = 0; c < DPL; ++c)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sm_o[wave][c][r][lane] = acc[c][r];
-    __syncthreads();
-    float M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < kAttnWaves; ++ww) M = fmaxf(M, sm_m[ww][n]);
-    const float Mref = M == -INFINITY ? 0.f : M;
-    float f[kAttnWaves];
-    float Lsum = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kAttnWaves; ++ww) {
-      f[ww] = fast_exp2(sm_m[ww][n] - Mref);
-      Lsum += f[ww] * sm_l[ww][n];
-    }
-    // this wave finalises registers r = 4*wave .. 4*wave+3, i.e. output
-    // d = DPL*(8*wave + 4*hh) + (0 .. 4*DPL-1), contiguous
-    float ov[4 * DPL];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-      for (int c = 0; c < DPL; ++c) {
-        float v = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < kAttnWaves; ++ww) v += f[ww] * sm_o[ww][c][4 * wave + rr][lane];
-        ov[DPL * rr + c] = v;
+    for (int tt = 0; tt < kUnitTiles; ++tt) {
+      if (tt >= nt) break;
+      if (tt > 0) __syncthreads();  // every wave has read the previous tile's sm_o
+      const float lt = l[tt] + __shfl_xor(l[tt], 32);  // both lane halves summed different keys of a row
+      if (hh == 0) {
+        sm_m[wave][n] = m[tt];
+        sm_l[wave][n] = lt;
       }
-    const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
-    const int d0 = DPL * (8 * wave + 4 * hh);
-    const int R = Wc.rg * kTileRows + n;
-    if (R < G * Wc.qn) {
-      const int tok = R / G, gq = R - tok * G;
-      const bool whole = Wc.ps == Wc.ub && Wc.pe == Wc.ub + Wc.nblk;
-      if (whole) {
-        uint16_t *orow = a.out + ((size_t)(Wc.o + tok) * a.num_q_heads + (size_t)Wc.h * G + gq) * D + d0;
-        uint32_t pk[2 * DPL];
 #pragma unroll
-        for (int t = 0; t < 2 * DPL; ++t) pk[t] = pack_bf16x2(ov[2 * t] * inv, ov[2 * t + 1] * inv);
+      for (int c = 0; c < DPL; ++c)
 #pragma unroll
-        for (int t = 0; t < DPL / 2; ++t)
-          reinterpret_cast<uint4 *>(orow)[t] = make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]);
-      } else {
-        const int slot = 2 * w + (Wc.u == first_unit ? 0 : 1);
-        float *po = reinterpret_cast<float *>(a.ws + a.lay.part_o) + ((size_t)slot * kTileRows + n) * D + d0;
+        for (int r = 0; r < 16; ++r) sm_o[wave][c][r][lane] = acc[tt][c][r];
+      __syncthreads();
+      float M = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < DPL; ++t)
-          reinterpret_cast<float4 *>(po)[t] =
-              make_float4(ov[4 * t] * inv, ov[4 * t + 1] * inv, ov[4 * t + 2] * inv, ov[4 * t + 3] * inv);
-        if (wave == 0 && hh == 0) {
-          float *pl = reinterpret_cast<float *>(a.ws + a.lay.part_lse);
-          pl[(size_t)slot * kTileRows + n] = Lsum > 0.f ? Mref + fast_log2(Lsum) : -INFINITY;
+      for (int ww = 0; ww < kAttnWaves; ++ww) M = fmaxf(M, sm_m[ww][n]);
+      const float Mref = M == -INFINITY ? 0.f : M;
+      float f[kAttnWaves];
+      float Lsum = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kAttnWaves; ++ww) {
+        f[ww] = fast_exp2(sm_m[ww][n] - Mref);
+        Lsum += f[ww] * sm_l[ww][n];
+      }
+      // this wave finalises registers r = 4*wave .. 4*wave+3, i.e. output
+      // d = DPL*(8*wave + 4*hh) + (0 .. 4*DPL-1), contiguous
+      float ov[4 * DPL];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int c = 0; c < DPL; ++c) {
+          float v = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < kAttnWaves; ++ww) v += f[ww] * sm_o[ww][c][4 * wave + rr][lane];
+          ov[DPL * rr + c] = v;
+        }
+      const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
+      const int d0 = DPL * (8 * wave + 4 * hh);
+      const int R = (Wc.rg * kUnitTiles + tt) * kTileRows + n;
+      if (R < G * Wc.qn) {
+        const int tok = R / G, gq = R - tok * G;
+        if (whole) {
+          uint16_t *orow = a.out + ((size_t)(Wc.o + tok) * a.num_q_heads + (size_t)Wc.h * G + gq) * D + d0;
+          uint32_t pk[2 * DPL];
+#pragma unroll
+          for (int t = 0; t < 2 * DPL; ++t) pk[t] = pack_bf16x2(ov[2 * t] * inv, ov[2 * t + 1] * inv);
+#pragma unroll
+          for (int t = 0; t < DPL / 2; ++t)
+            reinterpret_cast<uint4 *>(orow)[t] = make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]);
+        } else {
+          const size_t slot = (2 * (size_t)w + side) * kUnitTiles + tt;
+          float *po = reinterpret_cast<float *>(a.ws + a.lay.part_o) + (slot * kTileRows + n) * D + d0;
+#pragma unroll
+          for (int t = 0; t < DPL; ++t)
+            reinterpret_cast<float4 *>(po)[t] =
+                make_float4(ov[4 * t] * inv, ov[4 * t + 1] * inv, ov[4 * t + 2] * inv, ov[4 * t + 3] * inv);
+          if (wave == 0 && hh == 0) {
+            float *pl = reinterpret_cast<float *>(a.ws + a.lay.part_lse);
+            pl[slot * kTileRows + n] = Lsum > 0.f ? Mref + fast_log2(Lsum) : -INFINITY;
+          }
         }
       }
     }
   };
 
-  // one round g: issue the loads of round g+2 into `into` (freed by round
+  // one round g: issue the loads of round g+1 into `into` (freed by round
   // g-1), compute round g from `cur`; true once the last unit is finished
   auto round = [&](int g, KVBlock<D> &cur, KVBlock<D> &into) -> bool {
     produce(into);
-    fetch_pages(g + 3);
-    // prefetch the next unit's Q once this unit is under way
+    fetch_pages(g + 2);
+    // prefetch the next unit's first Q tile once this unit is under way
     if (Wc.has_next && qpf_u != Wc.u + 1 && g == Wc.g0 + 1) {
       Walk Wn;
       walk_enter(Wn, Wc.u + 1, Wc.next, start, end, 0, units, 0);
-      load_q_chunks<D>(a, Wn, wave, n, hh, qpf);
+      load_q_chunks<D>(a, Wn, 0, wave, n, hh, qpf);
       qpf_u = Wc.u + 1;
     }
     const int gb = Wc.ps + kAttnWaves * (g - Wc.g0) + wave;  // this wave's global block
     if (gb < Wc.pe)
-      compute_block<D>(cur, &sm_q[0][lane], (gb - Wc.ub) * kBlockKeys, Wc.L, nk, anc, hh,
+      compute_block<D>(cur, &sm_q[0][0][lane], nt, (gb - Wc.ub) * kBlockKeys, Wc.L, nk, anc, hh,
                        a.scale_log2, m, l, acc);
     if (g + 1 == Wc.g0 + Wc.nr) {
       finish_unit();
@@ -613,18 +642,15 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
 
   // the first K/V loads go out before the Q operands are staged, so the
   // two memory round trips overlap
-  KVBlock<D> A, Bb, Cc;
+  KVBlock<D> A, Bb;
   fetch_pages(0);
   produce(A);
   fetch_pages(1);
-  produce(Bb);
-  fetch_pages(2);
   enter_unit();
   __syncthreads();
-  for (int g = 0;; g += 3) {
-    if (round(g, A, Cc)) break;
+  for (int g = 0;; g += 2) {
+    if (round(g, A, Bb)) break;
     if (round(g + 1, Bb, A)) break;
-    if (round(g + 2, Cc, Bb)) break;
   }
   if (bad_page) atomicOr(reinterpret_cast<unsigned *>(a.ws + a.lay.hdr), SV_DEV_BAD_PAGE);
 }
