@@ -57,7 +57,13 @@ def main():
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MB "
                          "(reference for the HBM traffic counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="no GPU run: turn the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE outputs of a "
+                         "--calibrate-copy-mb run into profiles/verify_attn_<config>_traffic.json")
     args = ap.parse_args()
+    if args.pmc_summary:
+        write_traffic_summary(args.config, *args.pmc_summary, copy_mb=args.calibrate_copy_mb or 1024)
+        return
 
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
@@ -254,6 +260,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, K[0], V[0], logits, args.cpu_sample_requests, layers)
 
+    traffic = measured_traffic(name)
     rec = {
         "metric": "verify-step µs/layer & KV-stream HBM GB/s (% peak), Llama-3-70B shape",
         "value": round(value, 2),
@@ -283,29 +290,90 @@ def main():
         "roofline": {"kernel": "spec_verify_attn_run (verify_attn_kernel + attn_merge_kernel, per layer)",
                      "bound": "hbm", "achieved": round(attn_gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(attn_gbs / PEAK_HBM_GBS, 4),
-                     "algorithmic_bytes": attn_bytes, "traffic": measured_traffic(name)},
+                     "algorithmic_bytes": attn_bytes,
+                     "traffic": None if traffic is None else traffic["total_bytes"],
+                     "traffic_detail": traffic},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+TRAFFIC_SOURCES = ["speculative_decoding_verification_attn_amd/csrc/verify_attn.hip",
+                   "speculative_decoding_verification_attn_amd/csrc/sv_device.h",
+                   "speculative_decoding_verification_attn_amd/csrc/sv_internal.h"]
+
+
+def _sources_sha256(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
+def _pmc_per_kernel(run_dir, counter):
+    """({kernel name: [value per dispatch]}, value of the last dispatch) from a
+    rocprofv3 --pmc csv directory."""
+    import csv
+    import glob
+    out, last = {}, (-1, None)
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                v = float(r["Counter_Value"])
+                out.setdefault(r["Kernel_Name"], []).append(v)
+                if int(r["Dispatch_Id"]) > last[0]:
+                    last = (int(r["Dispatch_Id"]), v)
+    if not out:
+        raise SystemExit(f"no {counter} records under {run_dir}")
+    return out, last[1]
+
+
+def write_traffic_summary(name, fetch_dir, write_dir, copy_mb):
+    """HBM traffic per launch of the attention kernel: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) scaled by what the same counters read for
+    the plain device copy of copy_mb MiB that the profiled run ends with."""
+    # the calibration copy is the profiled run's last dispatch
+    fetch, fetch_copy = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
+    write, write_copy = _pmc_per_kernel(write_dir, "WRITE_SIZE")
+    copy_bytes = copy_mb * (1 << 20)
+    fetch_scale = copy_bytes / (fetch_copy * 1024.0)
+    write_scale = copy_bytes / (write_copy * 1024.0)
+    kname = next(k for k in fetch if "verify_attn_kernel" in k)
+    f_kib = float(np.mean(fetch[kname]))
+    w_kib = float(np.mean(write[kname]))
+    rec = {
+        "kernel": kname, "workload": name,
+        "source_sha256": _sources_sha256(TRAFFIC_SOURCES), "sources": TRAFFIC_SOURCES,
+        "fetch_kib_per_launch": round(f_kib, 1), "write_kib_per_launch": round(w_kib, 1),
+        "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+        "read_bytes_per_launch": int(f_kib * 1024 * fetch_scale),
+        "write_bytes_per_launch": int(w_kib * 1024 * write_scale),
+        "calibration": {"copy_bytes": copy_bytes, "fetch_kib": round(fetch_copy, 1),
+                        "write_kib": round(write_copy, 1)},
+        "other_kernels_kib_per_launch": {k: {"fetch": round(float(np.mean(v)), 1),
+                                             "write": round(float(np.mean(write.get(k, [0]))), 1)}
+                                         for k, v in fetch.items() if "sv::" in k and k != kname},
+    }
+    path = os.path.join(ROOT, "profiles", f"verify_attn_{name}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def measured_traffic(name):
     """HBM bytes per launch of the attention kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on this
     workload and on the current kernel sources; else None."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"verify_attn_{name}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    h = hashlib.sha256()
-    for f in rec["sources"]:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if h.hexdigest() != rec["source_sha256"]:
+    if _sources_sha256(rec["sources"]) != rec["source_sha256"]:
         return None
     return {"read_bytes": rec["read_bytes_per_launch"], "write_bytes": rec["write_bytes_per_launch"],
             "total_bytes": rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"],
-            "source": "rocprofv3 --pmc FETCH_SIZE x%.4f, WRITE_SIZE x%.1f (plain-copy calibration)"
+            "source": "rocprofv3 --pmc FETCH_SIZE x%.4f, WRITE_SIZE x%.4f (plain-copy calibration)"
                       % (rec["fetch_scale"], rec["write_scale"])}
 
 
