@@ -108,7 +108,8 @@ size_t spec_verify_attn_workspace_size(int batch, int total_q, int num_q_heads, 
  *   cu_q         int32 [batch+1] prefix sums of q_i
  *   tree_parent  int32 [total_q] local parents, or NULL for chains
  *   out          bf16 [total_q, num_q_heads, head_dim]; must not overlap q/k/v
- *   softmax_scale  0 selects 1/sqrt(head_dim)
+ *   softmax_scale  > 0, or 0 for 1/sqrt(head_dim); negative or non-finite
+ *                  values return SV_ERR_SHAPE
  *   workspace    device buffer of at least spec_verify_attn_workspace_size()
  *                bytes (contents need no initialisation; overwritten)
  * Supported: head_dim 64 or 128, page_size 16, num_q_heads % num_kv_heads == 0

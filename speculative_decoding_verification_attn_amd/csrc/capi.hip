@@ -142,8 +142,8 @@ int attn_data(const void *q, const void *k_cache, const void *v_cache, const int
               void *out, int head_dim, int page_size, float softmax_scale, sv::AttnArgs *a) {
   if (!q || !k_cache || !v_cache || !out)
     return fail(SV_ERR_NULL, "spec_verify_attn: a required pointer is NULL");
-  if (!(softmax_scale == 0.0f || isfinite(softmax_scale)))
-    return fail(SV_ERR_SHAPE, "softmax_scale must be finite");
+  if (!(softmax_scale >= 0.0f && isfinite(softmax_scale)))
+    return fail(SV_ERR_SHAPE, "softmax_scale must be finite and >= 0 (0 selects 1/sqrt(head_dim))");
   const size_t qo_bytes = (size_t)a->total_q * a->num_q_heads * head_dim * 2;
   const size_t kv_bytes = (size_t)a->num_pages * a->num_kv_heads * page_size * head_dim * 2;
   if (overlaps(out, qo_bytes, q, qo_bytes) || overlaps(out, qo_bytes, k_cache, kv_bytes) ||

@@ -19,8 +19,23 @@ __device__ inline uint32_t bf16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, b);
 }
 
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// {lo, hi} rounded to bf16 (nearest even) in one packed conversion
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+  const bf16x2v b = __builtin_convertvector((float2v){lo, hi}, bf16x2v);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// low halves of x0 and x1 as {x0.lo, x1.lo} (lo16 of the result from x0)
+__device__ inline uint32_t pack_lo16(uint32_t x0, uint32_t x1) {
+  return __builtin_amdgcn_perm(x1, x0, 0x05040100u);
+}
+
+// high halves of x0 and x1 as {x0.hi, x1.hi}
+__device__ inline uint32_t pack_hi16(uint32_t x0, uint32_t x1) {
+  return __builtin_amdgcn_perm(x1, x0, 0x07060302u);
 }
 
 // Ancestor-or-self bitmask of token `lane` of a request with q tokens whose

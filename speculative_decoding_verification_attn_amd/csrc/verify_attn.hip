@@ -229,6 +229,8 @@ __device__ inline void load_block(KVBlock<D> &buf, const uint16_t *kh, const uin
 // One 32-key block for each of the unit's nt query tiles: S^T = K.Q_t^T,
 // mask, online softmax, O_t^T += V^T.P_t^T.  The block's K and V registers
 // serve every tile, so K/V is read once per unit whatever its row count.
+constexpr float kRescaleSlack = 8.0f;  // log2 units
+
 template <int D>
 __device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 *qop_lds, int nt, int key0, int L,
                                      int nk, const uint64_t (&anc)[kUnitTiles], int hh, float scale_log2,
@@ -256,37 +258,40 @@ __device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 *qop_lds, int
     for (int kk = 0; kk < KK; ++kk)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf.k[kk], qop_lds[(tt * KK + kk) * 64], s, 0, 0, 0);
 
-    // keys of acc reg r: key0 + 8*(r/4) + 4*hh + r%4
+    // keys of acc reg r: key0 + 8*(r/4) + 4*hh + r%4.  Scores stay unscaled
+    // here; the (positive) scale is folded into the exponent below, and the
+    // running max m is kept in the scaled log2 domain.
     if (need_mask) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
         const bool vis = key < L || (key < nk && ((anc[tt] >> (unsigned)(key - L)) & 1ull));
-        s[r] = vis ? s[r] * scale_log2 : -INFINITY;
+        s[r] = vis ? s[r] : -INFINITY;
       }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] *= scale_log2;
     }
     float mb = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mb = fmaxf(mb, s[r]);
     mb = fmaxf(mb, __shfl_xor(mb, 32));
-    const float mnew = fmaxf(m[tt], mb);
-    const float mref = mnew == -INFINITY ? 0.f : mnew;
-    if (__builtin_amdgcn_ballot_w64(mnew != m[tt]) != 0ull) {  // some row's running max moved
-      const float alpha = fast_exp2(m[tt] - mref);
+    // Lazy rescaling: the reference max m only moves (and the accumulators
+    // are rescaled) once some row's block max exceeds it by more than
+    // kRescaleSlack; until then p <= 2^kRescaleSlack, exact in fp32 sums
+    // and bf16 P.  m is also taken on the first visible key (m = -inf).
+    const float mcand = fmaxf(m[tt], mb * scale_log2);
+    if (__builtin_amdgcn_ballot_w64(mcand > m[tt] + kRescaleSlack) != 0ull) {
+      const float alpha = fast_exp2(m[tt] - (mcand == -INFINITY ? 0.f : mcand));
       l[tt] *= alpha;
 #pragma unroll
       for (int c = 0; c < DPL; ++c) acc[tt][c] *= alpha;
+      m[tt] = mcand;
     }
-    m[tt] = mnew;
+    const float mref = m[tt] == -INFINITY ? 0.f : m[tt];
     float psum = 0.f;
     uint32_t pw[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float p0 = fast_exp2(s[r] - mref);
-      const float p1 = fast_exp2(s[r + 1] - mref);
+      const float p0 = fast_exp2(__builtin_fmaf(s[r], scale_log2, -mref));
+      const float p1 = fast_exp2(__builtin_fmaf(s[r + 1], scale_log2, -mref));
       psum += p0 + p1;
       pw[r >> 1] = pack_bf16x2(p0, p1);
     }
@@ -304,7 +309,7 @@ __device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 *qop_lds, int
           const int s0 = 2 * pr, s1 = 2 * pr + 1;
           const uint32_t x0 = buf.v[m2][s0 >> 2][s0 & 3][c >> 1];
           const uint32_t x1 = buf.v[m2][s1 >> 2][s1 & 3][c >> 1];
-          w4[pr] = (c & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+          w4[pr] = (c & 1) ? pack_hi16(x0, x1) : pack_lo16(x0, x1);
         }
         const bf16x8 vop = __builtin_bit_cast(bf16x8, w4);
         acc[tt][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, acc[tt][c], 0, 0, 0);

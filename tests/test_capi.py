@@ -70,6 +70,7 @@ def test_verify_attn_validation(lib):
     assert attn(lib, mb=0) == ops.SV_ERR_SHAPE
     assert attn(lib, wsb=16) == ops.SV_ERR_WORKSPACE
     assert attn(lib, scale=float("inf")) == ops.SV_ERR_SHAPE
+    assert attn(lib, scale=-0.125) == ops.SV_ERR_SHAPE    # the scale is folded into exp2 args
     assert attn(lib, out=FAKE) == ops.SV_ERR_ALIAS       # out overlaps q
     attn(lib, D=96)
     assert b"head_dim" in lib.sv_last_error()
