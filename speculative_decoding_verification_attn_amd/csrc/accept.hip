@@ -69,15 +69,17 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_partial_kernel(AcceptAr
   Best b{-INFINITY, -1};
   if ((V & 3) == 0) {
     // each thread walks its float4s in increasing index order; strict '>'
-    // keeps the lowest index among equal values within the thread
+    // keeps the lowest index among equal values within the thread.  Every
+    // load instruction covers 1 KB of the row contiguously and no byte is
+    // read twice, so the loads are nontemporal (streamed, not kept).
     const int nv = (hi - lo) >> 2;
-    const float4 *x4 = reinterpret_cast<const float4 *>(x + lo);
+    const float4v *x4 = reinterpret_cast<const float4v *>(x + lo);
     constexpr int U = 4;
     int k = threadIdx.x;
     for (; k + (U - 1) * kArgmaxThreads < nv; k += U * kArgmaxThreads) {
-      float4 v[U];
+      float4v v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = x4[k + u * kArgmaxThreads];
+      for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(x4 + k + u * kArgmaxThreads);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int base = lo + 4 * (k + u * kArgmaxThreads);
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_partial_kernel(AcceptAr
       }
     }
     for (; k < nv; k += kArgmaxThreads) {
-      const float4 v = x4[k];
+      const float4v v = __builtin_nontemporal_load(x4 + k);
       const int base = lo + 4 * k;
       if (b.i < 0 || v.x > b.v) { b.v = v.x; b.i = base; }
       if (v.y > b.v) { b.v = v.y; b.i = base + 1; }

@@ -21,6 +21,8 @@ __device__ inline uint32_t bf16_bits(float x) {
 
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
 
 // {lo, hi} rounded to bf16 (nearest even) in one packed conversion
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {

@@ -200,6 +200,12 @@ __device__ inline int2 block_pages(const_i32_ptr bt, int b, int npages, int num_
   return make_int2(p0, p1);
 }
 
+// K and V take different cache policies.  A V load instruction covers whole
+// rows (32 lanes x DPL*2 B = D*2 B contiguous), so it is issued nontemporal:
+// streamed through the caches without being kept.  A K load instruction
+// covers only 32 B of each of 32 rows (one key per lane, as the MFMA A
+// operand needs), and the rest of each line is read by the next three
+// instructions, so K uses ordinary loads that keep the line for them.
 template <int D>
 __device__ inline void load_block(KVBlock<D> &buf, const uint16_t *kh, const uint16_t *vh,
                                   int2 pg, int n, int hh, size_t page_stride) {
@@ -216,11 +222,11 @@ __device__ inline void load_block(KVBlock<D> &buf, const uint16_t *kh, const uin
       for (int e = 0; e < 4; ++e) {
         const uint16_t *vrow = vpage + (size_t)(8 * t + 4 * hh + e) * D;
         if constexpr (DPL == 4) {
-          const uint2 x = *reinterpret_cast<const uint2 *>(vrow);
+          const u32x2v x = __builtin_nontemporal_load(reinterpret_cast<const u32x2v *>(vrow));
           buf.v[m2][t][e][0] = x.x;
           buf.v[m2][t][e][1] = x.y;
         } else {
-          buf.v[m2][t][e][0] = *reinterpret_cast<const uint32_t *>(vrow);
+          buf.v[m2][t][e][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(vrow));
         }
       }
   }
