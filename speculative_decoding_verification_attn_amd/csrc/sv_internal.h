@@ -18,6 +18,13 @@ constexpr int kUnitTiles = 2;      // query tiles of one (request, KV head) shar
 constexpr int kAttnWaves = 4;      // waves per attention workgroup (they split the keys)
 constexpr int kMaxGrid = 512;      // persistent attention workgroups (one per CU, capped)
 constexpr int kMinBlocksPerWG = 4; // keep at least one 32-key block per wave
+// Range sizing charges each unit start (after the first) this many blocks:
+// finishing a unit (merging it across the waves, writing it out) and entering
+// the next one stalls a workgroup's stream for two to three rounds of four
+// blocks (measured per-workgroup time grows by 4.4-7 us per unit entered, a
+// round takes about 2.7 us); a sweep of 4, 8, 12 and 16 put 12 at or near the
+// best on every workload measured.
+constexpr int kUnitStartCost = 12;
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanLdsRequests = 4096;  // per-request plan data kept in LDS up to this batch
 
@@ -27,8 +34,8 @@ constexpr int kPlanLdsRequests = 4096;  // per-request plan data kept in LDS up 
 // A "unit" is one (request, KV head, group of up to kUnitTiles 32-row query
 // tiles) triple; its keys are the request's ceil((L+q)/32) blocks of 32 keys,
 // and every block a unit loads serves all of its tiles.  All units' blocks form one
-// global block sequence, cut into equal contiguous ranges, one per
-// persistent workgroup.  A unit wholly inside one range is written straight
+// global block sequence, cut into contiguous ranges of equal cost (blocks plus
+// a fixed charge per unit start), one per persistent workgroup.  A unit wholly inside one range is written straight
 // to the output; a unit cut by range boundaries leaves one partial per
 // workgroup that touched it (at most two per workgroup, each with one partial
 // per tile), merged afterwards.
@@ -44,6 +51,7 @@ struct AttnLayout {
   size_t hdr;        // int32[8]: 0 status bits, 1 active workgroups P, 2 total blocks, 3 units
   size_t req_meta;   // int32[4][B]: unit base, block base, row tiles, blocks per unit (large batches)
   size_t units;      // UnitRec[unit_bound]
+  size_t wg_start;   // int32[kMaxGrid + 1]: first global block of each workgroup's range
   size_t wg_first;   // int32[kMaxGrid]: first unit of each workgroup's range
   size_t wg_rec;     // UnitRec[kMaxGrid]: a copy of that first unit's record
   size_t merge_rec;  // UnitRec[kMaxGrid]: {cut unit merged here or -1, w0, w1, side of w0}, {o, q, head, tile}
@@ -67,6 +75,7 @@ __host__ __device__ inline AttnLayout attn_layout(int batch, int total_q, int nu
   l.hdr = off;        off = align256(off + 8 * sizeof(int32_t));
   l.req_meta = off;   off = align256(off + size_t(batch) * 16);
   l.units = off;      off = align256(off + size_t(l.unit_bound) * sizeof(UnitRec));
+  l.wg_start = off;   off = align256(off + size_t(kMaxGrid + 1) * sizeof(int32_t));
   l.wg_first = off;   off = align256(off + size_t(kMaxGrid) * sizeof(int32_t));
   l.wg_rec = off;     off = align256(off + size_t(kMaxGrid) * sizeof(UnitRec));
   l.merge_rec = off;  off = align256(off + size_t(kMaxGrid) * sizeof(UnitRec));

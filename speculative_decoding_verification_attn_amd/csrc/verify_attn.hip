@@ -45,10 +45,16 @@ namespace sv {
 
 namespace {
 
-// index of the workgroup whose range [start(w), start(w+1)) holds block x,
-// where start(w) = floor(w*NB/P)
-__device__ inline int wg_of_block(long long x, long long nb, int p) {
-  return (int)(((x + 1) * p - 1) / nb);
+// index of the workgroup whose range [start[w], start[w+1]) holds block x:
+// the last w < p with start[w] <= x (a workgroup with an empty range shares
+// its start with the next one and is never returned)
+__device__ inline int wg_of_block(const int32_t *start, int p, int x) {
+  int lo = 0, hi = p - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (start[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
 }
 
 // --------------------------------------------------------------------------
@@ -62,6 +68,7 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a) {
   __shared__ int s_req[4][kPlanLdsRequests];
   int32_t *hdr = reinterpret_cast<int32_t *>(a.ws + a.lay.hdr);
   UnitRec *units = reinterpret_cast<UnitRec *>(a.ws + a.lay.units);
+  int32_t *wg_start = reinterpret_cast<int32_t *>(a.ws + a.lay.wg_start);
   int32_t *wg_first = reinterpret_cast<int32_t *>(a.ws + a.lay.wg_first);
   UnitRec *wg_rec = reinterpret_cast<UnitRec *>(a.ws + a.lay.wg_rec);
   UnitRec *merge_rec = reinterpret_cast<UnitRec *>(a.ws + a.lay.merge_rec);
@@ -136,29 +143,62 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a) {
         units[u0 + k] = UnitRec{make_int4(i, h, r, b0 + k * nblk), make_int4(o, qn, L, nblk)};
       }
     }
-    // pass 3: per workgroup w, the unit holding start(w) = floor(w*nb/P) (the
-    // request whose block span holds it, by binary search) with a copy of its
-    // record, and the cut unit this workgroup merges afterwards: the unit
-    // whose first block lies in range w-1 and which continues into range w
+    // pass 3: range boundaries.  Block x costs 1 and the start of every unit
+    // after the first costs kUnitStartCost more, so the cost before block x
+    // is F(x) = x + kUnitStartCost * (index of x's unit).  Workgroup w starts
+    // at the first block with F >= w * F_total / P: the request by binary
+    // search over F at its first block, the unit and block by division.
+    const long long kc = kUnitStartCost;
+    const long long ftot = nb + kc * (unit_carry > 0 ? unit_carry - 1 : 0);
+    for (int w = tid; w <= P && nb > 0; w += kPlanThreads) {
+      if (w == P) {
+        wg_start[w] = (int)nb;
+        continue;
+      }
+      const long long c = (long long)w * ftot / P;
+      int lo = 0, hi = B - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (bbase[mid] + kc * ubase[mid] <= c) lo = mid; else hi = mid - 1;
+      }
+      // requests without units share their bases with the next request, so
+      // the last request at or before c has units unless c precedes them all
+      long long x = 0;
+      if (rgs[lo] > 0) {
+        const long long span = nblks[lo] + kc;  // cost of one unit with its start
+        const long long off = c - (bbase[lo] + kc * ubase[lo]);
+        const long long k = min(off / span, (long long)rgs[lo] * Hkv - 1);
+        const long long r = off - k * span;  // >= 0
+        x = bbase[lo] + k * nblks[lo] + min(r, (long long)nblks[lo]);
+      }
+      wg_start[w] = (int)min(x, nb);
+    }
+    __syncthreads();
+    // pass 4: per workgroup w, the unit holding its first block (the request
+    // whose block span holds it, by binary search) with a copy of its record,
+    // and the cut unit this workgroup merges afterwards: the unit whose first
+    // block lies in range w0 = w-1 and which continues into range w.  (A range
+    // is empty only when its cost share falls inside one unit-start charge;
+    // it then starts at a unit start and has no record.)
     for (int w = tid; w < P && nb > 0; w += kPlanThreads) {
-      const long long st = (long long)w * nb / P;
+      const int st = min(wg_start[w], (int)nb - 1);
       int lo = 0, hi = B - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (bbase[mid] <= st) lo = mid; else hi = mid - 1;
       }
       const int nblk = nblks[lo], rg = rgs[lo];
-      const int k = (int)((st - bbase[lo]) / nblk);
+      const int k = (st - bbase[lo]) / nblk;
       const int u = ubase[lo] + k;
       const int h = k / rg, r = k - h * rg;
       const int ub = bbase[lo] + k * nblk;
       const int o = a.cu_q[lo], qn = a.cu_q[lo + 1] - o, L = a.context_lens[lo];
       wg_first[w] = u;
       wg_rec[w] = UnitRec{make_int4(lo, h, r, ub), make_int4(o, qn, L, nblk)};
-      const int w0 = wg_of_block(ub, nb, P);
+      const int w0 = wg_of_block(wg_start, P, ub);
       if (w >= 1 && w0 == w - 1) {
-        const int w1 = wg_of_block((long long)ub + nblk - 1, nb, P);
-        const int side0 = ((long long)w0 * nb / P == ub) ? 0 : 1;
+        const int w1 = wg_of_block(wg_start, P, ub + nblk - 1);
+        const int side0 = wg_start[w0] == ub ? 0 : 1;
         merge_rec[w] = UnitRec{make_int4(u, w0, w1, side0), make_int4(o, qn, h, r)};
       } else {
         merge_rec[w] = UnitRec{make_int4(-1, 0, 0, 0), make_int4(0, 0, 0, 0)};
@@ -356,7 +396,9 @@ __global__ __launch_bounds__(64 * kMergeRows) void attn_merge_kernel(AttnArgs a)
   if (R >= G * qn) return;
   const int tok = R / G, gq = R - tok * G;
   // range w0 holds the unit's first block (its first or second partial
-  // slot); every later range starts inside the unit (first slot)
+  // slot); every later range starts inside the unit (first slot).  No range
+  // between w0 and w1 is empty: distinct cost targets inside one unit map to
+  // distinct blocks, so an empty range can only begin at a unit start.
   float M = -INFINITY, den = 0.f;
   float acc[DPT];
 #pragma unroll
@@ -396,6 +438,21 @@ __global__ __launch_bounds__(64 * kMergeRows) void attn_merge_kernel(AttnArgs a)
 // A unit piece of one workgroup's block range, placed on the workgroup's
 // sequence of rounds (in round r of a piece, wave w takes global block
 // ps + 4r + w).  Everything here is wave-uniform.
+// Unit records are written by the plan launch and only read here, so they are
+// read through the scalar cache: a vector load would be counted by vmcnt,
+// and waiting for it (its value is needed at once) would also wait for every
+// K/V load issued before it.
+struct const_unit_ptr {
+  const_i32_ptr p;  // UnitRec[]: 8 int32 each
+  __device__ UnitRec operator[](int u) const {
+    const const_i32_ptr q = p + 8 * (size_t)u;
+    UnitRec r;
+    r.a = make_int4(q[0], q[1], q[2], q[3]);
+    r.b = make_int4(q[4], q[5], q[6], q[7]);
+    return r;
+  }
+};
+
 struct Walk {
   int u, i, h, rg, ub, o, qn, L, nblk;
   int ps, pe;  // global blocks [ps, pe) of the unit processed by this workgroup
@@ -405,7 +462,7 @@ struct Walk {
 };
 
 __device__ inline void walk_enter(Walk &W, int u, const UnitRec &r, int start, int end, int g0,
-                                  const UnitRec *units, int n_units) {
+                                  const_unit_ptr units, int n_units) {
   W.u = u;
   W.i = r.a.x; W.h = r.a.y; W.rg = r.a.z; W.ub = r.a.w;
   W.o = r.b.x; W.qn = r.b.y; W.L = r.b.z; W.nblk = r.b.w;
@@ -419,7 +476,7 @@ __device__ inline void walk_enter(Walk &W, int u, const UnitRec &r, int start, i
 
 // Moves the walk forward until round g lies in its piece; false if g is past
 // the workgroup's last piece (the walk then stays on the last piece).
-__device__ inline bool walk_to(Walk &W, int g, int start, int end, const UnitRec *units,
+__device__ inline bool walk_to(Walk &W, int g, int start, int end, const_unit_ptr units,
                                int n_units) {
   while (g >= W.g0 + W.nr) {
     if (!W.has_next) return false;
@@ -458,7 +515,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   __shared__ float sm_l[kAttnWaves][32];
   __shared__ bf16x8 sm_q[kUnitTiles][KK][64];  // Q^T operands, [tile][kk][lane], shared by the waves
 
-  const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.lay.hdr);
+  // header words 1..3 are not written by this launch (word 0 only, by atomics)
+  const const_i32_ptr hdr = (const_i32_ptr)(uintptr_t)(a.ws + a.lay.hdr);
   const int P = hdr[1];
   // consecutive ranges on the same XCD (workgroups are dealt round-robin to
   // the 8 XCDs), so units that share K/V (tile groups of one head) meet in
@@ -466,12 +524,12 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   const int bx = blockIdx.x;
   const int w = (a.grid % 8 == 0) ? (bx % 8) * (a.grid / 8) + bx / 8 : bx;
   if (w >= P) return;
-  const long long nb = hdr[2];
-  const int start = (int)((long long)w * nb / P);
-  const int end = (int)((long long)(w + 1) * nb / P);
-  const UnitRec *units = reinterpret_cast<const UnitRec *>(a.ws + a.lay.units);
-  const int first_unit = reinterpret_cast<const int32_t *>(a.ws + a.lay.wg_first)[w];
-  const UnitRec rec0 = reinterpret_cast<const UnitRec *>(a.ws + a.lay.wg_rec)[w];
+  const const_i32_ptr wg_start = (const_i32_ptr)(uintptr_t)(a.ws + a.lay.wg_start);
+  const int start = wg_start[w];
+  const int end = wg_start[w + 1];
+  const const_unit_ptr units{(const_i32_ptr)(uintptr_t)(a.ws + a.lay.units)};
+  const int first_unit = ((const_i32_ptr)(uintptr_t)(a.ws + a.lay.wg_first))[w];
+  const UnitRec rec0 = const_unit_ptr{(const_i32_ptr)(uintptr_t)(a.ws + a.lay.wg_rec)}[w];
   const int n_units = hdr[3];
   if (first_unit < 0 || first_unit >= n_units || start >= end) return;  // not for a consistent plan
 
