@@ -7,24 +7,25 @@
 // request's committed context [0, L_i) and to those verify tokens that lie on
 // its own root path, all read through the request's block table.
 //
-// Work decomposition.  A unit is one (request, KV head, 32-row query tile);
-// the rows of a tile are (token, query head) pairs of that KV head's group,
-// token-major, so every K/V block a unit reads serves all its rows (GQA
-// sharing).  Every unit's keys form ceil((L+q)/32) blocks of 32 keys; all
-// units' blocks, in (request, head, tile) order, make one global sequence that
-// is cut into equal contiguous ranges, one per persistent workgroup (one per
-// CU).  Equal ranges balance ragged batches exactly; only the first and last
-// unit of a range can be cut, so at most two partial results per workgroup
-// need merging.
+// Work decomposition.  A unit is one (request, KV head, group of up to two
+// 32-row query tiles); the rows of a tile are (token, query head) pairs of that
+// KV head's group, token-major, so every K/V block a unit reads serves all its
+// rows (GQA sharing) in both tiles.  Every unit's keys form ceil((L+q)/32)
+// blocks of 32 keys; all units' blocks, in (request, head, tile group) order,
+// make one global sequence that is cut into contiguous ranges of equal cost
+// (blocks plus a fixed charge per unit start), one per persistent workgroup
+// (one per CU).  Only the first and last unit of a range can be cut, so at most
+// two partial results per workgroup need merging.
 //
 // Three launches:
-//   attn_plan_kernel     one workgroup: validates per-request metadata and
-//                        writes the unit table and each workgroup's first unit;
-//   verify_attn_kernel   the persistent workgroups; four waves (one per SIMD)
-//                        stream disjoint 32-key blocks straight from HBM into
-//                        MFMA operand registers, three blocks in flight per
-//                        wave, with an fp32 online softmax per query row, then
-//                        merge through LDS;
+//   attn_plan_kernel     one workgroup, once per step: validates per-request
+//                        metadata and writes the unit table, each workgroup's
+//                        range and first unit, and the merge records;
+//   verify_attn_kernel   the persistent workgroups, once per layer; four waves
+//                        (one per SIMD) stream disjoint 32-key blocks straight
+//                        from HBM into MFMA operand registers, one block in
+//                        flight beside the one computed, with an fp32 online
+//                        softmax per query row, then merge through LDS;
 //   attn_merge_kernel    log-sum-exp merge of the partials of cut units.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, A 32xK, B Kx32, C 32x32):
@@ -510,7 +511,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   constexpr int KK = D / 16;   // k-steps of the S^T product (16 d each)
   constexpr int KQ = D / 64;   // Q chunks staged per wave
   static_assert(D == 64 || D == 128, "head_dim");
-  __shared__ float sm_o[kAttnWaves][DPL][16][64];
+  // O^T accumulators of the waves, four registers per 16-byte entry:
+  // [wave][tile column c][register group j][lane] holds registers 4j..4j+3
+  __shared__ float4v sm_o[kAttnWaves][DPL][4][64];
   __shared__ float sm_m[kAttnWaves][32];
   __shared__ float sm_l[kAttnWaves][32];
   __shared__ bf16x8 sm_q[kUnitTiles][KK][64];  // Q^T operands, [tile][kk][lane], shared by the waves
@@ -629,7 +632,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
       for (int c = 0; c < DPL; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sm_o[wave][c][r][lane] = acc[tt][c][r];
+        for (int j = 0; j < 4; ++j)
+          sm_o[wave][c][j][lane] = float4v{acc[tt][c][4 * j], acc[tt][c][4 * j + 1], acc[tt][c][4 * j + 2],
+                                           acc[tt][c][4 * j + 3]};
       __syncthreads();
       float M = -INFINITY;
 #pragma unroll
@@ -646,13 +651,14 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
       // d = DPL*(8*wave + 4*hh) + (0 .. 4*DPL-1), contiguous
       float ov[4 * DPL];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
+      for (int i = 0; i < 4 * DPL; ++i) ov[i] = 0.f;
 #pragma unroll
-        for (int c = 0; c < DPL; ++c) {
-          float v = 0.f;
+      for (int c = 0; c < DPL; ++c)
 #pragma unroll
-          for (int ww = 0; ww < kAttnWaves; ++ww) v += f[ww] * sm_o[ww][c][4 * wave + rr][lane];
-          ov[DPL * rr + c] = v;
+        for (int ww = 0; ww < kAttnWaves; ++ww) {
+          const float4v x = sm_o[ww][c][wave][lane];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) ov[DPL * rr + c] += f[ww] * x[rr];
         }
       const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
       const int d0 = DPL * (8 * wave + 4 * hh);
