@@ -49,6 +49,7 @@ def _bind(path):
     lib.oracle_argmax.argtypes = [P, LL, LL, P]
     lib.oracle_accept.argtypes = [P, P, P, P, I, P, P, P]
     lib.oracle_compact.argtypes = [P, P, LL, I, P, I, P, P, P, P, P, I, I, I, I, I]
+    lib.oracle_accept_chunk_step.argtypes = [P, P, P, P, P, P, I, I, P, P, P, P, P]
     for f in (lib.oracle_verify_attn, lib.oracle_decode_attn, lib.oracle_argmax,
               lib.oracle_accept, lib.oracle_compact):
         f.restype = I
@@ -143,6 +144,60 @@ def accept(draft_tokens, target, cu_q, tree_parent):
     _check(lib.oracle_accept(_ptr(draft_tokens), _ptr(target), _ptr(cu_q), _ptr(tree_parent), B,
                              _ptr(acc), _ptr(path), _ptr(toks)), "oracle_accept")
     return acc, path, toks
+
+
+def accept_chunk_step(draft_tokens, target, cu_q, tree_parent, chunk_begin, chunk_len, chunk_size,
+                      accept_len, accepted_path, out_tokens):
+    """One step of chunked acceptance with early pruning (see oracle_accept_chunk_step).
+    Updates accept_len / accepted_path / out_tokens in place for requests that end;
+    returns (next_begin [B], next_len [B])."""
+    lib = _lib_override or _load()
+    draft_tokens = _c(draft_tokens, np.int32); target = _c(target, np.int32)
+    cu_q = _c(cu_q, np.int32); tree_parent = _c(tree_parent, np.int32)
+    chunk_begin = _c(chunk_begin, np.int32); chunk_len = _c(chunk_len, np.int32)
+    for a in (accept_len, accepted_path, out_tokens):
+        assert a.dtype == np.int32 and a.flags["C_CONTIGUOUS"]
+    B = len(cu_q) - 1
+    nb = np.empty(B, dtype=np.int32)
+    nl = np.empty(B, dtype=np.int32)
+    _check(lib.oracle_accept_chunk_step(_ptr(draft_tokens), _ptr(target), _ptr(cu_q), _ptr(tree_parent),
+                                        _ptr(chunk_begin), _ptr(chunk_len), B, int(chunk_size),
+                                        _ptr(accept_len), _ptr(accepted_path), _ptr(out_tokens),
+                                        _ptr(nb), _ptr(nl)), "oracle_accept_chunk_step")
+    return nb, nl
+
+
+def accept_chunked(draft_tokens, target, cu_q, tree_parent, chunk_size, *, hide_unverified=True):
+    """The whole chunk loop: first chunk = tokens [0, min(chunk_size, q_i)), then
+    accept_chunk_step until no request has rows left.  With hide_unverified, each
+    step sees target[] only for the tokens verified so far (the rest set to -2).
+    Returns (accept_len, accepted_path, out_tokens, steps) where steps lists the
+    (chunk_begin, chunk_len) of every chunk."""
+    cu_q = np.asarray(cu_q, dtype=np.int32)
+    target = np.asarray(target, dtype=np.int32)
+    B = len(cu_q) - 1
+    T = int(cu_q[-1])
+    q = np.diff(cu_q)
+    acc = np.full(B, -9, dtype=np.int32)
+    path = np.full(T, -9, dtype=np.int32)
+    toks = np.full(T, -9, dtype=np.int32)
+    begin = np.zeros(B, dtype=np.int32)
+    length = np.minimum(q, chunk_size).astype(np.int32)
+    seen = np.zeros(T, dtype=bool)
+    steps = []
+    while length.sum() > 0:
+        if len(steps) > 64:  # every chunk verifies >= 1 new token of <= 64
+            raise OracleError("chunk loop makes no progress")
+        steps.append((begin.copy(), length.copy()))
+        for i in range(B):
+            seen[cu_q[i] + begin[i]: cu_q[i] + begin[i] + length[i]] = True
+        t = np.where(seen, target, -2).astype(np.int32) if hide_unverified else target
+        begin, length = accept_chunk_step(draft_tokens, t, cu_q, tree_parent, begin, length, chunk_size,
+                                          acc, path, toks)
+    for i in range(B):
+        if q[i] == 0:
+            acc[i] = 0
+    return acc, path, toks, steps
 
 
 def compact(k_cache, v_cache, block_tables, context_lens, cu_q, accepted_path, accept_len, *,

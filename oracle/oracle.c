@@ -19,6 +19,8 @@
  *    drafted prefixes in parallel and accepts the longest matching prefix.
  *  - FASER, "Per-Request Length Adaptation": each request in a batch carries
  *    its own draft length gamma_i.
+ *  - FASER, "Early Token Pruning": verification over chunks of the verify
+ *    tokens drops, at each chunk boundary, the tokens behind a rejected prefix.
  *  - SSD, section on integrating recent inference optimisations: the engine
  *    uses PagedAttention, i.e. a paged KV cache addressed through per-request
  *    block tables.
@@ -269,6 +271,84 @@ int oracle_accept(const int32_t *draft, const int32_t *target, const int32_t *cu
             accepted_path[o + k] = path[k];
             out_tokens[o + k] = target[o + path[k]];
         }
+        free(path);
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * One step of chunked verification with early pruning (FASER, "Early Token
+ * Pruning": verification runs over chunks of the verify tokens, and at each
+ * chunk boundary the tokens behind an already rejected prefix are dropped).
+ * Request i verified tokens [0, e) so far, e = chunk_begin[i] + chunk_len[i];
+ * target[] is read for those tokens only.  For a token j >= 1 with parent p,
+ * the edge p -> j is decided when p < e and then matches iff
+ * draft[o+j] == target[o+p].  Token j is alive iff no decided edge on its
+ * root path fails to match.
+ *   - chunk_len[i] == 0: the request is not in this chunk; nothing changes
+ *     (next_len = 0, next_begin = chunk_begin).
+ *   - e < q_i and some token in [e, q_i) is alive: the request goes on,
+ *     next_begin = e, next_len = min(chunk_size, q_i - e).
+ *   - otherwise it ends: the result of oracle_accept computed with the
+ *     tokens < e only (a token >= e counts as not accepted), next_len = 0,
+ *     next_begin = e.
+ */
+int oracle_accept_chunk_step(const int32_t *draft, const int32_t *target, const int32_t *cu_q,
+                             const int32_t *tree_parent, const int32_t *chunk_begin,
+                             const int32_t *chunk_len, int batch, int chunk_size,
+                             int32_t *accept_len, int32_t *accepted_path, int32_t *out_tokens,
+                             int32_t *next_begin, int32_t *next_len) {
+    if (chunk_size <= 0) return ORACLE_BAD_ARG;
+    for (int i = 0; i < batch; ++i) {
+        const int o = cu_q[i];
+        const int qn = cu_q[i + 1] - cu_q[i];
+        const int s = chunk_begin[i], c = chunk_len[i];
+        if (qn < 0 || s < 0 || c < 0 || s + c > qn) return ORACLE_BAD_CONTENT;
+        if (c == 0) { next_begin[i] = s; next_len[i] = 0; continue; }
+        if (!check_parents(tree_parent, o, qn)) return ORACLE_BAD_CONTENT;
+        const int e = s + c;
+        /* alive tokens: walk every token's root path over the decided edges */
+        int go_on = 0;
+        for (int j = e; j < qn && !go_on; ++j) {
+            int alive = 1;
+            for (int a = j; a > 0; a = parent_of(tree_parent, o, a)) {
+                const int p = parent_of(tree_parent, o, a);
+                if (p < e && draft[o + a] != target[o + p]) { alive = 0; break; }
+            }
+            go_on = alive;
+        }
+        if (go_on) {
+            next_begin[i] = e;
+            next_len[i] = qn - e < chunk_size ? qn - e : chunk_size;
+            continue;
+        }
+        /* the request ends: greedy acceptance over the tokens < e */
+        for (int k = 0; k < qn; ++k) { accepted_path[o + k] = -1; out_tokens[o + k] = -1; }
+        int *acc = (int *)malloc(sizeof(int) * (size_t)qn);
+        int *depth = (int *)malloc(sizeof(int) * (size_t)qn);
+        int *path = (int *)malloc(sizeof(int) * (size_t)qn);
+        if (!acc || !depth || !path) { free(acc); free(depth); free(path); return ORACLE_NO_MEMORY; }
+        acc[0] = 1;
+        depth[0] = 0;
+        for (int j = 1; j < qn; ++j) {
+            const int p = parent_of(tree_parent, o, j);
+            acc[j] = j < e && acc[p] && draft[o + j] == target[o + p];
+            depth[j] = depth[p] + 1;
+        }
+        int best = 0;
+        for (int j = 1; j < qn; ++j)
+            if (acc[j] && depth[j] > depth[best]) { best = j; }
+        const int n = depth[best];
+        for (int a = best, k = n; a >= 0; a = parent_of(tree_parent, o, a), --k) path[k] = a;
+        accept_len[i] = n + 1;
+        for (int k = 0; k <= n; ++k) {
+            accepted_path[o + k] = path[k];
+            out_tokens[o + k] = target[o + accepted_path[o + k]];
+        }
+        next_begin[i] = e;
+        next_len[i] = 0;
+        free(acc);
+        free(depth);
         free(path);
     }
     return ORACLE_OK;

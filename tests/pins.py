@@ -407,7 +407,90 @@ def check_compact():
     assert np.array_equal(kk, ch.k_cache) and np.array_equal(vv, ch.v_cache)
 
 
+# ----------------------------------------------------------------------------
+# chunked acceptance with early pruning (FASER, "Early Token Pruning")
+# ----------------------------------------------------------------------------
+def _pack(requests):
+    """requests: list of (parent or None, draft, target) -> packed arrays."""
+    qs = [len(r[1]) for r in requests]
+    cu = np.zeros(len(qs) + 1, np.int32)
+    cu[1:] = np.cumsum(qs)
+    draft = np.concatenate([r[1] for r in requests]).astype(np.int32)
+    target = np.concatenate([r[2] for r in requests]).astype(np.int32)
+    trees = [r[0] for r in requests]
+    parent = None if all(t is None for t in trees) else np.concatenate(
+        [t if t is not None else chain_parent(len(r[1])) for t, r in zip(trees, requests)]).astype(np.int32)
+    return cu, draft, target, parent
+
+
+def check_chunk_chain_closed_form():
+    """Chains with gamma <= 6, every match pattern, every chunk size: the chunk loop
+    accepts exactly what unchunked acceptance does, and it verifies
+    ceil(m / c) chunks, m = index of the first mismatching draft (q if none)."""
+    for c in range(1, 8):
+        reqs, expect_steps = [], []
+        for gamma in range(0, 7):
+            for pattern in itertools.product([0, 1], repeat=gamma):
+                q = gamma + 1
+                tgt = np.arange(100, 100 + q, dtype=np.int32)
+                d = np.empty(q, np.int32)
+                d[0] = 7
+                for j in range(1, q):
+                    d[j] = tgt[j - 1] if pattern[j - 1] else tgt[j - 1] + 1000
+                m = next((j + 1 for j, b in enumerate(pattern) if not b), q)
+                reqs.append((None, d, tgt))
+                expect_steps.append(-(-min(m, q) // c))
+        cu, draft, target, _ = _pack(reqs)
+        full = oracle.accept(draft, target, cu, None)
+        acc, path, toks, steps = oracle.accept_chunked(draft, target, cu, None, c)
+        assert np.array_equal(acc, full[0]) and np.array_equal(path, full[1]) and np.array_equal(toks, full[2])
+        chunks_per_request = np.sum([l > 0 for _, l in steps], axis=0)
+        assert chunks_per_request.tolist() == expect_steps, c
+
+
+def _brute_alive(parent, draft, target, e, j):
+    """Node j is alive if every edge on its root path whose parent was verified (< e) matches."""
+    a = j
+    while parent[a] >= 0:
+        p = parent[a]
+        if p < e and draft[a] != target[p]:
+            return False
+        a = p
+    return True
+
+
+def check_chunk_tree_lossless_and_pruning(max_nodes=6):
+    """All topologically ordered trees up to max_nodes nodes x all edge-match patterns x
+    every chunk size: the chunk loop ends with the unchunked result, and after every
+    chunk a request goes on iff some unverified node is still alive (brute force)."""
+    for c in range(1, max_nodes + 1):
+        reqs = []
+        for n in range(1, max_nodes + 1):
+            for par in all_trees(n):
+                for pattern in itertools.product([0, 1], repeat=n - 1):
+                    tgt = np.arange(10, 10 + n, dtype=np.int32) * 3
+                    d = np.empty(n, np.int32)
+                    d[0] = 1
+                    for j in range(1, n):
+                        d[j] = tgt[par[j]] if pattern[j - 1] else tgt[par[j]] + 1
+                    reqs.append((par, d, tgt))
+        cu, draft, target, parent = _pack(reqs)
+        full = oracle.accept(draft, target, cu, parent)
+        acc, path, toks, steps = oracle.accept_chunked(draft, target, cu, parent, c)
+        assert np.array_equal(acc, full[0]) and np.array_equal(path, full[1]) and np.array_equal(toks, full[2])
+        # pruning decisions of every step against brute force
+        for k, (begin, length) in enumerate(steps):
+            nxt = steps[k + 1][1] if k + 1 < len(steps) else np.zeros_like(length)
+            for i, (par, d, tgt) in enumerate(reqs):
+                if length[i] == 0:
+                    continue
+                e = begin[i] + length[i]
+                alive = any(_brute_alive(par, d, tgt, e, j) for j in range(e, len(par)))
+                assert (nxt[i] > 0) == alive, (c, i, k)
+
+
 ALL_CHECKS = [check_attn_vs_sdpa, check_attn_closed_forms, check_attn_convexity,
               check_attn_decode_equivalence, check_decode_closed_form,
               check_attn_page_permutation_and_degenerate_tree, check_argmax,
-              check_accept_chain_exhaustive, check_accept_tree_bruteforce, check_compact]
+              check_accept_chain_exhaustive, check_accept_tree_bruteforce, check_compact,
+              check_chunk_chain_closed_form, check_chunk_tree_lossless_and_pruning]

@@ -35,6 +35,16 @@ MUTANTS = [
     ("decode_range", "const int nk = pos + 1;", "const int nk = pos;"),
     ("softmax_sign", "s[p] = exp(s[p] - m); /* masked: exp(-inf) = 0 */",
      "s[p] = exp(m - s[p]); /* masked: exp(-inf) = 0 */"),
+    ("chunk_alive_own_edge_only", "for (int a = j; a > 0; a = parent_of(tree_parent, o, a)) {",
+     "for (int a = j; a == j && a > 0; a = parent_of(tree_parent, o, a)) {"),
+    ("chunk_skips_first_unverified", "for (int j = e; j < qn && !go_on; ++j)",
+     "for (int j = e + 1; j < qn && !go_on; ++j)"),
+    ("chunk_next_len_unclamped", "next_len[i] = qn - e < chunk_size ? qn - e : chunk_size;",
+     "next_len[i] = chunk_size;"),
+    ("chunk_tie_break", "if (acc[j] && depth[j] > depth[best]) { best = j; }",
+     "if (acc[j] && depth[j] >= depth[best]) { best = j; }"),
+    ("chunk_next_begin_overlaps", "next_begin[i] = e;\n            next_len[i] = qn - e",
+     "next_begin[i] = e - 1;\n            next_len[i] = qn - e"),
 ]
 
 
