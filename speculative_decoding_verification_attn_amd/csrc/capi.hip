@@ -124,6 +124,21 @@ int attn_common(const int32_t *block_tables, int max_blocks_per_seq, const int32
   a->group = num_q_heads / num_kv_heads;
   a->max_blocks = max_blocks_per_seq;
   a->num_pages = num_pages;
+  a->cu_full = cu_q;
+  a->total_full = total_q;
+  return ok();
+}
+
+// Chunked rows: cu_rows packs the rows, cu_full and total_full all verify
+// tokens; chunk_begin gives each request's first token among the rows.
+int attn_chunk(const int32_t *cu_full, int total_full, const int32_t *chunk_begin, int batch,
+               sv::AttnArgs *a) {
+  if (!cu_full || !chunk_begin) return fail(SV_ERR_NULL, "chunked verify: cu_q or chunk_begin is NULL");
+  if (total_full < 0 || total_full > (long long)batch * sv::kMaxTokens)
+    return fail(SV_ERR_SHAPE, "total_q %d must be in [0, batch*64]", total_full);
+  a->chunk_begin = chunk_begin;
+  a->cu_full = cu_full;
+  a->total_full = total_full;
   return ok();
 }
 
@@ -217,6 +232,45 @@ int spec_verify_attn(const void *q, const void *k_cache, const void *v_cache,
   return check_launch("spec_verify_attn");
 }
 
+int spec_verify_attn_chunk_plan(const int32_t *context_lens, const int32_t *cu_q, int total_q,
+                                const int32_t *chunk_begin, const int32_t *cu_chunk, int total_chunk,
+                                int max_blocks_per_seq, int batch, int num_q_heads, int num_kv_heads,
+                                int head_dim, int num_pages, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  sv::AttnArgs a;
+  bool empty;
+  int rc = attn_common(nullptr, max_blocks_per_seq, context_lens, cu_chunk, batch, total_chunk,
+                       num_q_heads, num_kv_heads, head_dim, sv::kPage, num_pages, workspace,
+                       workspace_bytes, false, &a, &empty);
+  if (rc != SV_OK || empty) return rc;
+  if ((rc = attn_chunk(cu_q, total_q, chunk_begin, batch, &a)) != SV_OK) return rc;
+  if ((rc = set_grid(&a)) != SV_OK) return rc;
+  sv::launch_verify_attn_plan(a, static_cast<hipStream_t>(stream));
+  return check_launch("spec_verify_attn_chunk_plan");
+}
+
+int spec_verify_attn_chunk_run(const void *q, const void *k_cache, const void *v_cache,
+                               const int32_t *block_tables, int max_blocks_per_seq,
+                               const int32_t *context_lens, const int32_t *cu_q, int total_q,
+                               const int32_t *chunk_begin, const int32_t *cu_chunk, int total_chunk,
+                               const int32_t *tree_parent, void *out, int batch, int num_q_heads,
+                               int num_kv_heads, int head_dim, int page_size, int num_pages,
+                               float softmax_scale, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  sv::AttnArgs a;
+  bool empty;
+  int rc = attn_common(block_tables, max_blocks_per_seq, context_lens, cu_chunk, batch, total_chunk,
+                       num_q_heads, num_kv_heads, head_dim, page_size, num_pages, workspace,
+                       workspace_bytes, true, &a, &empty);
+  if (rc != SV_OK || empty) return rc;
+  if ((rc = attn_chunk(cu_q, total_q, chunk_begin, batch, &a)) != SV_OK) return rc;
+  rc = attn_data(q, k_cache, v_cache, tree_parent, out, head_dim, page_size, softmax_scale, &a);
+  if (rc != SV_OK) return rc;
+  if ((rc = set_grid(&a)) != SV_OK) return rc;
+  sv::launch_verify_attn_run(a, head_dim, static_cast<hipStream_t>(stream));
+  return check_launch("spec_verify_attn_chunk_run");
+}
+
 int spec_verify_attn_device_status(const void *workspace, uint32_t *flags, void *stream) {
   return read_status(workspace, 0, flags, stream);
 }
@@ -251,6 +305,7 @@ int spec_accept(const float *logits, int vocab, const int32_t *draft_tokens, con
       overlaps(accept_len, (size_t)batch * 4, out_tokens, tb))
     return fail(SV_ERR_ALIAS, "spec_accept outputs overlap");
   sv::AcceptArgs a;
+  memset(&a, 0, sizeof a);
   a.logits = logits;
   a.draft = draft_tokens;
   a.cu_q = cu_q;
@@ -264,8 +319,96 @@ int spec_accept(const float *logits, int vocab, const int32_t *draft_tokens, con
   a.batch = batch;
   a.total_q = total_q;
   a.vocab = vocab;
+  a.rows = total_q;
   sv::launch_accept(a, static_cast<hipStream_t>(stream));
   return check_launch("spec_accept");
+}
+
+size_t spec_accept_chunk_workspace_size(int batch, int total_q, int vocab) {
+  if (batch < 0 || total_q < 0 || vocab <= 0) return 0;
+  size_t m = sv::accept_layout(batch, 0, vocab).total;
+  for (int rows = 1; rows <= total_q; ++rows) {
+    const size_t t = sv::accept_layout(batch, rows, vocab).total;
+    if (t > m) m = t;
+  }
+  return m;
+}
+
+int spec_chunk_start(const int32_t *cu_q, int batch, int total_q, int chunk_size,
+                     int32_t *chunk_begin, int32_t *cu_chunk, void *stream) {
+  if (batch < 0 || total_q < 0 || total_q > (long long)batch * sv::kMaxTokens)
+    return fail(SV_ERR_SHAPE, "batch (%d) and total_q (%d) out of range", batch, total_q);
+  if (chunk_size <= 0) return fail(SV_ERR_SHAPE, "chunk_size %d must be > 0", chunk_size);
+  if (!cu_q || !cu_chunk || (batch > 0 && !chunk_begin))
+    return fail(SV_ERR_NULL, "spec_chunk_start: a required pointer is NULL");
+  if (overlaps(chunk_begin, (size_t)batch * 4, cu_chunk, (size_t)(batch + 1) * 4) ||
+      overlaps(cu_chunk, (size_t)(batch + 1) * 4, cu_q, (size_t)(batch + 1) * 4))
+    return fail(SV_ERR_ALIAS, "spec_chunk_start outputs overlap");
+  sv::AcceptArgs a;
+  memset(&a, 0, sizeof a);
+  a.cu_q = cu_q;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.chunk_size = chunk_size;
+  a.next_begin = chunk_begin;
+  a.next_cu = cu_chunk;
+  sv::launch_chunk_start(a, static_cast<hipStream_t>(stream));
+  return check_launch("spec_chunk_start");
+}
+
+int spec_accept_chunk(const float *logits, int vocab, const int32_t *draft_tokens,
+                      const int32_t *cu_q, const int32_t *tree_parent, const int32_t *chunk_begin,
+                      const int32_t *cu_chunk, int batch, int total_q, int total_chunk,
+                      int chunk_size, int32_t *target_argmax, int32_t *accept_len,
+                      int32_t *accepted_path, int32_t *out_tokens, int32_t *next_begin,
+                      int32_t *next_cu, void *workspace, size_t workspace_bytes, void *stream) {
+  if (batch < 0 || total_q < 0 || total_chunk < 0 || total_chunk > total_q)
+    return fail(SV_ERR_SHAPE, "batch (%d), total_q (%d), total_chunk (%d) out of range", batch,
+                total_q, total_chunk);
+  if (vocab <= 0) return fail(SV_ERR_SHAPE, "vocab %d must be > 0", vocab);
+  if (chunk_size <= 0) return fail(SV_ERR_SHAPE, "chunk_size %d must be > 0", chunk_size);
+  if (total_q > (long long)batch * sv::kMaxTokens)
+    return fail(SV_ERR_SHAPE, "total_q %d exceeds batch*64", total_q);
+  if (batch == 0) return ok();
+  if (!cu_q || !chunk_begin || !cu_chunk || !accept_len || !next_begin || !next_cu || !workspace)
+    return fail(SV_ERR_NULL, "spec_accept_chunk: a required pointer is NULL");
+  if (total_q > 0 && (!draft_tokens || !target_argmax || !accepted_path || !out_tokens))
+    return fail(SV_ERR_NULL, "spec_accept_chunk: a required pointer is NULL");
+  if (total_chunk > 0 && !logits) return fail(SV_ERR_NULL, "spec_accept_chunk: logits is NULL");
+  const sv::AcceptLayout lay = sv::accept_layout(batch, total_chunk, vocab);
+  if (workspace_bytes < lay.total)
+    return fail(SV_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, lay.total);
+  const size_t tb = (size_t)total_q * 4, bb = (size_t)batch * 4, cb = (size_t)(batch + 1) * 4;
+  if (overlaps(target_argmax, tb, accepted_path, tb) || overlaps(target_argmax, tb, out_tokens, tb) ||
+      overlaps(accepted_path, tb, out_tokens, tb) || overlaps(accept_len, bb, target_argmax, tb) ||
+      overlaps(accept_len, bb, accepted_path, tb) || overlaps(accept_len, bb, out_tokens, tb) ||
+      overlaps(next_begin, bb, chunk_begin, bb) || overlaps(next_begin, bb, cu_chunk, cb) ||
+      overlaps(next_cu, cb, chunk_begin, bb) || overlaps(next_cu, cb, cu_chunk, cb) ||
+      overlaps(next_begin, bb, next_cu, cb))
+    return fail(SV_ERR_ALIAS, "spec_accept_chunk outputs overlap each other or the chunk inputs");
+  sv::AcceptArgs a;
+  memset(&a, 0, sizeof a);
+  a.logits = logits;
+  a.draft = draft_tokens;
+  a.cu_q = cu_q;
+  a.tree_parent = tree_parent;
+  a.target_argmax = target_argmax;
+  a.accept_len = accept_len;
+  a.accepted_path = accepted_path;
+  a.out_tokens = out_tokens;
+  a.ws = static_cast<char *>(workspace);
+  a.lay = lay;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.vocab = vocab;
+  a.rows = total_chunk;
+  a.cu_rows = cu_chunk;
+  a.chunk_begin = chunk_begin;
+  a.chunk_size = chunk_size;
+  a.next_begin = next_begin;
+  a.next_cu = next_cu;
+  sv::launch_accept_chunk(a, static_cast<hipStream_t>(stream));
+  return check_launch("spec_accept_chunk");
 }
 
 int spec_accept_device_status(const void *workspace, uint32_t *flags, void *stream) {

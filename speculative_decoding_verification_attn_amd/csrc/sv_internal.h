@@ -40,11 +40,15 @@ constexpr int kPlanLdsRequests = 4096;  // per-request plan data kept in LDS up 
 // workgroup that touched it (at most two per workgroup, each with one partial
 // per tile), merged afterwards.
 // ---------------------------------------------------------------------------
-// A unit record: {request, kv head, tile group, first global block} and
-// {first verify row o, verify tokens q, context L, blocks per unit}.
+// A unit record: {request, kv head, tile group, first global block},
+// {first row o, rows q, context L, blocks per unit} and {first verify token s
+// of the rows, the request's first entry in the tree parent array, -, -}.
+// Row r of the unit's request is verify token s + r; its keys are the
+// L + s + q slots [0, L + s + q).  s = 0 except for chunked verification.
 struct UnitRec {
   int4 a;
   int4 b;
+  int4 c;
 };
 
 struct AttnLayout {
@@ -91,12 +95,15 @@ struct AttnArgs {
   const uint16_t *v_cache;
   const int32_t *block_tables;
   const int32_t *context_lens;
-  const int32_t *cu_q;
-  const int32_t *tree_parent;
+  const int32_t *cu_q;         // packing of the rows (the chunk's rows when chunked)
+  const int32_t *tree_parent;  // parents of all verify tokens, packed by cu_full
+  const int32_t *chunk_begin;  // first verify token of each request's rows, or nullptr
+  const int32_t *cu_full;      // packing of all verify tokens (== cu_q unless chunked)
   uint16_t *out;
   char *ws;
   AttnLayout lay;
   int batch, total_q, num_q_heads, num_kv_heads, group, max_blocks, num_pages;
+  int total_full;    // entries of tree_parent (== total_q unless chunked)
   int grid;          // persistent attention workgroups launched (<= kMaxGrid)
   float scale_log2;  // softmax scale * log2(e)
 };
@@ -113,8 +120,9 @@ constexpr int kArgmaxMinSlice = 4096;
 constexpr int kArgmaxMaxSplits = 64;
 
 struct AcceptLayout {
-  size_t hdr;     // int32[8]: 0 status bits
-  size_t part;    // {float value, int index}[total_q][splits]
+  size_t hdr;       // int32[8]: 0 status bits
+  size_t part;      // {float value, int index}[rows][splits]
+  size_t next_len;  // int32[batch]: rows of each request in the next chunk (chunked acceptance)
   size_t total;
   int splits;
 };
@@ -128,19 +136,20 @@ __host__ __device__ inline int argmax_splits(int total_q, int vocab) {
   return s;
 }
 
-__host__ __device__ inline AcceptLayout accept_layout(int batch, int total_q, int vocab) {
-  (void)batch;
+// rows = logits rows (all verify tokens, or one chunk's rows)
+__host__ __device__ inline AcceptLayout accept_layout(int batch, int rows, int vocab) {
   AcceptLayout l;
-  l.splits = argmax_splits(total_q, vocab);
+  l.splits = argmax_splits(rows, vocab);
   size_t off = 0;
-  l.hdr = off;   off = align256(off + 8 * sizeof(int32_t));
-  l.part = off;  off = align256(off + size_t(total_q) * l.splits * 8);
+  l.hdr = off;       off = align256(off + 8 * sizeof(int32_t));
+  l.part = off;      off = align256(off + size_t(rows) * l.splits * 8);
+  l.next_len = off;  off = align256(off + size_t(batch) * sizeof(int32_t));
   l.total = off;
   return l;
 }
 
 struct AcceptArgs {
-  const float *logits;
+  const float *logits;          // [rows, vocab]
   const int32_t *draft;
   const int32_t *cu_q;
   const int32_t *tree_parent;
@@ -151,9 +160,21 @@ struct AcceptArgs {
   char *ws;
   AcceptLayout lay;
   int batch, total_q, vocab;
+  int rows;                     // logits rows (== total_q unless chunked)
+  // chunked acceptance (FASER early pruning): the logits rows are the chunk's
+  // rows, packed by cu_rows; request i's rows are its verify tokens
+  // [chunk_begin[i], chunk_begin[i] + rows_i)
+  const int32_t *cu_rows;
+  const int32_t *chunk_begin;
+  int chunk_size;
+  int32_t *next_begin;          // [batch] out
+  int32_t *next_cu;             // [batch+1] out
 };
 
 void launch_accept(const AcceptArgs &a, hipStream_t stream);
+void launch_accept_chunk(const AcceptArgs &a, hipStream_t stream);
+// first chunk: next_begin = 0, rows min(chunk_size, q_i), packed in next_cu
+void launch_chunk_start(const AcceptArgs &a, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // KV compaction

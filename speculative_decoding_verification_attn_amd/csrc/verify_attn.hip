@@ -100,15 +100,25 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a) {
       const int q = c1 - c0;
       bool ok = true;
       if (c0 < 0 || c1 < c0 || c1 > a.total_q) { flags |= SV_DEV_BAD_CU_Q; ok = false; }
-      if (ok && q > kMaxTokens) { flags |= SV_DEV_TOO_MANY_TOKENS; ok = false; }
+      // chunked rows: tokens [s, s+q) of the request's q_full verify tokens
+      int s0 = 0;
+      if (a.chunk_begin) {
+        s0 = a.chunk_begin[i];
+        const int f0 = a.cu_full[i], f1 = a.cu_full[i + 1];
+        if (f0 < 0 || f1 < f0 || f1 > a.total_full || s0 < 0 || (ok && s0 + q > f1 - f0)) {
+          flags |= SV_DEV_BAD_CU_Q;
+          ok = false;
+        }
+      }
+      if (ok && s0 + q > kMaxTokens) { flags |= SV_DEV_TOO_MANY_TOKENS; ok = false; }
       if (L < 0) { flags |= SV_DEV_BAD_CONTEXT; ok = false; }
-      if (ok && ((long long)L + q + kPage - 1) / kPage > a.max_blocks) {
+      if (ok && ((long long)L + s0 + q + kPage - 1) / kPage > a.max_blocks) {
         flags |= SV_DEV_TOO_MANY_PAGES;
         ok = false;
       }
       if (ok && q > 0) {
         rg = (G * q + kTileRows * kUnitTiles - 1) / (kTileRows * kUnitTiles);
-        nblk = (L + q + kBlockKeys - 1) / kBlockKeys;
+        nblk = (L + s0 + q + kBlockKeys - 1) / kBlockKeys;
         n_blocks = (long long)rg * Hkv * nblk;
       }
     }
@@ -139,9 +149,11 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a) {
       const int rg = rgs[i], nblk = nblks[i], u0 = ubase[i], b0 = bbase[i];
       if (rg == 0) continue;
       const int o = a.cu_q[i], qn = a.cu_q[i + 1] - o, L = a.context_lens[i];
+      const int s0 = a.chunk_begin ? a.chunk_begin[i] : 0, ot = a.chunk_begin ? a.cu_full[i] : o;
       for (int k = 0; k < rg * Hkv; ++k) {
         const int h = k / rg, r = k - h * rg;
-        units[u0 + k] = UnitRec{make_int4(i, h, r, b0 + k * nblk), make_int4(o, qn, L, nblk)};
+        units[u0 + k] = UnitRec{make_int4(i, h, r, b0 + k * nblk), make_int4(o, qn, L, nblk),
+                                make_int4(s0, ot, 0, 0)};
       }
     }
     // pass 3: range boundaries.  Block x costs 1 and the start of every unit
@@ -194,15 +206,16 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a) {
       const int h = k / rg, r = k - h * rg;
       const int ub = bbase[lo] + k * nblk;
       const int o = a.cu_q[lo], qn = a.cu_q[lo + 1] - o, L = a.context_lens[lo];
+      const int s0 = a.chunk_begin ? a.chunk_begin[lo] : 0, ot = a.chunk_begin ? a.cu_full[lo] : o;
       wg_first[w] = u;
-      wg_rec[w] = UnitRec{make_int4(lo, h, r, ub), make_int4(o, qn, L, nblk)};
+      wg_rec[w] = UnitRec{make_int4(lo, h, r, ub), make_int4(o, qn, L, nblk), make_int4(s0, ot, 0, 0)};
       const int w0 = wg_of_block(wg_start, P, ub);
       if (w >= 1 && w0 == w - 1) {
         const int w1 = wg_of_block(wg_start, P, ub + nblk - 1);
         const int side0 = wg_start[w0] == ub ? 0 : 1;
-        merge_rec[w] = UnitRec{make_int4(u, w0, w1, side0), make_int4(o, qn, h, r)};
+        merge_rec[w] = UnitRec{make_int4(u, w0, w1, side0), make_int4(o, qn, h, r), make_int4(0, 0, 0, 0)};
       } else {
-        merge_rec[w] = UnitRec{make_int4(-1, 0, 0, 0), make_int4(0, 0, 0, 0)};
+        merge_rec[w] = UnitRec{make_int4(-1, 0, 0, 0), make_int4(0, 0, 0, 0), make_int4(0, 0, 0, 0)};
       }
     }
   }
@@ -444,18 +457,20 @@ __global__ __launch_bounds__(64 * kMergeRows) void attn_merge_kernel(AttnArgs a)
 // and waiting for it (its value is needed at once) would also wait for every
 // K/V load issued before it.
 struct const_unit_ptr {
-  const_i32_ptr p;  // UnitRec[]: 8 int32 each
+  const_i32_ptr p;  // UnitRec[]: 12 int32 each
   __device__ UnitRec operator[](int u) const {
-    const const_i32_ptr q = p + 8 * (size_t)u;
+    const const_i32_ptr q = p + 12 * (size_t)u;
     UnitRec r;
     r.a = make_int4(q[0], q[1], q[2], q[3]);
     r.b = make_int4(q[4], q[5], q[6], q[7]);
+    r.c = make_int4(q[8], q[9], q[10], q[11]);
     return r;
   }
 };
 
 struct Walk {
   int u, i, h, rg, ub, o, qn, L, nblk;
+  int s, ot;   // first verify token of the rows; the request's first parent entry
   int ps, pe;  // global blocks [ps, pe) of the unit processed by this workgroup
   int g0, nr;  // its rounds [g0, g0 + nr)
   bool has_next;
@@ -467,6 +482,7 @@ __device__ inline void walk_enter(Walk &W, int u, const UnitRec &r, int start, i
   W.u = u;
   W.i = r.a.x; W.h = r.a.y; W.rg = r.a.z; W.ub = r.a.w;
   W.o = r.b.x; W.qn = r.b.y; W.L = r.b.z; W.nblk = r.b.w;
+  W.s = r.c.x; W.ot = r.c.y;
   W.ps = max(W.ub, start);
   W.pe = min(W.ub + W.nblk, end);
   W.g0 = g0;
@@ -562,8 +578,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
 
   // enter the consumer's unit: ancestor masks of the lane's rows and Q in LDS
   auto enter_unit = [&]() {
+    // masks of the verify tokens [0, s+q) (keys L .. L+s+q-1); row r of the
+    // unit's tiles is token s + r / G
     bool parents_ok;
-    const uint64_t anc_all = ancestor_mask(a.tree_parent, Wc.o, Wc.qn, lane, &parents_ok);
+    const uint64_t anc_all = ancestor_mask(a.tree_parent, Wc.ot, Wc.s + Wc.qn, lane, &parents_ok);
     if (!parents_ok && threadIdx.x == 0 && Wc.ps == Wc.ub && Wc.h == 0 && Wc.rg == 0)
       atomicOr(reinterpret_cast<unsigned *>(a.ws + a.lay.hdr), SV_DEV_BAD_PARENT);
     nt = min(kUnitTiles, (G * Wc.qn + kTileRows - 1) / kTileRows - Wc.rg * kUnitTiles);
@@ -574,14 +592,14 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
       const int tok = row_ok ? R / G : 0;
       // the shuffle must run on every lane: a source lane whose own row is
       // past the end would be inactive and read back as zero
-      const uint64_t anc_tok = __shfl(anc_all, tok);
+      const uint64_t anc_tok = __shfl(anc_all, Wc.s + tok);
       anc[tt] = row_ok ? anc_tok : 0ull;
       m[tt] = -INFINITY;
       l[tt] = 0.f;
 #pragma unroll
       for (int c = 0; c < DPL; ++c) acc[tt][c] = floatx16{};
     }
-    nk = Wc.L + Wc.qn;
+    nk = Wc.L + Wc.s + Wc.qn;
     if (qpf_u != Wc.u) load_q_chunks<D>(a, Wc, 0, wave, n, hh, qpf);
 #pragma unroll
     for (int j = 0; j < KQ; ++j) sm_q[0][wave * KQ + j][lane] = qpf[j];
@@ -604,7 +622,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
     const int lbk = (Wp.ps - Wp.ub) + kAttnWaves * min(g - Wp.g0, Wp.nr - 1) + wave;
     const int lmax = Wp.pe - Wp.ub - 1;  // a wave without a block re-reads the piece's last one
     const const_i32_ptr bt = (const_i32_ptr)(uintptr_t)(a.block_tables + (size_t)Wp.i * a.max_blocks);
-    const int npages = (Wp.L + Wp.qn + kPage - 1) / kPage;
+    const int npages = (Wp.L + Wp.s + Wp.qn + kPage - 1) / kPage;
     int safe = bt[0];
     if (safe < 0 || safe >= a.num_pages) safe = 0;
     pg_next = block_pages(bt, min(lbk, lmax), npages, a.num_pages, safe, &bad_page);

@@ -33,7 +33,9 @@ DEV_TOO_MANY_PAGES = 0x20
 EXPORTED = ["spec_verify_attn_workspace_size", "spec_verify_attn", "spec_verify_attn_plan",
             "spec_verify_attn_run", "spec_verify_attn_device_status",
             "spec_accept_workspace_size", "spec_accept", "spec_accept_device_status",
-            "kv_compact", "sv_status_string", "sv_last_error"]
+            "kv_compact", "sv_status_string", "sv_last_error",
+            "spec_verify_attn_chunk_plan", "spec_verify_attn_chunk_run", "spec_chunk_start",
+            "spec_accept_chunk_workspace_size", "spec_accept_chunk"]
 
 _lib = None
 
@@ -72,6 +74,17 @@ def load_library():
     lib.spec_accept_device_status.restype = I
     lib.kv_compact.argtypes = [P, P, I64, I, P, I, P, P, P, P, P, I, I, I, I, I, I, P]
     lib.kv_compact.restype = I
+    lib.spec_verify_attn_chunk_plan.argtypes = [P, P, I, P, P, I, I, I, I, I, I, I, P, SZ, P]
+    lib.spec_verify_attn_chunk_plan.restype = I
+    lib.spec_verify_attn_chunk_run.argtypes = [P, P, P, P, I, P, P, I, P, P, I, P, P, I, I, I, I, I, I,
+                                               F, P, SZ, P]
+    lib.spec_verify_attn_chunk_run.restype = I
+    lib.spec_chunk_start.argtypes = [P, I, I, I, P, P, P]
+    lib.spec_chunk_start.restype = I
+    lib.spec_accept_chunk_workspace_size.argtypes = [I, I, I]
+    lib.spec_accept_chunk_workspace_size.restype = SZ
+    lib.spec_accept_chunk.argtypes = [P, I, P, P, P, P, P, I, I, I, I, P, P, P, P, P, P, P, SZ, P]
+    lib.spec_accept_chunk.restype = I
     lib.sv_status_string.argtypes = [I]
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_last_error.argtypes = []
@@ -247,3 +260,97 @@ def kv_compact(k_cache, v_cache, block_tables, context_lens, cu_q, accepted_path
                           _ptr(accepted_path), _ptr(accept_len), _ptr(new_context_lens), B, T,
                           num_kv_heads, head_dim, 16, num_pages, _stream(stream)))
     return new_context_lens
+
+
+# ----------------------------------------------------------------------------
+# Chunked verification with early pruning
+def spec_chunk_start(cu_q, chunk_size, *, total_q, chunk_begin=None, cu_chunk=None, stream=None):
+    """First chunk of a verify step: chunk_begin [B] = 0, cu_chunk [B+1] packs
+    min(chunk_size, q_i) rows per request.  Returns (chunk_begin, cu_chunk)."""
+    lib = load_library()
+    _dev(cu_q, torch.int32, "cu_q")
+    B = cu_q.shape[0] - 1
+    dev = cu_q.device
+    if chunk_begin is None:
+        chunk_begin = torch.empty(max(B, 1), dtype=torch.int32, device=dev)
+    if cu_chunk is None:
+        cu_chunk = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    _dev(chunk_begin, torch.int32, "chunk_begin")
+    _dev(cu_chunk, torch.int32, "cu_chunk")
+    _check(lib.spec_chunk_start(_ptr(cu_q), B, int(total_q), int(chunk_size), _ptr(chunk_begin), _ptr(cu_chunk),
+                                _stream(stream)))
+    return chunk_begin, cu_chunk
+
+
+def spec_verify_attn_chunk_plan(context_lens, cu_q, chunk_begin, cu_chunk, *, total_q, total_chunk,
+                                max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, num_pages,
+                                workspace, stream=None):
+    """Plan of verify attention over one chunk's rows into `workspace`."""
+    lib = load_library()
+    for t, nm in ((context_lens, "context_lens"), (cu_q, "cu_q"), (chunk_begin, "chunk_begin"),
+                  (cu_chunk, "cu_chunk")):
+        _dev(t, torch.int32, nm)
+    B = context_lens.shape[0]
+    _check(lib.spec_verify_attn_chunk_plan(_ptr(context_lens), _ptr(cu_q), int(total_q), _ptr(chunk_begin),
+                                           _ptr(cu_chunk), int(total_chunk), int(max_blocks_per_seq), B,
+                                           int(num_q_heads), int(num_kv_heads), int(head_dim),
+                                           int(num_pages), _ptr(workspace), workspace.numel(),
+                                           _stream(stream)))
+    return workspace
+
+
+def spec_verify_attn_chunk_run(q, k_cache, v_cache, block_tables, context_lens, cu_q, chunk_begin,
+                               cu_chunk, tree_parent=None, *, total_q, out=None, softmax_scale=0.0,
+                               workspace, num_pages=None, stream=None):
+    """q [Tc,Hq,D] bf16 (the chunk's rows, packed by cu_chunk) -> out [Tc,Hq,D]; the plan must be
+    in `workspace` (spec_verify_attn_chunk_plan)."""
+    lib = load_library()
+    _dev(q, torch.bfloat16, "q")
+    _dev(k_cache, torch.bfloat16, "k_cache")
+    _dev(v_cache, torch.bfloat16, "v_cache")
+    for t, nm in ((block_tables, "block_tables"), (context_lens, "context_lens"), (cu_q, "cu_q"),
+                  (chunk_begin, "chunk_begin"), (cu_chunk, "cu_chunk"), (tree_parent, "tree_parent")):
+        _dev(t, torch.int32, nm)
+    Tc, Hq, D = q.shape
+    pages, Hkv, P, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    B = context_lens.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, torch.bfloat16, "out")
+    _check(lib.spec_verify_attn_chunk_run(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                          block_tables.shape[1], _ptr(context_lens), _ptr(cu_q), int(total_q),
+                                          _ptr(chunk_begin), _ptr(cu_chunk), Tc, _ptr(tree_parent), _ptr(out),
+                                          B, Hq, Hkv, D, P, pages if num_pages is None else num_pages,
+                                          float(softmax_scale), _ptr(workspace), workspace.numel(),
+                                          _stream(stream)))
+    return out
+
+
+def spec_accept_chunk_workspace_size(batch, total_q, vocab) -> int:
+    return int(load_library().spec_accept_chunk_workspace_size(batch, total_q, vocab))
+
+
+def spec_accept_chunk(logits, draft_tokens, cu_q, chunk_begin, cu_chunk, tree_parent=None, *,
+                      chunk_size, target_argmax, accept_len, accepted_path, out_tokens, next_begin,
+                      next_cu, workspace, stream=None):
+    """Acceptance after one chunk: logits [Tc,V] fp32 are the chunk's rows.  Fills the chunk's
+    entries of target_argmax [T]; requests that end here get accept_len / accepted_path /
+    out_tokens; next_begin [B] and next_cu [B+1] describe the next chunk (next_cu[B] = its rows)."""
+    lib = load_library()
+    _dev(logits, torch.float32, "logits")
+    for t, nm in ((draft_tokens, "draft_tokens"), (cu_q, "cu_q"), (chunk_begin, "chunk_begin"),
+                  (cu_chunk, "cu_chunk"), (tree_parent, "tree_parent"), (target_argmax, "target_argmax"),
+                  (accept_len, "accept_len"), (accepted_path, "accepted_path"), (out_tokens, "out_tokens"),
+                  (next_begin, "next_begin"), (next_cu, "next_cu")):
+        _dev(t, torch.int32, nm)
+    Tc, V = logits.shape
+    B = cu_q.shape[0] - 1
+    T = draft_tokens.shape[0]
+    _check(lib.spec_accept_chunk(_ptr(logits), V, _ptr(draft_tokens), _ptr(cu_q), _ptr(tree_parent),
+                                 _ptr(chunk_begin), _ptr(cu_chunk), B, T, Tc, int(chunk_size),
+                                 _ptr(target_argmax), _ptr(accept_len), _ptr(accepted_path),
+                                 _ptr(out_tokens), _ptr(next_begin), _ptr(next_cu), _ptr(workspace),
+                                 workspace.numel(), _stream(stream)))
+    return next_begin, next_cu

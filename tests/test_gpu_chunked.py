@@ -1,0 +1,144 @@
+"""Chunked verification with early pruning (FASER, "Early Token Pruning") on the
+GPU, through the C ABI, against the oracle.
+
+Attention over a chunk's rows must give the rows of full verification (the
+mask and keys of a verify token do not depend on how the tokens are chunked);
+the chunk loop of spec_chunk_start / spec_accept_chunk must visit exactly the
+oracle's chunks and end with the oracle's unchunked acceptance, bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DEV, DevCase, assert_attn_close, i32, note, oracle_attn
+from speculative_decoding_verification_attn_amd import ops
+from speculative_decoding_verification_attn_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _tree(seed, nodes=64, depth=6):
+    return W.draw_tree(np.random.Generator(np.random.PCG64(seed)), nodes, depth, 4, 4)
+
+
+CASES = {
+    "chains_d128_g4": dict(context_lens=[0, 47, 64, 500, 1000, 3], q_lens=[4, 9, 1, 6, 3, 8], hq=32, hkv=8,
+                           d=128, vocab=700, match_p=0.8),
+    "chains_d64_g8": dict(context_lens=[130, 3, 999], q_lens=[9, 9, 4], hq=16, hkv=2, d=64, vocab=300,
+                          match_p=0.9),
+    "trees_d128_g8": dict(context_lens=[300, 0, 77], tree_parents=[_tree(1), _tree(2, 40, 9), _tree(3, 7, 3)],
+                          hq=64, hkv=8, d=128, vocab=512, tree_match=(0.8, 0.3)),
+}
+
+
+def _chunk_rows(cu, begin, length):
+    rows = [np.arange(cu[i] + begin[i], cu[i] + begin[i] + length[i]) for i in range(len(begin))]
+    rows = np.concatenate(rows).astype(np.int64) if rows else np.zeros(0, np.int64)
+    cu_chunk = np.zeros(len(begin) + 1, np.int32)
+    cu_chunk[1:] = np.cumsum(length)
+    return rows, cu_chunk
+
+
+def _chunk_attn(dc, begin, length):
+    case = dc.case
+    rows, cu_chunk = _chunk_rows(case.cu_q, begin, length)
+    Tc = len(rows)
+    ws = torch.empty(ops.spec_verify_attn_workspace_size(case.batch, max(Tc, 1), case.num_q_heads,
+                                                         case.num_kv_heads, case.head_dim),
+                     dtype=torch.uint8, device=DEV)
+    qc = dc.q[torch.from_numpy(rows).to(DEV)].contiguous()
+    b_dev, cu_dev = i32(begin), i32(cu_chunk)
+    ops.spec_verify_attn_chunk_plan(dc.ctx, dc.cu, b_dev, cu_dev, total_q=case.total_q, total_chunk=Tc,
+                                    max_blocks_per_seq=case.block_tables.shape[1],
+                                    num_q_heads=case.num_q_heads, num_kv_heads=case.num_kv_heads,
+                                    head_dim=case.head_dim, num_pages=case.num_pages, workspace=ws)
+    out = ops.spec_verify_attn_chunk_run(qc, dc.k, dc.v, dc.bt, dc.ctx, dc.cu, b_dev, cu_dev, dc.par,
+                                         total_q=case.total_q, workspace=ws)
+    torch.cuda.synchronize()
+    return rows, out, ws
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("name", list(CASES))
+def test_chunk_attention_rows_equal_full_verification(name, seed):
+    case = W.make_custom(300 + list(CASES).index(name), **CASES[name])
+    dc = DevCase(case)
+    ref = oracle_attn(case)
+    rng = np.random.default_rng(seed)
+    q = np.diff(case.cu_q)
+    begin = np.array([rng.integers(0, qi + 1) for qi in q], np.int32)
+    length = np.array([rng.integers(0, qi - b + 1) for qi, b in zip(q, begin)], np.int32)
+    if seed == 0:  # one chunk per request, the last one: every request's tail
+        begin = (q // 2).astype(np.int32)
+        length = (q - begin).astype(np.int32)
+    note(f"[gpu] chunk attention {name} seed {seed}: begin {begin.tolist()} len {length.tolist()}")
+    rows, out, ws = _chunk_attn(dc, begin, length)
+    if len(rows) == 0:
+        return
+    assert ops.spec_verify_attn_device_status(ws) == 0
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert_attn_close(got, ref[rows], f"{name} seed {seed}")
+
+
+def test_chunk_attention_bad_chunk_sets_status():
+    """A chunk that does not lie inside its request is flagged, not read out of range."""
+    case = W.make_custom(310, **CASES["chains_d128_g4"])
+    dc = DevCase(case)
+    q = np.diff(case.cu_q)
+    begin = np.zeros(case.batch, np.int32)
+    length = np.minimum(q, 2).astype(np.int32)
+    begin[1] = q[1] - 1  # begin + length > q for request 1
+    rows, out, ws = _chunk_attn(dc, begin, np.where(np.arange(case.batch) == 1, 2, length).astype(np.int32))
+    assert ops.spec_verify_attn_device_status(ws) & ops.DEV_BAD_CU_Q
+
+
+@pytest.mark.parametrize("chunk", [1, 2, 3, 8, 64])
+@pytest.mark.parametrize("name", list(CASES))
+def test_chunk_loop_ends_with_unchunked_acceptance(name, chunk):
+    case = W.make_custom(320 + list(CASES).index(name), **CASES[name])
+    dc = DevCase(case)
+    B, T, V = case.batch, case.total_q, case.vocab
+    t_ref = oracle.argmax(case.logits)
+    full = oracle.accept(case.draft_tokens, t_ref, case.cu_q, case.tree_parent)
+    o_acc, o_path, o_toks, steps = oracle.accept_chunked(case.draft_tokens, t_ref, case.cu_q,
+                                                         case.tree_parent, chunk)
+    assert np.array_equal(o_acc, full[0])
+    t_arg = torch.full((T,), -5, dtype=torch.int32, device=DEV)
+    acc = torch.full((B,), -9, dtype=torch.int32, device=DEV)
+    path = torch.full((T,), -9, dtype=torch.int32, device=DEV)
+    toks = torch.full((T,), -9, dtype=torch.int32, device=DEV)
+    ws = torch.empty(ops.spec_accept_chunk_workspace_size(B, T, V), dtype=torch.uint8, device=DEV)
+    begin, cu_chunk = ops.spec_chunk_start(dc.cu, chunk, total_q=T)
+    nb = torch.empty_like(begin)
+    ncu = torch.empty_like(cu_chunk)
+    k = 0
+    verified = 0
+    while True:
+        b_h = begin.cpu().numpy()
+        cu_h = cu_chunk.cpu().numpy()
+        len_h = np.diff(cu_h)
+        if k < len(steps):
+            note(f"[gpu] chunk loop {name} c={chunk} step {k}: rows {int(cu_h[-1])}")
+            assert np.array_equal(len_h, steps[k][1]), (k, len_h, steps[k][1])
+            assert np.array_equal(b_h[len_h > 0], steps[k][0][len_h > 0]), k
+        else:
+            assert cu_h[-1] == 0, k
+        if cu_h[-1] == 0:
+            break
+        rows, _ = _chunk_rows(case.cu_q, b_h, len_h)
+        verified += len(rows)
+        logits_c = dc.logits[torch.from_numpy(rows).to(DEV)].contiguous()
+        ops.spec_accept_chunk(logits_c, dc.draft, dc.cu, begin, cu_chunk, dc.par, chunk_size=chunk,
+                              target_argmax=t_arg, accept_len=acc, accepted_path=path, out_tokens=toks,
+                              next_begin=nb, next_cu=ncu, workspace=ws)
+        assert ops.spec_accept_device_status(ws) == 0
+        begin, cu_chunk, nb, ncu = nb, ncu, begin, cu_chunk
+        k += 1
+        assert k <= 64
+    assert k == len(steps)
+    note(f"  verified {verified} of {T} rows in {k} chunks")
+    assert np.array_equal(acc.cpu().numpy(), full[0])
+    assert np.array_equal(path.cpu().numpy(), full[1])
+    assert np.array_equal(toks.cpu().numpy(), full[2])
+    seen = t_arg.cpu().numpy()
+    assert np.array_equal(seen[seen != -5], t_ref[seen != -5])
