@@ -311,6 +311,32 @@ int spec_accept_chunk(const float *logits, int vocab, const int32_t *draft_token
                       int32_t *next_cu, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------- */
+/* Verify-budget scheduling (host)                                            */
+/* ------------------------------------------------------------------------- */
+/*
+ * DSpark, "Hardware-aware prefix scheduler": choose how many draft positions
+ * of each request to verify so that the expected tokens emitted per second,
+ * Theta = tau * SPS(B), is largest.  Request i has gamma_i = cu_draft[i+1] -
+ * cu_draft[i] draft positions with conditional survival probabilities
+ * c = cond_survival[cu_draft[i] .. cu_draft[i+1]) (chance that draft k is
+ * accepted once drafts 1..k-1 were); S_k = c_1 * ... * c_k.  All (request,
+ * position) candidates are sorted by S, largest first (equal S: earlier
+ * position, then lower request), and admitted one at a time on top of the
+ * batch's root rows; for B = batch + admitted rows, tau = batch (one bonus
+ * token per request) + the admitted S values, and SPS(B) is the engine's
+ * verify steps per second at B rows, linearly interpolated in the table
+ * (sps_rows strictly increasing, > 0; sps_value >= 0) and clamped at its
+ * ends.  The first batch with the largest Theta is returned:
+ * verify_len[i] = drafts of request i to verify (a prefix), *batch_rows = B,
+ * *theta = Theta.  All pointers are HOST pointers; nothing runs on the GPU.
+ * Errors: SV_ERR_NULL, SV_ERR_SHAPE (gamma_i outside [0, 63], cu_draft[0]
+ * != 0, a survival value outside [0, 1] or NaN, a bad SPS table).
+ */
+int spec_verify_budget(const float *cond_survival, const int32_t *cu_draft, int batch,
+                       const float *sps_rows, const float *sps_value, int n_sps,
+                       int32_t *verify_len, int32_t *batch_rows, double *theta);
+
+/* ------------------------------------------------------------------------- */
 /* Diagnostics (host)                                                         */
 /* ------------------------------------------------------------------------- */
 

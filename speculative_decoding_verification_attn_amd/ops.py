@@ -35,7 +35,7 @@ EXPORTED = ["spec_verify_attn_workspace_size", "spec_verify_attn", "spec_verify_
             "spec_accept_workspace_size", "spec_accept", "spec_accept_device_status",
             "kv_compact", "sv_status_string", "sv_last_error",
             "spec_verify_attn_chunk_plan", "spec_verify_attn_chunk_run", "spec_chunk_start",
-            "spec_accept_chunk_workspace_size", "spec_accept_chunk"]
+            "spec_accept_chunk_workspace_size", "spec_accept_chunk", "spec_verify_budget"]
 
 _lib = None
 
@@ -85,6 +85,8 @@ def load_library():
     lib.spec_accept_chunk_workspace_size.restype = SZ
     lib.spec_accept_chunk.argtypes = [P, I, P, P, P, P, P, I, I, I, I, P, P, P, P, P, P, P, SZ, P]
     lib.spec_accept_chunk.restype = I
+    lib.spec_verify_budget.argtypes = [P, P, I, P, P, I, P, P, ctypes.POINTER(ctypes.c_double)]
+    lib.spec_verify_budget.restype = I
     lib.sv_status_string.argtypes = [I]
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_last_error.argtypes = []
@@ -354,3 +356,23 @@ def spec_accept_chunk(logits, draft_tokens, cu_q, chunk_begin, cu_chunk, tree_pa
                                  _ptr(out_tokens), _ptr(next_begin), _ptr(next_cu), _ptr(workspace),
                                  workspace.numel(), _stream(stream)))
     return next_begin, next_cu
+
+
+# ----------------------------------------------------------------------------
+# Verify-budget scheduling (host function; numpy in, numpy out)
+def spec_verify_budget(cond_survival, cu_draft, sps_rows, sps_value):
+    """Returns (verify_len [B] int32, batch_rows, theta) -- see spec_verify_budget in the header."""
+    import numpy as np
+    lib = load_library()
+    c = np.ascontiguousarray(cond_survival, dtype=np.float32)
+    cu = np.ascontiguousarray(cu_draft, dtype=np.int32)
+    r = np.ascontiguousarray(sps_rows, dtype=np.float32)
+    v = np.ascontiguousarray(sps_value, dtype=np.float32)
+    B = len(cu) - 1
+    out = np.zeros(max(B, 1), dtype=np.int32)
+    rows = ctypes.c_int32(0)
+    th = ctypes.c_double(0.0)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    _check(lib.spec_verify_budget(p(c) if c.size else None, p(cu), B, p(r), p(v), len(r), p(out),
+                                  ctypes.byref(rows), ctypes.byref(th)))
+    return out[:B], int(rows.value), float(th.value)
