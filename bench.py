@@ -57,6 +57,8 @@ def main():
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MB "
                          "(reference for the HBM traffic counters)")
+    ap.add_argument("--fused", action="store_true",
+                    help="acceptance and compaction as one launch (spec_accept_compact)")
     ap.add_argument("--chunk", type=int, default=0,
                     help="time chunked verification with early pruning (FASER) in chunks of this many "
                          "verify tokens instead of the default step")
@@ -126,6 +128,8 @@ def main():
     path = torch.empty(T, dtype=torch.int32, device=dev)
     toks = torch.empty(T, dtype=torch.int32, device=dev)
     new_len = torch.empty(B, dtype=torch.int32, device=dev)
+    ws_fused = torch.zeros(ops.spec_accept_compact_workspace_size(B, T, case.vocab), dtype=torch.uint8,
+                           device=dev) if args.fused else None
     stream = torch.cuda.current_stream()
     log(f"resident: {copies} KV copies x {kv_bytes / 1e9:.3f} GB, logits {T * case.vocab * 4 / 1e6:.1f} MB")
 
@@ -149,10 +153,17 @@ def main():
         ops.spec_verify_attn_run(q, K[c], V[c], bt, ctx, cu, par, out=out, workspace=ws_attn, stream=st)
 
     def phase_accept(st):
+        if args.fused:  # acceptance and compaction in one launch; the compact phase is then empty
+            ops.spec_accept_compact(logits, draft, cu, par, K, V, bt, ctx, workspace=ws_fused, num_layers=copies,
+                                    target_argmax=t_arg, accept_len=acc, accepted_path=path, out_tokens=toks,
+                                    new_context_lens=new_len, stream=st)
+            return
         ops.spec_accept(logits, draft, cu, par, target_argmax=t_arg, accept_len=acc, accepted_path=path,
                         out_tokens=toks, workspace=ws_acc, stream=st)
 
     def phase_compact(st):
+        if args.fused:
+            return
         ops.kv_compact(K, V, bt, ctx, cu, path, acc, num_layers=copies, new_context_lens=new_len, stream=st)
 
     def step_eager(record):
@@ -190,7 +201,8 @@ def main():
         # timing events between the replays (outside the graphs).  Batch-1
         # kernels run for a few microseconds, less than a host-side launch,
         # so eager launches would leave the GPU idle between layers.
-        graphs = {k: torch.cuda.CUDAGraph() for k in ("plan", "attn", "accept", "compact")}
+        phases = ("plan", "attn", "accept") if args.fused else ("plan", "attn", "accept", "compact")
+        graphs = {k: torch.cuda.CUDAGraph() for k in phases}
         with torch.cuda.graph(graphs["plan"]):
             phase_plan(None)
         with torch.cuda.graph(graphs["attn"]):
@@ -198,10 +210,11 @@ def main():
                 phase_layer(layer, None)
         with torch.cuda.graph(graphs["accept"]):
             phase_accept(None)
-        with torch.cuda.graph(graphs["compact"]):
-            phase_compact(None)
+        if "compact" in graphs:
+            with torch.cuda.graph(graphs["compact"]):
+                phase_compact(None)
         for _ in range(2):
-            for k in ("plan", "attn", "accept", "compact"):
+            for k in phases:
                 graphs[k].replay()
         torch.cuda.synchronize()
         log("captured one graph per phase")
@@ -214,7 +227,8 @@ def main():
         e2 = mark()
         graphs["accept"].replay()
         e3 = mark()
-        graphs["compact"].replay()
+        if "compact" in graphs:
+            graphs["compact"].replay()
         e4 = mark()
         timings["plan"].append((e0, e1))
         timings["attn"].append((e1, e2))
@@ -294,6 +308,7 @@ def main():
         "accept_us": round(accept_ms * 1e3, 2),
         "accept_gbs": round(logits_bytes / (accept_ms * 1e-3) / 1e9, 1),
         "compact_us": round(compact_ms * 1e3, 2),
+        "accept_compact": "one launch (spec_accept_compact)" if args.fused else "two calls (spec_accept, kv_compact)",
         "verified_tokens_per_s": round(verified_tok_s, 1),
         "mean_accept_len": round(float(acc_np.mean()), 4),
         "roofline": {"kernel": "spec_verify_attn_run (verify_attn_kernel + attn_merge_kernel, per layer)",

@@ -85,6 +85,7 @@ typedef enum sv_status {
 #define SV_DEV_BAD_PARENT 0x8u      /* tree_parent violates root=-1, 0<=parent[j]<j */
 #define SV_DEV_BAD_PAGE 0x10u       /* a needed block-table entry is outside [0, num_pages) */
 #define SV_DEV_TOO_MANY_PAGES 0x20u /* ceil((L_i+q_i)/page_size) > max_blocks_per_seq */
+#define SV_DEV_SYNC_TIMEOUT 0x40u   /* spec_accept_compact: a bounded wait between work items ran out */
 
 /* ------------------------------------------------------------------------- */
 /* Verify attention                                                           */
@@ -215,6 +216,40 @@ int kv_compact(void *k_cache, void *v_cache, int64_t layer_stride_elems, int num
                const int32_t *cu_q, const int32_t *accepted_path, const int32_t *accept_len,
                int32_t *new_context_lens, int batch, int total_q, int num_kv_heads, int head_dim,
                int page_size, int num_pages, void *stream);
+
+/* ------------------------------------------------------------------------- */
+/* Fused acceptance + compaction                                              */
+/* ------------------------------------------------------------------------- */
+/*
+ * SwiftSpec, "Fused Latency-Optimized Kernels": the verification result and
+ * the KV update come out of one kernel.  spec_accept_compact = spec_accept
+ * followed by kv_compact, in ONE launch: the argmax slices, each request's
+ * walk and (for draft trees) the K/V moves are work items that workgroups
+ * take in that order from a counter in the workspace; a walk starts once
+ * its rows' slices are done and a move group once its request's walk is.
+ * Outputs are those of spec_accept and kv_compact with the same arguments.
+ *
+ *   arguments    as for spec_accept (logits .. out_tokens) and kv_compact
+ *                (k_cache .. num_pages); accepted_path and accept_len are
+ *                both outputs here and inputs of the moves.
+ *   workspace    at least spec_accept_compact_workspace_size() bytes, and
+ *                ZERO-FILLED before its first use (allocate it with zeros);
+ *                every completed call leaves it ready for the next one.  Two
+ *                calls on one workspace must not overlap in time.
+ * Device status (spec_accept_device_status on this workspace): the bits of
+ * spec_accept, plus SV_DEV_SYNC_TIMEOUT if a wait between work items gave up
+ * (its request's outputs are then unspecified).
+ */
+size_t spec_accept_compact_workspace_size(int batch, int total_q, int vocab);
+
+int spec_accept_compact(const float *logits, int vocab, const int32_t *draft_tokens,
+                        const int32_t *cu_q, const int32_t *tree_parent, int batch, int total_q,
+                        int32_t *target_argmax, int32_t *accept_len, int32_t *accepted_path,
+                        int32_t *out_tokens, void *k_cache, void *v_cache,
+                        int64_t layer_stride_elems, int num_layers, const int32_t *block_tables,
+                        int max_blocks_per_seq, const int32_t *context_lens,
+                        int32_t *new_context_lens, int num_kv_heads, int head_dim, int page_size,
+                        int num_pages, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------- */
 /* Chunked verification with early pruning                                    */

@@ -19,6 +19,7 @@
 //                          ballot of edge matches against ancestor masks.
 #include <limits.h>
 
+#include "compact_device.h"
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -50,22 +51,18 @@ __device__ inline Best wave_best(Best x) {
   return x;
 }
 
-__global__ __launch_bounds__(kArgmaxThreads) void argmax_partial_kernel(AcceptArgs a) {
+// (value, lowest index) of the maximum of logits row `row` over slice `split`
+// of `splits`; the workgroup (kArgmaxThreads) cooperates, the result is valid
+// in thread 0.
+__device__ inline Best argmax_slice(const float *logits, int V, int row, int split, int splits) {
   __shared__ float s_v[kArgmaxThreads / 64];
   __shared__ int s_i[kArgmaxThreads / 64];
-  const int split = blockIdx.x;
-  const int row = blockIdx.y;
-  const int splits = a.lay.splits;
-  const int V = a.vocab;
-  if (split == 0 && row == 0 && threadIdx.x == 0)
-    reinterpret_cast<int32_t *>(a.ws + a.lay.hdr)[0] = 0;
-  if (row >= a.rows) return;  // the grid has one row even when there are none
   // slice bounds, multiples of 4 so 16-byte loads stay aligned when V % 4 == 0
   int per = (V + splits - 1) / splits;
   per = (per + 3) & ~3;
   const int lo = min(V, split * per);
   const int hi = min(V, lo + per);
-  const float *x = a.logits + (size_t)row * V;
+  const float *x = logits + (size_t)row * V;
   Best b{-INFINITY, -1};
   if ((V & 3) == 0) {
     // each thread walks its float4s in increasing index order; strict '>'
@@ -110,53 +107,57 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_partial_kernel(AcceptAr
     s_i[wave] = b.i;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    Best r{s_v[0], s_i[0]};
+  Best r{s_v[0], s_i[0]};
 #pragma unroll
-    for (int w = 1; w < kArgmaxThreads / 64; ++w) r = better(r, Best{s_v[w], s_i[w]});
+  for (int w = 1; w < kArgmaxThreads / 64; ++w) r = better(r, Best{s_v[w], s_i[w]});
+  return r;
+}
+
+__global__ __launch_bounds__(kArgmaxThreads) void argmax_partial_kernel(AcceptArgs a) {
+  const int split = blockIdx.x;
+  const int row = blockIdx.y;
+  const int splits = a.lay.splits;
+  if (split == 0 && row == 0 && threadIdx.x == 0)
+    reinterpret_cast<int32_t *>(a.ws + a.lay.hdr)[0] = 0;
+  if (row >= a.rows) return;  // the grid has one row even when there are none
+  const Best r = argmax_slice(a.logits, a.vocab, row, split, splits);
+  if (threadIdx.x == 0) {
     float2 *part = reinterpret_cast<float2 *>(a.ws + a.lay.part);
     part[(size_t)row * splits + split] = make_float2(r.v, __int_as_float(r.i));
   }
 }
 
-__global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
-  __shared__ float s_pv[kMaxTokens * kArgmaxMaxSplits];
-  __shared__ int s_pi[kMaxTokens * kArgmaxMaxSplits];
+// Acceptance of request i (rows o..o+q-1, 1 <= q <= 64) from the slice
+// partials in the workspace: finishes the row argmaxes, then one wave walks
+// the request.  Called by a whole 256-thread workgroup.
+template <bool kCoherent = false>
+__device__ inline void accept_request(const AcceptArgs &a, int i, int o, int q) {
   __shared__ int s_t[kMaxTokens];
-  const int i = blockIdx.x;
   const int tid = threadIdx.x;
   const int splits = a.lay.splits;
   unsigned *status = reinterpret_cast<unsigned *>(a.ws + a.lay.hdr);
-  const int o = a.cu_q[i];
-  const int c1 = a.cu_q[i + 1];
-  const int q = c1 - o;
-  if (o < 0 || c1 < o || c1 > a.total_q || q > kMaxTokens) {
-    if (tid == 0) {
-      atomicOr(status, q > kMaxTokens && o >= 0 && c1 <= a.total_q ? SV_DEV_TOO_MANY_TOKENS
-                                                                   : SV_DEV_BAD_CU_Q);
-      a.accept_len[i] = 0;
-    }
-    return;
-  }
-  if (i == 0 && tid == 0 && (a.cu_q[0] != 0 || a.cu_q[a.batch] != a.total_q))
-    atomicOr(status, SV_DEV_BAD_CU_Q);
-  if (q == 0) {
-    if (tid == 0) a.accept_len[i] = 0;
-    return;
-  }
-  // 1. gather the slice partials of this request's rows
+  // 1-2. one thread per row reduces the row's slice partials (splits in index order)
   const float2 *part = reinterpret_cast<const float2 *>(a.ws + a.lay.part);
-  const int np = q * splits;
-  for (int k = tid; k < np; k += 256) {
-    const float2 p = part[(size_t)o * splits + k];
-    s_pv[k] = p.x;
-    s_pi[k] = __float_as_int(p.y);
-  }
-  __syncthreads();
-  // 2. one thread per row finishes the argmax (splits in index order)
   if (tid < q) {
-    Best b{s_pv[tid * splits], s_pi[tid * splits]};
-    for (int s = 1; s < splits; ++s) b = better(b, Best{s_pv[tid * splits + s], s_pi[tid * splits + s]});
+    const float2 *pr = part + (size_t)(o + tid) * splits;
+    Best b{-INFINITY, -1};
+    for (int s0 = 0; s0 < splits; s0 += 8) {
+      float2 p[8];  // eight independent loads in flight, then reduced in index order
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float2 *src = pr + min(s0 + u, splits - 1);
+        if constexpr (kCoherent) {  // written by other workgroups of the same launch
+          const uint64_t bits = __hip_atomic_load(reinterpret_cast<const uint64_t *>(src), __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+          p[u] = __builtin_bit_cast(float2, bits);
+        } else {
+          p[u] = *src;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < splits) b = better(b, Best{p[u].x, __float_as_int(p[u].y)});
+    }
     s_t[tid] = b.i;
     a.target_argmax[o + tid] = b.i;
   }
@@ -193,6 +194,30 @@ __global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
     }
   }
   if (j == 0) a.accept_len[i] = n + 1;
+}
+
+__global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a) {
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  unsigned *status = reinterpret_cast<unsigned *>(a.ws + a.lay.hdr);
+  const int o = a.cu_q[i];
+  const int c1 = a.cu_q[i + 1];
+  const int q = c1 - o;
+  if (o < 0 || c1 < o || c1 > a.total_q || q > kMaxTokens) {
+    if (tid == 0) {
+      atomicOr(status, q > kMaxTokens && o >= 0 && c1 <= a.total_q ? SV_DEV_TOO_MANY_TOKENS
+                                                                   : SV_DEV_BAD_CU_Q);
+      a.accept_len[i] = 0;
+    }
+    return;
+  }
+  if (i == 0 && tid == 0 && (a.cu_q[0] != 0 || a.cu_q[a.batch] != a.total_q))
+    atomicOr(status, SV_DEV_BAD_CU_Q);
+  if (q == 0) {
+    if (tid == 0) a.accept_len[i] = 0;
+    return;
+  }
+  accept_request(a, i, o, q);
 }
 
 // --------------------------------------------------------------------------
@@ -332,6 +357,206 @@ __global__ __launch_bounds__(kPlanThreads) void chunk_scan_kernel(AcceptArgs a, 
   if (threadIdx.x == 0) a.next_cu[a.batch] = carry;
 }
 
+// --------------------------------------------------------------------------
+// Acceptance and compaction in one launch (SwiftSpec, "Fused Latency-
+// Optimized Kernels": the verification result and the KV update come out of
+// one kernel).
+//
+// The work items, in order: the argmax slices (row, split), which never wait;
+// the walk of each request, which waits until the slices of its rows are
+// done; then, for draft trees, the compaction groups (request, every
+// groups-th (layer, head) pair), each waiting until its request's walk is
+// done.  The slices are workgroups 0 .. n_slices-1; every later workgroup
+// takes its item from a ticket counter, so an item only waits for items that
+// come before it and were taken by workgroups already running (the slices
+// have lower workgroup indices, which the dispatcher starts first).  Every
+// wait is bounded: one that runs out sets SV_DEV_SYNC_TIMEOUT and makes the
+// remaining waits give up, so the launch always ends.  The last waiting item
+// to finish clears the counters, so the workspace is ready for the next call.
+// --------------------------------------------------------------------------
+constexpr int kSpinLimit = 1 << 21;
+constexpr int kFusedCompactItems = 128;
+
+// Data passed between workgroups of the launch (slice partials, move lists,
+// flags) is written and read only with agent-scope atomic loads and stores,
+// which reach the coherent level directly; a producer waits until its data
+// stores are complete before it raises a flag.  No acquire or release
+// fence is needed, so no waiting workgroup invalidates or writes back the
+// L2 of its XCD while the slices stream.
+__device__ inline void store_coherent(int32_t *p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline int load_coherent(const int32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// this thread's stores have completed before anything it issues next
+__device__ inline void stores_complete() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// thread-level bounded wait until *p >= need.  The first wait that runs out
+// raises *abort, and every later wait of the launch gives up at once, so a
+// broken launch still ends quickly.
+__device__ inline bool wait_at_least(int32_t *p, int need, int32_t *abort) {
+  for (int it = 0; it < kSpinLimit; ++it) {
+    if (load_coherent(p) >= need) return true;
+    if (load_coherent(abort) != 0) return false;
+    __builtin_amdgcn_s_sleep(32);  // about 2048 cycles between polls
+  }
+  store_coherent(abort, 1);
+  return false;
+}
+
+// eight workgroups per CU for the streaming slices (the compaction items
+// then keep part of their move buffer in scratch)
+// wave-level bounded wait (called by all 64 lanes of one wave): lane r
+// waits until arrive[r] >= need for r < n; true once all are there
+__device__ inline bool wave_wait_all(const int32_t *arrive, int n, int need, int32_t *abort) {
+  const int lane = threadIdx.x & 63;
+  bool ready = lane >= n;
+  for (int it = 0; it < kSpinLimit; ++it) {
+    if (!ready) ready = load_coherent(arrive + lane) >= need;
+    if (__all(ready)) return true;
+    if (load_coherent(abort) != 0) return false;
+    __builtin_amdgcn_s_sleep(32);
+  }
+  store_coherent(abort, 1);
+  return false;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void accept_compact_kernel(AcceptArgs a, CompactArgs c, int n_slices,
+                                                             int groups, int n_total) {
+  __shared__ int s_item, s_flag, s_nmove;
+  __shared__ int s_src[kMaxTokens], s_dst[kMaxTokens];
+  int32_t *hdr = reinterpret_cast<int32_t *>(a.ws + a.lay.hdr);
+  unsigned *status = reinterpret_cast<unsigned *>(hdr);
+  int32_t *arrive = reinterpret_cast<int32_t *>(a.ws + a.lay.arrive);
+  int32_t *done = reinterpret_cast<int32_t *>(a.ws + a.lay.done);
+  int32_t *moves = reinterpret_cast<int32_t *>(a.ws + a.lay.moves);
+  const int tid = threadIdx.x;
+  const int splits = a.lay.splits;
+  int32_t *abort = &hdr[5];
+  // The slices (which never wait) are workgroups 0 .. n_slices-1; the other
+  // workgroups take the items that wait from a ticket counter, in order.
+  int t = blockIdx.x;
+  if (t >= n_slices) {
+    if (tid == 0) s_item = n_slices + __hip_atomic_fetch_add(&hdr[2], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    t = s_item;
+    if (t < n_slices || t >= n_total) {  // counters not cleared (workspace not zero-filled)
+      if (tid == 0) {
+        atomicOr(status, SV_DEV_SYNC_TIMEOUT);
+        __hip_atomic_store(abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      t = n_total;  // no item
+    }
+  }
+  if (t == 0 && tid == 0) {  // the first item clears the status word for this call
+    store_coherent(&hdr[0], 0);
+    stores_complete();
+    store_coherent(&hdr[4], 1);
+  }
+  if (t < n_slices) {
+    // 1. one argmax slice
+    const int row = t / splits, split = t - (t / splits) * splits;
+    const Best r = argmax_slice(a.logits, a.vocab, row, split, splits);
+    if (tid == 0) {
+      uint64_t *part = reinterpret_cast<uint64_t *>(a.ws + a.lay.part);
+      __hip_atomic_store(part + (size_t)row * splits + split,
+                         __builtin_bit_cast(uint64_t, make_float2(r.v, __int_as_float(r.i))), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      stores_complete();
+      __hip_atomic_fetch_add(&arrive[row], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else if (t < n_slices + a.batch) {
+    // 2. the walk of request i, then its move list
+    const int i = t - n_slices;
+    const int o = a.cu_q[i], c1 = a.cu_q[i + 1], q = c1 - o;
+    const bool valid = o >= 0 && c1 >= o && c1 <= a.total_q && q <= kMaxTokens;
+    if (tid < 64) {  // one wave: the status word is cleared and every row's slices are done
+      bool ok = true;
+      if (tid == 0) ok = wait_at_least(&hdr[4], 1, abort);
+      ok = __shfl(ok, 0);
+      if (ok && valid) ok = wave_wait_all(arrive + o, q, splits, abort);
+      if (tid == 0) s_flag = ok;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      const bool ok = s_flag;
+      if (!ok) atomicOr(status, SV_DEV_SYNC_TIMEOUT);
+      if (!valid)
+        atomicOr(status, q > kMaxTokens && o >= 0 && c1 <= a.total_q ? SV_DEV_TOO_MANY_TOKENS : SV_DEV_BAD_CU_Q);
+      if (i == 0 && (a.cu_q[0] != 0 || a.cu_q[a.batch] != a.total_q)) atomicOr(status, SV_DEV_BAD_CU_Q);
+      s_flag = ok && valid;
+    }
+    __syncthreads();
+    const bool go = s_flag;
+    if (go && q > 0) accept_request<true>(a, i, o, q);
+    __syncthreads();
+    if (tid == 0) {
+      if (!go || q == 0) a.accept_len[i] = 0;
+      __threadfence_block();
+      const int32_t *bt = c.block_tables + (size_t)i * c.max_blocks;
+      const int L = c.context_lens[i];
+      int *mv = moves + (size_t)i * kFusedMoveWords;
+      const int nmove = go ? compact_moves(a.accepted_path + o, a.accept_len[i], q, L, bt, c.max_blocks,
+                                           c.num_pages, s_src, s_dst)
+                           : -1;
+      store_coherent(&mv[0], nmove);
+      for (int m = 0; m < nmove; ++m) {
+        store_coherent(&mv[1 + m], s_src[m]);
+        store_coherent(&mv[1 + (kMaxTokens - 1) + m], s_dst[m]);
+      }
+      c.new_context_lens[i] = nmove >= 0 ? L + a.accept_len[i] : -1;
+      stores_complete();
+      store_coherent(&done[i], 1);
+    }
+  } else if (t < n_total) {
+    // 3. one compaction group of request i (trees only)
+    const int ci = t - n_slices - a.batch;
+    const int i = ci / groups, g = ci - (ci / groups) * groups;
+    if (tid < 64) {  // one wave: wait for the walk, then lane m fetches move m
+      bool ok = true;
+      if (tid == 0) ok = wait_at_least(&done[i], 1, abort);
+      ok = __shfl(ok, 0);
+      if (!ok && tid == 0) atomicOr(status, SV_DEV_SYNC_TIMEOUT);
+      const int *mv = moves + (size_t)i * kFusedMoveWords;
+      const int n = ok ? load_coherent(&mv[0]) : 0;
+      if (tid < n) {
+        s_src[tid] = load_coherent(&mv[1 + tid]);
+        s_dst[tid] = load_coherent(&mv[1 + (kMaxTokens - 1) + tid]);
+      }
+      if (tid == 0) s_nmove = n > 0 ? n : 0;
+    }
+    __syncthreads();
+    if (s_nmove > 0)
+      compact_pairs<D>(c.k_cache, c.v_cache, c.layer_stride, c.num_layers, c.num_kv_heads,
+                       c.block_tables + (size_t)i * c.max_blocks, s_src, s_dst, s_nmove, g, groups);
+  }
+  // The last waiting item to finish clears the counters for the next call.
+  // Only the waiting items count: every slice is done before its request's
+  // walk starts, so once all walks and moves are done, so is everything.
+  if (blockIdx.x < n_slices) return;
+  __syncthreads();
+  if (tid == 0)
+    s_flag = __hip_atomic_fetch_add(&hdr[3], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             n_total - n_slices - 1;
+  __syncthreads();
+  if (s_flag) {
+    for (int r = tid; r < a.total_q; r += 256) arrive[r] = 0;
+    for (int i = tid; i < a.batch; i += 256) done[i] = 0;
+    if (tid == 0) {
+      hdr[2] = 0;
+      hdr[3] = 0;
+      hdr[4] = 0;
+      hdr[5] = 0;
+    }
+  }
+}
+
 }  // namespace
 
 void launch_accept(const AcceptArgs &a, hipStream_t stream) {
@@ -349,6 +574,28 @@ void launch_accept_chunk(const AcceptArgs &a, hipStream_t stream) {
 
 void launch_chunk_start(const AcceptArgs &a, hipStream_t stream) {
   chunk_scan_kernel<<<1, kPlanThreads, 0, stream>>>(a, true);
+}
+
+}  // namespace sv
+
+namespace sv {
+
+void launch_accept_compact(const AcceptArgs &a, const CompactArgs &c, hipStream_t stream) {
+  const int n_slices = a.total_q * a.lay.splits;
+  const int pairs = c.num_layers * c.num_kv_heads;
+  int groups = 0;
+  if (a.tree_parent != nullptr && pairs > 0) {
+    // fewer, longer compaction items than kv_compact's grid: each item takes a
+    // ticket and counts itself out with an atomic on one address
+    groups = kFusedCompactItems / (a.batch > 0 ? a.batch : 1);
+    if (groups > pairs) groups = pairs;
+    if (groups < 1) groups = 1;
+  }
+  const int n_total = n_slices + a.batch + a.batch * groups;
+  if (c.head_dim == 128)
+    accept_compact_kernel<128><<<n_total, 256, 0, stream>>>(a, c, n_slices, groups, n_total);
+  else
+    accept_compact_kernel<64><<<n_total, 256, 0, stream>>>(a, c, n_slices, groups, n_total);
 }
 
 }  // namespace sv

@@ -48,6 +48,107 @@ int read_status(const void *workspace, size_t offset, uint32_t *flags, void *str
   return ok();
 }
 
+int accept_args(const float *logits, int vocab, const int32_t *draft_tokens, const int32_t *cu_q,
+                const int32_t *tree_parent, int batch, int total_q, int32_t *target_argmax,
+                int32_t *accept_len, int32_t *accepted_path, int32_t *out_tokens, void *workspace,
+                size_t workspace_bytes, bool fused, sv::AcceptArgs *out, bool *empty) {
+  *empty = false;
+  if (batch < 0 || total_q < 0)
+    return fail(SV_ERR_SHAPE, "batch (%d) and total_q (%d) must be >= 0", batch, total_q);
+  if (vocab <= 0) return fail(SV_ERR_SHAPE, "vocab %d must be > 0", vocab);
+  if (total_q > (long long)batch * sv::kMaxTokens)
+    return fail(SV_ERR_SHAPE, "total_q %d exceeds batch*64", total_q);
+  if (batch == 0) {
+    *empty = true;
+    return ok();
+  }
+  if (!cu_q || !accept_len || !workspace)
+    return fail(SV_ERR_NULL, "acceptance: a required pointer is NULL");
+  if (total_q > 0 && (!logits || !draft_tokens || !target_argmax || !accepted_path || !out_tokens))
+    return fail(SV_ERR_NULL, "acceptance: a required pointer is NULL");
+  const sv::AcceptLayout lay = fused ? sv::fused_layout(batch, total_q, vocab)
+                                     : sv::accept_layout(batch, total_q, vocab);
+  if (workspace_bytes < lay.total)
+    return fail(SV_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, lay.total);
+  const size_t tb = (size_t)total_q * 4;
+  if (overlaps(target_argmax, tb, accepted_path, tb) || overlaps(target_argmax, tb, out_tokens, tb) ||
+      overlaps(accepted_path, tb, out_tokens, tb) ||
+      overlaps(accept_len, (size_t)batch * 4, target_argmax, tb) ||
+      overlaps(accept_len, (size_t)batch * 4, accepted_path, tb) ||
+      overlaps(accept_len, (size_t)batch * 4, out_tokens, tb))
+    return fail(SV_ERR_ALIAS, "spec_accept outputs overlap");
+  sv::AcceptArgs a;
+  memset(&a, 0, sizeof a);
+  a.logits = logits;
+  a.draft = draft_tokens;
+  a.cu_q = cu_q;
+  a.tree_parent = tree_parent;
+  a.target_argmax = target_argmax;
+  a.accept_len = accept_len;
+  a.accepted_path = accepted_path;
+  a.out_tokens = out_tokens;
+  a.ws = static_cast<char *>(workspace);
+  a.lay = lay;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.vocab = vocab;
+  a.rows = total_q;
+  *out = a;
+  return ok();
+}
+
+int compact_args(void *k_cache, void *v_cache, int64_t layer_stride_elems, int num_layers,
+                 const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+                 const int32_t *cu_q, const int32_t *accepted_path, const int32_t *accept_len,
+                 int32_t *new_context_lens, int batch, int total_q, int num_kv_heads, int head_dim,
+                 int page_size, int num_pages, sv::CompactArgs *out, bool *empty) {
+  *empty = false;
+  if (batch < 0 || total_q < 0 || num_layers < 0)
+    return fail(SV_ERR_SHAPE, "batch, total_q and num_layers must be >= 0");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+  if (page_size != sv::kPage)
+    return fail(SV_ERR_UNSUPPORTED, "page_size %d (supported: 16)", page_size);
+  if (num_kv_heads <= 0) return fail(SV_ERR_SHAPE, "num_kv_heads must be > 0");
+  if (batch == 0) {
+    *empty = true;
+    return ok();
+  }
+  if (!block_tables || !context_lens || !cu_q || !accept_len || !new_context_lens)
+    return fail(SV_ERR_NULL, "kv_compact: a required pointer is NULL");
+  if (num_layers > 0 && (!k_cache || !v_cache))
+    return fail(SV_ERR_NULL, "kv_compact: cache pointers are NULL");
+  if (total_q > 0 && !accepted_path) return fail(SV_ERR_NULL, "kv_compact: accepted_path is NULL");
+  if (max_blocks_per_seq <= 0 || num_pages <= 0)
+    return fail(SV_ERR_SHAPE, "max_blocks_per_seq and num_pages must be > 0");
+  const long long pool = (long long)num_pages * num_kv_heads * page_size * head_dim;
+  if (num_layers > 1 && layer_stride_elems < pool)
+    return fail(SV_ERR_SHAPE, "layer_stride_elems %lld smaller than one pool (%lld)",
+                (long long)layer_stride_elems, pool);
+  if (new_context_lens == context_lens ||
+      overlaps(new_context_lens, (size_t)batch * 4, context_lens, (size_t)batch * 4))
+    return fail(SV_ERR_ALIAS, "new_context_lens must not alias context_lens");
+  sv::CompactArgs a;
+  a.k_cache = static_cast<uint16_t *>(k_cache);
+  a.v_cache = static_cast<uint16_t *>(v_cache);
+  a.layer_stride = layer_stride_elems;
+  a.num_layers = num_layers;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.cu_q = cu_q;
+  a.accepted_path = accepted_path;
+  a.accept_len = accept_len;
+  a.new_context_lens = new_context_lens;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_pages = num_pages;
+  *out = a;
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -284,42 +385,11 @@ int spec_accept(const float *logits, int vocab, const int32_t *draft_tokens, con
                 const int32_t *tree_parent, int batch, int total_q, int32_t *target_argmax,
                 int32_t *accept_len, int32_t *accepted_path, int32_t *out_tokens, void *workspace,
                 size_t workspace_bytes, void *stream) {
-  if (batch < 0 || total_q < 0)
-    return fail(SV_ERR_SHAPE, "batch (%d) and total_q (%d) must be >= 0", batch, total_q);
-  if (vocab <= 0) return fail(SV_ERR_SHAPE, "vocab %d must be > 0", vocab);
-  if (total_q > (long long)batch * sv::kMaxTokens)
-    return fail(SV_ERR_SHAPE, "total_q %d exceeds batch*64", total_q);
-  if (batch == 0) return ok();
-  if (!cu_q || !accept_len || !workspace)
-    return fail(SV_ERR_NULL, "spec_accept: a required pointer is NULL");
-  if (total_q > 0 && (!logits || !draft_tokens || !target_argmax || !accepted_path || !out_tokens))
-    return fail(SV_ERR_NULL, "spec_accept: a required pointer is NULL");
-  const sv::AcceptLayout lay = sv::accept_layout(batch, total_q, vocab);
-  if (workspace_bytes < lay.total)
-    return fail(SV_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, lay.total);
-  const size_t tb = (size_t)total_q * 4;
-  if (overlaps(target_argmax, tb, accepted_path, tb) || overlaps(target_argmax, tb, out_tokens, tb) ||
-      overlaps(accepted_path, tb, out_tokens, tb) ||
-      overlaps(accept_len, (size_t)batch * 4, target_argmax, tb) ||
-      overlaps(accept_len, (size_t)batch * 4, accepted_path, tb) ||
-      overlaps(accept_len, (size_t)batch * 4, out_tokens, tb))
-    return fail(SV_ERR_ALIAS, "spec_accept outputs overlap");
   sv::AcceptArgs a;
-  memset(&a, 0, sizeof a);
-  a.logits = logits;
-  a.draft = draft_tokens;
-  a.cu_q = cu_q;
-  a.tree_parent = tree_parent;
-  a.target_argmax = target_argmax;
-  a.accept_len = accept_len;
-  a.accepted_path = accepted_path;
-  a.out_tokens = out_tokens;
-  a.ws = static_cast<char *>(workspace);
-  a.lay = lay;
-  a.batch = batch;
-  a.total_q = total_q;
-  a.vocab = vocab;
-  a.rows = total_q;
+  bool empty;
+  int rc = accept_args(logits, vocab, draft_tokens, cu_q, tree_parent, batch, total_q, target_argmax,
+                       accept_len, accepted_path, out_tokens, workspace, workspace_bytes, false, &a, &empty);
+  if (rc != SV_OK || empty) return rc;
   sv::launch_accept(a, static_cast<hipStream_t>(stream));
   return check_launch("spec_accept");
 }
@@ -420,47 +490,45 @@ int kv_compact(void *k_cache, void *v_cache, int64_t layer_stride_elems, int num
                const int32_t *cu_q, const int32_t *accepted_path, const int32_t *accept_len,
                int32_t *new_context_lens, int batch, int total_q, int num_kv_heads, int head_dim,
                int page_size, int num_pages, void *stream) {
-  if (batch < 0 || total_q < 0 || num_layers < 0)
-    return fail(SV_ERR_SHAPE, "batch, total_q and num_layers must be >= 0");
-  if (head_dim != 64 && head_dim != 128)
-    return fail(SV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
-  if (page_size != sv::kPage)
-    return fail(SV_ERR_UNSUPPORTED, "page_size %d (supported: 16)", page_size);
-  if (num_kv_heads <= 0) return fail(SV_ERR_SHAPE, "num_kv_heads must be > 0");
-  if (batch == 0) return ok();
-  if (!block_tables || !context_lens || !cu_q || !accept_len || !new_context_lens)
-    return fail(SV_ERR_NULL, "kv_compact: a required pointer is NULL");
-  if (num_layers > 0 && (!k_cache || !v_cache))
-    return fail(SV_ERR_NULL, "kv_compact: cache pointers are NULL");
-  if (total_q > 0 && !accepted_path) return fail(SV_ERR_NULL, "kv_compact: accepted_path is NULL");
-  if (max_blocks_per_seq <= 0 || num_pages <= 0)
-    return fail(SV_ERR_SHAPE, "max_blocks_per_seq and num_pages must be > 0");
-  const long long pool = (long long)num_pages * num_kv_heads * page_size * head_dim;
-  if (num_layers > 1 && layer_stride_elems < pool)
-    return fail(SV_ERR_SHAPE, "layer_stride_elems %lld smaller than one pool (%lld)",
-                (long long)layer_stride_elems, pool);
-  if (new_context_lens == context_lens ||
-      overlaps(new_context_lens, (size_t)batch * 4, context_lens, (size_t)batch * 4))
-    return fail(SV_ERR_ALIAS, "new_context_lens must not alias context_lens");
   sv::CompactArgs a;
-  a.k_cache = static_cast<uint16_t *>(k_cache);
-  a.v_cache = static_cast<uint16_t *>(v_cache);
-  a.layer_stride = layer_stride_elems;
-  a.num_layers = num_layers;
-  a.block_tables = block_tables;
-  a.max_blocks = max_blocks_per_seq;
-  a.context_lens = context_lens;
-  a.cu_q = cu_q;
-  a.accepted_path = accepted_path;
-  a.accept_len = accept_len;
-  a.new_context_lens = new_context_lens;
-  a.batch = batch;
-  a.total_q = total_q;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.num_pages = num_pages;
+  bool empty;
+  int rc = compact_args(k_cache, v_cache, layer_stride_elems, num_layers, block_tables, max_blocks_per_seq,
+                        context_lens, cu_q, accepted_path, accept_len, new_context_lens, batch, total_q,
+                        num_kv_heads, head_dim, page_size, num_pages, &a, &empty);
+  if (rc != SV_OK || empty) return rc;
   sv::launch_kv_compact(a, static_cast<hipStream_t>(stream));
   return check_launch("kv_compact");
+}
+
+size_t spec_accept_compact_workspace_size(int batch, int total_q, int vocab) {
+  if (batch < 0 || total_q < 0 || vocab <= 0) return 0;
+  return sv::fused_layout(batch, total_q, vocab).total;
+}
+
+int spec_accept_compact(const float *logits, int vocab, const int32_t *draft_tokens,
+                        const int32_t *cu_q, const int32_t *tree_parent, int batch, int total_q,
+                        int32_t *target_argmax, int32_t *accept_len, int32_t *accepted_path,
+                        int32_t *out_tokens, void *k_cache, void *v_cache,
+                        int64_t layer_stride_elems, int num_layers, const int32_t *block_tables,
+                        int max_blocks_per_seq, const int32_t *context_lens,
+                        int32_t *new_context_lens, int num_kv_heads, int head_dim, int page_size,
+                        int num_pages, void *workspace, size_t workspace_bytes, void *stream) {
+  sv::AcceptArgs a;
+  sv::CompactArgs c;
+  bool empty_a, empty_c;
+  int rc = accept_args(logits, vocab, draft_tokens, cu_q, tree_parent, batch, total_q, target_argmax,
+                       accept_len, accepted_path, out_tokens, workspace, workspace_bytes, true, &a, &empty_a);
+  if (rc != SV_OK) return rc;
+  rc = compact_args(k_cache, v_cache, layer_stride_elems, num_layers, block_tables, max_blocks_per_seq,
+                    context_lens, cu_q, accepted_path, accept_len, new_context_lens, batch, total_q,
+                    num_kv_heads, head_dim, page_size, num_pages, &c, &empty_c);
+  if (rc != SV_OK || empty_a || empty_c) return rc;
+  const size_t tb = (size_t)total_q * 4, bb = (size_t)batch * 4;
+  if (overlaps(new_context_lens, bb, accept_len, bb) || overlaps(new_context_lens, bb, target_argmax, tb) ||
+      overlaps(new_context_lens, bb, accepted_path, tb) || overlaps(new_context_lens, bb, out_tokens, tb))
+    return fail(SV_ERR_ALIAS, "spec_accept_compact outputs overlap");
+  sv::launch_accept_compact(a, c, static_cast<hipStream_t>(stream));
+  return check_launch("spec_accept_compact");
 }
 
 }  // extern "C"

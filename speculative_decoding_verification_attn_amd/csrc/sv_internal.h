@@ -120,12 +120,17 @@ constexpr int kArgmaxMinSlice = 4096;
 constexpr int kArgmaxMaxSplits = 64;
 
 struct AcceptLayout {
-  size_t hdr;       // int32[8]: 0 status bits
+  size_t hdr;       // int32[8]: 0 status bits; fused launch: 2 ticket, 3 finished, 4 status cleared, 5 abort
   size_t part;      // {float value, int index}[rows][splits]
   size_t next_len;  // int32[batch]: rows of each request in the next chunk (chunked acceptance)
+  // fused acceptance + compaction only (0 otherwise)
+  size_t arrive;    // int32[rows]: slices of each row done
+  size_t done;      // int32[batch]: request walked, moves listed
+  size_t moves;     // int32[batch][kFusedMoveWords]: move count (-1: bad path), then src, dst lists
   size_t total;
   int splits;
 };
+constexpr int kFusedMoveWords = 2 * kMaxTokens;
 
 __host__ __device__ inline int argmax_splits(int total_q, int vocab) {
   int s = (kArgmaxTargetGroups + (total_q > 0 ? total_q : 1) - 1) / (total_q > 0 ? total_q : 1);
@@ -144,6 +149,17 @@ __host__ __device__ inline AcceptLayout accept_layout(int batch, int rows, int v
   l.hdr = off;       off = align256(off + 8 * sizeof(int32_t));
   l.part = off;      off = align256(off + size_t(rows) * l.splits * 8);
   l.next_len = off;  off = align256(off + size_t(batch) * sizeof(int32_t));
+  l.arrive = l.done = l.moves = 0;
+  l.total = off;
+  return l;
+}
+
+__host__ __device__ inline AcceptLayout fused_layout(int batch, int rows, int vocab) {
+  AcceptLayout l = accept_layout(batch, rows, vocab);
+  size_t off = l.total;
+  l.arrive = off;  off = align256(off + size_t(rows) * sizeof(int32_t));
+  l.done = off;    off = align256(off + size_t(batch) * sizeof(int32_t));
+  l.moves = off;   off = align256(off + size_t(batch) * kFusedMoveWords * sizeof(int32_t));
   l.total = off;
   return l;
 }
@@ -172,6 +188,7 @@ struct AcceptArgs {
 };
 
 void launch_accept(const AcceptArgs &a, hipStream_t stream);
+
 void launch_accept_chunk(const AcceptArgs &a, hipStream_t stream);
 // first chunk: next_begin = 0, rows min(chunk_size, q_i), packed in next_cu
 void launch_chunk_start(const AcceptArgs &a, hipStream_t stream);
@@ -195,5 +212,8 @@ struct CompactArgs {
 };
 
 void launch_kv_compact(const CompactArgs &a, hipStream_t stream);
+
+// acceptance and compaction in one launch (a.lay from fused_layout)
+void launch_accept_compact(const AcceptArgs &a, const CompactArgs &c, hipStream_t stream);
 
 }  // namespace sv

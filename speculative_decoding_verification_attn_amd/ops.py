@@ -29,13 +29,15 @@ DEV_TOO_MANY_TOKENS = 0x4
 DEV_BAD_PARENT = 0x8
 DEV_BAD_PAGE = 0x10
 DEV_TOO_MANY_PAGES = 0x20
+DEV_SYNC_TIMEOUT = 0x40
 
 EXPORTED = ["spec_verify_attn_workspace_size", "spec_verify_attn", "spec_verify_attn_plan",
             "spec_verify_attn_run", "spec_verify_attn_device_status",
             "spec_accept_workspace_size", "spec_accept", "spec_accept_device_status",
             "kv_compact", "sv_status_string", "sv_last_error",
             "spec_verify_attn_chunk_plan", "spec_verify_attn_chunk_run", "spec_chunk_start",
-            "spec_accept_chunk_workspace_size", "spec_accept_chunk", "spec_verify_budget"]
+            "spec_accept_chunk_workspace_size", "spec_accept_chunk", "spec_verify_budget",
+            "spec_accept_compact_workspace_size", "spec_accept_compact"]
 
 _lib = None
 
@@ -87,6 +89,11 @@ def load_library():
     lib.spec_accept_chunk.restype = I
     lib.spec_verify_budget.argtypes = [P, P, I, P, P, I, P, P, ctypes.POINTER(ctypes.c_double)]
     lib.spec_verify_budget.restype = I
+    lib.spec_accept_compact_workspace_size.argtypes = [I, I, I]
+    lib.spec_accept_compact_workspace_size.restype = SZ
+    lib.spec_accept_compact.argtypes = [P, I, P, P, P, I, I, P, P, P, P, P, P, I64, I, P, I, P, P, I, I, I, I,
+                                        P, SZ, P]
+    lib.spec_accept_compact.restype = I
     lib.sv_status_string.argtypes = [I]
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_last_error.argtypes = []
@@ -376,3 +383,45 @@ def spec_verify_budget(cond_survival, cu_draft, sps_rows, sps_value):
     _check(lib.spec_verify_budget(p(c) if c.size else None, p(cu), B, p(r), p(v), len(r), p(out),
                                   ctypes.byref(rows), ctypes.byref(th)))
     return out[:B], int(rows.value), float(th.value)
+
+
+# ----------------------------------------------------------------------------
+# Fused acceptance + compaction
+def spec_accept_compact_workspace_size(batch, total_q, vocab) -> int:
+    return int(load_library().spec_accept_compact_workspace_size(batch, total_q, vocab))
+
+
+def spec_accept_compact(logits, draft_tokens, cu_q, tree_parent, k_cache, v_cache, block_tables,
+                        context_lens, *, workspace, num_layers=1, layer_stride_elems=None,
+                        target_argmax=None, accept_len=None, accepted_path=None, out_tokens=None,
+                        new_context_lens=None, stream=None):
+    """spec_accept + kv_compact in one launch.  `workspace` (uint8, at least
+    spec_accept_compact_workspace_size bytes) must be zero-filled before its first use.
+    Returns (target_argmax, accept_len, accepted_path, out_tokens, new_context_lens)."""
+    lib = load_library()
+    _dev(logits, torch.float32, "logits")
+    _dev(k_cache, torch.bfloat16, "k_cache")
+    _dev(v_cache, torch.bfloat16, "v_cache")
+    for t, nm in ((draft_tokens, "draft_tokens"), (cu_q, "cu_q"), (tree_parent, "tree_parent"),
+                  (block_tables, "block_tables"), (context_lens, "context_lens")):
+        _dev(t, torch.int32, nm)
+    T, V = logits.shape
+    B = cu_q.shape[0] - 1
+    dev = logits.device
+    mk = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
+    target_argmax = mk(T) if target_argmax is None else target_argmax
+    accept_len = mk(B) if accept_len is None else accept_len
+    accepted_path = mk(T) if accepted_path is None else accepted_path
+    out_tokens = mk(T) if out_tokens is None else out_tokens
+    new_context_lens = mk(B) if new_context_lens is None else new_context_lens
+    shp = k_cache.shape
+    num_kv_heads, head_dim, num_pages = shp[-3], shp[-1], shp[-4]
+    if layer_stride_elems is None:
+        layer_stride_elems = num_pages * num_kv_heads * 16 * head_dim
+    _check(lib.spec_accept_compact(_ptr(logits), V, _ptr(draft_tokens), _ptr(cu_q), _ptr(tree_parent), B, T,
+                                   _ptr(target_argmax), _ptr(accept_len), _ptr(accepted_path), _ptr(out_tokens),
+                                   _ptr(k_cache), _ptr(v_cache), int(layer_stride_elems), int(num_layers),
+                                   _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                                   _ptr(new_context_lens), num_kv_heads, head_dim, 16, num_pages,
+                                   _ptr(workspace), workspace.numel(), _stream(stream)))
+    return target_argmax, accept_len, accepted_path, out_tokens, new_context_lens

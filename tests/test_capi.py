@@ -162,3 +162,25 @@ def test_chunk_validation(lib):
     assert plan(D=96) == ops.SV_ERR_UNSUPPORTED
     assert plan(wsb=8) == ops.SV_ERR_WORKSPACE
     assert plan(Tc=0) == ops.SV_OK
+
+
+def test_fused_validation(lib):
+    def call(**kw):
+        a = dict(logits=FAKE, V=100, dr=FAKE, cu=FAKE, par=NULL, B=2, T=8, t=ctypes.c_void_p(0x100000),
+                 acc=ctypes.c_void_p(0x200000), path=ctypes.c_void_p(0x300000), toks=ctypes.c_void_p(0x400000),
+                 k=FAKE, v=FAKE, stride=10 * 2 * 16 * 64, L=1, bt=FAKE, mb=4, ctx=ctypes.c_void_p(0x500000),
+                 new=ctypes.c_void_p(0x600000), Hkv=2, D=64, P=16, pages=10, ws=FAKE, wsb=1 << 30, stream=NULL)
+        a.update(kw)
+        return lib.spec_accept_compact(a["logits"], a["V"], a["dr"], a["cu"], a["par"], a["B"], a["T"], a["t"],
+                                       a["acc"], a["path"], a["toks"], a["k"], a["v"], a["stride"], a["L"],
+                                       a["bt"], a["mb"], a["ctx"], a["new"], a["Hkv"], a["D"], a["P"], a["pages"],
+                                       a["ws"], a["wsb"], a["stream"])
+    assert call(V=0) == ops.SV_ERR_SHAPE
+    assert call(D=96) == ops.SV_ERR_UNSUPPORTED
+    assert call(logits=NULL) == ops.SV_ERR_NULL
+    assert call(bt=NULL) == ops.SV_ERR_NULL
+    assert call(wsb=8) == ops.SV_ERR_WORKSPACE
+    assert call(new=ctypes.c_void_p(0x500000)) == ops.SV_ERR_ALIAS
+    assert call(new=ctypes.c_void_p(0x200004)) == ops.SV_ERR_ALIAS
+    assert call(B=0, T=0) == ops.SV_OK
+    assert lib.spec_accept_compact_workspace_size(4, 20, 128256) > lib.spec_accept_workspace_size(4, 20, 128256)

@@ -1,0 +1,120 @@
+"""Acceptance and compaction in one launch (SwiftSpec, "Fused Latency-Optimized
+Kernels") on the GPU, through the C ABI: the outputs and the whole multi-layer
+caches must equal the oracle's acceptance followed by its copy-based
+compaction, bit for bit, on several calls in a row on one workspace (the launch
+clears its own counters), eagerly and replayed from a HIP graph."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pins
+from gpu_util import DEV, DevCase, bf16_dev_to_u16, i32, note, u16_to_bf16_dev
+from speculative_decoding_verification_attn_amd import ops
+from speculative_decoding_verification_attn_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+LAYERS = 3
+
+
+def _tree(seed, nodes=64, depth=6):
+    return W.draw_tree(np.random.Generator(np.random.PCG64(seed)), nodes, depth, 4, 4)
+
+
+CASES = {
+    "trees_d128": dict(context_lens=[5, 18, 0, 250, 40],
+                       tree_parents=[pins.SMALL_TREES[0], pins.SMALL_TREES[1], np.array([-1, 0, 1, 1, 2], np.int32),
+                                     _tree(5), _tree(6, 30, 5)],
+                       hq=16, hkv=8, d=128, vocab=600, tree_match=(0.7, 0.6)),
+    "trees_d64": dict(context_lens=[100, 3, 17], tree_parents=[_tree(7), _tree(8, 20, 4), _tree(9, 9, 3)],
+                      hq=8, hkv=2, d=64, vocab=300, tree_match=(0.8, 0.7)),
+    "chains_d128": dict(context_lens=[0, 47, 64, 500], q_lens=[4, 9, 1, 6], hq=32, hkv=8, d=128, vocab=700,
+                        match_p=0.8),
+}
+
+
+def _caches(case):
+    rng = np.random.default_rng(1)
+    extra = lambda shp: W.f32_to_bf16_bits(rng.standard_normal(shp).astype(np.float32))
+    k = np.stack([case.k_cache] + [extra(case.k_cache.shape) for _ in range(LAYERS - 1)])
+    v = np.stack([case.v_cache] + [extra(case.v_cache.shape) for _ in range(LAYERS - 1)])
+    return k, v
+
+
+def _oracle(case, k_all, v_all):
+    t_ref = oracle.argmax(case.logits)
+    acc, path, toks = oracle.accept(case.draft_tokens, t_ref, case.cu_q, case.tree_parent)
+    k_ref, v_ref = k_all.copy(), v_all.copy()
+    new = oracle.compact(k_ref, v_ref, case.block_tables, case.context_lens, case.cu_q, path, acc,
+                         num_kv_heads=case.num_kv_heads, head_dim=case.head_dim, page_size=16,
+                         num_pages=case.num_pages, num_layers=LAYERS)
+    return dict(t=t_ref, acc=acc, path=path, toks=toks, new=new, k=k_ref, v=v_ref)
+
+
+def _check(ref, outs, kd, vd, tag):
+    t, acc, path, toks, new = [x.cpu().numpy() for x in outs]
+    assert np.array_equal(t, ref["t"]), tag
+    assert np.array_equal(acc, ref["acc"]), tag
+    assert np.array_equal(path, ref["path"]), tag
+    assert np.array_equal(toks, ref["toks"]), tag
+    assert np.array_equal(new, ref["new"]), tag
+    assert np.array_equal(bf16_dev_to_u16(kd), ref["k"]), tag
+    assert np.array_equal(bf16_dev_to_u16(vd), ref["v"]), tag
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_fused_equals_oracle_on_repeated_calls(name):
+    case = W.make_custom(400 + list(CASES).index(name), **CASES[name])
+    dc = DevCase(case)
+    k_all, v_all = _caches(case)
+    ref = _oracle(case, k_all, v_all)
+    if case.tree_parent is not None:
+        assert not np.array_equal(ref["k"], k_all)  # something really moves
+    ws = torch.zeros(ops.spec_accept_compact_workspace_size(case.batch, case.total_q, case.vocab),
+                     dtype=torch.uint8, device=DEV)
+    for rep in range(3):
+        note(f"[gpu] spec_accept_compact {name} call {rep}")
+        kd, vd = u16_to_bf16_dev(k_all), u16_to_bf16_dev(v_all)
+        outs = ops.spec_accept_compact(dc.logits, dc.draft, dc.cu, dc.par, kd, vd, dc.bt, dc.ctx,
+                                       workspace=ws, num_layers=LAYERS)
+        torch.cuda.synchronize()
+        assert ops.spec_accept_device_status(ws) == 0
+        _check(ref, outs, kd, vd, f"{name} call {rep}")
+
+
+def test_fused_graph_replays():
+    """The fused call captured in a HIP graph, replayed with eager cache restores between."""
+    name = "trees_d128"
+    case = W.make_custom(400, **CASES[name])
+    dc = DevCase(case)
+    k_all, v_all = _caches(case)
+    ref = _oracle(case, k_all, v_all)
+    k0, v0 = u16_to_bf16_dev(k_all), u16_to_bf16_dev(v_all)
+    kd, vd = k0.clone(), v0.clone()
+    ws = torch.zeros(ops.spec_accept_compact_workspace_size(case.batch, case.total_q, case.vocab),
+                     dtype=torch.uint8, device=DEV)
+    B, T = case.batch, case.total_q
+    outs = [torch.empty(n, dtype=torch.int32, device=DEV) for n in (T, B, T, T, B)]
+
+    def call():
+        ops.spec_accept_compact(dc.logits, dc.draft, dc.cu, dc.par, kd, vd, dc.bt, dc.ctx, workspace=ws,
+                                num_layers=LAYERS, target_argmax=outs[0], accept_len=outs[1],
+                                accepted_path=outs[2], out_tokens=outs[3], new_context_lens=outs[4])
+
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        kd.copy_(k0)
+        vd.copy_(v0)
+        for o in outs:
+            o.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert ops.spec_accept_device_status(ws) == 0
+        _check(ref, outs, kd, vd, f"replay {rep}")
+        note(f"[gpu] fused replay {rep} ok")
