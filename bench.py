@@ -57,6 +57,9 @@ def main():
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MB "
                          "(reference for the HBM traffic counters)")
+    ap.add_argument("--stochastic", action="store_true",
+                    help="stochastic acceptance (speculative sampling) instead of greedy; synthetic drafter "
+                         "distributions = softmax of perturbed logits")
     ap.add_argument("--fused", action="store_true",
                     help="acceptance and compaction as one launch (spec_accept_compact)")
     ap.add_argument("--chunk", type=int, default=0,
@@ -128,6 +131,15 @@ def main():
     path = torch.empty(T, dtype=torch.int32, device=dev)
     toks = torch.empty(T, dtype=torch.int32, device=dev)
     new_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if args.stochastic:
+        if case.tree_parent is not None:
+            raise SystemExit("--stochastic covers chains only")
+        g = torch.Generator(device=dev).manual_seed(1234)
+        dprobs = torch.softmax(logits + 0.3 * torch.randn(logits.shape, device=dev, generator=g), dim=-1)
+        u_acc = torch.rand(T, device=dev, generator=g)
+        w_smp = torch.rand(B, device=dev, generator=g)
+        ws_sto = torch.empty(ops.spec_accept_stochastic_workspace_size(B, T, case.vocab), dtype=torch.uint8,
+                             device=dev)
     ws_fused = torch.zeros(ops.spec_accept_compact_workspace_size(B, T, case.vocab), dtype=torch.uint8,
                            device=dev) if args.fused else None
     stream = torch.cuda.current_stream()
@@ -153,6 +165,10 @@ def main():
         ops.spec_verify_attn_run(q, K[c], V[c], bt, ctx, cu, par, out=out, workspace=ws_attn, stream=st)
 
     def phase_accept(st):
+        if args.stochastic:
+            ops.spec_accept_stochastic(logits, dprobs, draft, u_acc, w_smp, cu, workspace=ws_sto, accept_len=acc,
+                                       accepted_path=path, out_tokens=toks, stream=st)
+            return
         if args.fused:  # acceptance and compaction in one launch; the compact phase is then empty
             ops.spec_accept_compact(logits, draft, cu, par, K, V, bt, ctx, workspace=ws_fused, num_layers=copies,
                                     target_argmax=t_arg, accept_len=acc, accepted_path=path, out_tokens=toks,
@@ -309,6 +325,7 @@ def main():
         "accept_gbs": round(logits_bytes / (accept_ms * 1e-3) / 1e9, 1),
         "compact_us": round(compact_ms * 1e3, 2),
         "accept_compact": "one launch (spec_accept_compact)" if args.fused else "two calls (spec_accept, kv_compact)",
+        "acceptance": "stochastic (speculative sampling)" if args.stochastic else "greedy",
         "verified_tokens_per_s": round(verified_tok_s, 1),
         "mean_accept_len": round(float(acc_np.mean()), 4),
         "roofline": {"kernel": "spec_verify_attn_run (verify_attn_kernel + attn_merge_kernel, per layer)",

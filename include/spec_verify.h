@@ -86,6 +86,7 @@ typedef enum sv_status {
 #define SV_DEV_BAD_PAGE 0x10u       /* a needed block-table entry is outside [0, num_pages) */
 #define SV_DEV_TOO_MANY_PAGES 0x20u /* ceil((L_i+q_i)/page_size) > max_blocks_per_seq */
 #define SV_DEV_SYNC_TIMEOUT 0x40u   /* spec_accept_compact: a bounded wait between work items ran out */
+#define SV_DEV_BAD_TOKEN 0x80u      /* spec_accept_stochastic: a draft token outside [0, vocab) */
 
 /* ------------------------------------------------------------------------- */
 /* Verify attention                                                           */
@@ -216,6 +217,44 @@ int kv_compact(void *k_cache, void *v_cache, int64_t layer_stride_elems, int num
                const int32_t *cu_q, const int32_t *accepted_path, const int32_t *accept_len,
                int32_t *new_context_lens, int batch, int total_q, int num_kv_heads, int head_dim,
                int page_size, int num_pages, void *stream);
+
+/* ------------------------------------------------------------------------- */
+/* Lossless stochastic acceptance (chains)                                    */
+/* ------------------------------------------------------------------------- */
+/*
+ * DSpark, glossary "Speculative Decoding": the verification rule keeps the
+ * target's distribution.  The rule is speculative sampling (rejection
+ * sampling): for request i with verify rows o..o+gamma (row o = root),
+ *   p_j = softmax(logits[o+j-1] / temperature), q_j = draft_probs[o+j];
+ *   draft j is accepted iff u[o+j] * q_j(x_j) < p_j(x_j), x_j = draft_tokens[o+j];
+ *   the walk stops at the first rejection; n = accepted drafts;
+ *   y = the smallest v whose cumulative weight exceeds w[i] * (total weight),
+ *   the weights being max(0, p_{n+1} - q_{n+1}) after a rejection (p_{n+1}
+ *   if those have no mass) and p_{gamma+1} when every draft was accepted.
+ * Outputs: accept_len[i] = n + 1; accepted_path[o+k] = k for k <= n, -1 after;
+ * out_tokens[o+k] = x_{k+1} for k < n, out_tokens[o+n] = y, -1 after.  The
+ * random numbers are inputs (uniform in [0, 1)), so a call is deterministic.
+ * Arithmetic is fp32 (exp2 of logit*log2(e)/T): an acceptance or a draw whose
+ * margin is within fp32 rounding may differ from an fp64 evaluation.
+ *
+ *   logits, draft_probs  fp32 [total_q, vocab] (draft_probs row o, the root, unused;
+ *                        each draft row sums to 1)
+ *   draft_tokens int32 [total_q]; uniform_accept fp32 [total_q]; uniform_sample fp32 [batch]
+ *   temperature  > 0;  chains only (no tree_parent)
+ *   workspace    at least spec_accept_stochastic_workspace_size() bytes (no initialisation)
+ * Device status (spec_accept_stochastic_device_status): SV_DEV_BAD_CU_Q,
+ * SV_DEV_BAD_TOKEN.
+ */
+size_t spec_accept_stochastic_workspace_size(int batch, int total_q, int vocab);
+
+int spec_accept_stochastic(const float *logits, const float *draft_probs, int vocab,
+                           float temperature, const int32_t *draft_tokens,
+                           const float *uniform_accept, const float *uniform_sample,
+                           const int32_t *cu_q, int batch, int total_q, int32_t *accept_len,
+                           int32_t *accepted_path, int32_t *out_tokens, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+int spec_accept_stochastic_device_status(const void *workspace, uint32_t *flags, void *stream);
 
 /* ------------------------------------------------------------------------- */
 /* Fused acceptance + compaction                                              */

@@ -500,6 +500,60 @@ int kv_compact(void *k_cache, void *v_cache, int64_t layer_stride_elems, int num
   return check_launch("kv_compact");
 }
 
+size_t spec_accept_stochastic_workspace_size(int batch, int total_q, int vocab) {
+  if (batch < 0 || total_q < 0 || vocab <= 0) return 0;
+  return sv::stoch_layout(batch, total_q, vocab).total;
+}
+
+int spec_accept_stochastic(const float *logits, const float *draft_probs, int vocab,
+                           float temperature, const int32_t *draft_tokens,
+                           const float *uniform_accept, const float *uniform_sample,
+                           const int32_t *cu_q, int batch, int total_q, int32_t *accept_len,
+                           int32_t *accepted_path, int32_t *out_tokens, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  if (batch < 0 || total_q < 0 || total_q > (long long)batch * sv::kMaxTokens)
+    return fail(SV_ERR_SHAPE, "batch (%d) and total_q (%d) out of range", batch, total_q);
+  if (vocab <= 0) return fail(SV_ERR_SHAPE, "vocab %d must be > 0", vocab);
+  if (!(temperature > 0.0f) || !isfinite(temperature))
+    return fail(SV_ERR_SHAPE, "temperature must be finite and > 0");
+  if (batch == 0) return ok();
+  if (!cu_q || !accept_len || !uniform_sample || !workspace)
+    return fail(SV_ERR_NULL, "spec_accept_stochastic: a required pointer is NULL");
+  if (total_q > 0 && (!logits || !draft_probs || !draft_tokens || !uniform_accept || !accepted_path ||
+                      !out_tokens))
+    return fail(SV_ERR_NULL, "spec_accept_stochastic: a required pointer is NULL");
+  const sv::StochLayout lay = sv::stoch_layout(batch, total_q, vocab);
+  if (workspace_bytes < lay.total)
+    return fail(SV_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, lay.total);
+  const size_t tb = (size_t)total_q * 4, bb = (size_t)batch * 4;
+  if (overlaps(accepted_path, tb, out_tokens, tb) || overlaps(accept_len, bb, accepted_path, tb) ||
+      overlaps(accept_len, bb, out_tokens, tb))
+    return fail(SV_ERR_ALIAS, "spec_accept_stochastic outputs overlap");
+  sv::StochArgs a;
+  memset(&a, 0, sizeof a);
+  a.logits = logits;
+  a.draft_probs = draft_probs;
+  a.draft = draft_tokens;
+  a.u = uniform_accept;
+  a.w = uniform_sample;
+  a.cu_q = cu_q;
+  a.accept_len = accept_len;
+  a.accepted_path = accepted_path;
+  a.out_tokens = out_tokens;
+  a.ws = static_cast<char *>(workspace);
+  a.lay = lay;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.vocab = vocab;
+  a.c = 1.4426950408889634f / temperature;
+  sv::launch_stochastic(a, static_cast<hipStream_t>(stream));
+  return check_launch("spec_accept_stochastic");
+}
+
+int spec_accept_stochastic_device_status(const void *workspace, uint32_t *flags, void *stream) {
+  return read_status(workspace, 0, flags, stream);
+}
+
 size_t spec_accept_compact_workspace_size(int batch, int total_q, int vocab) {
   if (batch < 0 || total_q < 0 || vocab <= 0) return 0;
   return sv::fused_layout(batch, total_q, vocab).total;

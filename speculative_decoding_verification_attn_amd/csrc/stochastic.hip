@@ -1,0 +1,365 @@
+// Lossless stochastic acceptance of drafted chains (speculative sampling) on
+// gfx950.
+//
+// What is computed: DSpark's glossary ("Speculative Decoding") requires the
+// verification rule to keep the target's distribution; the rule used is the
+// standard speculative-sampling rejection rule.  For request i (verify tokens
+// 0..gamma at rows o..o+gamma, token 0 = root):
+//   p_j = softmax(logits[o+j-1] / temperature)   target distribution of position j
+//   q_j = draft_probs[o+j]                        drafter's distribution of draft x_j
+//   draft j is accepted iff u[o+j] * q_j(x_j) < p_j(x_j); the walk stops at the
+//   first rejection; n = accepted drafts;
+//   the next token y is drawn with w[i] by inverse CDF from max(0, p - q) at
+//   position n+1 (a rejection), or from p_{gamma+1} (all accepted); a residual
+//   without mass falls back to p_{n+1}.
+//
+// Four launches, all but the walk streaming over the vocabulary:
+//   softmax_stats_kernel  grid (splits, rows): per slice of a logits row the
+//                         running (max, sum of 2^(x - max)) of x = logit*log2(e)/T;
+//   stochastic_walk_kernel  one wave per request: merges the slices' stats,
+//                         tests every draft, writes the accepted prefix and the
+//                         sampling job (target row, draft row or none, w);
+//   sample_mass_kernel    grid (sub-slices of 2048 entries, batch): mass of the
+//                         draw's weights per sub-slice;
+//   sample_pick_kernel    one workgroup per request: finds the sub-slice holding
+//                         w * total, then the entry (thread sums of 8 entries,
+//                         their prefix, then the thread's own 8).
+#include "sv_device.h"
+#include "sv_internal.h"
+
+namespace sv {
+
+namespace {
+
+constexpr int kPickThreads = 256;
+
+struct Stat {
+  float m;  // max of x (log2 domain)
+  float s;  // sum of 2^(x - m)
+};
+
+__device__ inline Stat merge(Stat a, Stat b) {
+  const float M = fmaxf(a.m, b.m);
+  if (M == -INFINITY) return Stat{-INFINITY, 0.f};
+  return Stat{M, a.s * fast_exp2(a.m - M) + b.s * fast_exp2(b.m - M)};
+}
+
+__device__ inline Stat wave_merge(Stat x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    Stat y{__shfl_xor(x.m, d), __shfl_xor(x.s, d)};
+    x = merge(x, y);
+  }
+  return x;
+}
+
+__device__ inline void slice_bounds(int V, int splits, int split, int *lo, int *hi) {
+  int per = (V + splits - 1) / splits;
+  per = (per + 3) & ~3;
+  *lo = min(V, split * per);
+  *hi = min(V, *lo + per);
+}
+
+__global__ __launch_bounds__(256) void softmax_stats_kernel(StochArgs a) {
+  __shared__ float s_m[4], s_s[4];
+  const int split = blockIdx.x, row = blockIdx.y;
+  if (split == 0 && row == 0 && threadIdx.x == 0) reinterpret_cast<int32_t *>(a.ws + a.lay.hdr)[0] = 0;
+  if (row >= a.total_q) return;
+  int lo, hi;
+  slice_bounds(a.vocab, a.lay.splits, split, &lo, &hi);
+  const float *x = a.logits + (size_t)row * a.vocab;
+  Stat st{-INFINITY, 0.f};
+  auto add = [&](float l) {
+    const float y = l * a.c;
+    if (y > st.m) {
+      st.s = st.s * fast_exp2(st.m - y) + 1.f;
+      st.m = y;
+    } else if (y > -INFINITY) {
+      st.s += fast_exp2(y - st.m);
+    }
+  };
+  if ((a.vocab & 3) == 0) {
+    // 16-byte nontemporal loads, four in flight per thread (the row is read once)
+    const int nv = (hi - lo) >> 2;
+    const float4v *x4 = reinterpret_cast<const float4v *>(x + lo);
+    int k = threadIdx.x;
+    for (; k + 3 * 256 < nv; k += 4 * 256) {
+      float4v v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(x4 + k + u * 256);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        add(v[u].x);
+        add(v[u].y);
+        add(v[u].z);
+        add(v[u].w);
+      }
+    }
+    for (; k < nv; k += 256) {
+      const float4v v = __builtin_nontemporal_load(x4 + k);
+      add(v.x);
+      add(v.y);
+      add(v.z);
+      add(v.w);
+    }
+  } else {
+    for (int k = lo + threadIdx.x; k < hi; k += 256) add(__builtin_nontemporal_load(x + k));
+  }
+  st = wave_merge(st);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    s_m[wave] = st.m;
+    s_s[wave] = st.s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    Stat r{s_m[0], s_s[0]};
+    for (int w = 1; w < 4; ++w) r = merge(r, Stat{s_m[w], s_s[w]});
+    reinterpret_cast<float2 *>(a.ws + a.lay.stats)[(size_t)row * a.lay.splits + split] = make_float2(r.m, r.s);
+  }
+}
+
+// one wave per request
+__global__ __launch_bounds__(64) void stochastic_walk_kernel(StochArgs a) {
+  const int i = blockIdx.x;
+  const int j = threadIdx.x;
+  unsigned *status = reinterpret_cast<unsigned *>(a.ws + a.lay.hdr);
+  StochJob *jobs = reinterpret_cast<StochJob *>(a.ws + a.lay.jobs);
+  const int o = a.cu_q[i], c1 = a.cu_q[i + 1], q = c1 - o;
+  if (o < 0 || c1 < o || c1 > a.total_q || q > kMaxTokens) {
+    if (j == 0) {
+      atomicOr(status, SV_DEV_BAD_CU_Q);
+      a.accept_len[i] = 0;
+      jobs[i].tr = -1;
+    }
+    return;
+  }
+  if (i == 0 && j == 0 && (a.cu_q[0] != 0 || a.cu_q[a.batch] != a.total_q)) atomicOr(status, SV_DEV_BAD_CU_Q);
+  if (q == 0) {
+    if (j == 0) {
+      a.accept_len[i] = 0;
+      jobs[i].tr = -1;
+    }
+    return;
+  }
+  // stats of row o+j
+  Stat st{-INFINITY, 0.f};
+  if (j < q) {
+    const float2 *ps = reinterpret_cast<const float2 *>(a.ws + a.lay.stats) + (size_t)(o + j) * a.lay.splits;
+    for (int k = 0; k < a.lay.splits; ++k) {
+      const float2 v = ps[k];
+      st = merge(st, Stat{v.x, v.y});
+    }
+  }
+  // draft j (j >= 1) against row j-1
+  const Stat prev{__shfl(st.m, max(j - 1, 0)), __shfl(st.s, max(j - 1, 0))};
+  bool reject = false;
+  if (j >= 1 && j < q) {
+    const int x = a.draft[o + j];
+    if (x < 0 || x >= a.vocab) {
+      atomicOr(status, SV_DEV_BAD_TOKEN);
+      reject = true;
+    } else {
+      const float px = fast_exp2(a.logits[(size_t)(o + j - 1) * a.vocab + x] * a.c - prev.m) / prev.s;
+      const float qx = a.draft_probs[(size_t)(o + j) * a.vocab + x];
+      reject = !(a.u[o + j] * qx < px);
+    }
+  }
+  const uint64_t rej = __ballot(reject);
+  const int n = rej ? __builtin_ctzll(rej) - 1 : q - 1;
+  const Stat sn{__shfl(st.m, n), __shfl(st.s, n)};
+  if (j < q) {
+    a.accepted_path[o + j] = j <= n ? j : -1;
+    if (j < n) a.out_tokens[o + j] = a.draft[o + j + 1];
+    if (j > n) a.out_tokens[o + j] = -1;
+  }
+  if (j == 0) {
+    a.accept_len[i] = n + 1;
+    StochJob jb;
+    jb.tr = o + n;
+    jb.dr = n < q - 1 ? o + n + 1 : -1;
+    jb.m = sn.m;
+    jb.s = sn.s;
+    jb.w = a.w[i];
+    jb.out = o + n;
+    jobs[i] = jb;
+  }
+}
+
+// weight of vocabulary entry v for a job
+__device__ inline float job_weight(const StochArgs &a, const StochJob &jb, int v, bool residual) {
+  const float p = fast_exp2(a.logits[(size_t)jb.tr * a.vocab + v] * a.c - jb.m) / jb.s;
+  if (!residual) return p;
+  return fmaxf(0.f, p - a.draft_probs[(size_t)jb.dr * a.vocab + v]);
+}
+
+// the draw's weights are summed per sub-slice of kSub entries: thread t of
+// the workgroup sums entries base + 8t .. base + 8t + 7, in index order
+constexpr int kSub = 2048;
+constexpr int kPerThread = kSub / 256;
+
+__device__ inline float thread_weights(const StochArgs &a, const StochJob &jb, int base, bool residual,
+                                       float (&wv)[kPerThread]) {
+  const int v0 = base + kPerThread * (int)threadIdx.x;
+  float l[kPerThread], d[kPerThread];
+  if (v0 + kPerThread <= a.vocab && (a.vocab & 3) == 0) {
+    // two 16-byte loads per array (v0 is a multiple of 8 and rows start 16-byte aligned)
+    const float4v *lp = reinterpret_cast<const float4v *>(a.logits + (size_t)jb.tr * a.vocab + v0);
+#pragma unroll
+    for (int h = 0; h < kPerThread / 4; ++h) {
+      const float4v x = lp[h];
+      l[4 * h] = x.x; l[4 * h + 1] = x.y; l[4 * h + 2] = x.z; l[4 * h + 3] = x.w;
+    }
+    if (residual) {
+      const float4v *dp = reinterpret_cast<const float4v *>(a.draft_probs + (size_t)jb.dr * a.vocab + v0);
+#pragma unroll
+      for (int h = 0; h < kPerThread / 4; ++h) {
+        const float4v x = dp[h];
+        d[4 * h] = x.x; d[4 * h + 1] = x.y; d[4 * h + 2] = x.z; d[4 * h + 3] = x.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int v = min(v0 + e, a.vocab - 1);
+      l[e] = a.logits[(size_t)jb.tr * a.vocab + v];
+      d[e] = residual ? a.draft_probs[(size_t)jb.dr * a.vocab + v] : 0.f;
+    }
+  }
+  float own = 0.f;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    float p = fast_exp2(l[e] * a.c - jb.m) / jb.s;
+    if (residual) p = fmaxf(0.f, p - d[e]);
+    wv[e] = v0 + e < a.vocab ? p : 0.f;
+    own += wv[e];
+  }
+  return own;
+}
+
+__device__ inline float block_sum_256(float x, float *scratch) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
+  __syncthreads();
+  const float r = (scratch[0] + scratch[1]) + (scratch[2] + scratch[3]);
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(256) void sample_mass_kernel(StochArgs a) {
+  __shared__ float s_r[4];
+  const int sb = blockIdx.x, i = blockIdx.y;
+  const StochJob jb = reinterpret_cast<const StochJob *>(a.ws + a.lay.jobs)[i];
+  if (jb.tr < 0) return;
+  float wv[kPerThread];
+  const float own = thread_weights(a, jb, sb * kSub, jb.dr >= 0, wv);
+  const float tot = block_sum_256(own, s_r);
+  if (threadIdx.x == 0) reinterpret_cast<float *>(a.ws + a.lay.mass)[(size_t)i * a.lay.nsub + sb] = tot;
+}
+
+__global__ __launch_bounds__(kPickThreads) void sample_pick_kernel(StochArgs a) {
+  __shared__ float s_seg[kPickThreads];
+  __shared__ float s_r[4];
+  __shared__ int s_k, s_pick, s_residual;
+  __shared__ float s_target;
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const StochJob jb = reinterpret_cast<const StochJob *>(a.ws + a.lay.jobs)[i];
+  if (jb.tr < 0) return;
+  const int nsub = a.lay.nsub;
+  float *mass = reinterpret_cast<float *>(a.ws + a.lay.mass) + (size_t)i * nsub;
+  if (tid == 0) {
+    float tot = 0.f;
+    for (int k = 0; k < nsub; ++k) tot += mass[k];
+    s_residual = jb.dr >= 0 && tot > 0.f;
+  }
+  __syncthreads();
+  const bool residual = s_residual;
+  if (jb.dr >= 0 && !residual) {
+    // a residual without mass: draw from p instead (rare); this workgroup
+    // recomputes the sub-slice masses of p
+    for (int k = 0; k < nsub; ++k) {
+      float wv[kPerThread];
+      const float tot = block_sum_256(thread_weights(a, jb, k * kSub, false, wv), s_r);
+      if (tid == 0) mass[k] = tot;
+    }
+    __syncthreads();
+  }
+  // the sub-slice holding w * total: first k whose running mass exceeds it
+  if (tid == 0) {
+    float tot = 0.f;
+    for (int k = 0; k < nsub; ++k) tot += mass[k];
+    const float target = jb.w * tot;
+    float run = 0.f;
+    int kk = -1, last = 0;
+    for (int k = 0; k < nsub; ++k) {
+      if (mass[k] > 0.f) last = k;
+      if (kk < 0 && run + mass[k] > target) kk = k;
+      if (kk < 0) run += mass[k];
+    }
+    if (kk < 0) {  // rounding: the last sub-slice with mass
+      kk = last;
+      run = 0.f;
+      for (int k = 0; k < kk; ++k) run += mass[k];
+    }
+    s_k = kk;
+    s_target = target - run;
+    s_pick = -1;
+  }
+  __syncthreads();
+  const int base = s_k * kSub;
+  float wv[kPerThread];
+  s_seg[tid] = thread_weights(a, jb, base, residual, wv);
+  __syncthreads();
+  if (tid == 0) {  // exclusive prefix of the thread sums, in index order
+    float run = 0.f;
+    for (int u = 0; u < kPickThreads; ++u) {
+      const float x = s_seg[u];
+      s_seg[u] = run;
+      run += x;
+    }
+  }
+  __syncthreads();
+  const float t = s_target;
+  const float before = s_seg[tid];
+  const float after = tid + 1 < kPickThreads ? s_seg[tid + 1] : INFINITY;
+  if (before <= t && t < after) {
+    float run = before;
+    int pick = -1, lastpos = -1;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      if (pick < 0 && wv[e] > 0.f) {
+        lastpos = base + kPerThread * tid + e;
+        run += wv[e];
+        if (run > t) pick = lastpos;
+      }
+    }
+    if (pick < 0) pick = lastpos;
+    if (pick >= 0) atomicMax(&s_pick, pick);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int y = s_pick;
+    if (y < 0) {  // rounding left the target past the sub-slice: its last entry with weight
+      for (int v = min(a.vocab, base + kSub) - 1; v >= base; --v)
+        if (job_weight(a, jb, v, residual) > 0.f) {
+          y = v;
+          break;
+        }
+    }
+    a.out_tokens[jb.out] = y < 0 ? base : y;
+  }
+}
+
+}  // namespace
+
+void launch_stochastic(const StochArgs &a, hipStream_t stream) {
+  const int rows = a.total_q > 0 ? a.total_q : 1;
+  softmax_stats_kernel<<<dim3(a.lay.splits, rows), 256, 0, stream>>>(a);
+  stochastic_walk_kernel<<<a.batch, 64, 0, stream>>>(a);
+  sample_mass_kernel<<<dim3(a.lay.nsub, a.batch), 256, 0, stream>>>(a);
+  sample_pick_kernel<<<a.batch, kPickThreads, 0, stream>>>(a);
+}
+
+}  // namespace sv

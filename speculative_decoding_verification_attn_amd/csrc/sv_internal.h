@@ -194,6 +194,60 @@ void launch_accept_chunk(const AcceptArgs &a, hipStream_t stream);
 void launch_chunk_start(const AcceptArgs &a, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
+// Stochastic acceptance (speculative sampling)
+// ---------------------------------------------------------------------------
+struct StochJob {
+  int tr;    // target row whose distribution the next token is drawn from (-1: none)
+  int dr;    // draft row subtracted for the residual, or -1 (draw from p itself)
+  int out;   // out_tokens entry of the drawn token
+  int pad;
+  float m, s;  // the target row's softmax stats (log2 domain)
+  float w;     // the request's uniform for the draw
+  float pad2;
+};
+
+struct StochLayout {
+  size_t hdr;    // int32[8]: 0 status bits
+  size_t stats;  // float2 [total_q][splits]: (max, sum) of each slice of each logits row
+  size_t jobs;   // StochJob [batch]
+  size_t mass;   // float [batch][nsub]: weight of each 2048-entry sub-slice of the draw
+  size_t total;
+  int splits;
+  int nsub;
+};
+
+__host__ __device__ inline StochLayout stoch_layout(int batch, int total_q, int vocab) {
+  StochLayout l;
+  l.splits = argmax_splits(total_q, vocab);
+  size_t off = 0;
+  l.hdr = off;    off = align256(off + 8 * sizeof(int32_t));
+  l.stats = off;  off = align256(off + size_t(total_q) * l.splits * 8);
+  l.jobs = off;   off = align256(off + size_t(batch) * sizeof(StochJob));
+  l.nsub = (vocab + 2047) / 2048;
+  l.mass = off;   off = align256(off + size_t(batch) * l.nsub * sizeof(float));
+  l.total = off;
+  return l;
+}
+
+struct StochArgs {
+  const float *logits;       // [total_q, vocab]
+  const float *draft_probs;  // [total_q, vocab]
+  const int32_t *draft;
+  const float *u;            // [total_q]
+  const float *w;            // [batch]
+  const int32_t *cu_q;
+  int32_t *accept_len;
+  int32_t *accepted_path;
+  int32_t *out_tokens;
+  char *ws;
+  StochLayout lay;
+  int batch, total_q, vocab;
+  float c;                   // log2(e) / temperature
+};
+
+void launch_stochastic(const StochArgs &a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
 // KV compaction
 // ---------------------------------------------------------------------------
 struct CompactArgs {

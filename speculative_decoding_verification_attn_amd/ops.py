@@ -30,6 +30,7 @@ DEV_BAD_PARENT = 0x8
 DEV_BAD_PAGE = 0x10
 DEV_TOO_MANY_PAGES = 0x20
 DEV_SYNC_TIMEOUT = 0x40
+DEV_BAD_TOKEN = 0x80
 
 EXPORTED = ["spec_verify_attn_workspace_size", "spec_verify_attn", "spec_verify_attn_plan",
             "spec_verify_attn_run", "spec_verify_attn_device_status",
@@ -37,7 +38,9 @@ EXPORTED = ["spec_verify_attn_workspace_size", "spec_verify_attn", "spec_verify_
             "kv_compact", "sv_status_string", "sv_last_error",
             "spec_verify_attn_chunk_plan", "spec_verify_attn_chunk_run", "spec_chunk_start",
             "spec_accept_chunk_workspace_size", "spec_accept_chunk", "spec_verify_budget",
-            "spec_accept_compact_workspace_size", "spec_accept_compact"]
+            "spec_accept_compact_workspace_size", "spec_accept_compact",
+            "spec_accept_stochastic_workspace_size", "spec_accept_stochastic",
+            "spec_accept_stochastic_device_status"]
 
 _lib = None
 
@@ -94,6 +97,12 @@ def load_library():
     lib.spec_accept_compact.argtypes = [P, I, P, P, P, I, I, P, P, P, P, P, P, I64, I, P, I, P, P, I, I, I, I,
                                         P, SZ, P]
     lib.spec_accept_compact.restype = I
+    lib.spec_accept_stochastic_workspace_size.argtypes = [I, I, I]
+    lib.spec_accept_stochastic_workspace_size.restype = SZ
+    lib.spec_accept_stochastic.argtypes = [P, P, I, F, P, P, P, P, I, I, P, P, P, P, SZ, P]
+    lib.spec_accept_stochastic.restype = I
+    lib.spec_accept_stochastic_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
+    lib.spec_accept_stochastic_device_status.restype = I
     lib.sv_status_string.argtypes = [I]
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_last_error.argtypes = []
@@ -425,3 +434,43 @@ def spec_accept_compact(logits, draft_tokens, cu_q, tree_parent, k_cache, v_cach
                                    _ptr(new_context_lens), num_kv_heads, head_dim, 16, num_pages,
                                    _ptr(workspace), workspace.numel(), _stream(stream)))
     return target_argmax, accept_len, accepted_path, out_tokens, new_context_lens
+
+
+# ----------------------------------------------------------------------------
+# Lossless stochastic acceptance (chains)
+def spec_accept_stochastic_workspace_size(batch, total_q, vocab) -> int:
+    return int(load_library().spec_accept_stochastic_workspace_size(batch, total_q, vocab))
+
+
+def spec_accept_stochastic(logits, draft_probs, draft_tokens, uniform_accept, uniform_sample, cu_q, *,
+                           temperature=1.0, workspace=None, accept_len=None, accepted_path=None,
+                           out_tokens=None, stream=None):
+    """Speculative sampling over chains; returns (accept_len [B], accepted_path [T], out_tokens [T])."""
+    lib = load_library()
+    _dev(logits, torch.float32, "logits")
+    _dev(draft_probs, torch.float32, "draft_probs")
+    _dev(uniform_accept, torch.float32, "uniform_accept")
+    _dev(uniform_sample, torch.float32, "uniform_sample")
+    _dev(draft_tokens, torch.int32, "draft_tokens")
+    _dev(cu_q, torch.int32, "cu_q")
+    T, V = logits.shape
+    B = cu_q.shape[0] - 1
+    dev = logits.device
+    mk = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
+    accept_len = mk(B) if accept_len is None else accept_len
+    accepted_path = mk(T) if accepted_path is None else accepted_path
+    out_tokens = mk(T) if out_tokens is None else out_tokens
+    if workspace is None:
+        workspace = torch.empty(spec_accept_stochastic_workspace_size(B, T, V), dtype=torch.uint8, device=dev)
+    _check(lib.spec_accept_stochastic(_ptr(logits), _ptr(draft_probs), V, float(temperature), _ptr(draft_tokens),
+                                      _ptr(uniform_accept), _ptr(uniform_sample), _ptr(cu_q), B, T,
+                                      _ptr(accept_len), _ptr(accepted_path), _ptr(out_tokens), _ptr(workspace),
+                                      workspace.numel(), _stream(stream)))
+    return accept_len, accepted_path, out_tokens
+
+
+def spec_accept_stochastic_device_status(workspace, stream=None) -> int:
+    flags = ctypes.c_uint32(0)
+    _check(load_library().spec_accept_stochastic_device_status(_ptr(workspace), ctypes.byref(flags),
+                                                               _stream(stream)))
+    return int(flags.value)

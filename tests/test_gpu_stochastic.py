@@ -1,0 +1,112 @@
+"""Lossless stochastic acceptance (speculative sampling) on the GPU, through
+the C ABI, against the fp64 oracle on the same inputs and random numbers.
+
+The GPU works in fp32, so a decision whose margin lies within fp32 rounding
+may legitimately differ from the fp64 oracle: an acceptance test counts as
+decided only when |u*q - p| exceeds 1e-4 of p, and a draw is checked to lie
+at the oracle's inverse-CDF point within 1e-4 of the total weight.  Outside
+those margins the results must be identical."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DEV, i32, note
+from oracle import stochastic as S
+from speculative_decoding_verification_attn_amd import ops
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, B, V, qmax, temperature, sigma=2.0, noise=0.3):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(1, qmax + 1, B)
+    q[0] = 1  # a request with no draft
+    cu = np.zeros(B + 1, np.int64)
+    cu[1:] = np.cumsum(q)
+    T = int(cu[-1])
+    logits = (rng.standard_normal((T, V)) * sigma).astype(np.float32)
+    dprobs = np.zeros((T, V), np.float32)
+    draft = np.zeros(T, np.int32)
+    for i in range(B):
+        o = cu[i]
+        for j in range(1, q[i]):
+            # the drafter: a perturbed copy of the target's distribution at position j
+            d = S.target_probs(logits[o + j - 1].astype(np.float64) + rng.standard_normal(V) * noise, temperature)
+            dprobs[o + j] = d.astype(np.float32)
+            dprobs[o + j] /= dprobs[o + j].sum(dtype=np.float64)
+            draft[o + j] = rng.choice(V, p=dprobs[o + j].astype(np.float64) / dprobs[o + j].sum(dtype=np.float64))
+    u = rng.random(T).astype(np.float32)
+    w = rng.random(B).astype(np.float32)
+    return cu, logits, dprobs, draft, u, w
+
+
+def _compare(cu, logits, dprobs, draft, u, w, temperature, acc, path, toks):
+    B = len(cu) - 1
+    exact = borderline = 0
+    for i in range(B):
+        o, q = int(cu[i]), int(cu[i + 1] - cu[i])
+        # oracle walk with margins
+        n_ref, undecided = 0, False
+        for j in range(1, q):
+            p = S.target_probs(logits[o + j - 1], temperature)
+            x = int(draft[o + j])
+            lhs = float(u[o + j]) * float(dprobs[o + j][x])
+            if abs(lhs - p[x]) <= 1e-4 * max(p[x], 1e-30):
+                undecided = True
+                break
+            if lhs < p[x]:
+                n_ref += 1
+            else:
+                break
+        n = int(acc[i]) - 1
+        assert 0 <= n < q, (i, n)
+        assert path[o:o + n + 1].tolist() == list(range(n + 1)) and np.all(path[o + n + 1:o + q] == -1)
+        assert toks[o:o + n].tolist() == draft[o + 1:o + n + 1].tolist() and np.all(toks[o + n + 1:o + q] == -1)
+        if undecided and n != n_ref:
+            borderline += 1
+            continue
+        assert n == n_ref, (i, n, n_ref)
+        # the draw: at the oracle's inverse-CDF point, within 1e-4 of the total weight
+        p = S.target_probs(logits[o + n], temperature)
+        r = np.maximum(0.0, p - dprobs[o + n + 1].astype(np.float64)) if n < q - 1 else p
+        if r.sum() <= 0.0:
+            r = p
+        c = np.cumsum(r)
+        tgt = float(w[i]) * c[-1]
+        y = int(toks[o + n])
+        tol = 1e-4 * c[-1]
+        assert 0 <= y < len(r) and r[y] > 0.0, (i, y)
+        assert (c[y - 1] if y > 0 else 0.0) <= tgt + tol and c[y] >= tgt - tol, (i, y, tgt)
+        exact += int(y == S.inverse_cdf(r, w[i]))
+    return exact, borderline
+
+
+@pytest.mark.parametrize("seed,B,V,qmax,temp", [(0, 16, 1000, 8, 1.0), (1, 32, 4099, 6, 0.7),
+                                                (2, 8, 128256, 5, 1.0), (3, 4, 151936, 8, 1.3)])
+def test_stochastic_acceptance_matches_oracle(seed, B, V, qmax, temp):
+    cu, logits, dprobs, draft, u, w = _case(seed, B, V, qmax, temp)
+    T = int(cu[-1])
+    note(f"[gpu] spec_accept_stochastic seed={seed} B={B} T={T} V={V} T={temp}")
+    ws = torch.empty(ops.spec_accept_stochastic_workspace_size(B, T, V), dtype=torch.uint8, device=DEV)
+    acc, path, toks = ops.spec_accept_stochastic(torch.from_numpy(logits).to(DEV), torch.from_numpy(dprobs).to(DEV),
+                                                 i32(draft), torch.from_numpy(u).to(DEV), torch.from_numpy(w).to(DEV),
+                                                 i32(cu), temperature=temp, workspace=ws)
+    torch.cuda.synchronize()
+    assert ops.spec_accept_stochastic_device_status(ws) == 0
+    exact, borderline = _compare(cu, logits, dprobs, draft, u, w, temp, acc.cpu().numpy(), path.cpu().numpy(),
+                                 toks.cpu().numpy())
+    note(f"  draws equal to the oracle's: {exact}/{B}, borderline acceptances: {borderline}")
+    assert borderline <= 1 and exact >= B - 2
+
+
+def test_stochastic_bad_token_sets_status():
+    cu, logits, dprobs, draft, u, w = _case(5, 4, 300, 4, 1.0)
+    draft[int(cu[1]) + 1] = 300 if cu[2] - cu[1] > 1 else draft[int(cu[1]) + 1]
+    draft[1] = -3 if cu[1] > 1 else draft[1]
+    draft[int(cu[3]) + 1] = 1000 if cu[4] - cu[3] > 1 else draft[int(cu[3]) + 1]
+    ws = torch.empty(ops.spec_accept_stochastic_workspace_size(4, int(cu[-1]), 300), dtype=torch.uint8, device=DEV)
+    ops.spec_accept_stochastic(torch.from_numpy(logits).to(DEV), torch.from_numpy(dprobs).to(DEV), i32(draft),
+                               torch.from_numpy(u).to(DEV), torch.from_numpy(w).to(DEV), i32(cu), workspace=ws)
+    torch.cuda.synchronize()
+    if (cu[2] - cu[1] > 1) or (cu[4] - cu[3] > 1):
+        assert ops.spec_accept_stochastic_device_status(ws) & ops.DEV_BAD_TOKEN
