@@ -24,6 +24,16 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
+// max(x[lane], x[lane ^ 32]) on every lane.  The permlane32 swap exchanges
+// the upper half of its first operand with the lower half of its second, so
+// with x in both each lane ends up holding x of itself and of its partner in
+// the other half: a VALU op, where a shuffle would go through LDS.
+__device__ inline float max_across_halves(float x) {
+  const unsigned b = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // {lo, hi} rounded to bf16 (nearest even) in one packed conversion
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   const bf16x2v b = __builtin_convertvector((float2v){lo, hi}, bf16x2v);

@@ -292,7 +292,7 @@ __device__ inline void load_block(KVBlock<D> &buf, const uint16_t *kh, const uin
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 template <int D>
-__device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 *qop_lds, int nt, int key0, int L,
+__device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 (&qop)[kUnitTiles][D / 16], int nt, int key0, int L,
                                      int nk, const uint64_t (&anc)[kUnitTiles], int hh, float scale_log2,
                                      float (&m)[kUnitTiles], float (&l)[kUnitTiles],
                                      floatx16 (&acc)[kUnitTiles][D / 32]) {
@@ -316,7 +316,7 @@ __device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 *qop_lds, int
     floatx16 s = floatx16{};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf.k[kk], qop_lds[(tt * KK + kk) * 64], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf.k[kk], qop[tt][kk], s, 0, 0, 0);
 
     // keys of acc reg r: key0 + 8*(r/4) + 4*hh + r%4.  Scores stay unscaled
     // here; the (positive) scale is folded into the exponent below, and the
@@ -332,7 +332,7 @@ __device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 *qop_lds, int
     float mb = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mb = fmaxf(mb, s[r]);
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    mb = max_across_halves(mb);
     // Lazy rescaling: the reference max m only moves (and the accumulators
     // are rescaled) once some row's block max exceeds it by more than
     // kRescaleSlack; until then p <= 2^kRescaleSlack, exact in fp32 sums
@@ -614,6 +614,19 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
     }
   };
 
+  // The unit's Q^T operands stay in registers while it runs: read from LDS
+  // once per unit instead of once per block, the hot loop has no LDS reads
+  // to wait for before its MFMAs.
+  bf16x8 qop[kUnitTiles][KK];
+  auto load_qop = [&]() {
+#pragma unroll
+    for (int tt = 0; tt < kUnitTiles; ++tt) {
+      if (tt >= nt) break;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) qop[tt][kk] = sm_q[tt][kk][lane];
+    }
+  };
+
   // producer: page ids and head of the round it will load next
   int2 pg_next = make_int2(0, 0);
   int h_next = Wp.h;
@@ -721,7 +734,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
     }
     const int gb = Wc.ps + kAttnWaves * (g - Wc.g0) + wave;  // this wave's global block
     if (gb < Wc.pe)
-      compute_block<D>(cur, &sm_q[0][0][lane], nt, (gb - Wc.ub) * kBlockKeys, Wc.L, nk, anc, hh,
+      compute_block<D>(cur, qop, nt, (gb - Wc.ub) * kBlockKeys, Wc.L, nk, anc, hh,
                        a.scale_log2, m, l, acc);
     if (g + 1 == Wc.g0 + Wc.nr) {
       finish_unit();
@@ -729,6 +742,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
       walk_to(Wc, g + 1, start, end, units, n_units);
       enter_unit();
       __syncthreads();  // the next unit's Q is in LDS; sm_o may be reused
+      load_qop();
     }
     return false;
   };
@@ -741,6 +755,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   fetch_pages(1);
   enter_unit();
   __syncthreads();
+  load_qop();
   for (int g = 0;; g += 2) {
     if (round(g, A, Bb)) break;
     if (round(g + 1, Bb, A)) break;
