@@ -26,6 +26,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak, TFLOP/s
+MI355X_SIMDS = 256 * 4  # compute units x SIMDs
+MI355X_XCDS = 8
 
 WORKLOAD_TEXT = {
     "tiny_chain": "tiny chain verify: B=1, gamma=4, 8/2 heads, D=64, L=256, V=1024",
@@ -68,7 +71,14 @@ def main():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="no GPU run: turn the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE outputs of a "
                          "--calibrate-copy-mb run into profiles/verify_attn_<config>_traffic.json")
+    ap.add_argument("--mfma-summary", metavar="PMC_DIR", default=None,
+                    help="no GPU run: turn a rocprofv3 --pmc run of SQ_INSTS_MFMA, "
+                         "SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE (among others) into "
+                         "profiles/verify_attn_<config>_mfma.json")
     args = ap.parse_args()
+    if args.mfma_summary:
+        write_mfma_summary(args.config, args.mfma_summary)
+        return
     if args.pmc_summary:
         write_traffic_summary(args.config, *args.pmc_summary, copy_mb=args.calibrate_copy_mb or 1024)
         return
@@ -282,6 +292,12 @@ def main():
     logits_bytes = T * case.vocab * 4
     step_bytes = layers * attn_bytes + logits_bytes
     attn_gbs = attn_bytes / (attn_ms * 1e-3) / 1e9
+    # algorithmic flops: S = QK^T and O = PV over every verify row and its
+    # L_i + q_i keys (masked keys included), 2 flops per multiply-add
+    attn_flops = case.attn_flops()
+    attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    intensity = attn_flops / attn_bytes
+    mfma_bound = intensity > PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     verified_tok_s = float(acc_np.sum()) / (ms_per_step * 1e-3)
 
@@ -300,6 +316,14 @@ def main():
         cpu = cpu_baseline(case, K[0], V[0], logits, args.cpu_sample_requests, layers)
 
     traffic = measured_traffic(name)
+    mfma = measured_mfma(name)
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": PEAK_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4),
+                "algorithmic_flops": attn_flops}
+    else:
+        roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(attn_gbs / PEAK_HBM_GBS, 4)}
     rec = {
         "metric": "verify-step µs/layer & KV-stream HBM GB/s (% peak), Llama-3-70B shape",
         "value": round(value, 2),
@@ -328,9 +352,12 @@ def main():
         "acceptance": "stochastic (speculative sampling)" if args.stochastic else "greedy",
         "verified_tokens_per_s": round(verified_tok_s, 1),
         "mean_accept_len": round(float(acc_np.mean()), 4),
+        "attn_tflops": round(attn_tflops, 1),
+        "attn_flop_per_byte": round(intensity, 1),
+        "mfma": {"algorithmic_frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4), "peak_tflops": PEAK_MFMA_TFLOPS,
+                 "counters": mfma},
         "roofline": {"kernel": "spec_verify_attn_run (verify_attn_kernel + attn_merge_kernel, per layer)",
-                     "bound": "hbm", "achieved": round(attn_gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(attn_gbs / PEAK_HBM_GBS, 4),
+                     **roof,
                      "algorithmic_bytes": attn_bytes,
                      "traffic": None if traffic is None else traffic["total_bytes"],
                      "traffic_detail": traffic},
@@ -498,6 +525,67 @@ def write_traffic_summary(name, fetch_dir, write_dir, copy_mb):
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
+
+
+def write_mfma_summary(name, pmc_dir):
+    """MFMA use of the attention kernel from one rocprofv3 --pmc run.
+    SQ_VALU_MFMA_BUSY_CYCLES is summed over the SIMDs (a 32x32x16 bf16 MFMA
+    counts 32 cycles, so 1024 SIMDs busy all the time is the 2.5 PFLOP/s
+    peak); GRBM_GUI_ACTIVE is summed over the 8 XCDs, so the dispatch lasted
+    GRBM_GUI_ACTIVE / 8 cycles (profiler set-up included, which inflates it
+    for short kernels).  SQ_WAVE_CYCLES counts the kernel's resident
+    wave-cycles in units of 4 cycles; with one wave per SIMD that is the SIMD
+    time the kernel held."""
+    counters = ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU",
+                "SQ_ACTIVE_INST_VALU", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES", "SQ_WAVES", "SQ_BUSY_CYCLES"]
+    got = {}
+    kname = None
+    for c in counters:
+        try:
+            per, _ = _pmc_per_kernel(pmc_dir, c)
+        except SystemExit:
+            continue
+        k = next((k for k in per if "verify_attn_kernel" in k), None)
+        if k is None:
+            continue
+        kname = k
+        got[c] = float(np.mean(per[k]))
+    need = ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+    if kname is None or any(c not in got for c in need):
+        raise SystemExit(f"{pmc_dir}: needs {need} for the attention kernel")
+    busy = got["SQ_VALU_MFMA_BUSY_CYCLES"] / (got["GRBM_GUI_ACTIVE"] / MI355X_XCDS * MI355X_SIMDS)
+    rec = {"kernel": kname, "workload": name,
+           "source_sha256": _sources_sha256(TRAFFIC_SOURCES), "sources": TRAFFIC_SOURCES,
+           "counters_per_launch": {c: round(v, 1) for c, v in got.items()},
+           "simds": MI355X_SIMDS, "xcds": MI355X_XCDS,
+           "mfma_busy_frac": round(busy, 4),
+           "mfma_busy_cycles_per_instruction": round(got["SQ_VALU_MFMA_BUSY_CYCLES"] / got["SQ_INSTS_MFMA"], 2)}
+    if "SQ_WAVE_CYCLES" in got:
+        rec["mfma_busy_frac_of_resident_wave_cycles"] = round(
+            got["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * got["SQ_WAVE_CYCLES"]), 4)
+    if "SQ_WAVE_CYCLES" in got and "SQ_ACTIVE_INST_VALU" in got:
+        rec["valu_active_frac_of_wave_cycles"] = round(got["SQ_ACTIVE_INST_VALU"] / got["SQ_WAVE_CYCLES"], 4)
+    if "SQ_WAVE_CYCLES" in got and "SQ_WAIT_ANY" in got:
+        rec["wait_frac_of_wave_cycles"] = round(got["SQ_WAIT_ANY"] / got["SQ_WAVE_CYCLES"], 4)
+    path = os.path.join(ROOT, "profiles", f"verify_attn_{name}_mfma.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def measured_mfma(name):
+    """MFMA busy fraction of the attention kernel from the committed counter
+    summary, if taken on this workload and the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"verify_attn_{name}_mfma.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if _sources_sha256(rec["sources"]) != rec["source_sha256"]:
+        return None
+    return {"busy_frac": rec["mfma_busy_frac"],
+            "busy_frac_of_resident_wave_cycles": rec.get("mfma_busy_frac_of_resident_wave_cycles"),
+            "source": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / %d XCDs x %d SIMDs)"
+                      % (rec["xcds"], rec["simds"])}
 
 
 def measured_traffic(name):
