@@ -34,6 +34,34 @@ __device__ inline float max_across_halves(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Maximum and sum over the 64 lanes of a wave, returned wave-uniform.  DPP
+// moves combine within each row of 16 lanes (quad swaps, then the row's
+// half-mirror and mirror, after which every lane of a row holds the row's
+// result), and the four rows are combined from their lanes 0, 16, 32, 48:
+// no LDS round trip, and the same order on every call.
+template <int Ctrl>
+__device__ inline float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xF, 0xF, false));
+}
+
+template <typename Op>
+__device__ inline float wave_reduce(float x, Op op) {
+  x = op(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = op(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = op(x, dpp_mov<0x141>(x));  // row_half_mirror
+  x = op(x, dpp_mov<0x140>(x));  // row_mirror
+  auto lane_of = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); };
+  return op(op(lane_of(0), lane_of(16)), op(lane_of(32), lane_of(48)));
+}
+
+__device__ inline float wave_max(float x) {
+  return wave_reduce(x, [](float u, float v) { return fmaxf(u, v); });
+}
+
+__device__ inline float wave_sum(float x) {
+  return wave_reduce(x, [](float u, float v) { return u + v; });
+}
+
 // {lo, hi} rounded to bf16 (nearest even) in one packed conversion
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   const bf16x2v b = __builtin_convertvector((float2v){lo, hi}, bf16x2v);

@@ -17,7 +17,7 @@ constexpr int kTileRows = 32;      // query rows per MFMA tile
 constexpr int kUnitTiles = 2;      // query tiles of one (request, KV head) sharing each K/V block
 constexpr int kAttnWaves = 4;      // waves per attention workgroup (they split the keys)
 constexpr int kMaxGrid = 512;      // persistent attention workgroups (one per CU, capped)
-constexpr int kMinBlocksPerWG = 4; // keep at least one 32-key block per wave
+constexpr int kMinBlocksPerWG = 8; // at least two 32-key blocks per wave: fewer, longer ranges for small problems
 // Range sizing charges each unit start (after the first) this many blocks:
 // finishing a unit (merging it across the waves, writing it out) and entering
 // the next one stalls a workgroup's stream for two to three rounds of four

@@ -383,10 +383,12 @@ __device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 (&qop)[kUnitT
 // u spans ranges w0 < w1; it is merged by the workgroups of merge slot
 // w0 + 1 (the first range that starts inside it), so each cut unit is merged
 // exactly once.  Each merge slot has kTileRows / kMergeRows workgroups of
-// kMergeRows waves; a wave merges row n of each of the unit's tiles in turn:
-// one pass over the unit's partials with a running log-sum-exp, every lane
-// holding D/64 consecutive columns, so a row's partials are read as 64-lane
-// contiguous runs and a unit cut into many ranges is merged by many CUs.
+// kMergeRows waves; a wave merges row n of each of the unit's tiles in turn.
+// First the lanes read the pieces' log-sum-exps side by side (64 pieces per
+// load) for the common maximum and the normaliser; then the weighted rows are
+// summed with every lane holding D/64 consecutive columns, so a row's
+// partials are read as 64-lane contiguous runs, eight pieces' loads in flight
+// at a time (none of them waits on the sum so far).
 // --------------------------------------------------------------------------
 constexpr int kMergeRows = 4;
 
@@ -413,29 +415,62 @@ __global__ __launch_bounds__(64 * kMergeRows) void attn_merge_kernel(AttnArgs a)
   // slot); every later range starts inside the unit (first slot).  No range
   // between w0 and w1 is empty: distinct cost targets inside one unit map to
   // distinct blocks, so an empty range can only begin at a unit start.
-  float M = -INFINITY, den = 0.f;
+  const int np = w1 - w0 + 1;
+  auto slot_of = [&](int k) {
+    const int w = w0 + k;
+    return (2 * (size_t)w + (k == 0 ? side0 : 0)) * kUnitTiles + tt;
+  };
+  // rows of pieces k0 + j0 .. k0 + j0 + 7 (past the last piece: the last one
+  // again, weighted 0 by the caller)
+  auto load8 = [&](int k0, int j0, int kn, float (&x)[8][DPT]) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t row = (slot_of(k0 + min(j0 + u, kn - 1)) * kTileRows + n) * D;
+      if constexpr (DPT == 2) {
+        const float2 xv = reinterpret_cast<const float2 *>(po + row)[lane];
+        x[u][0] = xv.x;
+        x[u][1] = xv.y;
+      } else {
+        x[u][0] = po[row + lane];
+      }
+    }
+  };
   float acc[DPT];
 #pragma unroll
   for (int t = 0; t < DPT; ++t) acc[t] = 0.f;
-#pragma unroll 4
-  for (int w = w0; w <= w1; ++w) {
-    const size_t slot = (2 * (size_t)w + (w == w0 ? side0 : 0)) * kUnitTiles + tt;
-    const float ls = pl[slot * kTileRows + n];
-    float v[DPT];
-    if constexpr (DPT == 2) {
-      const float2 x = reinterpret_cast<const float2 *>(po + (slot * kTileRows + n) * D)[lane];
-      v[0] = x.x;
-      v[1] = x.y;
-    } else {
-      v[0] = po[(slot * kTileRows + n) * D + lane];
-    }
-    const float Mn = fmaxf(M, ls);
-    const float sc = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
-    const float wt = ls == -INFINITY ? 0.f : fast_exp2(ls - Mn);
-    den = den * sc + wt;
+  auto add8 = [&](int j0, int kn, float wl, const float (&x)[8][DPT]) {
 #pragma unroll
-    for (int t = 0; t < DPT; ++t) acc[t] = acc[t] * sc + wt * v[t];
-    M = Mn;
+    for (int u = 0; u < 8; ++u) {
+      const int j = min(j0 + u, kn - 1);
+      const float wt = j0 + u < kn ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wl), j)) : 0.f;
+#pragma unroll
+      for (int t = 0; t < DPT; ++t) acc[t] += wt * x[u][t];
+    }
+  };
+  // the common maximum over the pieces' log-sum-exps, 64 pieces per load
+  // (lane k holds piece k0 + k); with at most 64 pieces the first eight
+  // rows are loaded alongside, so a few pieces cost one memory round trip
+  float M = -INFINITY, den = 0.f;
+  float x[8][DPT];
+  float ls0 = -INFINITY;
+  for (int k0 = 0; k0 < np; k0 += 64) {
+    const float ls = k0 + lane < np ? pl[slot_of(k0 + lane) * kTileRows + n] : -INFINITY;
+    if (k0 == 0) {
+      ls0 = ls;
+      load8(0, 0, min(64, np), x);
+    }
+    M = fmaxf(M, wave_max(ls));
+  }
+  const float Mref = M == -INFINITY ? 0.f : M;
+  for (int k0 = 0; k0 < np; k0 += 64) {
+    const float ls = k0 == 0 ? ls0 : (k0 + lane < np ? pl[slot_of(k0 + lane) * kTileRows + n] : -INFINITY);
+    const float wl = ls == -INFINITY ? 0.f : fast_exp2(ls - Mref);  // piece k0+lane's weight
+    den += wave_sum(wl);
+    const int kn = min(64, np - k0);
+    for (int j0 = 0; j0 < kn; j0 += 8) {
+      if (k0 > 0 || j0 > 0) load8(k0, j0, kn, x);
+      add8(j0, kn, wl, x);
+    }
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   uint16_t *orow = a.out + ((size_t)(o + tok) * a.num_q_heads + (size_t)h * G + gq) * D;
