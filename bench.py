@@ -301,6 +301,8 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     verified_tok_s = float(acc_np.sum()) / (ms_per_step * 1e-3)
 
+    ceiling = read_ceiling(case, ops, K[0], V[0], stream, kv_bytes / (attn_ms * 1e-3) / 1e9)
+
     if args.calibrate_copy_mb > 0:
         nbytes = args.calibrate_copy_mb * (1 << 20)
         src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -361,9 +363,46 @@ def main():
                      "algorithmic_bytes": attn_bytes,
                      "traffic": None if traffic is None else traffic["total_bytes"],
                      "traffic_detail": traffic},
+        "read_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def read_ceiling(case, ops, k_cache, v_cache, stream, attn_kv_gbs, reps=10):
+    """What a pure read kernel reaches on the pages the attention streams:
+    spec_hbm_read_probe over every (page, KV head) block of K and V that the
+    step's units read, in the attention's order (request, head, page) and
+    with its load pattern, timed with HIP events on the launch stream.  Only
+    for caches far larger than the 256 MB last-level cache (else None)."""
+    import torch
+    if case.kv_bytes_per_layer() < 1e9:
+        return None
+    hkv = case.num_kv_heads
+    lists = []
+    for i in range(case.batch):
+        npg = (int(case.context_lens[i]) + int(case.q_lens[i]) + 15) // 16
+        pg = case.block_tables[i, :npg].astype(np.int64)
+        lists.append((pg[None, :] * hkv + np.arange(hkv)[:, None]).ravel())
+    chunks = torch.from_numpy(np.concatenate(lists).astype(np.int32)).to(k_cache.device)
+    sink = torch.zeros(ops.PROBE_SINK_WORDS, dtype=torch.int32, device=k_cache.device)
+    for _ in range(3):
+        ops.spec_hbm_read_probe(k_cache, v_cache, chunks, sink=sink, stream=stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        ops.spec_hbm_read_probe(k_cache, v_cache, chunks, sink=sink, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = int(chunks.numel()) * 2 * 16 * case.head_dim * 2
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "us": round(us, 2),
+            "bytes": nbytes, "attn_kv_gbs": round(attn_kv_gbs, 1),
+            "attn_kv_frac_of_ceiling": round(attn_kv_gbs / gbs, 4),
+            "probe": "spec_hbm_read_probe: the step's K and V (page, head) blocks in the attention's order, "
+                     "16-byte nontemporal loads, 1 KB per instruction, one pair of blocks in flight per wave"}
 
 
 def chunked_bench(args, case, ops, r):

@@ -411,6 +411,35 @@ int spec_verify_budget(const float *cond_survival, const int32_t *cu_draft, int 
                        int32_t *verify_len, int32_t *batch_rows, double *theta);
 
 /* ------------------------------------------------------------------------- */
+/* HBM read-ceiling probe (measurement aid, not part of the verify step)      */
+/* ------------------------------------------------------------------------- */
+
+#define SV_PROBE_SINK_WORDS 131072 /* uint32 words spec_hbm_read_probe may write to sink */
+
+/* Streams the listed K and V cache blocks with the verify-attention kernel's
+ * load pattern (16-byte nontemporal loads, 1 KB per instruction, one pair of
+ * blocks in flight per wave while the previous pair is consumed) and does
+ * nothing else with them, so the attention's KV-stream rate can be compared
+ * with what a pure read kernel reaches on the same pages of the same device.
+ * chunks[c] (DEVICE, int32 [n_chunks]) names one (page, KV head) block:
+ * chunk_bytes at byte offset chunks[c] * chunk_bytes of k_cache and of
+ * v_cache (DEVICE) - for the [num_pages, Hkv, 16, D] layout, page * Hkv + h
+ * with chunk_bytes = 16 * D * 2 (2048 or 4096).  buffer_chunks is the number
+ * of blocks each cache holds; an index outside [0, buffer_chunks) reads
+ * block 0 instead.  Each lane writes the XOR of the 32-bit words it read to
+ * one word of sink (DEVICE, uint32 [sink_words >= SV_PROBE_SINK_WORDS]; 256
+ * words per workgroup, two workgroups per compute unit up to 512, the rest
+ * untouched),
+ * which keeps the loads: over a zeroed sink, the XOR of all its words is the
+ * XOR of every word of the listed blocks of both caches.
+ * Asynchronous on `stream`; n_chunks = 0 does nothing.  Errors: SV_ERR_NULL,
+ * SV_ERR_SHAPE (n_chunks < 0, buffer_chunks <= 0, sink too small),
+ * SV_ERR_UNSUPPORTED (chunk_bytes not 2048 or 4096), SV_ERR_HIP. */
+int spec_hbm_read_probe(const void *k_cache, const void *v_cache, const int32_t *chunks, int64_t n_chunks,
+                        int chunk_bytes, int64_t buffer_chunks, uint32_t *sink, int64_t sink_words,
+                        void *stream);
+
+/* ------------------------------------------------------------------------- */
 /* Diagnostics (host)                                                         */
 /* ------------------------------------------------------------------------- */
 

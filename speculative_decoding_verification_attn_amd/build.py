@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["capi.hip", "verify_attn.hip", "accept.hip", "kv_compact.hip", "verify_budget.hip", "stochastic.hip"]
+SOURCES = ["capi.hip", "verify_attn.hip", "accept.hip", "kv_compact.hip", "verify_budget.hip", "stochastic.hip",
+           "read_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include "sv_internal.h"
+#include "read_probe.h"
 
 namespace {
 
@@ -370,6 +371,28 @@ int spec_verify_attn_chunk_run(const void *q, const void *k_cache, const void *v
   if ((rc = set_grid(&a)) != SV_OK) return rc;
   sv::launch_verify_attn_run(a, head_dim, static_cast<hipStream_t>(stream));
   return check_launch("spec_verify_attn_chunk_run");
+}
+
+int spec_hbm_read_probe(const void *k_cache, const void *v_cache, const int32_t *chunks, int64_t n_chunks,
+                        int chunk_bytes, int64_t buffer_chunks, uint32_t *sink, int64_t sink_words,
+                        void *stream) {
+  if (n_chunks < 0 || buffer_chunks <= 0)
+    return fail(SV_ERR_SHAPE, "n_chunks (%lld) must be >= 0 and buffer_chunks (%lld) > 0",
+                (long long)n_chunks, (long long)buffer_chunks);
+  if (chunk_bytes != 2048 && chunk_bytes != 4096)
+    return fail(SV_ERR_UNSUPPORTED, "chunk_bytes %d (supported: 2048, 4096)", chunk_bytes);
+  if (sink_words < SV_PROBE_SINK_WORDS)
+    return fail(SV_ERR_SHAPE, "sink holds %lld words < %d", (long long)sink_words, SV_PROBE_SINK_WORDS);
+  if (n_chunks == 0) return ok();
+  if (!k_cache || !v_cache || !chunks || !sink) return fail(SV_ERR_NULL, "spec_hbm_read_probe: a pointer is NULL");
+  sv::AttnArgs a;
+  int rc = set_grid(&a);
+  if (rc != SV_OK) return rc;
+  static_assert(sv::kMaxGrid * 256 <= SV_PROBE_SINK_WORDS, "probe sink");
+  const int grid = a.grid * sv::kProbeWgPerCu > sv::kMaxGrid ? sv::kMaxGrid : a.grid * sv::kProbeWgPerCu;
+  sv::launch_hbm_read_probe(k_cache, v_cache, chunks, n_chunks, chunk_bytes, buffer_chunks, sink, grid,
+                            static_cast<hipStream_t>(stream));
+  return check_launch("spec_hbm_read_probe");
 }
 
 int spec_verify_attn_device_status(const void *workspace, uint32_t *flags, void *stream) {

@@ -40,7 +40,7 @@ EXPORTED = ["spec_verify_attn_workspace_size", "spec_verify_attn", "spec_verify_
             "spec_accept_chunk_workspace_size", "spec_accept_chunk", "spec_verify_budget",
             "spec_accept_compact_workspace_size", "spec_accept_compact",
             "spec_accept_stochastic_workspace_size", "spec_accept_stochastic",
-            "spec_accept_stochastic_device_status"]
+            "spec_accept_stochastic_device_status", "spec_hbm_read_probe"]
 
 _lib = None
 
@@ -103,6 +103,8 @@ def load_library():
     lib.spec_accept_stochastic.restype = I
     lib.spec_accept_stochastic_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
     lib.spec_accept_stochastic_device_status.restype = I
+    lib.spec_hbm_read_probe.argtypes = [P, P, P, I64, I, I64, P, I64, P]
+    lib.spec_hbm_read_probe.restype = I
     lib.sv_status_string.argtypes = [I]
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_last_error.argtypes = []
@@ -474,3 +476,28 @@ def spec_accept_stochastic_device_status(workspace, stream=None) -> int:
     _check(load_library().spec_accept_stochastic_device_status(_ptr(workspace), ctypes.byref(flags),
                                                                _stream(stream)))
     return int(flags.value)
+
+
+# ----------------------------------------------------------------------------
+# HBM read-ceiling probe (a measurement aid beside the verify step)
+# ----------------------------------------------------------------------------
+PROBE_SINK_WORDS = 131072
+
+
+def spec_hbm_read_probe(k_cache, v_cache, chunks, *, sink=None, stream=None):
+    """Stream the (page, KV head) blocks listed in `chunks` (int32, page * Hkv +
+    head) of both caches with the attention kernel's load pattern; returns the
+    sink tensor (zeroed here unless given) the lanes write their XOR to."""
+    lib = load_library()
+    _dev(k_cache, torch.bfloat16, "k_cache")
+    _dev(v_cache, torch.bfloat16, "v_cache")
+    _dev(chunks, torch.int32, "chunks")
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [num_pages, Hkv, 16, D] and alike")
+    chunk_bytes = k_cache.shape[2] * k_cache.shape[3] * 2
+    buffer_chunks = k_cache.shape[0] * k_cache.shape[1]
+    if sink is None:
+        sink = torch.zeros(PROBE_SINK_WORDS, dtype=torch.int32, device=k_cache.device)
+    _check(lib.spec_hbm_read_probe(_ptr(k_cache), _ptr(v_cache), _ptr(chunks), chunks.numel(), chunk_bytes,
+                                   buffer_chunks, _ptr(sink), sink.numel(), _stream(stream)))
+    return sink

@@ -184,3 +184,17 @@ def test_fused_validation(lib):
     assert call(new=ctypes.c_void_p(0x200004)) == ops.SV_ERR_ALIAS
     assert call(B=0, T=0) == ops.SV_OK
     assert lib.spec_accept_compact_workspace_size(4, 20, 128256) > lib.spec_accept_workspace_size(4, 20, 128256)
+
+
+def test_read_probe_validation(lib):
+    def call(**kw):
+        a = dict(k=FAKE, v=FAKE, ch=FAKE, n=10, cb=4096, nb=100, sink=FAKE, sw=ops.PROBE_SINK_WORDS, stream=NULL)
+        a.update(kw)
+        return lib.spec_hbm_read_probe(a["k"], a["v"], a["ch"], a["n"], a["cb"], a["nb"], a["sink"], a["sw"],
+                                       a["stream"])
+    assert call(cb=1024) == ops.SV_ERR_UNSUPPORTED
+    assert call(n=-1) == ops.SV_ERR_SHAPE
+    assert call(nb=0) == ops.SV_ERR_SHAPE
+    assert call(sw=ops.PROBE_SINK_WORDS - 1) == ops.SV_ERR_SHAPE
+    assert call(ch=NULL) == ops.SV_ERR_NULL
+    assert call(n=0, k=NULL, v=NULL, ch=NULL, sink=NULL) == ops.SV_OK  # nothing to read
