@@ -84,7 +84,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "the verify step runs on one GPU; --gpus must be 1 "
                                    "(the path shards by request or KV head across GPUs, not implemented here)"}))
         sys.exit(2)
 
