@@ -56,7 +56,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from the host each step instead of replaying HIP graphs")
-    ap.add_argument("--cpu-sample-requests", type=int, default=16)
+    ap.add_argument("--cpu-sample-requests", type=int, default=64,
+                    help="requests of the workload the CPU oracle is timed on (about 10 s of CPU work at B=256)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MB "
                          "(reference for the HBM traffic counters)")
