@@ -691,7 +691,13 @@ def cpu_baseline(case, k_dev, v_dev, logits_dev, n_req, layers):
     t_step = layers * t_attn + t_acc
     gbs = (layers * attn_bytes + logit_bytes) / t_step / 1e9
     log(f"cpu oracle sample: {n_req} requests, attention {t_attn:.2f}s/layer, accept {t_acc:.3f}s")
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle", "cpu_model": cpu_model,
             "sample": f"first {n_req} of {case.batch} requests ({len(rows)} verify rows, {keys} keys/layer): "
                       f"one layer of fp64 verify attention timed and scaled to {layers} layers, plus "
                       f"argmax+acceptance of those rows; single-threaded C oracle",
