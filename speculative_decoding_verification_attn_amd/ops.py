@@ -162,9 +162,20 @@ def _attn_call(fn, q, k_cache, v_cache, block_tables, context_lens, cu_q, tree_p
     if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("cache shapes do not match q")
     B = context_lens.shape[0]
+    # sizes the library cannot see behind device pointers
+    if cu_q.numel() != B + 1 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("cu_q must hold batch+1 entries and block_tables batch rows")
+    if tree_parent is not None and tree_parent.numel() != T:
+        raise ValueError("tree_parent must hold one entry per verify token")
+    if num_pages is not None and not 0 < num_pages <= pages:
+        raise ValueError(f"num_pages {num_pages} exceeds the {pages} pages of the caches")
     if out is None:
         out = torch.empty_like(q)
     _dev(out, torch.bfloat16, "out")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have the shape of q")
+    if workspace is not None and (workspace.device != q.device or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on the device of q")
     if workspace is None:
         workspace = torch.empty(spec_verify_attn_workspace_size(B, T, Hq, Hkv, D),
                                 dtype=torch.uint8, device=q.device)

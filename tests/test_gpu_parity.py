@@ -307,3 +307,20 @@ def test_plan_once_run_per_layer():
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), layer
     assert ops.spec_verify_attn_device_status(ws) == 0
+
+
+def test_binding_rejects_mismatched_shapes():
+    """The binding checks the sizes the library cannot see behind device
+    pointers and raises before anything is launched."""
+    case = W.make_custom(7, context_lens=[40, 9], q_lens=[3, 2], hq=8, hkv=2, d=64)
+    dc = DevCase(case)
+    with pytest.raises(ValueError):
+        ops.spec_verify_attn(dc.q, dc.k, dc.v, dc.bt, dc.ctx, dc.cu[:-1], None)
+    with pytest.raises(ValueError):
+        ops.spec_verify_attn(dc.q, dc.k, dc.v, dc.bt[:1], dc.ctx, dc.cu, None)
+    with pytest.raises(ValueError):
+        ops.spec_verify_attn(dc.q, dc.k, dc.v, dc.bt, dc.ctx, dc.cu, i32(np.full(3, -1, np.int32)))
+    with pytest.raises(ValueError):
+        ops.spec_verify_attn(dc.q, dc.k, dc.v, dc.bt, dc.ctx, dc.cu, None, num_pages=case.num_pages + 1)
+    with pytest.raises(ValueError):
+        ops.spec_verify_attn(dc.q, dc.k, dc.v, dc.bt, dc.ctx, dc.cu, None, out=torch.empty_like(dc.q[:-1]))
