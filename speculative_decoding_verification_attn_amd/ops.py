@@ -237,6 +237,8 @@ def spec_accept(logits, draft_tokens, cu_q, tree_parent=None, *, target_argmax=N
     T, V = logits.shape
     B = cu_q.shape[0] - 1
     dev = logits.device
+    if draft_tokens.numel() != T or (tree_parent is not None and tree_parent.numel() != T):
+        raise ValueError("draft_tokens (and tree_parent) must hold one entry per logits row")
     if target_argmax is None:
         target_argmax = torch.empty(T, dtype=torch.int32, device=dev)
     if accept_len is None:
@@ -245,9 +247,11 @@ def spec_accept(logits, draft_tokens, cu_q, tree_parent=None, *, target_argmax=N
         accepted_path = torch.empty(T, dtype=torch.int32, device=dev)
     if out_tokens is None:
         out_tokens = torch.empty(T, dtype=torch.int32, device=dev)
-    for t, nm in ((target_argmax, "target_argmax"), (accept_len, "accept_len"),
-                  (accepted_path, "accepted_path"), (out_tokens, "out_tokens")):
+    for t, nm, n in ((target_argmax, "target_argmax", T), (accept_len, "accept_len", B),
+                     (accepted_path, "accepted_path", T), (out_tokens, "out_tokens", T)):
         _dev(t, torch.int32, nm)
+        if t.numel() != n:
+            raise ValueError(f"{nm} must hold {n} entries")
     if workspace is None:
         workspace = torch.empty(spec_accept_workspace_size(B, T, V), dtype=torch.uint8, device=dev)
     _check(lib.spec_accept(_ptr(logits), V, _ptr(draft_tokens), _ptr(cu_q), _ptr(tree_parent), B, T,
@@ -279,10 +283,19 @@ def kv_compact(k_cache, v_cache, block_tables, context_lens, cu_q, accepted_path
     if num_kv_heads is None:
         num_kv_heads, head_dim = shp[-3], shp[-1]
         num_pages = shp[-4]
+    elif head_dim is None or num_pages is None:
+        raise ValueError("with num_kv_heads given, head_dim and num_pages are needed too")
     if layer_stride_elems is None:
         layer_stride_elems = num_pages * num_kv_heads * 16 * head_dim
     B = context_lens.shape[0]
     T = accepted_path.shape[0]
+    # the kernel writes every layer in place: all of them must lie inside both tensors
+    need = (int(num_layers) - 1) * int(layer_stride_elems) + int(num_pages) * num_kv_heads * 16 * head_dim
+    if num_layers > 0 and (need > k_cache.numel() or tuple(v_cache.shape) != tuple(shp)):
+        raise ValueError(f"{num_layers} layers {layer_stride_elems} elements apart do not fit the caches")
+    if cu_q.numel() != B + 1 or accept_len.numel() != B or block_tables.dim() != 2 \
+            or block_tables.shape[0] != B:
+        raise ValueError("cu_q, accept_len and block_tables must match the batch of context_lens")
     if new_context_lens is None:
         new_context_lens = torch.empty(B, dtype=torch.int32, device=k_cache.device)
     _dev(new_context_lens, torch.int32, "new_context_lens")
@@ -430,6 +443,8 @@ def spec_accept_compact(logits, draft_tokens, cu_q, tree_parent, k_cache, v_cach
     T, V = logits.shape
     B = cu_q.shape[0] - 1
     dev = logits.device
+    if draft_tokens.numel() != T or (tree_parent is not None and tree_parent.numel() != T):
+        raise ValueError("draft_tokens (and tree_parent) must hold one entry per logits row")
     mk = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
     target_argmax = mk(T) if target_argmax is None else target_argmax
     accept_len = mk(B) if accept_len is None else accept_len
@@ -440,6 +455,12 @@ def spec_accept_compact(logits, draft_tokens, cu_q, tree_parent, k_cache, v_cach
     num_kv_heads, head_dim, num_pages = shp[-3], shp[-1], shp[-4]
     if layer_stride_elems is None:
         layer_stride_elems = num_pages * num_kv_heads * 16 * head_dim
+    # the launch moves K/V of every layer in place: all of them must lie inside both tensors
+    need = (int(num_layers) - 1) * int(layer_stride_elems) + num_pages * num_kv_heads * 16 * head_dim
+    if num_layers > 0 and (need > k_cache.numel() or tuple(v_cache.shape) != tuple(shp)):
+        raise ValueError(f"{num_layers} layers {layer_stride_elems} elements apart do not fit the caches")
+    if context_lens.numel() != B or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("context_lens and block_tables must match the batch of cu_q")
     _check(lib.spec_accept_compact(_ptr(logits), V, _ptr(draft_tokens), _ptr(cu_q), _ptr(tree_parent), B, T,
                                    _ptr(target_argmax), _ptr(accept_len), _ptr(accepted_path), _ptr(out_tokens),
                                    _ptr(k_cache), _ptr(v_cache), int(layer_stride_elems), int(num_layers),
@@ -469,6 +490,10 @@ def spec_accept_stochastic(logits, draft_probs, draft_tokens, uniform_accept, un
     T, V = logits.shape
     B = cu_q.shape[0] - 1
     dev = logits.device
+    if draft_tokens.numel() != T or uniform_accept.numel() != T or uniform_sample.numel() != B \
+            or tuple(draft_probs.shape) != (T, V):
+        raise ValueError("draft_tokens, uniform_accept and draft_probs must match the logits rows, "
+                         "uniform_sample the batch")
     mk = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
     accept_len = mk(B) if accept_len is None else accept_len
     accepted_path = mk(T) if accepted_path is None else accepted_path

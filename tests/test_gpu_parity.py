@@ -324,3 +324,10 @@ def test_binding_rejects_mismatched_shapes():
         ops.spec_verify_attn(dc.q, dc.k, dc.v, dc.bt, dc.ctx, dc.cu, None, num_pages=case.num_pages + 1)
     with pytest.raises(ValueError):
         ops.spec_verify_attn(dc.q, dc.k, dc.v, dc.bt, dc.ctx, dc.cu, None, out=torch.empty_like(dc.q[:-1]))
+    # compaction: more layers than the caches hold would write past them
+    path = i32(np.zeros(case.total_q, np.int32))
+    acc = i32(np.ones(case.batch, np.int32))
+    with pytest.raises(ValueError):
+        ops.kv_compact(dc.k, dc.v, dc.bt, dc.ctx, dc.cu, path, acc, num_layers=2)
+    with pytest.raises(ValueError):
+        ops.spec_accept(dc.logits, dc.draft[:-1], dc.cu)
