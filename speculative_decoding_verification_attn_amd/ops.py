@@ -360,9 +360,18 @@ def spec_verify_attn_chunk_run(q, k_cache, v_cache, block_tables, context_lens, 
     if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("cache shapes do not match q")
     B = context_lens.shape[0]
+    if cu_q.numel() != B + 1 or cu_chunk.numel() != B + 1 or chunk_begin.numel() < B \
+            or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("cu_q, cu_chunk, chunk_begin and block_tables must match the batch of context_lens")
+    if tree_parent is not None and tree_parent.numel() != total_q:
+        raise ValueError("tree_parent must hold one entry per verify token of the step")
+    if num_pages is not None and not 0 < num_pages <= pages:
+        raise ValueError(f"num_pages {num_pages} exceeds the {pages} pages of the caches")
     if out is None:
         out = torch.empty_like(q)
     _dev(out, torch.bfloat16, "out")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have the shape of q")
     _check(lib.spec_verify_attn_chunk_run(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                           block_tables.shape[1], _ptr(context_lens), _ptr(cu_q), int(total_q),
                                           _ptr(chunk_begin), _ptr(cu_chunk), Tc, _ptr(tree_parent), _ptr(out),
@@ -392,6 +401,11 @@ def spec_accept_chunk(logits, draft_tokens, cu_q, chunk_begin, cu_chunk, tree_pa
     Tc, V = logits.shape
     B = cu_q.shape[0] - 1
     T = draft_tokens.shape[0]
+    if any(t.numel() != T for t in (target_argmax, accepted_path, out_tokens)) or \
+            (tree_parent is not None and tree_parent.numel() != T) or accept_len.numel() != B or \
+            next_cu.numel() != B + 1 or cu_chunk.numel() != B + 1 or chunk_begin.numel() < B or \
+            next_begin.numel() < B:
+        raise ValueError("chunk acceptance arrays do not match the batch or the step's verify tokens")
     _check(lib.spec_accept_chunk(_ptr(logits), V, _ptr(draft_tokens), _ptr(cu_q), _ptr(tree_parent),
                                  _ptr(chunk_begin), _ptr(cu_chunk), B, T, Tc, int(chunk_size),
                                  _ptr(target_argmax), _ptr(accept_len), _ptr(accepted_path),
