@@ -331,3 +331,37 @@ def test_binding_rejects_mismatched_shapes():
         ops.kv_compact(dc.k, dc.v, dc.bt, dc.ctx, dc.cu, path, acc, num_layers=2)
     with pytest.raises(ValueError):
         ops.spec_accept(dc.logits, dc.draft[:-1], dc.cu)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes(seed):
+    """Seeded random batches: 1-8 requests, contexts 0-1500 (some 0), chains of
+    1-64 tokens or trees of 1-64 nodes, 1-8 KV heads, GQA ratio 1-16, head_dim
+    64 or 128; attention, argmax and acceptance against the oracle."""
+    rng = np.random.default_rng(500 + seed)
+    for c in range(5):
+        B = int(rng.integers(1, 9))
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        g = int(rng.choice([1, 2, 4, 8, 16]))
+        d = int(rng.choice([64, 128]))
+        ctx = [int(x) for x in rng.integers(0, 1500, B)]
+        if rng.random() < 0.3:
+            ctx[int(rng.integers(0, B))] = 0
+        cs = 3000 + 10 * seed + c
+        if rng.random() < 0.4:
+            trees = []
+            for i in range(B):
+                nodes = int(rng.integers(1, 65))
+                depth = nodes - 1 if nodes < 8 else min(nodes - 1, int(rng.integers(6, 13)))
+                trees.append(W.draw_tree(np.random.Generator(np.random.PCG64(cs * 100 + i)), nodes, depth, 4, 4))
+            case = W.make_custom(cs, context_lens=ctx, tree_parents=trees, hq=g * hkv, hkv=hkv, d=d, vocab=300)
+        else:
+            ql = [int(x) for x in rng.integers(1, 65, B)]
+            case = W.make_custom(cs, context_lens=ctx, q_lens=ql, hq=g * hkv, hkv=hkv, d=d, vocab=300)
+        tag = f"seed {seed} case {c}: B={B} hkv={hkv} G={g} D={d} T={case.total_q}"
+        note(tag)
+        dc = DevCase(case)
+        out, ws = gpu_attn(dc)
+        assert ops.spec_verify_attn_device_status(ws) == 0, tag
+        assert_attn_close(bf16_out_to_f64(out), oracle_attn(case), tag)
+        _check_accept(case, dc)
