@@ -119,9 +119,11 @@ def main():
         # distinct caches so layers do not hit in the 256 MB last-level cache
         copies = min(layers, max(2, int(np.ceil(1.0e9 / max(kv_bytes, 1)))))
     k0 = case.k_cache_dev if big else bf16(case.k_cache)
-    v0 = case.v_cache_dev if big else bf16(case.v_cache)
+    # V pages go to the library transposed ([pages, Hkv, D, 16]); the
+    # device-drawn pools already are
+    v0 = case.v_cache_dev if big else bf16(np.swapaxes(case.v_cache, -1, -2))
     K = torch.empty((copies,) + tuple(k0.shape), dtype=torch.bfloat16, device=dev)
-    V = torch.empty_like(K)
+    V = torch.empty((copies,) + tuple(v0.shape), dtype=torch.bfloat16, device=dev)
     for c in range(copies):
         K[c].copy_(k0)
         V[c].copy_(v0)
@@ -664,7 +666,9 @@ def cpu_baseline(case, k_dev, v_dev, logits_dev, n_req, layers):
         pages.extend(int(p) for p in case.block_tables[i, :n])
     idx = torch.tensor(pages, dtype=torch.long, device=k_dev.device)
     k = k_dev.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
-    v = v_dev.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+    # the oracle takes V pages untransposed: [pages, Hkv, 16, D]
+    v = np.ascontiguousarray(np.swapaxes(v_dev.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16),
+                                         -1, -2))
     mb = max(len(r) for r in rows_bt)
     bt = np.zeros((n_req, mb), np.int32)
     for r, row in enumerate(rows_bt):

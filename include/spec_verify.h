@@ -37,9 +37,13 @@
  *     request is the root (the last committed token); a chain's row j is the
  *     j-th draft token; a tree's rows are its nodes with tree_parent[o+0] = -1
  *     and 0 <= tree_parent[o+j] < j (local indices).
- *   - The KV cache of one layer is [num_pages][num_kv_heads][page_size][head_dim]
- *     bf16; request i's logical slot p is physical page
- *     block_tables[i*max_blocks_per_seq + p/page_size], slot p % page_size.
+ *   - The K cache of one layer is [num_pages][num_kv_heads][page_size][head_dim]
+ *     bf16 and the V cache [num_pages][num_kv_heads][head_dim][page_size] bf16:
+ *     each (page, head) block of V is stored transposed, so that the keys of
+ *     one column d are contiguous (the attention reads V by columns).  Request
+ *     i's logical slot p is physical page
+ *     block_tables[i*max_blocks_per_seq + p/page_size], slot p % page_size:
+ *     K row, resp. V column, p % page_size of that page.
  *     The committed context occupies slots [0, L_i) (L_i = context_lens[i]) and
  *     the verify tokens' K/V, written by the caller's QKV projection, occupy
  *     slots [L_i, L_i+q_i) in row order.
@@ -104,7 +108,7 @@ size_t spec_verify_attn_workspace_size(int batch, int total_q, int num_q_heads, 
  *
  *   q            bf16 [total_q, num_q_heads, head_dim]
  *   k_cache      bf16 [num_pages, num_kv_heads, page_size, head_dim] (one layer)
- *   v_cache      same layout as k_cache
+ *   v_cache      bf16 [num_pages, num_kv_heads, head_dim, page_size] (one layer)
  *   block_tables int32 [batch, max_blocks_per_seq]
  *   context_lens int32 [batch]  L_i (verify tokens excluded)
  *   cu_q         int32 [batch+1] prefix sums of q_i
@@ -204,7 +208,7 @@ int spec_accept_device_status(const void *workspace, uint32_t *flags, void *stre
  * releases pages beyond ceil(new_len/page_size).  NOT idempotent: run once per
  * verify step.
  *
- *   k_cache, v_cache  bf16 caches, modified in place
+ *   k_cache, v_cache  bf16 caches in the layouts above, modified in place
  *   context_lens      int32 [batch] L_i before the step (not modified)
  *   cu_q         int32 [batch+1] as for spec_verify_attn (total_q = cu_q[batch])
  *   accepted_path, accept_len  as produced by spec_accept
@@ -423,7 +427,7 @@ int spec_verify_budget(const float *cond_survival, const int32_t *cu_draft, int 
  * with what a pure read kernel reaches on the same pages of the same device.
  * chunks[c] (DEVICE, int32 [n_chunks]) names one (page, KV head) block:
  * chunk_bytes at byte offset chunks[c] * chunk_bytes of k_cache and of
- * v_cache (DEVICE) - for the [num_pages, Hkv, 16, D] layout, page * Hkv + h
+ * v_cache (DEVICE) - for the cache layouts above, page * Hkv + h
  * with chunk_bytes = 16 * D * 2 (2048 or 4096).  buffer_chunks is the number
  * of blocks each cache holds; an index outside [0, buffer_chunks) reads
  * block 0 instead.  Each lane writes the XOR of the 32-bit words it read to

@@ -42,50 +42,63 @@ __device__ inline int compact_moves(const int32_t *path, int n1, int qn, int L, 
 
 // The workgroup (256 threads) moves the listed slots (src/dst in shared
 // memory) for (layer, head) pairs p = p0, p0 + pstep, ... < num_layers * Hkv:
-// every source row is read into registers with 16-byte loads, all loads have
-// returned in every thread (barrier), and only then are destinations written.
+// every source is read into registers, all loads have returned in every
+// thread (barrier), and only then are destinations written.  A K slot is a
+// row of D contiguous values (16-byte chunks); a V page is stored transposed
+// ([D][16 tokens]), so a V slot is a column: D values 32 bytes apart, moved
+// one 2-byte element at a time.
 template <int D>
 __device__ inline void compact_pairs(uint16_t *k_cache, uint16_t *v_cache, int64_t layer_stride,
                                      int num_layers, int num_kv_heads, const int32_t *bt,
                                      const int *src, const int *dst, int nmove, int p0, int pstep) {
-  constexpr int CPR = D / 8;                                       // 16-byte chunks per row
-  constexpr int MAXU = ((kMaxTokens - 1) * CPR * 2 + 255) / 256;  // units per thread
+  constexpr int CPR = D / 8;                                       // 16-byte chunks of a K row
+  constexpr int MAXK = ((kMaxTokens - 1) * CPR + 255) / 256;       // K chunks per thread
+  constexpr int MAXV = ((kMaxTokens - 1) * D + 255) / 256;         // V elements per thread
   const int tid = threadIdx.x;
   const size_t page_stride = (size_t)num_kv_heads * kPage * D;
-  const int units = nmove * CPR * 2;  // (move, chunk, K|V)
+  const int kunits = nmove * CPR, vunits = nmove * D;
   const int pairs = num_layers * num_kv_heads;
   for (int p = p0; p < pairs; p += pstep) {
     const int layer = p / num_kv_heads;
     const int g = p - layer * num_kv_heads;
-    uint16_t *kc = k_cache + (size_t)layer * layer_stride;
-    uint16_t *vc = v_cache + (size_t)layer * layer_stride;
-    uint4 buf[MAXU];
+    uint16_t *kc = k_cache + (size_t)layer * layer_stride + (size_t)g * kPage * D;
+    uint16_t *vc = v_cache + (size_t)layer * layer_stride + (size_t)g * kPage * D;
+    auto krow = [&](int slot) { return kc + (size_t)bt[slot / kPage] * page_stride + (size_t)(slot % kPage) * D; };
+    auto vcol = [&](int slot) { return vc + (size_t)bt[slot / kPage] * page_stride + (slot % kPage); };
+    uint4 kb[MAXK];
+    uint16_t vb[MAXV];
 #pragma unroll
-    for (int u = 0; u < MAXU; ++u) {
+    for (int u = 0; u < MAXK; ++u) {
       const int idx = tid + u * 256;
-      if (idx < units) {
-        const int which = idx / (nmove * CPR);
-        const int rem = idx - which * nmove * CPR;
-        const int mv = rem / CPR, ch = rem - mv * CPR;
-        const int s = src[mv];
-        const uint16_t *base = (which ? vc : kc) + (size_t)bt[s / kPage] * page_stride +
-                               (size_t)g * kPage * D + (size_t)(s % kPage) * D + ch * 8;
-        buf[u] = *reinterpret_cast<const uint4 *>(base);
+      if (idx < kunits) {
+        const int mv = idx / CPR, ch = idx - mv * CPR;
+        kb[u] = *reinterpret_cast<const uint4 *>(krow(src[mv]) + ch * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < MAXV; ++u) {
+      const int idx = tid + u * 256;
+      if (idx < vunits) {
+        const int mv = idx / D, d = idx - mv * D;
+        vb[u] = vcol(src[mv])[(size_t)d * kPage];
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this thread's source loads have returned
     __syncthreads();                // ... and so have every other thread's
 #pragma unroll
-    for (int u = 0; u < MAXU; ++u) {
+    for (int u = 0; u < MAXK; ++u) {
       const int idx = tid + u * 256;
-      if (idx < units) {
-        const int which = idx / (nmove * CPR);
-        const int rem = idx - which * nmove * CPR;
-        const int mv = rem / CPR, ch = rem - mv * CPR;
-        const int d = dst[mv];
-        uint16_t *base = (which ? vc : kc) + (size_t)bt[d / kPage] * page_stride +
-                         (size_t)g * kPage * D + (size_t)(d % kPage) * D + ch * 8;
-        *reinterpret_cast<uint4 *>(base) = buf[u];
+      if (idx < kunits) {
+        const int mv = idx / CPR, ch = idx - mv * CPR;
+        *reinterpret_cast<uint4 *>(krow(dst[mv]) + ch * 8) = kb[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < MAXV; ++u) {
+      const int idx = tid + u * 256;
+      if (idx < vunits) {
+        const int mv = idx / D, d = idx - mv * D;
+        vcol(dst[mv])[(size_t)d * kPage] = vb[u];
       }
     }
     __syncthreads();  // the next pair's reads come after this pair's writes

@@ -32,11 +32,16 @@
 //   S^T[key][row] = K[key][:] . Q^T[:][row]     A = K rows (one key per lane,
 //                                               8 contiguous d per lane),
 //                                               B = Q^T (staged once in LDS)
-//   O^T[d][row]  += V^T[d][key] . P^T[key][row] A = V^T (each lane holds 4
-//                                               contiguous d of 8 keys, so a
-//                                               V row is one 256-byte read by
-//                                               32 lanes), B = P^T straight
-//                                               from the S^T accumulator.
+//   O^T[d][row]  += V^T[d][key] . P^T[key][row] A = V^T (the V page is stored
+//                                               transposed, [D][16 tokens], so
+//                                               a lane's 8 keys at one d are
+//                                               one 16-byte load and 32 lanes
+//                                               read 1 KB contiguous), B = P^T
+//                                               straight from the S^T
+//                                               accumulator (K rows are loaded
+//                                               in the lane order that makes
+//                                               each lane's 8 P values 8
+//                                               consecutive keys).
 // Both accumulators keep a query row per lane, so the softmax statistics of a
 // row live in one lane pair (lanes n and n+32) and never need a transpose.
 #include "sv_device.h"
@@ -227,14 +232,21 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a) {
   }
 }
 
-// Registers of one 32-key block in flight: K rows as MFMA A operands and the
-// lane's run of DPL contiguous d from 16 V rows (two 16-key groups x slots
-// 8t+4hh+e).
+// Registers of one 32-key block in flight: K rows as MFMA A operands (lane n
+// holds key key_of_lane(n)) and V^T operands: vt[m2][c] holds, for d-row
+// n + 32c of the block's page m2, the 8 consecutive keys 8hh .. 8hh+7.
 template <int D>
 struct KVBlock {
   bf16x8 k[D / 16];
-  uint32_t v[2][2][4][D / 64];
+  bf16x8 vt[2][D / 32];
 };
+
+// Key (0..31 within a 32-key block) whose K row lane n of the S^T product
+// loads: n with bits 2 and 3 swapped.  The S^T accumulator then holds in
+// register r of lane half hh the score of key 16*(r/8) + 8*hh + r%8, so the
+// eight P values a lane packs for one P.V product are 8 consecutive keys:
+// the run a transposed V page row stores contiguously.
+__device__ inline int key_of_lane(int n) { return (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1); }
 
 typedef const __attribute__((address_space(4))) int32_t *const_i32_ptr;
 
@@ -254,35 +266,31 @@ __device__ inline int2 block_pages(const_i32_ptr bt, int b, int npages, int num_
   return make_int2(p0, p1);
 }
 
-// K and V take different cache policies.  A V load instruction covers whole
-// rows (32 lanes x DPL*2 B = D*2 B contiguous), so it is issued nontemporal:
-// streamed through the caches without being kept.  A K load instruction
-// covers only 32 B of each of 32 rows (one key per lane, as the MFMA A
-// operand needs), and the rest of each line is read by the next three
-// instructions, so K uses ordinary loads that keep the line for them.
+// K and V take different cache policies.  A V load instruction reads 16 B
+// of 32 consecutive d-rows of one transposed page, i.e. 1 KB contiguous,
+// so it is issued nontemporal: streamed through the caches without being
+// kept.  A K load instruction covers only 32 B of each of 32 rows (one key
+// per lane, as the MFMA A operand needs), and the rest of each line is read
+// by the next three instructions, so K uses ordinary loads that keep the
+// line for them.
 template <int D>
 __device__ inline void load_block(KVBlock<D> &buf, const uint16_t *kh, const uint16_t *vh,
                                   int2 pg, int n, int hh, size_t page_stride) {
   constexpr int KK = D / 16, DPL = D / 32;
-  const uint16_t *krow = kh + (size_t)(n < 16 ? pg.x : pg.y) * page_stride + (size_t)(n & 15) * D + 8 * hh;
+  const int kn = key_of_lane(n);
+  const uint16_t *krow = kh + (size_t)(kn < 16 ? pg.x : pg.y) * page_stride + (size_t)(kn & 15) * D + 8 * hh;
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) buf.k[kk] = *reinterpret_cast<const bf16x8 *>(krow + 16 * kk);
 #pragma unroll
   for (int m2 = 0; m2 < 2; ++m2) {
-    const uint16_t *vpage = vh + (size_t)(m2 ? pg.y : pg.x) * page_stride + DPL * n;
+    const uint16_t *vpage = vh + (size_t)(m2 ? pg.y : pg.x) * page_stride + 8 * hh;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint16_t *vrow = vpage + (size_t)(8 * t + 4 * hh + e) * D;
-        if constexpr (DPL == 4) {
-          const u32x2v x = __builtin_nontemporal_load(reinterpret_cast<const u32x2v *>(vrow));
-          buf.v[m2][t][e][0] = x.x;
-          buf.v[m2][t][e][1] = x.y;
-        } else {
-          buf.v[m2][t][e][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(vrow));
-        }
-      }
+    for (int c = 0; c < DPL; ++c) {
+      typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+      const u32x4v x =
+          __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(vpage + (size_t)(n + 32 * c) * kPage));
+      buf.vt[m2][c] = __builtin_bit_cast(bf16x8, x);
+    }
   }
 }
 
@@ -298,16 +306,27 @@ __device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 (&qop)[kUnitT
                                      floatx16 (&acc)[kUnitTiles][D / 32]) {
   constexpr int KK = D / 16, DPL = D / 32;
   if (key0 + kBlockKeys > nk) {
-    // keys past the request: their V is stale memory (maybe non-finite)
+    // keys past the request: their V is stale memory (maybe non-finite);
+    // element j of vt[m2][c] is key key0 + 16*m2 + 8*hh + j
 #pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2)
+    for (int m2 = 0; m2 < 2; ++m2) {
+      uint32_t keep[4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int pr = 0; pr < 4; ++pr) {
+        const int k0 = key0 + 16 * m2 + 8 * hh + 2 * pr;
+        keep[pr] = (k0 < nk ? 0x0000FFFFu : 0u) | (k0 + 1 < nk ? 0xFFFF0000u : 0u);
+      }
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int c = 0; c < DPL / 2; ++c)
-            buf.v[m2][t][e][c] = key0 + 16 * m2 + 8 * t + 4 * hh + e < nk ? buf.v[m2][t][e][c] : 0u;
+      for (int c = 0; c < DPL; ++c) {
+        typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+        u32x4v x = __builtin_bit_cast(u32x4v, buf.vt[m2][c]);
+        x.x &= keep[0];
+        x.y &= keep[1];
+        x.z &= keep[2];
+        x.w &= keep[3];
+        buf.vt[m2][c] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
   }
   const bool need_mask = key0 + kBlockKeys > L;
 #pragma unroll
@@ -318,13 +337,13 @@ __device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 (&qop)[kUnitT
     for (int kk = 0; kk < KK; ++kk)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf.k[kk], qop[tt][kk], s, 0, 0, 0);
 
-    // keys of acc reg r: key0 + 8*(r/4) + 4*hh + r%4.  Scores stay unscaled
+    // keys of acc reg r: key0 + 16*(r/8) + 8*hh + r%8.  Scores stay unscaled
     // here; the (positive) scale is folded into the exponent below, and the
     // running max m is kept in the scaled log2 domain.
     if (need_mask) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const int key = key0 + 16 * (r >> 3) + 8 * hh + (r & 7);
         const bool vis = key < L || (key < nk && ((anc[tt] >> (unsigned)(key - L)) & 1ull));
         s[r] = vis ? s[r] : -INFINITY;
       }
@@ -360,20 +379,10 @@ __device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 (&qop)[kUnitT
     for (int m2 = 0; m2 < 2; ++m2) {
       uint32_t w4p[4] = {pw[4 * m2], pw[4 * m2 + 1], pw[4 * m2 + 2], pw[4 * m2 + 3]};
       const bf16x8 pop = __builtin_bit_cast(bf16x8, w4p);
+      // k-slot 8hh + j <-> key 16*m2 + 8hh + j in both operands
 #pragma unroll
-      for (int c = 0; c < DPL; ++c) {
-        // k-slot 4t+e <-> key 16*m2 + 8t + 4hh + e; element c of the lane's d-run
-        uint32_t w4[4];
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-          const int s0 = 2 * pr, s1 = 2 * pr + 1;
-          const uint32_t x0 = buf.v[m2][s0 >> 2][s0 & 3][c >> 1];
-          const uint32_t x1 = buf.v[m2][s1 >> 2][s1 & 3][c >> 1];
-          w4[pr] = (c & 1) ? pack_hi16(x0, x1) : pack_lo16(x0, x1);
-        }
-        const bf16x8 vop = __builtin_bit_cast(bf16x8, w4);
-        acc[tt][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, acc[tt][c], 0, 0, 0);
-      }
+      for (int c = 0; c < DPL; ++c)
+        acc[tt][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf.vt[m2][c], pop, acc[tt][c], 0, 0, 0);
     }
   }
 }
@@ -713,8 +722,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
         f[ww] = fast_exp2(sm_m[ww][n] - Mref);
         Lsum += f[ww] * sm_l[ww][n];
       }
-      // this wave finalises registers r = 4*wave .. 4*wave+3, i.e. output
-      // d = DPL*(8*wave + 4*hh) + (0 .. 4*DPL-1), contiguous
+      // this wave finalises registers r = 4*wave .. 4*wave+3 of every tile c:
+      // output d = 32*c + 8*wave + 4*hh + (0..3), four contiguous per c
       float ov[4 * DPL];
 #pragma unroll
       for (int i = 0; i < 4 * DPL; ++i) ov[i] = 0.f;
@@ -724,28 +733,27 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
         for (int ww = 0; ww < kAttnWaves; ++ww) {
           const float4v x = sm_o[ww][c][wave][lane];
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) ov[DPL * rr + c] += f[ww] * x[rr];
+          for (int rr = 0; rr < 4; ++rr) ov[4 * c + rr] += f[ww] * x[rr];
         }
       const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
-      const int d0 = DPL * (8 * wave + 4 * hh);
+      const int d0 = 8 * wave + 4 * hh;
       const int R = (Wc.rg * kUnitTiles + tt) * kTileRows + n;
       if (R < G * Wc.qn) {
         const int tok = R / G, gq = R - tok * G;
         if (whole) {
           uint16_t *orow = a.out + ((size_t)(Wc.o + tok) * a.num_q_heads + (size_t)Wc.h * G + gq) * D + d0;
-          uint32_t pk[2 * DPL];
 #pragma unroll
-          for (int t = 0; t < 2 * DPL; ++t) pk[t] = pack_bf16x2(ov[2 * t] * inv, ov[2 * t + 1] * inv);
-#pragma unroll
-          for (int t = 0; t < DPL / 2; ++t)
-            reinterpret_cast<uint4 *>(orow)[t] = make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]);
+          for (int c = 0; c < DPL; ++c)
+            *reinterpret_cast<uint2 *>(orow + 32 * c) =
+                make_uint2(pack_bf16x2(ov[4 * c] * inv, ov[4 * c + 1] * inv),
+                           pack_bf16x2(ov[4 * c + 2] * inv, ov[4 * c + 3] * inv));
         } else {
           const size_t slot = (2 * (size_t)w + side) * kUnitTiles + tt;
           float *po = reinterpret_cast<float *>(a.ws + a.lay.part_o) + (slot * kTileRows + n) * D + d0;
 #pragma unroll
-          for (int t = 0; t < DPL; ++t)
-            reinterpret_cast<float4 *>(po)[t] =
-                make_float4(ov[4 * t] * inv, ov[4 * t + 1] * inv, ov[4 * t + 2] * inv, ov[4 * t + 3] * inv);
+          for (int c = 0; c < DPL; ++c)
+            *reinterpret_cast<float4 *>(po + 32 * c) =
+                make_float4(ov[4 * c] * inv, ov[4 * c + 1] * inv, ov[4 * c + 2] * inv, ov[4 * c + 3] * inv);
           if (wave == 0 && hh == 0) {
             float *pl = reinterpret_cast<float *>(a.ws + a.lay.part_lse);
             pl[slot * kTileRows + n] = Lsum > 0.f ? Mref + fast_log2(Lsum) : -INFINITY;

@@ -159,8 +159,8 @@ def _attn_call(fn, q, k_cache, v_cache, block_tables, context_lens, cu_q, tree_p
     _dev(tree_parent, torch.int32, "tree_parent")
     T, Hq, D = q.shape
     pages, Hkv, P, D2 = k_cache.shape
-    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
-        raise ValueError("cache shapes do not match q")
+    if D2 != D or tuple(v_cache.shape) != (pages, Hkv, D, P):
+        raise ValueError("caches must be K [pages, Hkv, 16, D] and V [pages, Hkv, D, 16] matching q")
     B = context_lens.shape[0]
     # sizes the library cannot see behind device pointers
     if cu_q.numel() != B + 1 or block_tables.dim() != 2 or block_tables.shape[0] != B:
@@ -188,7 +188,8 @@ def _attn_call(fn, q, k_cache, v_cache, block_tables, context_lens, cu_q, tree_p
 
 def spec_verify_attn(q, k_cache, v_cache, block_tables, context_lens, cu_q, tree_parent=None,
                      out=None, softmax_scale=0.0, workspace=None, num_pages=None, stream=None):
-    """q [T,Hq,D] bf16; caches [pages,Hkv,16,D] bf16; returns out [T,Hq,D] bf16 (plan + run)."""
+    """q [T,Hq,D] bf16; k_cache [pages,Hkv,16,D], v_cache [pages,Hkv,D,16] (each page's V
+    transposed) bf16; returns out [T,Hq,D] bf16 (plan + run)."""
     return _attn_call("spec_verify_attn", q, k_cache, v_cache, block_tables, context_lens, cu_q,
                       tree_parent, out, softmax_scale, workspace, num_pages, stream)
 
@@ -270,8 +271,9 @@ def spec_accept_device_status(workspace, stream=None) -> int:
 def kv_compact(k_cache, v_cache, block_tables, context_lens, cu_q, accepted_path, accept_len, *,
                num_layers=1, layer_stride_elems=None, num_kv_heads=None, head_dim=None,
                num_pages=None, new_context_lens=None, stream=None):
-    """In-place compaction of every layer.  With num_layers > 1, k_cache/v_cache are
-    [layers, pages, Hkv, 16, D] (or flat pools `layer_stride_elems` apart).
+    """In-place compaction of every layer.  With num_layers > 1, k_cache is
+    [layers, pages, Hkv, 16, D] and v_cache [layers, pages, Hkv, D, 16] (or flat pools
+    `layer_stride_elems` apart).
     Returns new_context_lens [B]."""
     lib = load_library()
     _dev(k_cache, torch.bfloat16, "k_cache")
@@ -291,7 +293,7 @@ def kv_compact(k_cache, v_cache, block_tables, context_lens, cu_q, accepted_path
     T = accepted_path.shape[0]
     # the kernel writes every layer in place: all of them must lie inside both tensors
     need = (int(num_layers) - 1) * int(layer_stride_elems) + int(num_pages) * num_kv_heads * 16 * head_dim
-    if num_layers > 0 and (need > k_cache.numel() or tuple(v_cache.shape) != tuple(shp)):
+    if num_layers > 0 and (need > k_cache.numel() or v_cache.numel() != k_cache.numel()):
         raise ValueError(f"{num_layers} layers {layer_stride_elems} elements apart do not fit the caches")
     if cu_q.numel() != B + 1 or accept_len.numel() != B or block_tables.dim() != 2 \
             or block_tables.shape[0] != B:
@@ -357,8 +359,8 @@ def spec_verify_attn_chunk_run(q, k_cache, v_cache, block_tables, context_lens, 
         _dev(t, torch.int32, nm)
     Tc, Hq, D = q.shape
     pages, Hkv, P, D2 = k_cache.shape
-    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
-        raise ValueError("cache shapes do not match q")
+    if D2 != D or tuple(v_cache.shape) != (pages, Hkv, D, P):
+        raise ValueError("caches must be K [pages, Hkv, 16, D] and V [pages, Hkv, D, 16] matching q")
     B = context_lens.shape[0]
     if cu_q.numel() != B + 1 or cu_chunk.numel() != B + 1 or chunk_begin.numel() < B \
             or block_tables.dim() != 2 or block_tables.shape[0] != B:
@@ -471,7 +473,7 @@ def spec_accept_compact(logits, draft_tokens, cu_q, tree_parent, k_cache, v_cach
         layer_stride_elems = num_pages * num_kv_heads * 16 * head_dim
     # the launch moves K/V of every layer in place: all of them must lie inside both tensors
     need = (int(num_layers) - 1) * int(layer_stride_elems) + num_pages * num_kv_heads * 16 * head_dim
-    if num_layers > 0 and (need > k_cache.numel() or tuple(v_cache.shape) != tuple(shp)):
+    if num_layers > 0 and (need > k_cache.numel() or v_cache.numel() != k_cache.numel()):
         raise ValueError(f"{num_layers} layers {layer_stride_elems} elements apart do not fit the caches")
     if context_lens.numel() != B or block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("context_lens and block_tables must match the batch of cu_q")
@@ -542,8 +544,8 @@ def spec_hbm_read_probe(k_cache, v_cache, chunks, *, sink=None, stream=None):
     _dev(k_cache, torch.bfloat16, "k_cache")
     _dev(v_cache, torch.bfloat16, "v_cache")
     _dev(chunks, torch.int32, "chunks")
-    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
-        raise ValueError("caches must be [num_pages, Hkv, 16, D] and alike")
+    if k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape[:2]) + (k_cache.shape[3], k_cache.shape[2]):
+        raise ValueError("caches must be K [num_pages, Hkv, 16, D] and V [num_pages, Hkv, D, 16]")
     chunk_bytes = k_cache.shape[2] * k_cache.shape[3] * 2
     buffer_chunks = k_cache.shape[0] * k_cache.shape[1]
     if sink is None:

@@ -85,8 +85,8 @@ class VerifyCase:
     qkv_scale: float = 1.0
     logit_sigma: float = 1.0
     kv_device: Optional[str] = None
-    k_cache_dev: object = None        # torch tensors when the pool is drawn on device
-    v_cache_dev: object = None
+    k_cache_dev: object = None        # torch tensors when the pool is drawn on device: K as
+    v_cache_dev: object = None        # k_cache, V with every (page, head) block transposed [.., D, P]
     logits_dev: object = None
     extra: dict = field(default_factory=dict)
 
@@ -376,7 +376,10 @@ def _draw_kv_on_device(rng, shape, scale, device, poison_page, block_tables, con
                 s0 = used - (n - 1) * page_size
                 t[pg, :, s0:, :] = POISON_MAGNITUDE
         out.append(t)
-    return out[0], out[1]
+    # the library's V layout: every (page, head) block transposed, [pages, Hkv, D, P]
+    v = out[1].transpose(-1, -2).contiguous()
+    del out[1]
+    return out[0], v
 
 
 def make_case(name: str, seed: Optional[int] = None, *, unit_scale: bool = False,

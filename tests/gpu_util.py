@@ -37,6 +37,18 @@ def bf16_dev_to_u16(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def v_to_dev(v):
+    """V pages in the generator's (and the oracle's) layout, uint16 [..., page_size, D],
+    to the device in the library's layout: every (page, head) block transposed,
+    [..., D, page_size]."""
+    return u16_to_bf16_dev(np.ascontiguousarray(np.swapaxes(v, -1, -2)))
+
+
+def v_from_dev(vd):
+    """The inverse of v_to_dev: device V [..., D, page_size] as uint16 [..., page_size, D]."""
+    return np.ascontiguousarray(np.swapaxes(bf16_dev_to_u16(vd), -1, -2))
+
+
 def i32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
 
@@ -52,7 +64,7 @@ class DevCase:
             self.v = case.v_cache_dev
         else:
             self.k = u16_to_bf16_dev(case.k_cache)
-            self.v = u16_to_bf16_dev(case.v_cache)
+            self.v = v_to_dev(case.v_cache)
         self.bt = i32(case.block_tables)
         self.ctx = i32(case.context_lens)
         self.cu = i32(case.cu_q)
@@ -120,7 +132,7 @@ def subcase_from_device(dc, reqs):
         bt_rows.append(row)
     idx = torch.tensor(pages, dtype=torch.long, device=DEV)
     k = bf16_dev_to_u16(dc.k.index_select(0, idx))
-    v = bf16_dev_to_u16(dc.v.index_select(0, idx))
+    v = v_from_dev(dc.v.index_select(0, idx))
     mb = max(len(r) for r in bt_rows)
     bt = np.zeros((len(reqs), mb), np.int32)
     for r, row in enumerate(bt_rows):

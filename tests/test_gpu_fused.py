@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import pins
-from gpu_util import DEV, DevCase, bf16_dev_to_u16, i32, note, u16_to_bf16_dev
+from gpu_util import DEV, DevCase, bf16_dev_to_u16, i32, note, u16_to_bf16_dev, v_from_dev, v_to_dev
 from speculative_decoding_verification_attn_amd import ops
 from speculative_decoding_verification_attn_amd import workloads as W
 
@@ -60,7 +60,7 @@ def _check(ref, outs, kd, vd, tag):
     assert np.array_equal(toks, ref["toks"]), tag
     assert np.array_equal(new, ref["new"]), tag
     assert np.array_equal(bf16_dev_to_u16(kd), ref["k"]), tag
-    assert np.array_equal(bf16_dev_to_u16(vd), ref["v"]), tag
+    assert np.array_equal(v_from_dev(vd), ref["v"]), tag
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -75,7 +75,7 @@ def test_fused_equals_oracle_on_repeated_calls(name):
                      dtype=torch.uint8, device=DEV)
     for rep in range(3):
         note(f"[gpu] spec_accept_compact {name} call {rep}")
-        kd, vd = u16_to_bf16_dev(k_all), u16_to_bf16_dev(v_all)
+        kd, vd = u16_to_bf16_dev(k_all), v_to_dev(v_all)
         outs = ops.spec_accept_compact(dc.logits, dc.draft, dc.cu, dc.par, kd, vd, dc.bt, dc.ctx,
                                        workspace=ws, num_layers=LAYERS)
         torch.cuda.synchronize()
@@ -90,7 +90,7 @@ def test_fused_graph_replays():
     dc = DevCase(case)
     k_all, v_all = _caches(case)
     ref = _oracle(case, k_all, v_all)
-    k0, v0 = u16_to_bf16_dev(k_all), u16_to_bf16_dev(v_all)
+    k0, v0 = u16_to_bf16_dev(k_all), v_to_dev(v_all)
     kd, vd = k0.clone(), v0.clone()
     ws = torch.zeros(ops.spec_accept_compact_workspace_size(case.batch, case.total_q, case.vocab),
                      dtype=torch.uint8, device=DEV)

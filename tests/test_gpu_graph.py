@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import DEV, DevCase, note, u16_to_bf16_dev
+from gpu_util import DEV, DevCase, note, u16_to_bf16_dev, v_to_dev
 from speculative_decoding_verification_attn_amd import ops
 from speculative_decoding_verification_attn_amd import workloads as W
 
@@ -34,7 +34,7 @@ def test_graph_replay_equals_eager(kind):
     # three layers: distinct K/V pools stacked so one compaction call covers them
     K = torch.stack([dc.k] + [u16_to_bf16_dev(W.f32_to_bf16_bits(
         rng.standard_normal(case.k_cache.shape).astype(np.float32))) for _ in range(layers - 1)])
-    V = torch.stack([dc.v] + [u16_to_bf16_dev(W.f32_to_bf16_bits(
+    V = torch.stack([dc.v] + [v_to_dev(W.f32_to_bf16_bits(
         rng.standard_normal(case.v_cache.shape).astype(np.float32))) for _ in range(layers - 1)])
     K0, V0 = K.clone(), V.clone()
     ws = torch.empty(ops.spec_verify_attn_workspace_size(B, T, 32, 8, 128), dtype=torch.uint8, device=DEV)

@@ -13,7 +13,7 @@ import oracle
 import pins
 from gpu_util import (DEV, DevCase, assert_attn_close, bf16_dev_to_u16, bf16_out_to_f64,
                       gpu_accept, gpu_attn, i32, note, oracle_attn, oracle_attn_sub,
-                      subcase_from_device, u16_to_bf16_dev)
+                      subcase_from_device, u16_to_bf16_dev, v_from_dev, v_to_dev)
 from speculative_decoding_verification_attn_amd import ops
 from speculative_decoding_verification_attn_amd import workloads as W
 
@@ -118,7 +118,7 @@ def test_attn_chain_equals_degenerate_tree_and_page_permutation():
     v2 = np.empty_like(case.v_cache)
     k2[perm] = case.k_cache
     v2[perm] = case.v_cache
-    out3 = ops.spec_verify_attn(dc.q, u16_to_bf16_dev(k2), u16_to_bf16_dev(v2),
+    out3 = ops.spec_verify_attn(dc.q, u16_to_bf16_dev(k2), v_to_dev(v2),
                                 i32(perm[case.block_tables]), dc.ctx, dc.cu, None)
     torch.cuda.synchronize()
     a, b, c = (bf16_dev_to_u16(x) for x in (out1, out2, out3))
@@ -242,7 +242,7 @@ def test_kv_compact_trees_multilayer():
                                        for _ in range(layers - 1)])
     v_all = np.stack([case.v_cache] + [W.f32_to_bf16_bits(rng.standard_normal(case.v_cache.shape).astype(np.float32))
                                        for _ in range(layers - 1)])
-    kd, vd = u16_to_bf16_dev(k_all), u16_to_bf16_dev(v_all)
+    kd, vd = u16_to_bf16_dev(k_all), v_to_dev(v_all)
     new = ops.kv_compact(kd, vd, i32(case.block_tables), i32(case.context_lens), i32(case.cu_q),
                          i32(ap), i32(acc), num_layers=layers)
     torch.cuda.synchronize()
@@ -252,7 +252,7 @@ def test_kv_compact_trees_multilayer():
                              num_layers=layers)
     assert np.array_equal(new.cpu().numpy(), new_ref)
     assert np.array_equal(bf16_dev_to_u16(kd), k_ref)
-    assert np.array_equal(bf16_dev_to_u16(vd), v_ref)
+    assert np.array_equal(v_from_dev(vd), v_ref)
     assert not np.array_equal(k_ref, k_all)  # something really moved
 
 
@@ -276,10 +276,11 @@ def test_kv_compact_chain_config_is_noop():
 def test_empty_inputs_are_noops():
     q = torch.empty((0, 8, 64), dtype=torch.bfloat16, device=DEV)
     k = torch.zeros((1, 2, 16, 64), dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros((1, 2, 64, 16), dtype=torch.bfloat16, device=DEV)  # V pages transposed
     bt = torch.zeros((0, 1), dtype=torch.int32, device=DEV)
     ctx = torch.zeros(0, dtype=torch.int32, device=DEV)
     cu = torch.zeros(1, dtype=torch.int32, device=DEV)
-    ops.spec_verify_attn(q, k, k, bt, ctx, cu, None)
+    ops.spec_verify_attn(q, k, v, bt, ctx, cu, None)
     # requests with no verify tokens
     cu2 = i32([0, 0, 0])
     res = ops.spec_accept(torch.zeros((0, 16), device=DEV), torch.zeros(0, dtype=torch.int32, device=DEV),
@@ -301,7 +302,7 @@ def test_plan_once_run_per_layer():
     for layer in range(3):
         q = u16_to_bf16_dev(W.f32_to_bf16_bits(rng.standard_normal(case.q.shape).astype(np.float32)))
         k = u16_to_bf16_dev(W.f32_to_bf16_bits(rng.standard_normal(case.k_cache.shape).astype(np.float32)))
-        v = u16_to_bf16_dev(W.f32_to_bf16_bits(rng.standard_normal(case.v_cache.shape).astype(np.float32)))
+        v = v_to_dev(W.f32_to_bf16_bits(rng.standard_normal(case.v_cache.shape).astype(np.float32)))
         got = ops.spec_verify_attn_run(q, k, v, dc.bt, dc.ctx, dc.cu, None, workspace=ws)
         ref = ops.spec_verify_attn(q, k, v, dc.bt, dc.ctx, dc.cu, None)
         torch.cuda.synchronize()

@@ -17,7 +17,7 @@ def test_probe_xor_of_listed_blocks(d, n_list):
     rng = np.random.default_rng(n_list + d)
     pages, hkv = 700, 8
     k = rng.integers(0, 2**16, size=(pages, hkv, 16, d), dtype=np.uint16)
-    v = rng.integers(0, 2**16, size=(pages, hkv, 16, d), dtype=np.uint16)
+    v = rng.integers(0, 2**16, size=(pages, hkv, d, 16), dtype=np.uint16)  # V pages are stored transposed
     chunks = rng.choice(pages * hkv, size=n_list, replace=False).astype(np.int32)
     dev = "cuda:0"
     kd = torch.from_numpy(k.view(np.int16)).to(dev).view(torch.bfloat16)
