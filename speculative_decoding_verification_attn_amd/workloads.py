@@ -11,7 +11,9 @@ What is drawn, per case, in a fixed order so a seed fixes every byte:
 2. draft-tree shapes (parent arrays, root = -1, parent[j] < j, BFS order);
 3. the physical page permutation of the paged KV pool;
 4. queries Q (bf16 bit patterns, [T, Hq, D], packed padding-free by cu_q);
-5. the K/V pool (bf16 bit patterns, [num_pages, Hkv, page_size, D]);
+5. the K/V pool (bf16 bit patterns, [num_pages, Hkv, page_size, D]; the
+   library keeps V pages transposed, [num_pages, Hkv, D, page_size], and the
+   device-side generator below returns them that way);
 6. target logits (fp32, [T, V]);
 7. the planted greedy target token of every logits row: a uniformly drawn id
    whose logit is raised strictly above the row's maximum, so the row's
