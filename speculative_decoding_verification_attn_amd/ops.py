@@ -268,6 +268,15 @@ def spec_accept_device_status(workspace, stream=None) -> int:
     return int(flags.value)
 
 
+def _check_cache_pair(k_cache, v_cache):
+    """K pages [..., pages, Hkv, 16, D] and V pages [..., pages, Hkv, D, 16]: a V
+    tensor in the K (token-major) layout has the same size and would be moved
+    with the wrong strides, so the shapes are compared, not only the sizes."""
+    ks = tuple(k_cache.shape)
+    if len(ks) < 4 or tuple(v_cache.shape) != ks[:-2] + (ks[-1], ks[-2]):
+        raise ValueError("caches must be K [..., pages, Hkv, 16, D] and V [..., pages, Hkv, D, 16]")
+
+
 def kv_compact(k_cache, v_cache, block_tables, context_lens, cu_q, accepted_path, accept_len, *,
                num_layers=1, layer_stride_elems=None, num_kv_heads=None, head_dim=None,
                num_pages=None, new_context_lens=None, stream=None):
@@ -283,6 +292,7 @@ def kv_compact(k_cache, v_cache, block_tables, context_lens, cu_q, accepted_path
         _dev(t, torch.int32, nm)
     shp = k_cache.shape
     if num_kv_heads is None:
+        _check_cache_pair(k_cache, v_cache)
         num_kv_heads, head_dim = shp[-3], shp[-1]
         num_pages = shp[-4]
     elif head_dim is None or num_pages is None:
@@ -467,6 +477,7 @@ def spec_accept_compact(logits, draft_tokens, cu_q, tree_parent, k_cache, v_cach
     accepted_path = mk(T) if accepted_path is None else accepted_path
     out_tokens = mk(T) if out_tokens is None else out_tokens
     new_context_lens = mk(B) if new_context_lens is None else new_context_lens
+    _check_cache_pair(k_cache, v_cache)
     shp = k_cache.shape
     num_kv_heads, head_dim, num_pages = shp[-3], shp[-1], shp[-4]
     if layer_stride_elems is None:

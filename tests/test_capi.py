@@ -198,3 +198,18 @@ def test_read_probe_validation(lib):
     assert call(sw=ops.PROBE_SINK_WORDS - 1) == ops.SV_ERR_SHAPE
     assert call(ch=NULL) == ops.SV_ERR_NULL
     assert call(n=0, k=NULL, v=NULL, ch=NULL, sink=NULL) == ops.SV_OK  # nothing to read
+
+
+def test_cache_pair_layout_check():
+    """The binding tells K pages [.., pages, Hkv, 16, D] from V pages
+    [.., pages, Hkv, D, 16]; a token-major V (same size) is refused."""
+    import torch
+    k = torch.empty((3, 5, 2, 16, 64), dtype=torch.bfloat16)
+    ops._check_cache_pair(k, torch.empty((3, 5, 2, 64, 16), dtype=torch.bfloat16))
+    ops._check_cache_pair(k[0], torch.empty((5, 2, 64, 16), dtype=torch.bfloat16))
+    for bad in ((3, 5, 2, 16, 64), (5, 2, 64, 16), (3, 5, 2, 64, 8)):
+        with pytest.raises(ValueError):
+            ops._check_cache_pair(k, torch.empty(bad, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        ops._check_cache_pair(torch.empty((2, 16, 64), dtype=torch.bfloat16),
+                              torch.empty((2, 64, 16), dtype=torch.bfloat16))

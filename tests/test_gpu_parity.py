@@ -332,6 +332,16 @@ def test_binding_rejects_mismatched_shapes():
         ops.kv_compact(dc.k, dc.v, dc.bt, dc.ctx, dc.cu, path, acc, num_layers=2)
     with pytest.raises(ValueError):
         ops.spec_accept(dc.logits, dc.draft[:-1], dc.cu)
+    # V handed over in the token-major (K) layout: same size, wrong layout
+    v_tok = dc.v.transpose(-1, -2).contiguous()
+    with pytest.raises(ValueError):
+        ops.spec_verify_attn(dc.q, dc.k, v_tok, dc.bt, dc.ctx, dc.cu, None)
+    with pytest.raises(ValueError):
+        ops.kv_compact(dc.k, v_tok, dc.bt, dc.ctx, dc.cu, path, acc)
+    ws = torch.zeros(ops.spec_accept_compact_workspace_size(case.batch, case.total_q, case.vocab),
+                     dtype=torch.uint8, device=dc.k.device)
+    with pytest.raises(ValueError):
+        ops.spec_accept_compact(dc.logits, dc.draft, dc.cu, None, dc.k, v_tok, dc.bt, dc.ctx, workspace=ws)
 
 
 @pytest.mark.parametrize("seed", range(8))
