@@ -391,9 +391,8 @@ __device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 (&qop)[kUnitT
 // merge the partials of units cut by workgroup range boundaries.  A cut unit
 // u spans ranges w0 < w1; it is merged by the workgroups of merge slot
 // w0 + 1 (the first range that starts inside it), so each cut unit is merged
-// exactly once.  Each merge slot has merge_tiles x kTileRows / kMergeRows
-// workgroups of kMergeRows waves; a wave merges row n of one of the unit's
-// tiles.
+// exactly once.  Each merge slot has kTileRows / kMergeRows workgroups of
+// kMergeRows waves; a wave merges row n of each of the unit's tiles in turn.
 // First the lanes read the pieces' log-sum-exps side by side (64 pieces per
 // load) for the common maximum and the normaliser; then the weighted rows are
 // summed with every lane holding D/64 consecutive columns, so a row's
@@ -402,35 +401,24 @@ __device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 (&qop)[kUnitT
 // --------------------------------------------------------------------------
 constexpr int kMergeRows = 4;
 
-// Tiles per merge slot in the merge grid: a unit has a second tile only when
-// some request has more than kTileRows rows (G x its verify tokens), which
-// cannot happen when G x total_q <= kTileRows; the host launch and the kernel
-// take the same value.
-__host__ __device__ inline int merge_tiles(const AttnArgs &a) {
-  return (long long)a.group * a.total_q > kTileRows ? kUnitTiles : 1;
-}
-
 template <int D>
 __global__ __launch_bounds__(64 * kMergeRows) void attn_merge_kernel(AttnArgs a) {
   constexpr int DPT = D / 64;
   const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.lay.hdr);
   constexpr int kChunks = kTileRows / kMergeRows;
-  // workgroup -> (merge slot, tile of the unit, chunk of kMergeRows rows): the
-  // tiles of a unit merge side by side rather than one after the other
-  const int mt = merge_tiles(a);
-  const int wm = blockIdx.x / (kChunks * mt);
-  const int tt = (blockIdx.x / kChunks) % mt;
+  const int wm = blockIdx.x / kChunks;
   const UnitRec mr = reinterpret_cast<const UnitRec *>(a.ws + a.lay.merge_rec)[wm];
   if (wm >= hdr[1] || mr.a.x < 0) return;  // no cut unit to merge here
   const int w0 = mr.a.y, w1 = mr.a.z, side0 = mr.a.w;
   const int o = mr.b.x, qn = mr.b.y, h = mr.b.z, rowgroup = mr.b.w;
-  const int n = (blockIdx.x % kChunks) * kMergeRows + (threadIdx.x >> 6);
+  const int n = (blockIdx.x - wm * kChunks) * kMergeRows + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int G = a.group;
   const float *pl = reinterpret_cast<const float *>(a.ws + a.lay.part_lse);
   const float *po = reinterpret_cast<const float *>(a.ws + a.lay.part_o);
+  for (int tt = 0; tt < kUnitTiles; ++tt) {
   const int R = (rowgroup * kUnitTiles + tt) * kTileRows + n;
-  if (R >= G * qn) return;  // wave-uniform: a one-tile unit's second tile
+  if (R >= G * qn) return;
   const int tok = R / G, gq = R - tok * G;
   // range w0 holds the unit's first block (its first or second partial
   // slot); every later range starts inside the unit (first slot).  No range
@@ -499,6 +487,7 @@ __global__ __launch_bounds__(64 * kMergeRows) void attn_merge_kernel(AttnArgs a)
     reinterpret_cast<uint32_t *>(orow)[lane] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
   else
     orow[lane] = (uint16_t)bf16_bits(acc[0] * inv);
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -826,10 +815,10 @@ void launch_verify_attn_plan(const AttnArgs &a, hipStream_t stream) {
 void launch_verify_attn_run(const AttnArgs &a, int head_dim, hipStream_t stream) {
   if (head_dim == 128) {
     verify_attn_kernel<128><<<a.grid, 64 * kAttnWaves, 0, stream>>>(a);
-    attn_merge_kernel<128><<<a.grid * (kTileRows / kMergeRows) * merge_tiles(a), 64 * kMergeRows, 0, stream>>>(a);
+    attn_merge_kernel<128><<<a.grid * (kTileRows / kMergeRows), 64 * kMergeRows, 0, stream>>>(a);
   } else {
     verify_attn_kernel<64><<<a.grid, 64 * kAttnWaves, 0, stream>>>(a);
-    attn_merge_kernel<64><<<a.grid * (kTileRows / kMergeRows) * merge_tiles(a), 64 * kMergeRows, 0, stream>>>(a);
+    attn_merge_kernel<64><<<a.grid * (kTileRows / kMergeRows), 64 * kMergeRows, 0, stream>>>(a);
   }
 }
 
