@@ -11,7 +11,16 @@ Parity status of each function (what pins it is listed in the tests):
   decode_attn  -- pinned: closed forms, SDPA special case
   argmax       -- pinned: numpy.argmax (first occurrence), planted ties, +-0
   accept       -- pinned: brute-force path enumeration, chain closed form
-  compact      -- pinned: logical read-back, serial in-place copy, chain no-op
+  compact      -- pinned: logical read-back, serial in-place copy, chain no-op,
+                  non-idempotence on a path with moves
+  accept_chunk_step -- pinned: chain closed form, brute-force alive checks
+  stochastic.target_probs -- pinned: torch softmax (fp64), two-logit logistic
+                  closed form, -inf logits, shift invariance
+  stochastic.accept_request -- pinned: losslessness integral, special cases,
+                  inverse CDF by brute force
+  budget.sps_at -- pinned: hand-worked interpolation and clamping, numpy.interp
+  budget.verify_budget -- pinned: brute force over prefix-closed batches,
+                  closed forms
 """
 from __future__ import annotations
 

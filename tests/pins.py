@@ -407,6 +407,28 @@ def check_compact():
     assert np.array_equal(kk, ch.k_cache) and np.array_equal(vv, ch.v_cache)
 
 
+def check_compact_not_idempotent():
+    """Compaction moves slot L+path[k] to L+k once per verify step; applied a
+    second time to the same path [0, 2, 3] it moves the already moved rows
+    again (slot L+1 then holds the old slot L+3), so it is not idempotent."""
+    case = make_custom(53, context_lens=[7], tree_parents=[np.array([-1, 0, 0, 2], np.int32)], hq=2, hkv=1, d=8)
+    ap = np.array([0, 2, 3, -1], np.int32)
+    acc = np.array([3], np.int32)
+    kw = dict(num_kv_heads=1, head_dim=8, page_size=P, num_pages=case.num_pages)
+    k0 = case.k_cache.copy()
+    k1, v1 = case.k_cache.copy(), case.v_cache.copy()
+    oracle.compact(k1, v1, case.block_tables, case.context_lens, case.cu_q, ap, acc, **kw)
+    k2, v2 = k1.copy(), v1.copy()
+    oracle.compact(k2, v2, case.block_tables, case.context_lens, case.cu_q, ap, acc, **kw)
+    assert not np.array_equal(k1, k2) and not np.array_equal(v1, v2)
+    bt, L = case.block_tables[0], 7
+
+    def row(c, p):
+        return c[bt[p // P], 0, p % P]
+    assert np.array_equal(row(k1, L + 1), row(k0, L + 2))
+    assert np.array_equal(row(k2, L + 1), row(k0, L + 3))
+
+
 # ----------------------------------------------------------------------------
 # chunked acceptance with early pruning (FASER, "Early Token Pruning")
 # ----------------------------------------------------------------------------
@@ -493,4 +515,5 @@ ALL_CHECKS = [check_attn_vs_sdpa, check_attn_closed_forms, check_attn_convexity,
               check_attn_decode_equivalence, check_decode_closed_form,
               check_attn_page_permutation_and_degenerate_tree, check_argmax,
               check_accept_chain_exhaustive, check_accept_tree_bruteforce, check_compact,
+              check_compact_not_idempotent,
               check_chunk_chain_closed_form, check_chunk_tree_lossless_and_pruning]

@@ -46,6 +46,68 @@ def test_oracle_matches_brute_force_over_prefix_batches():
         assert brows == smallest == len(gam) + sum(verify)
 
 
+def test_sps_interpolation_hand_values():
+    """Linear interpolation between unequal table values, worked by hand, and
+    clamping at both ends of the table."""
+    rows, val = [2.0, 6.0, 10.0], [10.0, 30.0, 20.0]
+    cases = {1.0: 10.0, 2.0: 10.0, 3.0: 15.0, 5.0: 25.0, 6.0: 30.0, 7.0: 27.5, 8.0: 25.0, 9.5: 21.25,
+             10.0: 20.0, 64.0: 20.0}
+    for b, want in cases.items():
+        assert budget.sps_at(rows, val, b) == pytest.approx(want, rel=0, abs=1e-12), b
+    # one point: constant
+    assert budget.sps_at([4.0], [7.0], 1.0) == 7.0 and budget.sps_at([4.0], [7.0], 9.0) == 7.0
+
+
+def test_sps_interpolation_matches_numpy_interp():
+    """Library special case: numpy.interp is piecewise-linear interpolation with
+    the end values held outside the table."""
+    rng = np.random.default_rng(9)
+    for _ in range(300):
+        n = int(rng.integers(1, 7))
+        rows = np.sort(rng.choice(np.arange(1, 200), n, replace=False)).astype(np.float64)
+        val = rng.uniform(0.0, 100.0, n)
+        for b in rng.uniform(0.0, 210.0, 8):
+            assert budget.sps_at(rows, val, b) == pytest.approx(float(np.interp(b, rows, val)), rel=1e-12,
+                                                              abs=1e-12)
+
+
+def _budget_pins_fail():
+    try:
+        test_sps_interpolation_hand_values()
+        test_sps_interpolation_matches_numpy_interp()
+        test_oracle_closed_forms()
+        test_oracle_matches_brute_force_over_prefix_batches()
+    except AssertionError:
+        return True
+    return False
+
+
+BUDGET_MUTANTS = [
+    ("wrong_interval", "t = (b - rows[j - 1]) / (float(rows[j]) - float(rows[j - 1]))",
+     "t = (b - rows[j - 1]) / (float(rows[j]) - float(rows[0]))"),
+    ("swapped_weight", "return float(value[j - 1]) + t * (float(value[j]) - float(value[j - 1]))",
+     "return float(value[j]) + t * (float(value[j - 1]) - float(value[j]))"),
+    ("first_interval_only", "while rows[j] < b:", "while j < 1:"),
+    ("no_low_clamp", "if b <= rows[0]:\n        return float(value[0])", "if b < 0:\n        return float(value[0])"),
+    ("tau_without_bonus", "tau = float(n)\n    best", "tau = 0.0\n    best"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", BUDGET_MUTANTS, ids=[m[0] for m in BUDGET_MUTANTS])
+def test_budget_pins_catch_planted_mistake(tmp_path, monkeypatch, name, old, new):
+    import importlib.util
+    src = open(budget.__file__).read()
+    assert src.count(old) == 1, name
+    path = tmp_path / f"budget_{name}.py"
+    path.write_text(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location(f"budget_{name}", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    monkeypatch.setattr(budget, "sps_at", mod.sps_at)
+    monkeypatch.setattr(budget, "verify_budget", mod.verify_budget)
+    assert _budget_pins_fail(), f"no pin caught {name}"
+
+
 def test_oracle_closed_forms():
     # constant SPS: every draft with survival > 0 raises tau -> all of them
     cond = [np.array([0.5, 0.5, 0.0, 0.9], np.float32), np.array([1.0, 0.2], np.float32)]

@@ -1,6 +1,7 @@
-"""Pins of the stochastic-acceptance oracle (CPU): the rejection rule keeps the
-target's distribution (the defining property the pages state), plus special
-cases and the inverse CDF against brute force."""
+"""Pins of the stochastic-acceptance oracle (CPU): the target softmax against
+torch's softmax and the two-logit logistic closed form; the rejection rule
+keeps the target's distribution (the defining property the pages state), plus
+special cases and the inverse CDF against brute force."""
 import numpy as np
 import pytest
 
@@ -43,6 +44,38 @@ def test_lossless_first_token(seed):
     got = _first_token_distribution(logits, dprobs, temp)
     want = S.target_probs(logits[0], temp)
     assert np.abs(got - want).max() < 3e-3, (got, want)
+
+
+def test_target_probs_matches_torch_softmax():
+    """Library special case: torch's softmax of logits / T in float64."""
+    import torch
+    rng = np.random.default_rng(11)
+    for temp in (0.25, 0.7, 1.0, 1.9):
+        for V in (1, 2, 7, 1000):
+            x = rng.standard_normal(V) * 4.0
+            want = torch.softmax(torch.from_numpy(x) / temp, dim=0).numpy()
+            got = S.target_probs(x, temp)
+            assert np.abs(got - want).max() <= 1e-14, (temp, V)
+
+
+def test_target_probs_two_logit_closed_form():
+    """Two logits a, b: p(a) = 1 / (1 + e^{-(a-b)/T}), the logistic function."""
+    for a, b, temp in ((0.0, 0.0, 1.0), (1.0, 0.0, 1.0), (0.3, -1.2, 0.5), (-2.0, 3.0, 2.0), (5.0, 4.0, 0.1)):
+        p = S.target_probs(np.array([a, b]), temp)
+        want = 1.0 / (1.0 + np.exp(-(a - b) / temp))
+        assert abs(p[0] - want) <= 1e-15 and abs(p[1] - (1.0 - want)) <= 1e-15, (a, b, temp)
+
+
+def test_target_probs_neg_inf_logit_and_shift():
+    """A -inf logit has probability 0 exactly; adding a constant to every logit
+    changes nothing; the probabilities sum to 1."""
+    x = np.array([0.5, -np.inf, 2.0, -1.0])
+    p = S.target_probs(x, 1.0)
+    assert p[1] == 0.0
+    e = np.exp(np.array([0.5, 2.0, -1.0]))
+    assert np.abs(p[[0, 2, 3]] - e / e.sum()).max() <= 1e-15
+    assert abs(p.sum() - 1.0) <= 1e-15
+    assert np.abs(S.target_probs(x + 100.0, 1.0) - p).max() <= 1e-15
 
 
 def test_all_accepted_bonus_from_last_row():
@@ -127,6 +160,10 @@ MUTANTS = [
      "p = target_probs(logits[o + j], temperature)"),
     ("residual_wrong_draft_row", "r = np.maximum(0.0, p - np.asarray(draft_probs[o + n + 1], np.float64))",
      "r = np.maximum(0.0, p - np.asarray(draft_probs[o + n], np.float64))"),
+    ("softmax_exp2_without_log2e", "e = np.exp(x - x.max())", "e = np.exp2(x - x.max())"),
+    ("softmax_missing_normaliser", "return e / e.sum()", "return e"),
+    ("softmax_temperature_multiplies", "x = np.asarray(row_logits, np.float64) / float(temperature)",
+     "x = np.asarray(row_logits, np.float64) * float(temperature)"),
 ]
 
 
@@ -143,7 +180,9 @@ def test_pins_catch_planted_mistake(tmp_path, monkeypatch, name, old, new):
     monkeypatch.setattr(S, "accept_request", mod.accept_request)
     monkeypatch.setattr(S, "target_probs", mod.target_probs)
     failed = False
-    for check in (lambda: test_lossless_first_token(0), lambda: test_lossless_first_token(1),
+    for check in (test_target_probs_matches_torch_softmax, test_target_probs_two_logit_closed_form,
+                  test_target_probs_neg_inf_logit_and_shift,
+                  lambda: test_lossless_first_token(0), lambda: test_lossless_first_token(1),
                   test_all_accepted_bonus_from_last_row, test_zero_target_probability_is_never_accepted):
         try:
             check()
