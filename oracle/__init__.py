@@ -41,7 +41,7 @@ def build(force: bool = True) -> str:
     """Compile oracle.c into liboracle.so with gcc (host only)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-fPIC", "-shared", _SRC,
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-fopenmp", "-fPIC", "-shared", _SRC,
                                "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
@@ -59,6 +59,8 @@ def _bind(path):
     lib.oracle_accept.argtypes = [P, P, P, P, I, P, P, P]
     lib.oracle_compact.argtypes = [P, P, LL, I, P, I, P, P, P, P, P, I, I, I, I, I]
     lib.oracle_accept_chunk_step.argtypes = [P, P, P, P, P, P, I, I, P, P, P, P, P]
+    lib.oracle_set_threads.argtypes = [I]
+    lib.oracle_set_threads.restype = I
     for f in (lib.oracle_verify_attn, lib.oracle_decode_attn, lib.oracle_argmax,
               lib.oracle_accept, lib.oracle_compact):
         f.restype = I
@@ -71,6 +73,13 @@ def _load():
         build(force=False)
         _lib = _bind(_LIB)
     return _lib
+
+
+def set_threads(n: int = 0) -> int:
+    """Host threads of the oracle's verify attention (0 keeps the OpenMP
+    default, which follows OMP_NUM_THREADS); returns the count now in use."""
+    lib = _lib_override or _load()
+    return int(lib.oracle_set_threads(int(n)))
 
 
 class OracleError(RuntimeError):

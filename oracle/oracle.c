@@ -41,6 +41,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_OK 0
 #define ORACLE_BAD_ARG 1
@@ -89,6 +92,80 @@ static long long slot_offset(const int32_t *block_tables, int max_blocks, int i,
 }
 
 /*
+ * Host threads the oracle's verify attention uses (OpenMP over independent
+ * (request, KV head) pairs; 0 = the OpenMP default).  Every output element
+ * is computed by one thread with the same operations in the same order
+ * whatever the thread count, so the result does not depend on it.
+ */
+int oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
+/* Rows of one (request i, KV head g): every verify token j and every query
+ * head h of g's group, as defined above oracle_verify_attn. */
+static int verify_attn_group(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                             const int32_t *block_tables, int max_blocks, const int32_t *context_lens,
+                             const int32_t *cu_q, const int32_t *tree_parent, int num_q_heads,
+                             int num_kv_heads, int head_dim, int page_size, double scale, int i,
+                             int g, double *out) {
+    const int G = num_q_heads / num_kv_heads;
+    const int L = context_lens[i];
+    const int o = cu_q[i];
+    const int qn = cu_q[i + 1] - cu_q[i];
+    const int nk = L + qn;
+    /* explicit mask matrix M[j][p] */
+    double *mask = (double *)malloc(sizeof(double) * (size_t)qn * (size_t)nk);
+    double *s = (double *)malloc(sizeof(double) * (size_t)nk);
+    if (!mask || !s) { free(mask); free(s); return ORACLE_NO_MEMORY; }
+    for (int j = 0; j < qn; ++j)
+        for (int p = 0; p < nk; ++p) {
+            int vis = (p < L) || is_ancestor_or_self(tree_parent, o, p - L, j);
+            mask[(size_t)j * nk + p] = vis ? 0.0 : -INFINITY;
+        }
+    for (int j = 0; j < qn; ++j) {
+        for (int h = 0; h < num_q_heads; ++h) {
+            if (h / G != g) continue;
+            const uint16_t *qrow = q + ((long long)(o + j) * num_q_heads + h) * head_dim;
+            /* scores */
+            for (int p = 0; p < nk; ++p) {
+                const uint16_t *krow = k_cache + slot_offset(block_tables, max_blocks, i, p, g,
+                                                             num_kv_heads, page_size, head_dim);
+                double dot = 0.0;
+                for (int d = 0; d < head_dim; ++d)
+                    dot += bf16_to_double(qrow[d]) * bf16_to_double(krow[d]);
+                s[p] = scale * dot + mask[(size_t)j * nk + p];
+            }
+            /* two-pass softmax */
+            double m = -INFINITY;
+            for (int p = 0; p < nk; ++p)
+                if (s[p] > m) m = s[p];
+            double z = 0.0;
+            for (int p = 0; p < nk; ++p) {
+                s[p] = exp(s[p] - m); /* masked: exp(-inf) = 0 */
+                z += s[p];
+            }
+            double *orow = out + ((long long)(o + j) * num_q_heads + h) * head_dim;
+            for (int d = 0; d < head_dim; ++d) orow[d] = 0.0;
+            for (int p = 0; p < nk; ++p) {
+                const double w = s[p] / z;
+                const uint16_t *vrow = v_cache + slot_offset(block_tables, max_blocks, i, p, g,
+                                                             num_kv_heads, page_size, head_dim);
+                for (int d = 0; d < head_dim; ++d) orow[d] += w * bf16_to_double(vrow[d]);
+            }
+        }
+    }
+    free(mask);
+    free(s);
+    return ORACLE_OK;
+}
+
+/*
  * Verify attention (one layer), fp64, explicit mask matrix.
  * For request i in [req_begin, req_end), token j, query head h:
  *   visible(p) = p < L_i                                  (committed prefix)
@@ -97,6 +174,8 @@ static long long slot_offset(const int32_t *block_tables, int max_blocks, int i,
  *   s_p        = scale * sum_d q[j,h,d] * K[p,g,d] + M[j][p]
  *   out[j,h,:] = sum_p softmax(s)_p * V[p,g,:]
  * out is [T, Hq, D] fp64; rows of requests outside the range are untouched.
+ * The inputs of every request are checked first; then the independent
+ * (request, KV head) pairs are computed, in parallel over host threads.
  */
 int oracle_verify_attn(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
                        const int32_t *block_tables, int max_blocks, const int32_t *context_lens,
@@ -106,7 +185,6 @@ int oracle_verify_attn(const uint16_t *q, const uint16_t *k_cache, const uint16_
     if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || head_dim <= 0 || page_size <= 0)
         return ORACLE_BAD_ARG;
     if (req_begin < 0 || req_end > batch || req_begin > req_end) return ORACLE_BAD_ARG;
-    const int G = num_q_heads / num_kv_heads;
     for (int i = req_begin; i < req_end; ++i) {
         const int L = context_lens[i];
         const int o = cu_q[i];
@@ -120,51 +198,23 @@ int oracle_verify_attn(const uint16_t *q, const uint16_t *k_cache, const uint16_
             int pg = block_tables[(long long)i * max_blocks + p];
             if (pg < 0 || pg >= num_pages) return ORACLE_BAD_CONTENT;
         }
-        /* explicit mask matrix M[j][p] */
-        double *mask = (double *)malloc(sizeof(double) * (size_t)qn * (size_t)nk);
-        double *s = (double *)malloc(sizeof(double) * (size_t)nk);
-        if (!mask || !s) { free(mask); free(s); return ORACLE_NO_MEMORY; }
-        for (int j = 0; j < qn; ++j)
-            for (int p = 0; p < nk; ++p) {
-                int vis = (p < L) || is_ancestor_or_self(tree_parent, o, p - L, j);
-                mask[(size_t)j * nk + p] = vis ? 0.0 : -INFINITY;
-            }
-        for (int j = 0; j < qn; ++j) {
-            for (int h = 0; h < num_q_heads; ++h) {
-                const int g = h / G;
-                const uint16_t *qrow = q + ((long long)(o + j) * num_q_heads + h) * head_dim;
-                /* scores */
-                for (int p = 0; p < nk; ++p) {
-                    const uint16_t *krow = k_cache + slot_offset(block_tables, max_blocks, i, p, g,
-                                                                 num_kv_heads, page_size, head_dim);
-                    double dot = 0.0;
-                    for (int d = 0; d < head_dim; ++d)
-                        dot += bf16_to_double(qrow[d]) * bf16_to_double(krow[d]);
-                    s[p] = scale * dot + mask[(size_t)j * nk + p];
-                }
-                /* two-pass softmax */
-                double m = -INFINITY;
-                for (int p = 0; p < nk; ++p)
-                    if (s[p] > m) m = s[p];
-                double z = 0.0;
-                for (int p = 0; p < nk; ++p) {
-                    s[p] = exp(s[p] - m); /* masked: exp(-inf) = 0 */
-                    z += s[p];
-                }
-                double *orow = out + ((long long)(o + j) * num_q_heads + h) * head_dim;
-                for (int d = 0; d < head_dim; ++d) orow[d] = 0.0;
-                for (int p = 0; p < nk; ++p) {
-                    const double w = s[p] / z;
-                    const uint16_t *vrow = v_cache + slot_offset(block_tables, max_blocks, i, p, g,
-                                                                 num_kv_heads, page_size, head_dim);
-                    for (int d = 0; d < head_dim; ++d) orow[d] += w * bf16_to_double(vrow[d]);
-                }
-            }
-        }
-        free(mask);
-        free(s);
     }
-    return ORACLE_OK;
+    const long long n_tasks = (long long)(req_end - req_begin) * num_kv_heads;
+    int rc = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long t = 0; t < n_tasks; ++t) {
+        const int i = req_begin + (int)(t / num_kv_heads);
+        const int g = (int)(t % num_kv_heads);
+        if (cu_q[i + 1] - cu_q[i] == 0) continue;
+        int r = verify_attn_group(q, k_cache, v_cache, block_tables, max_blocks, context_lens, cu_q,
+                                  tree_parent, num_q_heads, num_kv_heads, head_dim, page_size, scale,
+                                  i, g, out);
+        if (r != ORACLE_OK) {
+#pragma omp atomic write
+            rc = r;
+        }
+    }
+    return rc;
 }
 
 /*

@@ -14,7 +14,7 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 MUTANTS = [
     ("dropped_scale", "s[p] = scale * dot + mask[(size_t)j * nk + p];",
      "s[p] = dot + mask[(size_t)j * nk + p];"),
-    ("gqa_head_map", "const int g = h / G;", "const int g = h % num_kv_heads;"),
+    ("gqa_head_map", "if (h / G != g) continue;", "if (h % num_kv_heads != g) continue;"),
     ("prefix_mask_off_by_one", "int vis = (p < L) ||", "int vis = (p + 1 < L) ||"),
     ("mask_excludes_self", "    int a = j;\n", "    int a = parent_of(tree_parent, o, j);\n"),
     ("missing_normaliser", "const double w = s[p] / z;", "const double w = s[p];"),
@@ -62,7 +62,7 @@ def test_pins_catch_mutant(tmp_path, name, old, new):
     c_path = tmp_path / f"oracle_{name}.c"
     so_path = tmp_path / f"liboracle_{name}.so"
     c_path.write_text(mutated)
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", str(c_path), "-o",
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", str(c_path), "-o",
                            str(so_path), "-lm"])
     caught = None
     with oracle.use_library(str(so_path)):
