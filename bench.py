@@ -29,6 +29,8 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak, TFLOP/s
 MI355X_SIMDS = 256 * 4  # compute units x SIMDs
 MI355X_XCDS = 8
+KV_RESIDENT_LIMIT = 96e9  # bytes of per-layer caches the bench keeps resident at most
+SWEEP_BATCHES = (16, 32, 64, 128, 256)  # 70B-shape batch sweep (the last is the default workload)
 
 WORKLOAD_TEXT = {
     "tiny_chain": "tiny chain verify: B=1, gamma=4, 8/2 heads, D=64, L=256, V=1024",
@@ -56,8 +58,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from the host each step instead of replaying HIP graphs")
-    ap.add_argument("--cpu-sample-requests", type=int, default=64,
-                    help="requests of the workload the CPU oracle is timed on (about 10 s of CPU work at B=256)")
+    ap.add_argument("--cpu-sample-requests", type=int, default=0,
+                    help="requests of the workload the CPU oracle is timed on (0 = all)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the 70B-shape batch sweep (and the SPS table built from it)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MB "
                          "(reference for the HBM traffic counters)")
@@ -115,6 +119,10 @@ def main():
     kv_bytes = case.kv_bytes_per_layer()
     if args.kv_copies:
         copies = args.kv_copies
+    elif layers * kv_bytes <= KV_RESIDENT_LIMIT:
+        # every layer's cache resident: attention never hits the 256 MB
+        # last-level cache and compaction covers all layers in one call
+        copies = layers
     else:
         # distinct caches so layers do not hit in the 256 MB last-level cache
         copies = min(layers, max(2, int(np.ceil(1.0e9 / max(kv_bytes, 1)))))
@@ -305,6 +313,12 @@ def main():
     verified_tok_s = float(acc_np.sum()) / (ms_per_step * 1e-3)
 
     ceiling = read_ceiling(case, ops, K[0], V[0], stream, kv_bytes / (attn_ms * 1e-3) / 1e9)
+    kv_for_cpu = None
+    if not args.no_cpu_baseline:
+        # host copy of layer 0 for the oracle (V back in token-major order)
+        kv_for_cpu = (K[0].view(torch.int16).cpu().numpy().view(np.uint16),
+                      np.ascontiguousarray(np.swapaxes(V[0].view(torch.int16).cpu().numpy().view(np.uint16),
+                                                       -1, -2)))
 
     if args.calibrate_copy_mb > 0:
         nbytes = args.calibrate_copy_mb * (1 << 20)
@@ -316,9 +330,20 @@ def main():
         log(f"calibration copy: {nbytes} bytes read, {nbytes} bytes written")
         del src, dst
 
+    sweep = None
+    if name == "llama3_70b_b256" and not args.no_sweep and args.batch is None:
+        main_point = {"batch": B, "verify_rows": T, "us_per_layer": round(attn_ms * 1e3, 2),
+                      "pct_hbm_peak": round(100 * attn_gbs / PEAK_HBM_GBS, 1),
+                      "attn_kv_frac_of_ceiling": None if ceiling is None else ceiling["attn_kv_frac_of_ceiling"],
+                      "accept_us": round(accept_ms * 1e3, 2), "compact_us": round(compact_ms * 1e3, 2),
+                      "plan_us": round(plan_ms * 1e3, 2)}
+        del K, V
+        torch.cuda.empty_cache()
+        sweep = batch_sweep(args, ops, W, main_point, layers)
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, K[0], V[0], logits, args.cpu_sample_requests, layers)
+        cpu = cpu_baseline(case, kv_for_cpu, logits, args.cpu_sample_requests, layers)
 
     traffic = measured_traffic(name)
     mfma = measured_mfma(name)
@@ -344,7 +369,7 @@ def main():
         "data": "synthetic (seeded; bf16 Q/K/V, fp32 logits)",
         "launch": "eager" if graphs is None else "one HIP graph per phase (plan, layers, accept, compact)",
         "config": {"workload": WORKLOAD_TEXT.get(name, name), "name": name, "batch": B, "total_q": T,
-                   "layers_per_step": layers, "kv_copies": copies,
+                   "layers_per_step": layers, "kv_copies": copies, "compact_layers_per_call": copies,
                    "kv_bytes_per_layer": kv_bytes, "logits_bytes": logits_bytes},
         "us_per_layer": round(attn_ms * 1e3, 2),
         "plan_us_per_step": round(plan_ms * 1e3, 2),
@@ -367,6 +392,8 @@ def main():
                      "traffic": None if traffic is None else traffic["total_bytes"],
                      "traffic_detail": traffic},
         "read_ceiling": ceiling,
+        "sweep": None if sweep is None else sweep["points"],
+        "sps_table": None if sweep is None else sweep["sps_table"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
@@ -646,66 +673,173 @@ def measured_traffic(name):
                       % (rec["fetch_scale"], rec["write_scale"])}
 
 
-def cpu_baseline(case, k_dev, v_dev, logits_dev, n_req, layers):
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    verify attention of the first n_req requests (one layer) plus argmax and
-    acceptance of their rows, on the host cores.  Reported in GB/s of the
-    same algorithmic bytes as the GPU figure."""
-    import torch
-
-    import oracle
-    from speculative_decoding_verification_attn_amd.workloads import VerifyCase  # noqa: F401
-
-    n_req = min(n_req, case.batch)
-    reqs = list(range(n_req))
-    P = case.page_size
-    pages, rows_bt = [], []
-    for i in reqs:
-        n = (int(case.context_lens[i]) + int(case.q_lens[i]) + P - 1) // P
-        rows_bt.append(list(range(len(pages), len(pages) + n)))
-        pages.extend(int(p) for p in case.block_tables[i, :n])
-    idx = torch.tensor(pages, dtype=torch.long, device=k_dev.device)
-    k = k_dev.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
-    # the oracle takes V pages untransposed: [pages, Hkv, 16, D]
-    v = np.ascontiguousarray(np.swapaxes(v_dev.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16),
-                                         -1, -2))
-    mb = max(len(r) for r in rows_bt)
-    bt = np.zeros((n_req, mb), np.int32)
-    for r, row in enumerate(rows_bt):
-        bt[r, :len(row)] = row
-    ql = case.q_lens[:n_req]
-    cu = np.zeros(n_req + 1, np.int32)
-    cu[1:] = np.cumsum(ql)
+def _oracle_step_times(oracle, case, k, v, logits, n_req):
+    """One layer of the oracle's verify attention over the first n_req requests
+    and argmax + acceptance of their rows: (attention s, acceptance s, keys,
+    rows)."""
+    n_req = min(n_req or case.batch, case.batch)
     rows = np.arange(int(case.cu_q[0]), int(case.cu_q[n_req]))
+    cu = case.cu_q[:n_req + 1]
     tp = None if case.tree_parent is None else case.tree_parent[rows]
-    lg = logits_dev[int(case.cu_q[0]):int(case.cu_q[n_req])].cpu().numpy()
     t0 = time.perf_counter()
-    oracle.verify_attn(case.q[rows], k, v, bt, case.context_lens[:n_req], cu, tp,
+    oracle.verify_attn(case.q[rows], k, v, case.block_tables[:n_req], case.context_lens[:n_req], cu, tp,
                        num_q_heads=case.num_q_heads, num_kv_heads=case.num_kv_heads,
-                       head_dim=case.head_dim, page_size=P, num_pages=len(pages))
+                       head_dim=case.head_dim, page_size=case.page_size, num_pages=case.num_pages)
     t_attn = time.perf_counter() - t0
     t0 = time.perf_counter()
-    tg = oracle.argmax(lg)
+    tg = oracle.argmax(logits[rows])
     oracle.accept(case.draft_tokens[rows], tg, cu, tp)
     t_acc = time.perf_counter() - t0
-    keys = int(np.sum(case.context_lens[:n_req].astype(np.int64) + ql))
-    attn_bytes = keys * case.num_kv_heads * case.head_dim * 4 + len(rows) * case.num_q_heads * case.head_dim * 4
-    logit_bytes = lg.size * 4
-    # one step of the sample = `layers` attention passes + one acceptance pass
+    keys = int(np.sum(case.context_lens[:n_req].astype(np.int64) + case.q_lens[:n_req]))
+    return t_attn, t_acc, keys, len(rows)
+
+
+def cpu_baseline(case, kv_host, logits_dev, n_req, layers):
+    """The oracle, as it stands, on the same workload: verify attention of the
+    whole batch (one layer, scaled to the step's layers) plus argmax and
+    acceptance of every row, on the host's cores (OpenMP over (request, KV
+    head); the thread count is OpenMP's default, i.e. OMP_NUM_THREADS when
+    set).  Reported in GB/s of the same algorithmic bytes as the GPU figure.
+    Also one thread on each of the three batch-1 workloads."""
+    import oracle
+    from speculative_decoding_verification_attn_amd import workloads as W
+
+    k, v = kv_host
+    lg = logits_dev.cpu().numpy() if case.logits is None else case.logits
+    threads = oracle.set_threads(0)
+    t_attn, t_acc, keys, n_rows = _oracle_step_times(oracle, case, k, v, lg, n_req)
+    n = min(n_req or case.batch, case.batch)
+    attn_bytes = keys * case.num_kv_heads * case.head_dim * 4 + n_rows * case.num_q_heads * case.head_dim * 4
+    logit_bytes = n_rows * case.vocab * 4
     t_step = layers * t_attn + t_acc
     gbs = (layers * attn_bytes + logit_bytes) / t_step / 1e9
-    log(f"cpu oracle sample: {n_req} requests, attention {t_attn:.2f}s/layer, accept {t_acc:.3f}s")
+    log(f"cpu oracle: {n} requests on {threads} threads, attention {t_attn:.2f}s/layer, accept {t_acc:.3f}s")
+    single = {}
+    oracle.set_threads(1)
+    try:
+        for nm in ("tiny_chain", "llama31_8b_chain", "llama3_70b_tree"):
+            c = W.make_case(nm)
+            ta, tc, _, _ = _oracle_step_times(oracle, c, c.k_cache, c.v_cache, c.logits, 0)
+            single[nm] = {"attn_s_per_layer": round(ta, 4), "accept_s": round(tc, 4)}
+            log(f"cpu oracle, 1 thread, {nm}: attention {ta:.3f}s/layer, accept {tc:.4f}s")
+    finally:
+        oracle.set_threads(threads)
     cpu_model = None
     try:
         with open("/proc/cpuinfo") as f:
             cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
     except OSError:
         pass
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle", "cpu_model": cpu_model,
-            "sample": f"first {n_req} of {case.batch} requests ({len(rows)} verify rows, {keys} keys/layer): "
-                      f"one layer of fp64 verify attention timed and scaled to {layers} layers, plus "
-                      f"argmax+acceptance of those rows; single-threaded C oracle",
-            "attn_s_per_layer": round(t_attn, 3), "accept_s": round(t_acc, 4)}
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model,
+            "cpus_in_affinity": affinity,
+            "sample": f"{'all' if n == case.batch else 'first %d of' % n} {case.batch} requests "
+                      f"({n_rows} verify rows, {keys} keys/layer): one layer of fp64 verify attention timed "
+                      f"and scaled to {layers} layers, plus argmax+acceptance of those rows; C oracle, "
+                      f"attention in parallel over (request, KV head) on {threads} threads",
+            "attn_s_per_layer": round(t_attn, 3), "accept_s": round(t_acc, 4),
+            "single_thread": single}
+
+
+def batch_sweep(args, ops, W, main_point, layers, timed_layers=20, reps=5):
+    """Verify-attention time per layer at the Llama-3-70B shape over batches
+    (the large-batch workload's distributions, batch overridden), each in its
+    own run of graph replays over resident caches, with acceptance,
+    compaction and the plan of one step; the read-ceiling probe beside it for
+    caches of 1 GB or more.  The largest batch is the main measurement.  From
+    the points: the verify path's steps per second at each row count (the
+    SPS table a verify-budget scheduler consumes; the model's GEMMs are not
+    part of it)."""
+    import torch
+    dev = "cuda:0"
+    points = []
+    for Bs in SWEEP_BATCHES:
+        if Bs == main_point["batch"]:
+            points.append(main_point)
+            continue
+        case = W.make_case("llama3_70b_b256", None, kv_device=dev, logits_device=dev, batch=Bs)
+        kvb = case.kv_bytes_per_layer()
+        copies = max(2, int(np.ceil(1.0e9 / kvb)))
+        K = torch.empty((copies,) + tuple(case.k_cache_dev.shape), dtype=torch.bfloat16, device=dev)
+        V = torch.empty((copies,) + tuple(case.v_cache_dev.shape), dtype=torch.bfloat16, device=dev)
+        for c in range(copies):
+            K[c].copy_(case.k_cache_dev)
+            V[c].copy_(case.v_cache_dev)
+        case.k_cache_dev = case.v_cache_dev = None
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+        q = torch.from_numpy(np.ascontiguousarray(case.q).view(np.int16)).to(dev).view(torch.bfloat16)
+        bt, ctx, cu = i32(case.block_tables), i32(case.context_lens), i32(case.cu_q)
+        draft = i32(case.draft_tokens)
+        T = case.total_q
+        out = torch.empty_like(q)
+        ws = torch.empty(ops.spec_verify_attn_workspace_size(Bs, T, case.num_q_heads, case.num_kv_heads,
+                                                             case.head_dim), dtype=torch.uint8, device=dev)
+        ws_acc = torch.empty(ops.spec_accept_workspace_size(Bs, T, case.vocab), dtype=torch.uint8, device=dev)
+        acc = torch.empty(Bs, dtype=torch.int32, device=dev)
+        path = torch.empty(T, dtype=torch.int32, device=dev)
+
+        def plan():
+            ops.spec_verify_attn_plan(ctx, cu, max_blocks_per_seq=bt.shape[1], num_q_heads=case.num_q_heads,
+                                      num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
+                                      num_pages=case.num_pages, total_q=T, workspace=ws)
+
+        def attn():
+            for layer in range(timed_layers):
+                c = layer % copies
+                ops.spec_verify_attn_run(q, K[c], V[c], bt, ctx, cu, None, out=out, workspace=ws)
+
+        def accept():
+            ops.spec_accept(case.logits_dev, draft, cu, None, accept_len=acc, accepted_path=path, workspace=ws_acc)
+
+        def compact():
+            ops.kv_compact(K, V, bt, ctx, cu, path, acc, num_layers=copies)
+
+        plan(); attn(); accept(); compact()
+        torch.cuda.synchronize()
+        graphs = {}
+        for nm, fn in (("plan", plan), ("attn", attn), ("accept", accept), ("compact", compact)):
+            graphs[nm] = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graphs[nm]):
+                fn()
+        us = {}
+        for nm, g in graphs.items():
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us[nm] = e0.elapsed_time(e1) * 1e3 / reps
+        us_layer = us["attn"] / timed_layers
+        attn_bytes = kvb + case.qo_bytes() + int(sum(((int(L) + int(qq) + 15) // 16) * 4
+                                                     for L, qq in zip(case.context_lens, case.q_lens)))
+        gbs = attn_bytes / (us_layer * 1e-6) / 1e9
+        ceiling = read_ceiling(case, ops, K[0], V[0], torch.cuda.current_stream(), kvb / (us_layer * 1e-6) / 1e9)
+        pt = {"batch": Bs, "verify_rows": T, "us_per_layer": round(us_layer, 2),
+              "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 1),
+              "attn_kv_frac_of_ceiling": None if ceiling is None else ceiling["attn_kv_frac_of_ceiling"],
+              "accept_us": round(us["accept"], 2), "compact_us": round(us["compact"], 2),
+              "plan_us": round(us["plan"], 2)}
+        points.append(pt)
+        log(f"sweep B={Bs}: {pt['us_per_layer']} us/layer, {pt['pct_hbm_peak']} % of 8 TB/s")
+        del K, V, graphs, case
+        torch.cuda.empty_cache()
+    rows, sps = [], []
+    for pt in points:
+        t_step_us = layers * pt["us_per_layer"] + pt["accept_us"] + pt["compact_us"] + pt["plan_us"]
+        pt["verify_steps_per_s"] = round(1e6 / t_step_us, 2)
+        rows.append(pt["verify_rows"])
+        sps.append(pt["verify_steps_per_s"])
+    table = {"rows": rows, "steps_per_s": sps,
+             "definition": f"verify steps per second of this path at the Llama-3-70B shape ({layers} layers of "
+                           "verify attention + plan + acceptance + compaction per step, graph replays); the "
+                           "model's GEMMs are not included"}
+    return {"points": points, "sps_table": table}
 
 
 if __name__ == "__main__":

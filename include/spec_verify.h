@@ -276,12 +276,17 @@ int spec_accept_stochastic_device_status(const void *workspace, uint32_t *flags,
  *                (k_cache .. num_pages); accepted_path and accept_len are
  *                both outputs here and inputs of the moves.
  *   workspace    at least spec_accept_compact_workspace_size() bytes, and
- *                ZERO-FILLED before its first use (allocate it with zeros);
- *                every completed call leaves it ready for the next one.  Two
- *                calls on one workspace must not overlap in time.
+ *                ZERO-FILLED before its first use (allocate it with zeros).
+ *                Every call ends by zeroing all it wrote there (apart from
+ *                the status word), so one workspace, sized for the largest
+ *                shape, serves calls of any (batch, total_q, vocab) in turn.
+ *                Two calls on one workspace must not overlap in time.
  * Device status (spec_accept_device_status on this workspace): the bits of
  * spec_accept, plus SV_DEV_SYNC_TIMEOUT if a wait between work items gave up
- * (its request's outputs are then unspecified).
+ * (outputs of the affected requests are then unspecified).  A call whose
+ * workspace was not zero at its start reports SV_DEV_SYNC_TIMEOUT and, if
+ * its counters cannot be brought back to zero, leaves them: zero-fill the
+ * workspace again before the next call.
  */
 size_t spec_accept_compact_workspace_size(int batch, int total_q, int vocab);
 

@@ -372,7 +372,11 @@ __global__ __launch_bounds__(kPlanThreads) void chunk_scan_kernel(AcceptArgs a, 
 // have lower workgroup indices, which the dispatcher starts first).  Every
 // wait is bounded: one that runs out sets SV_DEV_SYNC_TIMEOUT and makes the
 // remaining waits give up, so the launch always ends.  The last waiting item
-// to finish clears the counters, so the workspace is ready for the next call.
+// to finish waits until every slice has finished too and then zeroes all
+// that the call wrote to the workspace (counters, slice partials, move
+// lists): the counters of the next call lie at offsets that depend on its
+// shape, so the workspace must be all zero, not only where this call keeps
+// its counters.
 // --------------------------------------------------------------------------
 constexpr int kSpinLimit = 1 << 21;
 constexpr int kFusedCompactItems = 128;
@@ -448,8 +452,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void a
     t = s_item;
     if (t < n_slices || t >= n_total) {  // counters not cleared (workspace not zero-filled)
       if (tid == 0) {
-        atomicOr(status, SV_DEV_SYNC_TIMEOUT);
         __hip_atomic_store(abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the bit must land after item 0 has cleared the status word; item 0
+        // is a slice, which never waits, so this wait ends
+        for (int it = 0; it < kSpinLimit && load_coherent(&hdr[4]) == 0; ++it) __builtin_amdgcn_s_sleep(32);
+        atomicOr(status, SV_DEV_SYNC_TIMEOUT);
       }
       t = n_total;  // no item
     }
@@ -536,24 +543,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void a
       compact_pairs<D>(c.k_cache, c.v_cache, c.layer_stride, c.num_layers, c.num_kv_heads,
                        c.block_tables + (size_t)i * c.max_blocks, s_src, s_dst, s_nmove, g, groups);
   }
-  // The last waiting item to finish clears the counters for the next call.
-  // Only the waiting items count: every slice is done before its request's
-  // walk starts, so once all walks and moves are done, so is everything.
+  // The last waiting item to finish zeroes what the call wrote.  Only the
+  // waiting items count themselves out (one atomic each); the slices are
+  // waited for here through their per-row arrival counts, which in a valid
+  // call are already complete (every row's walk waited for them) and
+  // otherwise (bad cu_q, a wait that gave up) soon are: slices never wait.
   if (blockIdx.x < n_slices) return;
   __syncthreads();
   if (tid == 0)
     s_flag = __hip_atomic_fetch_add(&hdr[3], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
              n_total - n_slices - 1;
   __syncthreads();
-  if (s_flag) {
-    for (int r = tid; r < a.total_q; r += 256) arrive[r] = 0;
-    for (int i = tid; i < a.batch; i += 256) done[i] = 0;
-    if (tid == 0) {
-      hdr[2] = 0;
-      hdr[3] = 0;
-      hdr[4] = 0;
-      hdr[5] = 0;
+  if (!s_flag) return;
+  bool slices_done = true;
+  for (int r = tid; r < a.total_q; r += 256) {
+    int it = 0;
+    while (it < kSpinLimit && load_coherent(arrive + r) < splits) {
+      __builtin_amdgcn_s_sleep(32);
+      ++it;
     }
+    slices_done = slices_done && it < kSpinLimit;
+  }
+  if (!__syncthreads_and(slices_done)) {
+    // a slice never arrived: the counters were not zero at the start of the
+    // call; leave them for the caller to zero-fill again
+    if (tid == 0) atomicOr(status, SV_DEV_SYNC_TIMEOUT);
+    return;
+  }
+  uint64_t *part = reinterpret_cast<uint64_t *>(a.ws + a.lay.part);
+  for (size_t e = tid; e < (size_t)a.total_q * splits; e += 256) part[e] = 0;
+  for (int r = tid; r < a.total_q; r += 256) arrive[r] = 0;
+  for (int i = tid; i < a.batch; i += 256) {
+    done[i] = 0;
+    int *mv = moves + (size_t)i * kFusedMoveWords;
+    const int nmove = max(0, min(load_coherent(&mv[0]), kMaxTokens - 1));
+    for (int m = 0; m < nmove; ++m) {
+      mv[1 + m] = 0;
+      mv[1 + (kMaxTokens - 1) + m] = 0;
+    }
+    mv[0] = 0;
+  }
+  if (tid == 0) {
+    hdr[2] = 0;
+    hdr[3] = 0;
+    hdr[4] = 0;
+    hdr[5] = 0;
   }
 }
 

@@ -23,6 +23,16 @@ SV_ERR_WORKSPACE = 4
 SV_ERR_ALIAS = 5
 SV_ERR_HIP = 6
 
+# device status bits (the *_device_status calls)
+SV_DEV_BAD_CU_Q = 0x1
+SV_DEV_BAD_CONTEXT = 0x2
+SV_DEV_TOO_MANY_TOKENS = 0x4
+SV_DEV_BAD_PARENT = 0x8
+SV_DEV_BAD_PAGE = 0x10
+SV_DEV_TOO_MANY_PAGES = 0x20
+SV_DEV_SYNC_TIMEOUT = 0x40
+SV_DEV_BAD_TOKEN = 0x80
+
 DEV_BAD_CU_Q = 0x1
 DEV_BAD_CONTEXT = 0x2
 DEV_TOO_MANY_TOKENS = 0x4

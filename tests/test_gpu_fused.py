@@ -118,3 +118,80 @@ def test_fused_graph_replays():
         assert ops.spec_accept_device_status(ws) == 0
         _check(ref, outs, kd, vd, f"replay {rep}")
         note(f"[gpu] fused replay {rep} ok")
+
+
+def _ragged_trees(seed, batch, total):
+    """`batch` random trees (1 to 9 nodes) with `total` nodes in all."""
+    rng = np.random.default_rng(seed)
+    sizes = np.full(batch, total // batch)
+    sizes[: total % batch] += 1
+    for _ in range(4 * batch):  # reshuffle node counts, keeping the total
+        a, b = rng.integers(0, batch, 2)
+        if sizes[a] > 1 and sizes[b] < 9:
+            sizes[a] -= 1
+            sizes[b] += 1
+    trees = []
+    for k, n in enumerate(sizes):
+        depth = int(min(n - 1, rng.integers(1, 5)))
+        trees.append(np.array([-1], np.int32) if n == 1 else _tree(seed * 1000 + k, int(n), depth))
+    ctx = rng.integers(0, 90, batch).tolist()
+    return dict(context_lens=ctx, tree_parents=trees, hq=8, hkv=2, d=64, vocab=151936, tree_match=(0.8, 0.5))
+
+
+def test_fused_workspace_shared_across_shapes():
+    """One zero-filled workspace, sized for the largest shape, serves calls of
+    different (batch, total_q): a continuous batch changes shape every step.
+    Batch 64 with 300 then 290 verify rows puts the slice count per row (and so
+    every offset after the slice partials) at different places; then a smaller
+    batch, then the first shape again."""
+    shapes = [(64, 300), (64, 290), (40, 200), (64, 300)]
+    cases = [W.make_custom(470 + k, **_ragged_trees(470 + k, b, t)) for k, (b, t) in enumerate(shapes)]
+    size = max(ops.spec_accept_compact_workspace_size(c.batch, c.total_q, c.vocab) for c in cases)
+    ws = torch.zeros(size, dtype=torch.uint8, device=DEV)
+    for k, case in enumerate(cases):
+        assert case.total_q == shapes[k][1]
+        note(f"[gpu] spec_accept_compact shared workspace call {k}: B={case.batch} T={case.total_q}")
+        dc = DevCase(case)
+        k_all, v_all = _caches(case)
+        ref = _oracle(case, k_all, v_all)
+        kd, vd = u16_to_bf16_dev(k_all), v_to_dev(v_all)
+        outs = ops.spec_accept_compact(dc.logits, dc.draft, dc.cu, dc.par, kd, vd, dc.bt, dc.ctx,
+                                       workspace=ws, num_layers=LAYERS)
+        torch.cuda.synchronize()
+        assert ops.spec_accept_device_status(ws) == 0, k
+        _check(ref, outs, kd, vd, f"shared workspace call {k}")
+        # everything the call wrote is zero again, apart from the status word
+        rest = ws[4:].cpu().numpy()
+        assert not rest.any(), (k, np.flatnonzero(rest)[:8])
+
+
+def test_fused_waits_give_up_and_workspace_recovers():
+    """The ticket counter is preset from the host, so every waiting work item
+    draws a ticket past the last item: the launch must report
+    SV_DEV_SYNC_TIMEOUT and still end (every wait is bounded), and its last
+    item must leave the workspace zeroed, so the next call on the same
+    workspace is exact."""
+    name = "trees_d128"
+    case = W.make_custom(400, **CASES[name])
+    dc = DevCase(case)
+    k_all, v_all = _caches(case)
+    ref = _oracle(case, k_all, v_all)
+    ws = torch.zeros(ops.spec_accept_compact_workspace_size(case.batch, case.total_q, case.vocab),
+                     dtype=torch.uint8, device=DEV)
+    ws[8:12].view(torch.int32).fill_(1 << 30)  # header word 2: the ticket counter
+    torch.cuda.synchronize()
+    note("[gpu] spec_accept_compact with a preset ticket counter (bounded waits give up)")
+    kd, vd = u16_to_bf16_dev(k_all), v_to_dev(v_all)
+    ops.spec_accept_compact(dc.logits, dc.draft, dc.cu, dc.par, kd, vd, dc.bt, dc.ctx, workspace=ws,
+                            num_layers=LAYERS)
+    torch.cuda.synchronize()
+    st = ops.spec_accept_device_status(ws)
+    assert st & ops.SV_DEV_SYNC_TIMEOUT, st
+    assert not ws[4:].cpu().numpy().any()
+    note("[gpu] next call on the same workspace")
+    kd, vd = u16_to_bf16_dev(k_all), v_to_dev(v_all)
+    outs = ops.spec_accept_compact(dc.logits, dc.draft, dc.cu, dc.par, kd, vd, dc.bt, dc.ctx, workspace=ws,
+                                   num_layers=LAYERS)
+    torch.cuda.synchronize()
+    assert ops.spec_accept_device_status(ws) == 0
+    _check(ref, outs, kd, vd, "after give-up")
