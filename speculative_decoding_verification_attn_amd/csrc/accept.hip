@@ -556,13 +556,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void a
   __syncthreads();
   if (!s_flag) return;
   bool slices_done = true;
-  for (int r = tid; r < a.total_q; r += 256) {
+  for (int r = tid; r < a.total_q && slices_done; r += 256) {
     int it = 0;
     while (it < kSpinLimit && load_coherent(arrive + r) < splits) {
       __builtin_amdgcn_s_sleep(32);
       ++it;
     }
-    slices_done = slices_done && it < kSpinLimit;
+    slices_done = it < kSpinLimit;
   }
   if (!__syncthreads_and(slices_done)) {
     // a slice never arrived: the counters were not zero at the start of the
