@@ -60,6 +60,9 @@ def main():
                     help="launch every kernel from the host each step instead of replaying HIP graphs")
     ap.add_argument("--cpu-sample-requests", type=int, default=0,
                     help="requests of the workload the CPU oracle is timed on (0 = all)")
+    ap.add_argument("--v-layout", choices=("transposed", "token-major"), default="transposed",
+                    help="V page layout of the timed step: transposed page blocks (the *_vt calls) or "
+                         "token-major pages (the plain calls); the other layout's attention is timed beside it")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the 70B-shape batch sweep (and the SPS table built from it)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -126,10 +129,16 @@ def main():
     else:
         # distinct caches so layers do not hit in the 256 MB last-level cache
         copies = min(layers, max(2, int(np.ceil(1.0e9 / max(kv_bytes, 1)))))
+    vt = args.v_layout == "transposed"
+    attn_run = ops.spec_verify_attn_run_vt if vt else ops.spec_verify_attn_run
+    compact = ops.kv_compact_vt if vt else ops.kv_compact
+    accept_compact = ops.spec_accept_compact_vt if vt else ops.spec_accept_compact
+    chunk_run = ops.spec_verify_attn_chunk_run_vt if vt else ops.spec_verify_attn_chunk_run
     k0 = case.k_cache_dev if big else bf16(case.k_cache)
-    # V pages go to the library transposed ([pages, Hkv, D, 16]); the
-    # device-drawn pools already are
-    v0 = case.v_cache_dev if big else bf16(np.swapaxes(case.v_cache, -1, -2))
+    # generated pools are token-major; the *_vt calls take each V page block transposed
+    v0 = case.v_cache_dev if big else bf16(case.v_cache)
+    if vt:
+        v0 = v0.transpose(-1, -2).contiguous()
     K = torch.empty((copies,) + tuple(k0.shape), dtype=torch.bfloat16, device=dev)
     V = torch.empty((copies,) + tuple(v0.shape), dtype=torch.bfloat16, device=dev)
     for c in range(copies):
@@ -183,7 +192,7 @@ def main():
 
     def phase_layer(layer, st):
         c = layer % copies
-        ops.spec_verify_attn_run(q, K[c], V[c], bt, ctx, cu, par, out=out, workspace=ws_attn, stream=st)
+        attn_run(q, K[c], V[c], bt, ctx, cu, par, out=out, workspace=ws_attn, stream=st)
 
     def phase_accept(st):
         if args.stochastic:
@@ -191,9 +200,9 @@ def main():
                                        accepted_path=path, out_tokens=toks, stream=st)
             return
         if args.fused:  # acceptance and compaction in one launch; the compact phase is then empty
-            ops.spec_accept_compact(logits, draft, cu, par, K, V, bt, ctx, workspace=ws_fused, num_layers=copies,
-                                    target_argmax=t_arg, accept_len=acc, accepted_path=path, out_tokens=toks,
-                                    new_context_lens=new_len, stream=st)
+            accept_compact(logits, draft, cu, par, K, V, bt, ctx, workspace=ws_fused, num_layers=copies,
+                           target_argmax=t_arg, accept_len=acc, accepted_path=path, out_tokens=toks,
+                           new_context_lens=new_len, stream=st)
             return
         ops.spec_accept(logits, draft, cu, par, target_argmax=t_arg, accept_len=acc, accepted_path=path,
                         out_tokens=toks, workspace=ws_acc, stream=st)
@@ -201,7 +210,7 @@ def main():
     def phase_compact(st):
         if args.fused:
             return
-        ops.kv_compact(K, V, bt, ctx, cu, path, acc, num_layers=copies, new_context_lens=new_len, stream=st)
+        compact(K, V, bt, ctx, cu, path, acc, num_layers=copies, new_context_lens=new_len, stream=st)
 
     def step_eager(record):
         e0 = mark() if record else None
@@ -229,7 +238,7 @@ def main():
     if args.chunk > 0:
         print(json.dumps(chunked_bench(args, case, ops, dict(
             K=K, V=V, copies=copies, q=q, bt=bt, ctx=ctx, cu=cu, par=par, logits=logits, draft=draft,
-            layers=layers, stream=stream, step_eager=step_eager, acc=acc))), flush=True)
+            layers=layers, stream=stream, step_eager=step_eager, acc=acc, chunk_run=chunk_run))), flush=True)
         return
 
     graphs = None
@@ -315,10 +324,20 @@ def main():
     ceiling = read_ceiling(case, ops, K[0], V[0], stream, kv_bytes / (attn_ms * 1e-3) / 1e9)
     kv_for_cpu = None
     if not args.no_cpu_baseline:
-        # host copy of layer 0 for the oracle (V back in token-major order)
+        # host copy of layer 0 for the oracle (V in token-major order)
+        v_host = V[0].view(torch.int16).cpu().numpy().view(np.uint16)
         kv_for_cpu = (K[0].view(torch.int16).cpu().numpy().view(np.uint16),
-                      np.ascontiguousarray(np.swapaxes(V[0].view(torch.int16).cpu().numpy().view(np.uint16),
-                                                       -1, -2)))
+                      np.ascontiguousarray(np.swapaxes(v_host, -1, -2)) if vt else v_host)
+        del v_host
+    # the other V page layout's attention on the same pages, same plan
+    other_us = other_layout_us_per_layer(ops, not vt, q, K, V, bt, ctx, cu, par, out, ws_attn, copies,
+                                         min(layers, 20))
+    layouts = {("v_transposed" if vt else "token_major"): {"us_per_layer": round(attn_ms * 1e3, 2),
+                                                           "pct_hbm_peak": round(100 * attn_gbs / PEAK_HBM_GBS, 1)},
+               ("token_major" if vt else "v_transposed"): {
+                   "us_per_layer": round(other_us, 2),
+                   "pct_hbm_peak": round(100 * attn_bytes / (other_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 1)}}
+    log(f"other V layout: {other_us:.2f} us/layer")
 
     if args.calibrate_copy_mb > 0:
         nbytes = args.calibrate_copy_mb * (1 << 20)
@@ -339,7 +358,8 @@ def main():
                       "plan_us": round(plan_ms * 1e3, 2)}
         del K, V
         torch.cuda.empty_cache()
-        sweep = batch_sweep(args, ops, W, main_point, layers)
+        main_point["other_layout_us_per_layer"] = round(other_us, 2)
+        sweep = batch_sweep(args, ops, W, main_point, layers, vt)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -386,7 +406,11 @@ def main():
         "attn_flop_per_byte": round(intensity, 1),
         "mfma": {"algorithmic_frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4), "peak_tflops": PEAK_MFMA_TFLOPS,
                  "counters": mfma},
-        "roofline": {"kernel": "spec_verify_attn_run (verify_attn_kernel + attn_merge_kernel, per layer)",
+        "v_layout": "transposed V page blocks (spec_verify_attn_run_vt)" if vt
+                    else "token-major V pages (spec_verify_attn_run)",
+        "layouts": layouts,
+        "roofline": {"kernel": "%s (verify_attn_kernel + attn_merge_kernel, per layer)"
+                               % ("spec_verify_attn_run_vt" if vt else "spec_verify_attn_run"),
                      **roof,
                      "algorithmic_bytes": attn_bytes,
                      "traffic": None if traffic is None else traffic["total_bytes"],
@@ -486,7 +510,7 @@ def chunked_bench(args, case, ops, r):
                                             workspace=ws_a)
             for layer in range(r["layers"]):
                 c = layer % r["copies"]
-                ops.spec_verify_attn_chunk_run(qc, r["K"][c], r["V"][c], r["bt"], r["ctx"], r["cu"], begin, cuc,
+                r["chunk_run"](qc, r["K"][c], r["V"][c], r["bt"], r["ctx"], r["cu"], begin, cuc,
                                                r["par"], total_q=T, out=out[:Tc], workspace=ws_a)
             e1 = ev()
             nb, ncu = bufs[1 - cur]
@@ -744,7 +768,40 @@ def cpu_baseline(case, kv_host, logits_dev, n_req, layers):
             "single_thread": single}
 
 
-def batch_sweep(args, ops, W, main_point, layers, timed_layers=20, reps=5):
+def other_layout_us_per_layer(ops, vt, q, K, V, bt, ctx, cu, par, out, ws, copies, n_layers, reps=5):
+    """Attention time per layer with the other V page layout: the resident V
+    copies re-laid out, then a graph of n_layers runs (the plan already in ws)
+    replayed `reps` times."""
+    import torch
+    Vo = torch.empty(tuple(V.shape[:-2]) + (V.shape[-1], V.shape[-2]), dtype=V.dtype, device=V.device)
+    for c in range(copies):
+        Vo[c].copy_(V[c].transpose(-1, -2))
+    run = ops.spec_verify_attn_run_vt if vt else ops.spec_verify_attn_run
+
+    def layers_fn():
+        for layer in range(n_layers):
+            c = layer % copies
+            run(q, K[c], Vo[c], bt, ctx, cu, par, out=out, workspace=ws)
+
+    layers_fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layers_fn()
+    g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps / n_layers
+    del g, Vo
+    torch.cuda.empty_cache()
+    return us
+
+
+def batch_sweep(args, ops, W, main_point, layers, vt, timed_layers=20, reps=5):
     """Verify-attention time per layer at the Llama-3-70B shape over batches
     (the large-batch workload's distributions, batch overridden), each in its
     own run of graph replays over resident caches, with acceptance,
@@ -763,11 +820,13 @@ def batch_sweep(args, ops, W, main_point, layers, timed_layers=20, reps=5):
         case = W.make_case("llama3_70b_b256", None, kv_device=dev, logits_device=dev, batch=Bs)
         kvb = case.kv_bytes_per_layer()
         copies = max(2, int(np.ceil(1.0e9 / kvb)))
+        v_src = case.v_cache_dev.transpose(-1, -2) if vt else case.v_cache_dev
         K = torch.empty((copies,) + tuple(case.k_cache_dev.shape), dtype=torch.bfloat16, device=dev)
-        V = torch.empty((copies,) + tuple(case.v_cache_dev.shape), dtype=torch.bfloat16, device=dev)
+        V = torch.empty((copies,) + tuple(v_src.shape), dtype=torch.bfloat16, device=dev)
         for c in range(copies):
             K[c].copy_(case.k_cache_dev)
-            V[c].copy_(case.v_cache_dev)
+            V[c].copy_(v_src)
+        del v_src
         case.k_cache_dev = case.v_cache_dev = None
         i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
         q = torch.from_numpy(np.ascontiguousarray(case.q).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -789,13 +848,14 @@ def batch_sweep(args, ops, W, main_point, layers, timed_layers=20, reps=5):
         def attn():
             for layer in range(timed_layers):
                 c = layer % copies
-                ops.spec_verify_attn_run(q, K[c], V[c], bt, ctx, cu, None, out=out, workspace=ws)
+                (ops.spec_verify_attn_run_vt if vt else ops.spec_verify_attn_run)(
+                    q, K[c], V[c], bt, ctx, cu, None, out=out, workspace=ws)
 
         def accept():
             ops.spec_accept(case.logits_dev, draft, cu, None, accept_len=acc, accepted_path=path, workspace=ws_acc)
 
         def compact():
-            ops.kv_compact(K, V, bt, ctx, cu, path, acc, num_layers=copies)
+            (ops.kv_compact_vt if vt else ops.kv_compact)(K, V, bt, ctx, cu, path, acc, num_layers=copies)
 
         plan(); attn(); accept(); compact()
         torch.cuda.synchronize()
@@ -820,8 +880,9 @@ def batch_sweep(args, ops, W, main_point, layers, timed_layers=20, reps=5):
                                                      for L, qq in zip(case.context_lens, case.q_lens)))
         gbs = attn_bytes / (us_layer * 1e-6) / 1e9
         ceiling = read_ceiling(case, ops, K[0], V[0], torch.cuda.current_stream(), kvb / (us_layer * 1e-6) / 1e9)
+        other = other_layout_us_per_layer(ops, not vt, q, K, V, bt, ctx, cu, None, out, ws, copies, timed_layers)
         pt = {"batch": Bs, "verify_rows": T, "us_per_layer": round(us_layer, 2),
-              "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 1),
+              "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 1), "other_layout_us_per_layer": round(other, 2),
               "attn_kv_frac_of_ceiling": None if ceiling is None else ceiling["attn_kv_frac_of_ceiling"],
               "accept_us": round(us["accept"], 2), "compact_us": round(us["compact"], 2),
               "plan_us": round(us["plan"], 2)}

@@ -37,13 +37,16 @@
  *     request is the root (the last committed token); a chain's row j is the
  *     j-th draft token; a tree's rows are its nodes with tree_parent[o+0] = -1
  *     and 0 <= tree_parent[o+j] < j (local indices).
- *   - The K cache of one layer is [num_pages][num_kv_heads][page_size][head_dim]
- *     bf16 and the V cache [num_pages][num_kv_heads][head_dim][page_size] bf16:
- *     each (page, head) block of V is stored transposed, so that the keys of
- *     one column d are contiguous (the attention reads V by columns).  Request
- *     i's logical slot p is physical page
+ *   - The K and V caches of one layer are [num_pages][num_kv_heads][page_size]
+ *     [head_dim] bf16 (token-major pages, PagedAttention's layout).  The calls
+ *     named *_vt take the V cache with every (page, head) block stored
+ *     transposed instead, [num_pages][num_kv_heads][head_dim][page_size], so
+ *     that the keys of one column d are contiguous: the attention's P.V
+ *     product reads V by columns, and with this layout each of its operand
+ *     loads is one 16-byte read with no repacking (the K cache layout is the
+ *     same for both).  Request i's logical slot p is physical page
  *     block_tables[i*max_blocks_per_seq + p/page_size], slot p % page_size:
- *     K row, resp. V column, p % page_size of that page.
+ *     K row, and V row (V column for *_vt), p % page_size of that page.
  *     The committed context occupies slots [0, L_i) (L_i = context_lens[i]) and
  *     the verify tokens' K/V, written by the caller's QKV projection, occupy
  *     slots [L_i, L_i+q_i) in row order.
@@ -108,7 +111,8 @@ size_t spec_verify_attn_workspace_size(int batch, int total_q, int num_q_heads, 
  *
  *   q            bf16 [total_q, num_q_heads, head_dim]
  *   k_cache      bf16 [num_pages, num_kv_heads, page_size, head_dim] (one layer)
- *   v_cache      bf16 [num_pages, num_kv_heads, head_dim, page_size] (one layer)
+ *   v_cache      bf16 [num_pages, num_kv_heads, page_size, head_dim] (one layer);
+ *                spec_verify_attn_vt: [num_pages, num_kv_heads, head_dim, page_size]
  *   block_tables int32 [batch, max_blocks_per_seq]
  *   context_lens int32 [batch]  L_i (verify tokens excluded)
  *   cu_q         int32 [batch+1] prefix sums of q_i
@@ -128,6 +132,14 @@ int spec_verify_attn(const void *q, const void *k_cache, const void *v_cache,
                      int head_dim, int page_size, int num_pages, float softmax_scale,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* spec_verify_attn with the V cache's pages stored transposed (see above). */
+int spec_verify_attn_vt(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *block_tables, int max_blocks_per_seq,
+                        const int32_t *context_lens, const int32_t *cu_q, const int32_t *tree_parent,
+                        void *out, int batch, int total_q, int num_q_heads, int num_kv_heads,
+                        int head_dim, int page_size, int num_pages, float softmax_scale,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
 /*
  * The two halves of spec_verify_attn, for callers that verify many layers
  * with the same batch: the work decomposition (the "plan") depends only on
@@ -141,7 +153,8 @@ int spec_verify_attn(const void *q, const void *k_cache, const void *v_cache,
  * sizes as the plan it uses (stream-ordered after it) and must not overlap
  * another run or plan on the same workspace.  A run with metadata that
  * differs from its plan still reads only valid memory, but its outputs are
- * unspecified.
+ * unspecified.  spec_verify_attn_run_vt takes transposed V pages; one plan
+ * serves both layouts.
  */
 int spec_verify_attn_plan(const int32_t *context_lens, const int32_t *cu_q, int max_blocks_per_seq,
                           int batch, int total_q, int num_q_heads, int num_kv_heads, int head_dim,
@@ -154,6 +167,14 @@ int spec_verify_attn_run(const void *q, const void *k_cache, const void *v_cache
                          int num_q_heads, int num_kv_heads, int head_dim, int page_size,
                          int num_pages, float softmax_scale, void *workspace,
                          size_t workspace_bytes, void *stream);
+
+int spec_verify_attn_run_vt(const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, int max_blocks_per_seq,
+                            const int32_t *context_lens, const int32_t *cu_q,
+                            const int32_t *tree_parent, void *out, int batch, int total_q,
+                            int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                            int num_pages, float softmax_scale, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 /* Waits for `stream`, then stores the device status bits of the last
  * spec_verify_attn (plan and runs) that used `workspace` into *flags (host
@@ -208,7 +229,8 @@ int spec_accept_device_status(const void *workspace, uint32_t *flags, void *stre
  * releases pages beyond ceil(new_len/page_size).  NOT idempotent: run once per
  * verify step.
  *
- *   k_cache, v_cache  bf16 caches in the layouts above, modified in place
+ *   k_cache, v_cache  bf16 caches in the layouts above (kv_compact_vt:
+ *                     V pages transposed), modified in place
  *   context_lens      int32 [batch] L_i before the step (not modified)
  *   cu_q         int32 [batch+1] as for spec_verify_attn (total_q = cu_q[batch])
  *   accepted_path, accept_len  as produced by spec_accept
@@ -221,6 +243,12 @@ int kv_compact(void *k_cache, void *v_cache, int64_t layer_stride_elems, int num
                const int32_t *cu_q, const int32_t *accepted_path, const int32_t *accept_len,
                int32_t *new_context_lens, int batch, int total_q, int num_kv_heads, int head_dim,
                int page_size, int num_pages, void *stream);
+
+int kv_compact_vt(void *k_cache, void *v_cache, int64_t layer_stride_elems, int num_layers,
+                  const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+                  const int32_t *cu_q, const int32_t *accepted_path, const int32_t *accept_len,
+                  int32_t *new_context_lens, int batch, int total_q, int num_kv_heads, int head_dim,
+                  int page_size, int num_pages, void *stream);
 
 /* ------------------------------------------------------------------------- */
 /* Lossless stochastic acceptance (chains)                                    */
@@ -299,6 +327,16 @@ int spec_accept_compact(const float *logits, int vocab, const int32_t *draft_tok
                         int32_t *new_context_lens, int num_kv_heads, int head_dim, int page_size,
                         int num_pages, void *workspace, size_t workspace_bytes, void *stream);
 
+/* spec_accept_compact over caches whose V pages are stored transposed. */
+int spec_accept_compact_vt(const float *logits, int vocab, const int32_t *draft_tokens,
+                           const int32_t *cu_q, const int32_t *tree_parent, int batch, int total_q,
+                           int32_t *target_argmax, int32_t *accept_len, int32_t *accepted_path,
+                           int32_t *out_tokens, void *k_cache, void *v_cache,
+                           int64_t layer_stride_elems, int num_layers, const int32_t *block_tables,
+                           int max_blocks_per_seq, const int32_t *context_lens,
+                           int32_t *new_context_lens, int num_kv_heads, int head_dim, int page_size,
+                           int num_pages, void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------------- */
 /* Chunked verification with early pruning                                    */
 /* ------------------------------------------------------------------------- */
@@ -360,6 +398,15 @@ int spec_verify_attn_chunk_run(const void *q, const void *k_cache, const void *v
                                int num_kv_heads, int head_dim, int page_size, int num_pages,
                                float softmax_scale, void *workspace, size_t workspace_bytes,
                                void *stream);
+
+int spec_verify_attn_chunk_run_vt(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *block_tables, int max_blocks_per_seq,
+                                  const int32_t *context_lens, const int32_t *cu_q, int total_q,
+                                  const int32_t *chunk_begin, const int32_t *cu_chunk, int total_chunk,
+                                  const int32_t *tree_parent, void *out, int batch, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int page_size, int num_pages,
+                                  float softmax_scale, void *workspace, size_t workspace_bytes,
+                                  void *stream);
 
 /* Workspace bytes spec_accept_chunk needs for any chunk of a step with
  * total_q verify tokens (host function). */

@@ -430,7 +430,7 @@ __device__ inline bool wave_wait_all(const int32_t *arrive, int n, int need, int
   return false;
 }
 
-template <int D>
+template <int D, bool VT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void accept_compact_kernel(AcceptArgs a, CompactArgs c, int n_slices,
                                                              int groups, int n_total) {
   __shared__ int s_item, s_flag, s_nmove;
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void a
     }
     __syncthreads();
     if (s_nmove > 0)
-      compact_pairs<D>(c.k_cache, c.v_cache, c.layer_stride, c.num_layers, c.num_kv_heads,
+      compact_pairs<D, VT>(c.k_cache, c.v_cache, c.layer_stride, c.num_layers, c.num_kv_heads,
                        c.block_tables + (size_t)i * c.max_blocks, s_src, s_dst, s_nmove, g, groups);
   }
   // The last waiting item to finish zeroes what the call wrote.  Only the
@@ -626,10 +626,17 @@ void launch_accept_compact(const AcceptArgs &a, const CompactArgs &c, hipStream_
     if (groups < 1) groups = 1;
   }
   const int n_total = n_slices + a.batch + a.batch * groups;
-  if (c.head_dim == 128)
-    accept_compact_kernel<128><<<n_total, 256, 0, stream>>>(a, c, n_slices, groups, n_total);
-  else
-    accept_compact_kernel<64><<<n_total, 256, 0, stream>>>(a, c, n_slices, groups, n_total);
+  if (c.head_dim == 128) {
+    if (c.v_transposed)
+      accept_compact_kernel<128, true><<<n_total, 256, 0, stream>>>(a, c, n_slices, groups, n_total);
+    else
+      accept_compact_kernel<128, false><<<n_total, 256, 0, stream>>>(a, c, n_slices, groups, n_total);
+  } else {
+    if (c.v_transposed)
+      accept_compact_kernel<64, true><<<n_total, 256, 0, stream>>>(a, c, n_slices, groups, n_total);
+    else
+      accept_compact_kernel<64, false><<<n_total, 256, 0, stream>>>(a, c, n_slices, groups, n_total);
+  }
 }
 
 }  // namespace sv

@@ -256,7 +256,8 @@ int set_grid(sv::AttnArgs *a) {
 }
 
 int attn_data(const void *q, const void *k_cache, const void *v_cache, const int32_t *tree_parent,
-              void *out, int head_dim, int page_size, float softmax_scale, sv::AttnArgs *a) {
+              void *out, int head_dim, int page_size, float softmax_scale, bool v_transposed,
+              sv::AttnArgs *a) {
   if (!q || !k_cache || !v_cache || !out)
     return fail(SV_ERR_NULL, "spec_verify_attn: a required pointer is NULL");
   if (!(softmax_scale >= 0.0f && isfinite(softmax_scale)))
@@ -273,7 +274,48 @@ int attn_data(const void *q, const void *k_cache, const void *v_cache, const int
   a->out = static_cast<uint16_t *>(out);
   const float scale = softmax_scale == 0.0f ? 1.0f / sqrtf((float)head_dim) : softmax_scale;
   a->scale_log2 = scale * 1.4426950408889634f;
+  a->v_transposed = v_transposed;
   return ok();
+}
+
+int attn_run(const void *q, const void *k_cache, const void *v_cache, const int32_t *block_tables,
+             int max_blocks_per_seq, const int32_t *context_lens, const int32_t *cu_q,
+             const int32_t *tree_parent, void *out, int batch, int total_q, int num_q_heads,
+             int num_kv_heads, int head_dim, int page_size, int num_pages, float softmax_scale,
+             void *workspace, size_t workspace_bytes, void *stream, bool with_plan, bool v_transposed,
+             const char *what) {
+  sv::AttnArgs a;
+  bool empty;
+  int rc = attn_common(block_tables, max_blocks_per_seq, context_lens, cu_q, batch, total_q,
+                       num_q_heads, num_kv_heads, head_dim, page_size, num_pages, workspace,
+                       workspace_bytes, true, &a, &empty);
+  if (rc != SV_OK || empty) return rc;
+  rc = attn_data(q, k_cache, v_cache, tree_parent, out, head_dim, page_size, softmax_scale, v_transposed, &a);
+  if (rc != SV_OK) return rc;
+  if ((rc = set_grid(&a)) != SV_OK) return rc;
+  if (with_plan) sv::launch_verify_attn_plan(a, static_cast<hipStream_t>(stream));
+  sv::launch_verify_attn_run(a, head_dim, static_cast<hipStream_t>(stream));
+  return check_launch(what);
+}
+
+int attn_chunk_run(const void *q, const void *k_cache, const void *v_cache, const int32_t *block_tables,
+                   int max_blocks_per_seq, const int32_t *context_lens, const int32_t *cu_q, int total_q,
+                   const int32_t *chunk_begin, const int32_t *cu_chunk, int total_chunk,
+                   const int32_t *tree_parent, void *out, int batch, int num_q_heads, int num_kv_heads,
+                   int head_dim, int page_size, int num_pages, float softmax_scale, void *workspace,
+                   size_t workspace_bytes, void *stream, bool v_transposed, const char *what) {
+  sv::AttnArgs a;
+  bool empty;
+  int rc = attn_common(block_tables, max_blocks_per_seq, context_lens, cu_chunk, batch, total_chunk,
+                       num_q_heads, num_kv_heads, head_dim, page_size, num_pages, workspace,
+                       workspace_bytes, true, &a, &empty);
+  if (rc != SV_OK || empty) return rc;
+  if ((rc = attn_chunk(cu_q, total_q, chunk_begin, batch, &a)) != SV_OK) return rc;
+  rc = attn_data(q, k_cache, v_cache, tree_parent, out, head_dim, page_size, softmax_scale, v_transposed, &a);
+  if (rc != SV_OK) return rc;
+  if ((rc = set_grid(&a)) != SV_OK) return rc;
+  sv::launch_verify_attn_run(a, head_dim, static_cast<hipStream_t>(stream));
+  return check_launch(what);
 }
 
 }  // namespace
@@ -301,17 +343,21 @@ int spec_verify_attn_run(const void *q, const void *k_cache, const void *v_cache
                          int num_q_heads, int num_kv_heads, int head_dim, int page_size,
                          int num_pages, float softmax_scale, void *workspace,
                          size_t workspace_bytes, void *stream) {
-  sv::AttnArgs a;
-  bool empty;
-  int rc = attn_common(block_tables, max_blocks_per_seq, context_lens, cu_q, batch, total_q,
-                       num_q_heads, num_kv_heads, head_dim, page_size, num_pages, workspace,
-                       workspace_bytes, true, &a, &empty);
-  if (rc != SV_OK || empty) return rc;
-  rc = attn_data(q, k_cache, v_cache, tree_parent, out, head_dim, page_size, softmax_scale, &a);
-  if (rc != SV_OK) return rc;
-  if ((rc = set_grid(&a)) != SV_OK) return rc;
-  sv::launch_verify_attn_run(a, head_dim, static_cast<hipStream_t>(stream));
-  return check_launch("spec_verify_attn_run");
+  return attn_run(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, cu_q, tree_parent, out,
+                  batch, total_q, num_q_heads, num_kv_heads, head_dim, page_size, num_pages, softmax_scale,
+                  workspace, workspace_bytes, stream, false, false, "spec_verify_attn_run");
+}
+
+int spec_verify_attn_run_vt(const void *q, const void *k_cache, const void *v_cache,
+                            const int32_t *block_tables, int max_blocks_per_seq,
+                            const int32_t *context_lens, const int32_t *cu_q,
+                            const int32_t *tree_parent, void *out, int batch, int total_q,
+                            int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                            int num_pages, float softmax_scale, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  return attn_run(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, cu_q, tree_parent, out,
+                  batch, total_q, num_q_heads, num_kv_heads, head_dim, page_size, num_pages, softmax_scale,
+                  workspace, workspace_bytes, stream, false, true, "spec_verify_attn_run_vt");
 }
 
 int spec_verify_attn(const void *q, const void *k_cache, const void *v_cache,
@@ -320,18 +366,20 @@ int spec_verify_attn(const void *q, const void *k_cache, const void *v_cache,
                      void *out, int batch, int total_q, int num_q_heads, int num_kv_heads,
                      int head_dim, int page_size, int num_pages, float softmax_scale,
                      void *workspace, size_t workspace_bytes, void *stream) {
-  sv::AttnArgs a;
-  bool empty;
-  int rc = attn_common(block_tables, max_blocks_per_seq, context_lens, cu_q, batch, total_q,
-                       num_q_heads, num_kv_heads, head_dim, page_size, num_pages, workspace,
-                       workspace_bytes, true, &a, &empty);
-  if (rc != SV_OK || empty) return rc;
-  rc = attn_data(q, k_cache, v_cache, tree_parent, out, head_dim, page_size, softmax_scale, &a);
-  if (rc != SV_OK) return rc;
-  if ((rc = set_grid(&a)) != SV_OK) return rc;
-  sv::launch_verify_attn_plan(a, static_cast<hipStream_t>(stream));
-  sv::launch_verify_attn_run(a, head_dim, static_cast<hipStream_t>(stream));
-  return check_launch("spec_verify_attn");
+  return attn_run(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, cu_q, tree_parent, out,
+                  batch, total_q, num_q_heads, num_kv_heads, head_dim, page_size, num_pages, softmax_scale,
+                  workspace, workspace_bytes, stream, true, false, "spec_verify_attn");
+}
+
+int spec_verify_attn_vt(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *block_tables, int max_blocks_per_seq,
+                        const int32_t *context_lens, const int32_t *cu_q, const int32_t *tree_parent,
+                        void *out, int batch, int total_q, int num_q_heads, int num_kv_heads,
+                        int head_dim, int page_size, int num_pages, float softmax_scale,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  return attn_run(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, cu_q, tree_parent, out,
+                  batch, total_q, num_q_heads, num_kv_heads, head_dim, page_size, num_pages, softmax_scale,
+                  workspace, workspace_bytes, stream, true, true, "spec_verify_attn_vt");
 }
 
 int spec_verify_attn_chunk_plan(const int32_t *context_lens, const int32_t *cu_q, int total_q,
@@ -359,18 +407,24 @@ int spec_verify_attn_chunk_run(const void *q, const void *k_cache, const void *v
                                int num_kv_heads, int head_dim, int page_size, int num_pages,
                                float softmax_scale, void *workspace, size_t workspace_bytes,
                                void *stream) {
-  sv::AttnArgs a;
-  bool empty;
-  int rc = attn_common(block_tables, max_blocks_per_seq, context_lens, cu_chunk, batch, total_chunk,
-                       num_q_heads, num_kv_heads, head_dim, page_size, num_pages, workspace,
-                       workspace_bytes, true, &a, &empty);
-  if (rc != SV_OK || empty) return rc;
-  if ((rc = attn_chunk(cu_q, total_q, chunk_begin, batch, &a)) != SV_OK) return rc;
-  rc = attn_data(q, k_cache, v_cache, tree_parent, out, head_dim, page_size, softmax_scale, &a);
-  if (rc != SV_OK) return rc;
-  if ((rc = set_grid(&a)) != SV_OK) return rc;
-  sv::launch_verify_attn_run(a, head_dim, static_cast<hipStream_t>(stream));
-  return check_launch("spec_verify_attn_chunk_run");
+  return attn_chunk_run(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, cu_q, total_q,
+                        chunk_begin, cu_chunk, total_chunk, tree_parent, out, batch, num_q_heads, num_kv_heads,
+                        head_dim, page_size, num_pages, softmax_scale, workspace, workspace_bytes, stream, false,
+                        "spec_verify_attn_chunk_run");
+}
+
+int spec_verify_attn_chunk_run_vt(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *block_tables, int max_blocks_per_seq,
+                                  const int32_t *context_lens, const int32_t *cu_q, int total_q,
+                                  const int32_t *chunk_begin, const int32_t *cu_chunk, int total_chunk,
+                                  const int32_t *tree_parent, void *out, int batch, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int page_size, int num_pages,
+                                  float softmax_scale, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+  return attn_chunk_run(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, cu_q, total_q,
+                        chunk_begin, cu_chunk, total_chunk, tree_parent, out, batch, num_q_heads, num_kv_heads,
+                        head_dim, page_size, num_pages, softmax_scale, workspace, workspace_bytes, stream, true,
+                        "spec_verify_attn_chunk_run_vt");
 }
 
 int spec_hbm_read_probe(const void *k_cache, const void *v_cache, const int32_t *chunks, int64_t n_chunks,
@@ -508,19 +562,48 @@ int spec_accept_device_status(const void *workspace, uint32_t *flags, void *stre
   return read_status(workspace, 0, flags, stream);
 }
 
-int kv_compact(void *k_cache, void *v_cache, int64_t layer_stride_elems, int num_layers,
-               const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
-               const int32_t *cu_q, const int32_t *accepted_path, const int32_t *accept_len,
-               int32_t *new_context_lens, int batch, int total_q, int num_kv_heads, int head_dim,
-               int page_size, int num_pages, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int compact_call(void *k_cache, void *v_cache, int64_t layer_stride_elems, int num_layers,
+                 const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+                 const int32_t *cu_q, const int32_t *accepted_path, const int32_t *accept_len,
+                 int32_t *new_context_lens, int batch, int total_q, int num_kv_heads, int head_dim,
+                 int page_size, int num_pages, void *stream, bool v_transposed, const char *what) {
   sv::CompactArgs a;
   bool empty;
   int rc = compact_args(k_cache, v_cache, layer_stride_elems, num_layers, block_tables, max_blocks_per_seq,
                         context_lens, cu_q, accepted_path, accept_len, new_context_lens, batch, total_q,
                         num_kv_heads, head_dim, page_size, num_pages, &a, &empty);
   if (rc != SV_OK || empty) return rc;
+  a.v_transposed = v_transposed;
   sv::launch_kv_compact(a, static_cast<hipStream_t>(stream));
-  return check_launch("kv_compact");
+  return check_launch(what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_compact(void *k_cache, void *v_cache, int64_t layer_stride_elems, int num_layers,
+               const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+               const int32_t *cu_q, const int32_t *accepted_path, const int32_t *accept_len,
+               int32_t *new_context_lens, int batch, int total_q, int num_kv_heads, int head_dim,
+               int page_size, int num_pages, void *stream) {
+  return compact_call(k_cache, v_cache, layer_stride_elems, num_layers, block_tables, max_blocks_per_seq,
+                      context_lens, cu_q, accepted_path, accept_len, new_context_lens, batch, total_q,
+                      num_kv_heads, head_dim, page_size, num_pages, stream, false, "kv_compact");
+}
+
+int kv_compact_vt(void *k_cache, void *v_cache, int64_t layer_stride_elems, int num_layers,
+                  const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+                  const int32_t *cu_q, const int32_t *accepted_path, const int32_t *accept_len,
+                  int32_t *new_context_lens, int batch, int total_q, int num_kv_heads, int head_dim,
+                  int page_size, int num_pages, void *stream) {
+  return compact_call(k_cache, v_cache, layer_stride_elems, num_layers, block_tables, max_blocks_per_seq,
+                      context_lens, cu_q, accepted_path, accept_len, new_context_lens, batch, total_q,
+                      num_kv_heads, head_dim, page_size, num_pages, stream, true, "kv_compact_vt");
 }
 
 size_t spec_accept_stochastic_workspace_size(int batch, int total_q, int vocab) {
@@ -582,14 +665,17 @@ size_t spec_accept_compact_workspace_size(int batch, int total_q, int vocab) {
   return sv::fused_layout(batch, total_q, vocab).total;
 }
 
-int spec_accept_compact(const float *logits, int vocab, const int32_t *draft_tokens,
-                        const int32_t *cu_q, const int32_t *tree_parent, int batch, int total_q,
-                        int32_t *target_argmax, int32_t *accept_len, int32_t *accepted_path,
-                        int32_t *out_tokens, void *k_cache, void *v_cache,
-                        int64_t layer_stride_elems, int num_layers, const int32_t *block_tables,
-                        int max_blocks_per_seq, const int32_t *context_lens,
-                        int32_t *new_context_lens, int num_kv_heads, int head_dim, int page_size,
-                        int num_pages, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int accept_compact_call(const float *logits, int vocab, const int32_t *draft_tokens, const int32_t *cu_q,
+                        const int32_t *tree_parent, int batch, int total_q, int32_t *target_argmax,
+                        int32_t *accept_len, int32_t *accepted_path, int32_t *out_tokens, void *k_cache,
+                        void *v_cache, int64_t layer_stride_elems, int num_layers, const int32_t *block_tables,
+                        int max_blocks_per_seq, const int32_t *context_lens, int32_t *new_context_lens,
+                        int num_kv_heads, int head_dim, int page_size, int num_pages, void *workspace,
+                        size_t workspace_bytes, void *stream, bool v_transposed, const char *what) {
   sv::AcceptArgs a;
   sv::CompactArgs c;
   bool empty_a, empty_c;
@@ -604,8 +690,43 @@ int spec_accept_compact(const float *logits, int vocab, const int32_t *draft_tok
   if (overlaps(new_context_lens, bb, accept_len, bb) || overlaps(new_context_lens, bb, target_argmax, tb) ||
       overlaps(new_context_lens, bb, accepted_path, tb) || overlaps(new_context_lens, bb, out_tokens, tb))
     return fail(SV_ERR_ALIAS, "spec_accept_compact outputs overlap");
+  c.v_transposed = v_transposed;
   sv::launch_accept_compact(a, c, static_cast<hipStream_t>(stream));
-  return check_launch("spec_accept_compact");
+  return check_launch(what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_accept_compact(const float *logits, int vocab, const int32_t *draft_tokens,
+                        const int32_t *cu_q, const int32_t *tree_parent, int batch, int total_q,
+                        int32_t *target_argmax, int32_t *accept_len, int32_t *accepted_path,
+                        int32_t *out_tokens, void *k_cache, void *v_cache,
+                        int64_t layer_stride_elems, int num_layers, const int32_t *block_tables,
+                        int max_blocks_per_seq, const int32_t *context_lens,
+                        int32_t *new_context_lens, int num_kv_heads, int head_dim, int page_size,
+                        int num_pages, void *workspace, size_t workspace_bytes, void *stream) {
+  return accept_compact_call(logits, vocab, draft_tokens, cu_q, tree_parent, batch, total_q, target_argmax,
+                             accept_len, accepted_path, out_tokens, k_cache, v_cache, layer_stride_elems,
+                             num_layers, block_tables, max_blocks_per_seq, context_lens, new_context_lens,
+                             num_kv_heads, head_dim, page_size, num_pages, workspace, workspace_bytes, stream,
+                             false, "spec_accept_compact");
+}
+
+int spec_accept_compact_vt(const float *logits, int vocab, const int32_t *draft_tokens,
+                           const int32_t *cu_q, const int32_t *tree_parent, int batch, int total_q,
+                           int32_t *target_argmax, int32_t *accept_len, int32_t *accepted_path,
+                           int32_t *out_tokens, void *k_cache, void *v_cache,
+                           int64_t layer_stride_elems, int num_layers, const int32_t *block_tables,
+                           int max_blocks_per_seq, const int32_t *context_lens,
+                           int32_t *new_context_lens, int num_kv_heads, int head_dim, int page_size,
+                           int num_pages, void *workspace, size_t workspace_bytes, void *stream) {
+  return accept_compact_call(logits, vocab, draft_tokens, cu_q, tree_parent, batch, total_q, target_argmax,
+                             accept_len, accepted_path, out_tokens, k_cache, v_cache, layer_stride_elems,
+                             num_layers, block_tables, max_blocks_per_seq, context_lens, new_context_lens,
+                             num_kv_heads, head_dim, page_size, num_pages, workspace, workspace_bytes, stream,
+                             true, "spec_accept_compact_vt");
 }
 
 }  // extern "C"

@@ -44,19 +44,20 @@ __device__ inline int compact_moves(const int32_t *path, int n1, int qn, int L, 
 // memory) for (layer, head) pairs p = p0, p0 + pstep, ... < num_layers * Hkv:
 // every source is read into registers, all loads have returned in every
 // thread (barrier), and only then are destinations written.  A K slot is a
-// row of D contiguous values (16-byte chunks); a V page is stored transposed
-// ([D][16 tokens]), so a V slot is a column: D values 32 bytes apart, moved
+// row of D contiguous values (16-byte chunks).  A V slot is a row too when
+// V pages are token-major (VT false); when they are stored transposed
+// ([D][16 tokens], VT true) it is a column: D values 32 bytes apart, moved
 // one 2-byte element at a time.
-template <int D>
+template <int D, bool VT>
 __device__ inline void compact_pairs(uint16_t *k_cache, uint16_t *v_cache, int64_t layer_stride,
                                      int num_layers, int num_kv_heads, const int32_t *bt,
                                      const int *src, const int *dst, int nmove, int p0, int pstep) {
-  constexpr int CPR = D / 8;                                       // 16-byte chunks of a K row
-  constexpr int MAXK = ((kMaxTokens - 1) * CPR + 255) / 256;       // K chunks per thread
-  constexpr int MAXV = ((kMaxTokens - 1) * D + 255) / 256;         // V elements per thread
+  constexpr int CPR = D / 8;                                       // 16-byte chunks of a row
+  constexpr int MAXK = ((kMaxTokens - 1) * CPR + 255) / 256;       // row chunks per thread
+  constexpr int MAXV = VT ? ((kMaxTokens - 1) * D + 255) / 256 : 1;  // V column elements per thread
   const int tid = threadIdx.x;
   const size_t page_stride = (size_t)num_kv_heads * kPage * D;
-  const int kunits = nmove * CPR, vunits = nmove * D;
+  const int kunits = nmove * CPR, vunits = VT ? nmove * D : 0;
   const int pairs = num_layers * num_kv_heads;
   for (int p = p0; p < pairs; p += pstep) {
     const int layer = p / num_kv_heads;
@@ -65,7 +66,8 @@ __device__ inline void compact_pairs(uint16_t *k_cache, uint16_t *v_cache, int64
     uint16_t *vc = v_cache + (size_t)layer * layer_stride + (size_t)g * kPage * D;
     auto krow = [&](int slot) { return kc + (size_t)bt[slot / kPage] * page_stride + (size_t)(slot % kPage) * D; };
     auto vcol = [&](int slot) { return vc + (size_t)bt[slot / kPage] * page_stride + (slot % kPage); };
-    uint4 kb[MAXK];
+    auto vrow = [&](int slot) { return vc + (size_t)bt[slot / kPage] * page_stride + (size_t)(slot % kPage) * D; };
+    uint4 kb[MAXK], vr[VT ? 1 : MAXK];
     uint16_t vb[MAXV];
 #pragma unroll
     for (int u = 0; u < MAXK; ++u) {
@@ -73,6 +75,7 @@ __device__ inline void compact_pairs(uint16_t *k_cache, uint16_t *v_cache, int64
       if (idx < kunits) {
         const int mv = idx / CPR, ch = idx - mv * CPR;
         kb[u] = *reinterpret_cast<const uint4 *>(krow(src[mv]) + ch * 8);
+        if constexpr (!VT) vr[u] = *reinterpret_cast<const uint4 *>(vrow(src[mv]) + ch * 8);
       }
     }
 #pragma unroll
@@ -91,6 +94,7 @@ __device__ inline void compact_pairs(uint16_t *k_cache, uint16_t *v_cache, int64
       if (idx < kunits) {
         const int mv = idx / CPR, ch = idx - mv * CPR;
         *reinterpret_cast<uint4 *>(krow(dst[mv]) + ch * 8) = kb[u];
+        if constexpr (!VT) *reinterpret_cast<uint4 *>(vrow(dst[mv]) + ch * 8) = vr[u];
       }
     }
 #pragma unroll

@@ -20,7 +20,7 @@ namespace sv {
 
 namespace {
 
-template <int D>
+template <int D, bool VT>
 __global__ __launch_bounds__(256) void kv_compact_kernel(CompactArgs a) {
   __shared__ int s_dst[kMaxTokens];
   __shared__ int s_src[kMaxTokens];
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void kv_compact_kernel(CompactArgs a) {
   __syncthreads();
   const int nmove = s_nmove;
   if (nmove == 0) return;
-  compact_pairs<D>(a.k_cache, a.v_cache, a.layer_stride, a.num_layers, a.num_kv_heads, bt, s_src, s_dst,
+  compact_pairs<D, VT>(a.k_cache, a.v_cache, a.layer_stride, a.num_layers, a.num_kv_heads, bt, s_src, s_dst,
                    nmove, blockIdx.y, gridDim.y);
 }
 
@@ -58,10 +58,17 @@ void launch_kv_compact(const CompactArgs &a, hipStream_t stream) {
   if (gy > 65535) gy = 65535;
   if (gy < 1) gy = 1;
   dim3 grid(a.batch, gy);
-  if (a.head_dim == 128)
-    kv_compact_kernel<128><<<grid, 256, 0, stream>>>(a);
-  else
-    kv_compact_kernel<64><<<grid, 256, 0, stream>>>(a);
+  if (a.head_dim == 128) {
+    if (a.v_transposed)
+      kv_compact_kernel<128, true><<<grid, 256, 0, stream>>>(a);
+    else
+      kv_compact_kernel<128, false><<<grid, 256, 0, stream>>>(a);
+  } else {
+    if (a.v_transposed)
+      kv_compact_kernel<64, true><<<grid, 256, 0, stream>>>(a);
+    else
+      kv_compact_kernel<64, false><<<grid, 256, 0, stream>>>(a);
+  }
 }
 
 }  // namespace sv

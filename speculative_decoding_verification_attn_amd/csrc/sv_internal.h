@@ -106,6 +106,7 @@ struct AttnArgs {
   int total_full;    // entries of tree_parent (== total_q unless chunked)
   int grid;          // persistent attention workgroups launched (<= kMaxGrid)
   float scale_log2;  // softmax scale * log2(e)
+  bool v_transposed; // V pages [D][16 tokens] (else token-major [16 tokens][D], like K)
 };
 
 void launch_verify_attn_plan(const AttnArgs &a, hipStream_t stream);
@@ -263,6 +264,7 @@ struct CompactArgs {
   const int32_t *accept_len;
   int32_t *new_context_lens;
   int batch, total_q, num_kv_heads, head_dim, num_pages;
+  bool v_transposed;  // V pages [D][16 tokens] (else token-major, like K)
 };
 
 void launch_kv_compact(const CompactArgs &a, hipStream_t stream);

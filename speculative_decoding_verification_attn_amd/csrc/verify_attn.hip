@@ -28,6 +28,12 @@
 //                        softmax per query row, then merge through LDS;
 //   attn_merge_kernel    log-sum-exp merge of the partials of cut units.
 //
+// Two V page layouts: token-major ([16 tokens][D] per (page, head), like K)
+// and transposed ([D][16 tokens]); the kernel is instantiated for each.  The
+// formulation below is the transposed one; with token-major pages a lane
+// loads DPL contiguous d of 8 V rows and packs the V^T operand from them, and
+// K rows are loaded in plain lane order (see KVBlock and key_of_lane).
+//
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, A 32xK, B Kx32, C 32x32):
 //   S^T[key][row] = K[key][:] . Q^T[:][row]     A = K rows (one key per lane,
 //                                               8 contiguous d per lane),
@@ -233,20 +239,46 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a) {
 }
 
 // Registers of one 32-key block in flight: K rows as MFMA A operands (lane n
-// holds key key_of_lane(n)) and V^T operands: vt[m2][c] holds, for d-row
-// n + 32c of the block's page m2, the 8 consecutive keys 8hh .. 8hh+7.
+// holds key key_of_lane<VT>(n)) and the lane's V values.
+//   VT (V pages stored transposed, [D][16 tokens]): vt[m2][c] holds, for
+//     d-row n + 32c of the block's page m2, the 8 consecutive keys 8hh..8hh+7,
+//     which is the V^T operand as it stands;
+//   token-major V pages ([16 tokens][D]): v[m2][t][e] holds the lane's DPL
+//     contiguous d (DPL*n ..) of key 16*m2 + 8t + 4hh + e (a V row is read by
+//     32 lanes, DPL*2 bytes each), and the V^T operand of column c is packed
+//     from element c of the 8 keys.
+template <int D, bool VT>
+struct KVBlock;
 template <int D>
-struct KVBlock {
+struct KVBlock<D, true> {
   bf16x8 k[D / 16];
   bf16x8 vt[2][D / 32];
 };
+template <int D>
+struct KVBlock<D, false> {
+  bf16x8 k[D / 16];
+  uint32_t v[2][2][4][D / 64];
+};
 
 // Key (0..31 within a 32-key block) whose K row lane n of the S^T product
-// loads: n with bits 2 and 3 swapped.  The S^T accumulator then holds in
-// register r of lane half hh the score of key 16*(r/8) + 8*hh + r%8, so the
-// eight P values a lane packs for one P.V product are 8 consecutive keys:
-// the run a transposed V page row stores contiguously.
-__device__ inline int key_of_lane(int n) { return (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1); }
+// loads.  Transposed V: n with bits 2 and 3 swapped; the S^T accumulator then
+// holds in register r of lane half hh the score of key 16*(r/8) + 8*hh + r%8,
+// so the eight P values a lane packs for one P.V product are 8 consecutive
+// keys, the run a transposed V page row stores contiguously.  Token-major V:
+// lane n loads key n, and register r of lane half hh holds key
+// 8*(r/4) + 4*hh + r%4, the keys whose V rows the lane loaded.
+template <bool VT>
+__device__ inline int key_of_lane(int n) {
+  if constexpr (VT) return (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
+  else return n;
+}
+
+// key of S^T accumulator register r of lane half hh, relative to the block
+template <bool VT>
+__device__ inline int key_of_reg(int r, int hh) {
+  if constexpr (VT) return 16 * (r >> 3) + 8 * hh + (r & 7);
+  else return 8 * (r >> 2) + 4 * hh + (r & 3);
+}
 
 typedef const __attribute__((address_space(4))) int32_t *const_i32_ptr;
 
@@ -266,30 +298,48 @@ __device__ inline int2 block_pages(const_i32_ptr bt, int b, int npages, int num_
   return make_int2(p0, p1);
 }
 
-// K and V take different cache policies.  A V load instruction reads 16 B
-// of 32 consecutive d-rows of one transposed page, i.e. 1 KB contiguous,
-// so it is issued nontemporal: streamed through the caches without being
-// kept.  A K load instruction covers only 32 B of each of 32 rows (one key
-// per lane, as the MFMA A operand needs), and the rest of each line is read
-// by the next three instructions, so K uses ordinary loads that keep the
-// line for them.
-template <int D>
-__device__ inline void load_block(KVBlock<D> &buf, const uint16_t *kh, const uint16_t *vh,
+// K and V take different cache policies.  A V load instruction consumes
+// whole lines: 16 B of 32 consecutive d-rows of one transposed page (1 KB
+// contiguous), or two whole token-major V rows (DPL*2 B per lane), so it is
+// issued nontemporal: streamed through the caches without being kept.  A K
+// load instruction covers only 32 B of each of 32 rows (one key per lane, as
+// the MFMA A operand needs), and the rest of each line is read by the next
+// three instructions, so K uses ordinary loads that keep the line for them.
+template <int D, bool VT>
+__device__ inline void load_block(KVBlock<D, VT> &buf, const uint16_t *kh, const uint16_t *vh,
                                   int2 pg, int n, int hh, size_t page_stride) {
   constexpr int KK = D / 16, DPL = D / 32;
-  const int kn = key_of_lane(n);
+  const int kn = key_of_lane<VT>(n);
   const uint16_t *krow = kh + (size_t)(kn < 16 ? pg.x : pg.y) * page_stride + (size_t)(kn & 15) * D + 8 * hh;
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) buf.k[kk] = *reinterpret_cast<const bf16x8 *>(krow + 16 * kk);
+  typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+  typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
 #pragma unroll
   for (int m2 = 0; m2 < 2; ++m2) {
-    const uint16_t *vpage = vh + (size_t)(m2 ? pg.y : pg.x) * page_stride + 8 * hh;
+    if constexpr (VT) {
+      const uint16_t *vpage = vh + (size_t)(m2 ? pg.y : pg.x) * page_stride + 8 * hh;
 #pragma unroll
-    for (int c = 0; c < DPL; ++c) {
-      typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
-      const u32x4v x =
-          __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(vpage + (size_t)(n + 32 * c) * kPage));
-      buf.vt[m2][c] = __builtin_bit_cast(bf16x8, x);
+      for (int c = 0; c < DPL; ++c) {
+        const u32x4v x =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(vpage + (size_t)(n + 32 * c) * kPage));
+        buf.vt[m2][c] = __builtin_bit_cast(bf16x8, x);
+      }
+    } else {
+      const uint16_t *vpage = vh + (size_t)(m2 ? pg.y : pg.x) * page_stride + DPL * n;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint16_t *vrow = vpage + (size_t)(8 * t + 4 * hh + e) * D;
+          if constexpr (DPL == 4) {
+            const u32x2v x = __builtin_nontemporal_load(reinterpret_cast<const u32x2v *>(vrow));
+            buf.v[m2][t][e][0] = x.x;
+            buf.v[m2][t][e][1] = x.y;
+          } else {
+            buf.v[m2][t][e][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(vrow));
+          }
+        }
     }
   }
 }
@@ -299,32 +349,42 @@ __device__ inline void load_block(KVBlock<D> &buf, const uint16_t *kh, const uin
 // serve every tile, so K/V is read once per unit whatever its row count.
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
-template <int D>
-__device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 (&qop)[kUnitTiles][D / 16], int nt, int key0, int L,
-                                     int nk, const uint64_t (&anc)[kUnitTiles], int hh, float scale_log2,
+template <int D, bool VT>
+__device__ inline void compute_block(KVBlock<D, VT> &buf, const bf16x8 (&qop)[kUnitTiles][D / 16], int nt, int key0,
+                                     int L, int nk, const uint64_t (&anc)[kUnitTiles], int hh, float scale_log2,
                                      float (&m)[kUnitTiles], float (&l)[kUnitTiles],
                                      floatx16 (&acc)[kUnitTiles][D / 32]) {
   constexpr int KK = D / 16, DPL = D / 32;
   if (key0 + kBlockKeys > nk) {
-    // keys past the request: their V is stale memory (maybe non-finite);
-    // element j of vt[m2][c] is key key0 + 16*m2 + 8*hh + j
+    // keys past the request: their V is stale memory (maybe non-finite)
 #pragma unroll
     for (int m2 = 0; m2 < 2; ++m2) {
-      uint32_t keep[4];
+      if constexpr (VT) {
+        // element j of vt[m2][c] is key key0 + 16*m2 + 8*hh + j
+        uint32_t keep[4];
 #pragma unroll
-      for (int pr = 0; pr < 4; ++pr) {
-        const int k0 = key0 + 16 * m2 + 8 * hh + 2 * pr;
-        keep[pr] = (k0 < nk ? 0x0000FFFFu : 0u) | (k0 + 1 < nk ? 0xFFFF0000u : 0u);
-      }
+        for (int pr = 0; pr < 4; ++pr) {
+          const int k0 = key0 + 16 * m2 + 8 * hh + 2 * pr;
+          keep[pr] = (k0 < nk ? 0x0000FFFFu : 0u) | (k0 + 1 < nk ? 0xFFFF0000u : 0u);
+        }
 #pragma unroll
-      for (int c = 0; c < DPL; ++c) {
-        typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
-        u32x4v x = __builtin_bit_cast(u32x4v, buf.vt[m2][c]);
-        x.x &= keep[0];
-        x.y &= keep[1];
-        x.z &= keep[2];
-        x.w &= keep[3];
-        buf.vt[m2][c] = __builtin_bit_cast(bf16x8, x);
+        for (int c = 0; c < DPL; ++c) {
+          typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+          u32x4v x = __builtin_bit_cast(u32x4v, buf.vt[m2][c]);
+          x.x &= keep[0];
+          x.y &= keep[1];
+          x.z &= keep[2];
+          x.w &= keep[3];
+          buf.vt[m2][c] = __builtin_bit_cast(bf16x8, x);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int w = 0; w < D / 64; ++w)
+              buf.v[m2][t][e][w] = key0 + 16 * m2 + 8 * t + 4 * hh + e < nk ? buf.v[m2][t][e][w] : 0u;
       }
     }
   }
@@ -337,13 +397,13 @@ __device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 (&qop)[kUnitT
     for (int kk = 0; kk < KK; ++kk)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf.k[kk], qop[tt][kk], s, 0, 0, 0);
 
-    // keys of acc reg r: key0 + 16*(r/8) + 8*hh + r%8.  Scores stay unscaled
+    // keys of acc reg r: key0 + key_of_reg(r, hh).  Scores stay unscaled
     // here; the (positive) scale is folded into the exponent below, and the
     // running max m is kept in the scaled log2 domain.
     if (need_mask) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 16 * (r >> 3) + 8 * hh + (r & 7);
+        const int key = key0 + key_of_reg<VT>(r, hh);
         const bool vis = key < L || (key < nk && ((anc[tt] >> (unsigned)(key - L)) & 1ull));
         s[r] = vis ? s[r] : -INFINITY;
       }
@@ -379,10 +439,28 @@ __device__ inline void compute_block(KVBlock<D> &buf, const bf16x8 (&qop)[kUnitT
     for (int m2 = 0; m2 < 2; ++m2) {
       uint32_t w4p[4] = {pw[4 * m2], pw[4 * m2 + 1], pw[4 * m2 + 2], pw[4 * m2 + 3]};
       const bf16x8 pop = __builtin_bit_cast(bf16x8, w4p);
-      // k-slot 8hh + j <-> key 16*m2 + 8hh + j in both operands
+      if constexpr (VT) {
+        // k-slot 8hh + j <-> key 16*m2 + 8hh + j in both operands
 #pragma unroll
-      for (int c = 0; c < DPL; ++c)
-        acc[tt][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf.vt[m2][c], pop, acc[tt][c], 0, 0, 0);
+        for (int c = 0; c < DPL; ++c)
+          acc[tt][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf.vt[m2][c], pop, acc[tt][c], 0, 0, 0);
+      } else {
+        // k-slot 8hh + 4t + e <-> key 16*m2 + 8t + 4hh + e in both operands;
+        // the V^T operand of column c is element c of the lane's d-run
+#pragma unroll
+        for (int c = 0; c < DPL; ++c) {
+          uint32_t w4[4];
+#pragma unroll
+          for (int pr = 0; pr < 4; ++pr) {
+            const int s0 = 2 * pr, s1 = 2 * pr + 1;
+            const uint32_t x0 = buf.v[m2][s0 >> 2][s0 & 3][c >> 1];
+            const uint32_t x1 = buf.v[m2][s1 >> 2][s1 & 3][c >> 1];
+            w4[pr] = (c & 1) ? pack_hi16(x0, x1) : pack_lo16(x0, x1);
+          }
+          const bf16x8 vop = __builtin_bit_cast(bf16x8, w4);
+          acc[tt][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, acc[tt][c], 0, 0, 0);
+        }
+      }
     }
   }
 }
@@ -565,7 +643,7 @@ __device__ inline void load_q_chunks(const AttnArgs &a, const Walk &W, int tt, i
     qc[j] = row_ok ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * (wave * KQ + j)) : bf16x8{};
 }
 
-template <int D>
+template <int D, bool VT>
 __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void verify_attn_kernel(AttnArgs a) {
   constexpr int DPL = D / 32;  // contiguous d per lane of a V row; O^T tiles
   constexpr int KK = D / 16;   // k-steps of the S^T product (16 d each)
@@ -685,8 +763,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
     pg_next = block_pages(bt, min(lbk, lmax), npages, a.num_pages, safe, &bad_page);
     h_next = Wp.h;
   };
-  auto produce = [&](KVBlock<D> &buf) {
-    load_block<D>(buf, a.k_cache + (size_t)h_next * kPage * D, a.v_cache + (size_t)h_next * kPage * D,
+  auto produce = [&](KVBlock<D, VT> &buf) {
+    load_block<D, VT>(buf, a.k_cache + (size_t)h_next * kPage * D, a.v_cache + (size_t)h_next * kPage * D,
                   pg_next, n, hh, page_stride);
   };
 
@@ -722,8 +800,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
         f[ww] = fast_exp2(sm_m[ww][n] - Mref);
         Lsum += f[ww] * sm_l[ww][n];
       }
-      // this wave finalises registers r = 4*wave .. 4*wave+3 of every tile c:
-      // output d = 32*c + 8*wave + 4*hh + (0..3), four contiguous per c
+      // this wave finalises registers r = 4*wave .. 4*wave+3 of every tile c,
+      // O^T rows i = 8*wave + 4*hh + rr: with transposed V pages output
+      // d = 32*c + i (ov[4c + rr], four contiguous per c); with token-major
+      // pages d = DPL*i + c (ov[DPL*rr + c], 4*DPL contiguous)
       float ov[4 * DPL];
 #pragma unroll
       for (int i = 0; i < 4 * DPL; ++i) ov[i] = 0.f;
@@ -733,27 +813,42 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
         for (int ww = 0; ww < kAttnWaves; ++ww) {
           const float4v x = sm_o[ww][c][wave][lane];
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) ov[4 * c + rr] += f[ww] * x[rr];
+          for (int rr = 0; rr < 4; ++rr) ov[VT ? 4 * c + rr : DPL * rr + c] += f[ww] * x[rr];
         }
       const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
-      const int d0 = 8 * wave + 4 * hh;
+      const int d0 = VT ? 8 * wave + 4 * hh : DPL * (8 * wave + 4 * hh);
       const int R = (Wc.rg * kUnitTiles + tt) * kTileRows + n;
       if (R < G * Wc.qn) {
         const int tok = R / G, gq = R - tok * G;
         if (whole) {
           uint16_t *orow = a.out + ((size_t)(Wc.o + tok) * a.num_q_heads + (size_t)Wc.h * G + gq) * D + d0;
+          if constexpr (VT) {
 #pragma unroll
-          for (int c = 0; c < DPL; ++c)
-            *reinterpret_cast<uint2 *>(orow + 32 * c) =
-                make_uint2(pack_bf16x2(ov[4 * c] * inv, ov[4 * c + 1] * inv),
-                           pack_bf16x2(ov[4 * c + 2] * inv, ov[4 * c + 3] * inv));
+            for (int c = 0; c < DPL; ++c)
+              *reinterpret_cast<uint2 *>(orow + 32 * c) =
+                  make_uint2(pack_bf16x2(ov[4 * c] * inv, ov[4 * c + 1] * inv),
+                             pack_bf16x2(ov[4 * c + 2] * inv, ov[4 * c + 3] * inv));
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4 * DPL; j += 8)
+              *reinterpret_cast<uint4 *>(orow + j) =
+                  make_uint4(pack_bf16x2(ov[j] * inv, ov[j + 1] * inv), pack_bf16x2(ov[j + 2] * inv, ov[j + 3] * inv),
+                             pack_bf16x2(ov[j + 4] * inv, ov[j + 5] * inv), pack_bf16x2(ov[j + 6] * inv, ov[j + 7] * inv));
+          }
         } else {
           const size_t slot = (2 * (size_t)w + side) * kUnitTiles + tt;
           float *po = reinterpret_cast<float *>(a.ws + a.lay.part_o) + (slot * kTileRows + n) * D + d0;
+          if constexpr (VT) {
 #pragma unroll
-          for (int c = 0; c < DPL; ++c)
-            *reinterpret_cast<float4 *>(po + 32 * c) =
-                make_float4(ov[4 * c] * inv, ov[4 * c + 1] * inv, ov[4 * c + 2] * inv, ov[4 * c + 3] * inv);
+            for (int c = 0; c < DPL; ++c)
+              *reinterpret_cast<float4 *>(po + 32 * c) =
+                  make_float4(ov[4 * c] * inv, ov[4 * c + 1] * inv, ov[4 * c + 2] * inv, ov[4 * c + 3] * inv);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4 * DPL; j += 4)
+              *reinterpret_cast<float4 *>(po + j) =
+                  make_float4(ov[j] * inv, ov[j + 1] * inv, ov[j + 2] * inv, ov[j + 3] * inv);
+          }
           if (wave == 0 && hh == 0) {
             float *pl = reinterpret_cast<float *>(a.ws + a.lay.part_lse);
             pl[slot * kTileRows + n] = Lsum > 0.f ? Mref + fast_log2(Lsum) : -INFINITY;
@@ -765,7 +860,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
 
   // one round g: issue the loads of round g+1 into `into` (freed by round
   // g-1), compute round g from `cur`; true once the last unit is finished
-  auto round = [&](int g, KVBlock<D> &cur, KVBlock<D> &into) -> bool {
+  auto round = [&](int g, KVBlock<D, VT> &cur, KVBlock<D, VT> &into) -> bool {
     produce(into);
     fetch_pages(g + 2);
     // prefetch the next unit's first Q tile once this unit is under way
@@ -777,7 +872,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
     }
     const int gb = Wc.ps + kAttnWaves * (g - Wc.g0) + wave;  // this wave's global block
     if (gb < Wc.pe)
-      compute_block<D>(cur, qop, nt, (gb - Wc.ub) * kBlockKeys, Wc.L, nk, anc, hh,
+      compute_block<D, VT>(cur, qop, nt, (gb - Wc.ub) * kBlockKeys, Wc.L, nk, anc, hh,
                        a.scale_log2, m, l, acc);
     if (g + 1 == Wc.g0 + Wc.nr) {
       finish_unit();
@@ -792,7 +887,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
 
   // the first K/V loads go out before the Q operands are staged, so the
   // two memory round trips overlap
-  KVBlock<D> A, Bb;
+  KVBlock<D, VT> A, Bb;
   fetch_pages(0);
   produce(A);
   fetch_pages(1);
@@ -813,11 +908,18 @@ void launch_verify_attn_plan(const AttnArgs &a, hipStream_t stream) {
 }
 
 void launch_verify_attn_run(const AttnArgs &a, int head_dim, hipStream_t stream) {
+  const dim3 grid(a.grid), block(64 * kAttnWaves);
   if (head_dim == 128) {
-    verify_attn_kernel<128><<<a.grid, 64 * kAttnWaves, 0, stream>>>(a);
+    if (a.v_transposed)
+      verify_attn_kernel<128, true><<<grid, block, 0, stream>>>(a);
+    else
+      verify_attn_kernel<128, false><<<grid, block, 0, stream>>>(a);
     attn_merge_kernel<128><<<a.grid * (kTileRows / kMergeRows), 64 * kMergeRows, 0, stream>>>(a);
   } else {
-    verify_attn_kernel<64><<<a.grid, 64 * kAttnWaves, 0, stream>>>(a);
+    if (a.v_transposed)
+      verify_attn_kernel<64, true><<<grid, block, 0, stream>>>(a);
+    else
+      verify_attn_kernel<64, false><<<grid, block, 0, stream>>>(a);
     attn_merge_kernel<64><<<a.grid * (kTileRows / kMergeRows), 64 * kMergeRows, 0, stream>>>(a);
   }
 }

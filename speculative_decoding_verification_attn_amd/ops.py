@@ -42,13 +42,13 @@ DEV_TOO_MANY_PAGES = 0x20
 DEV_SYNC_TIMEOUT = 0x40
 DEV_BAD_TOKEN = 0x80
 
-EXPORTED = ["spec_verify_attn_workspace_size", "spec_verify_attn", "spec_verify_attn_plan",
-            "spec_verify_attn_run", "spec_verify_attn_device_status",
+EXPORTED = ["spec_verify_attn_workspace_size", "spec_verify_attn", "spec_verify_attn_vt", "spec_verify_attn_plan",
+            "spec_verify_attn_run", "spec_verify_attn_run_vt", "spec_verify_attn_device_status",
             "spec_accept_workspace_size", "spec_accept", "spec_accept_device_status",
-            "kv_compact", "sv_status_string", "sv_last_error",
-            "spec_verify_attn_chunk_plan", "spec_verify_attn_chunk_run", "spec_chunk_start",
-            "spec_accept_chunk_workspace_size", "spec_accept_chunk", "spec_verify_budget",
-            "spec_accept_compact_workspace_size", "spec_accept_compact",
+            "kv_compact", "kv_compact_vt", "sv_status_string", "sv_last_error",
+            "spec_verify_attn_chunk_plan", "spec_verify_attn_chunk_run", "spec_verify_attn_chunk_run_vt",
+            "spec_chunk_start", "spec_accept_chunk_workspace_size", "spec_accept_chunk", "spec_verify_budget",
+            "spec_accept_compact_workspace_size", "spec_accept_compact", "spec_accept_compact_vt",
             "spec_accept_stochastic_workspace_size", "spec_accept_stochastic",
             "spec_accept_stochastic_device_status", "spec_hbm_read_probe"]
 
@@ -73,10 +73,9 @@ def load_library():
     P, I, F, SZ, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_int64
     lib.spec_verify_attn_workspace_size.argtypes = [I, I, I, I, I]
     lib.spec_verify_attn_workspace_size.restype = SZ
-    lib.spec_verify_attn.argtypes = [P, P, P, P, I, P, P, P, P, I, I, I, I, I, I, I, F, P, SZ, P]
-    lib.spec_verify_attn.restype = I
-    lib.spec_verify_attn_run.argtypes = [P, P, P, P, I, P, P, P, P, I, I, I, I, I, I, I, F, P, SZ, P]
-    lib.spec_verify_attn_run.restype = I
+    for fn in ("spec_verify_attn", "spec_verify_attn_vt", "spec_verify_attn_run", "spec_verify_attn_run_vt"):
+        getattr(lib, fn).argtypes = [P, P, P, P, I, P, P, P, P, I, I, I, I, I, I, I, F, P, SZ, P]
+        getattr(lib, fn).restype = I
     lib.spec_verify_attn_plan.argtypes = [P, P, I, I, I, I, I, I, I, P, SZ, P]
     lib.spec_verify_attn_plan.restype = I
     lib.spec_verify_attn_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
@@ -87,13 +86,14 @@ def load_library():
     lib.spec_accept.restype = I
     lib.spec_accept_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
     lib.spec_accept_device_status.restype = I
-    lib.kv_compact.argtypes = [P, P, I64, I, P, I, P, P, P, P, P, I, I, I, I, I, I, P]
-    lib.kv_compact.restype = I
+    for fn in ("kv_compact", "kv_compact_vt"):
+        getattr(lib, fn).argtypes = [P, P, I64, I, P, I, P, P, P, P, P, I, I, I, I, I, I, P]
+        getattr(lib, fn).restype = I
     lib.spec_verify_attn_chunk_plan.argtypes = [P, P, I, P, P, I, I, I, I, I, I, I, P, SZ, P]
     lib.spec_verify_attn_chunk_plan.restype = I
-    lib.spec_verify_attn_chunk_run.argtypes = [P, P, P, P, I, P, P, I, P, P, I, P, P, I, I, I, I, I, I,
-                                               F, P, SZ, P]
-    lib.spec_verify_attn_chunk_run.restype = I
+    for fn in ("spec_verify_attn_chunk_run", "spec_verify_attn_chunk_run_vt"):
+        getattr(lib, fn).argtypes = [P, P, P, P, I, P, P, I, P, P, I, P, P, I, I, I, I, I, I, F, P, SZ, P]
+        getattr(lib, fn).restype = I
     lib.spec_chunk_start.argtypes = [P, I, I, I, P, P, P]
     lib.spec_chunk_start.restype = I
     lib.spec_accept_chunk_workspace_size.argtypes = [I, I, I]
@@ -104,9 +104,9 @@ def load_library():
     lib.spec_verify_budget.restype = I
     lib.spec_accept_compact_workspace_size.argtypes = [I, I, I]
     lib.spec_accept_compact_workspace_size.restype = SZ
-    lib.spec_accept_compact.argtypes = [P, I, P, P, P, I, I, P, P, P, P, P, P, I64, I, P, I, P, P, I, I, I, I,
-                                        P, SZ, P]
-    lib.spec_accept_compact.restype = I
+    for fn in ("spec_accept_compact", "spec_accept_compact_vt"):
+        getattr(lib, fn).argtypes = [P, I, P, P, P, I, I, P, P, P, P, P, P, I64, I, P, I, P, P, I, I, I, I, P, SZ, P]
+        getattr(lib, fn).restype = I
     lib.spec_accept_stochastic_workspace_size.argtypes = [I, I, I]
     lib.spec_accept_stochastic_workspace_size.restype = SZ
     lib.spec_accept_stochastic.argtypes = [P, P, I, F, P, P, P, P, I, I, P, P, P, P, SZ, P]
@@ -157,8 +157,17 @@ def spec_verify_attn_workspace_size(batch, total_q, num_q_heads, num_kv_heads, h
                                                               num_kv_heads, head_dim))
 
 
+def _v_shape(k_shape, vt):
+    """V cache shape matching a K cache shape [..., pages, Hkv, 16, D]: the same
+    (token-major pages), or each page's block transposed, [..., pages, Hkv, D, 16]
+    (the *_vt calls)."""
+    k_shape = tuple(k_shape)
+    return k_shape[:-2] + (k_shape[-1], k_shape[-2]) if vt else k_shape
+
+
 def _attn_call(fn, q, k_cache, v_cache, block_tables, context_lens, cu_q, tree_parent, out,
                softmax_scale, workspace, num_pages, stream):
+    vt = fn.endswith("_vt")
     lib = load_library()
     _dev(q, torch.bfloat16, "q")
     _dev(k_cache, torch.bfloat16, "k_cache")
@@ -169,8 +178,9 @@ def _attn_call(fn, q, k_cache, v_cache, block_tables, context_lens, cu_q, tree_p
     _dev(tree_parent, torch.int32, "tree_parent")
     T, Hq, D = q.shape
     pages, Hkv, P, D2 = k_cache.shape
-    if D2 != D or tuple(v_cache.shape) != (pages, Hkv, D, P):
-        raise ValueError("caches must be K [pages, Hkv, 16, D] and V [pages, Hkv, D, 16] matching q")
+    if D2 != D or tuple(v_cache.shape) != _v_shape(k_cache.shape, vt):
+        raise ValueError("caches must be K [pages, Hkv, 16, D] and V [pages, Hkv, %s] matching q"
+                         % ("D, 16" if vt else "16, D"))
     B = context_lens.shape[0]
     # sizes the library cannot see behind device pointers
     if cu_q.numel() != B + 1 or block_tables.dim() != 2 or block_tables.shape[0] != B:
@@ -198,9 +208,16 @@ def _attn_call(fn, q, k_cache, v_cache, block_tables, context_lens, cu_q, tree_p
 
 def spec_verify_attn(q, k_cache, v_cache, block_tables, context_lens, cu_q, tree_parent=None,
                      out=None, softmax_scale=0.0, workspace=None, num_pages=None, stream=None):
-    """q [T,Hq,D] bf16; k_cache [pages,Hkv,16,D], v_cache [pages,Hkv,D,16] (each page's V
-    transposed) bf16; returns out [T,Hq,D] bf16 (plan + run)."""
+    """q [T,Hq,D] bf16; k_cache and v_cache [pages,Hkv,16,D] bf16; returns out [T,Hq,D]
+    bf16 (plan + run)."""
     return _attn_call("spec_verify_attn", q, k_cache, v_cache, block_tables, context_lens, cu_q,
+                      tree_parent, out, softmax_scale, workspace, num_pages, stream)
+
+
+def spec_verify_attn_vt(q, k_cache, v_cache, block_tables, context_lens, cu_q, tree_parent=None,
+                        out=None, softmax_scale=0.0, workspace=None, num_pages=None, stream=None):
+    """spec_verify_attn with v_cache [pages,Hkv,D,16] (each page's V block transposed)."""
+    return _attn_call("spec_verify_attn_vt", q, k_cache, v_cache, block_tables, context_lens, cu_q,
                       tree_parent, out, softmax_scale, workspace, num_pages, stream)
 
 
@@ -210,6 +227,15 @@ def spec_verify_attn_run(q, k_cache, v_cache, block_tables, context_lens, cu_q, 
     if workspace is None:
         raise ValueError("spec_verify_attn_run needs the workspace holding the plan")
     return _attn_call("spec_verify_attn_run", q, k_cache, v_cache, block_tables, context_lens, cu_q,
+                      tree_parent, out, softmax_scale, workspace, num_pages, stream)
+
+
+def spec_verify_attn_run_vt(q, k_cache, v_cache, block_tables, context_lens, cu_q, tree_parent=None,
+                            out=None, softmax_scale=0.0, workspace=None, num_pages=None, stream=None):
+    """spec_verify_attn_run with v_cache [pages,Hkv,D,16] (each page's V block transposed)."""
+    if workspace is None:
+        raise ValueError("spec_verify_attn_run_vt needs the workspace holding the plan")
+    return _attn_call("spec_verify_attn_run_vt", q, k_cache, v_cache, block_tables, context_lens, cu_q,
                       tree_parent, out, softmax_scale, workspace, num_pages, stream)
 
 
@@ -278,22 +304,39 @@ def spec_accept_device_status(workspace, stream=None) -> int:
     return int(flags.value)
 
 
-def _check_cache_pair(k_cache, v_cache):
-    """K pages [..., pages, Hkv, 16, D] and V pages [..., pages, Hkv, D, 16]: a V
-    tensor in the K (token-major) layout has the same size and would be moved
-    with the wrong strides, so the shapes are compared, not only the sizes."""
+def _check_cache_pair(k_cache, v_cache, vt):
+    """K pages [..., pages, Hkv, 16, D] and V pages of the same shape, or (vt)
+    [..., pages, Hkv, D, 16]: a V tensor in the other layout has the same size
+    and would be moved with the wrong strides, so the shapes are compared, not
+    only the sizes."""
     ks = tuple(k_cache.shape)
-    if len(ks) < 4 or tuple(v_cache.shape) != ks[:-2] + (ks[-1], ks[-2]):
-        raise ValueError("caches must be K [..., pages, Hkv, 16, D] and V [..., pages, Hkv, D, 16]")
+    if len(ks) < 4 or tuple(v_cache.shape) != _v_shape(ks, vt):
+        raise ValueError("caches must be K [..., pages, Hkv, 16, D] and V [..., pages, Hkv, %s]"
+                         % ("D, 16" if vt else "16, D"))
 
 
 def kv_compact(k_cache, v_cache, block_tables, context_lens, cu_q, accepted_path, accept_len, *,
                num_layers=1, layer_stride_elems=None, num_kv_heads=None, head_dim=None,
                num_pages=None, new_context_lens=None, stream=None):
-    """In-place compaction of every layer.  With num_layers > 1, k_cache is
-    [layers, pages, Hkv, 16, D] and v_cache [layers, pages, Hkv, D, 16] (or flat pools
-    `layer_stride_elems` apart).
+    """In-place compaction of every layer.  With num_layers > 1, k_cache and v_cache are
+    [layers, pages, Hkv, 16, D] (or flat pools `layer_stride_elems` apart).
     Returns new_context_lens [B]."""
+    return _kv_compact_call("kv_compact", k_cache, v_cache, block_tables, context_lens, cu_q, accepted_path,
+                            accept_len, num_layers, layer_stride_elems, num_kv_heads, head_dim, num_pages,
+                            new_context_lens, stream)
+
+
+def kv_compact_vt(k_cache, v_cache, block_tables, context_lens, cu_q, accepted_path, accept_len, *,
+                  num_layers=1, layer_stride_elems=None, num_kv_heads=None, head_dim=None,
+                  num_pages=None, new_context_lens=None, stream=None):
+    """kv_compact with v_cache [(layers,) pages, Hkv, D, 16] (each page's V block transposed)."""
+    return _kv_compact_call("kv_compact_vt", k_cache, v_cache, block_tables, context_lens, cu_q, accepted_path,
+                            accept_len, num_layers, layer_stride_elems, num_kv_heads, head_dim, num_pages,
+                            new_context_lens, stream)
+
+
+def _kv_compact_call(fn, k_cache, v_cache, block_tables, context_lens, cu_q, accepted_path, accept_len,
+                     num_layers, layer_stride_elems, num_kv_heads, head_dim, num_pages, new_context_lens, stream):
     lib = load_library()
     _dev(k_cache, torch.bfloat16, "k_cache")
     _dev(v_cache, torch.bfloat16, "v_cache")
@@ -302,7 +345,7 @@ def kv_compact(k_cache, v_cache, block_tables, context_lens, cu_q, accepted_path
         _dev(t, torch.int32, nm)
     shp = k_cache.shape
     if num_kv_heads is None:
-        _check_cache_pair(k_cache, v_cache)
+        _check_cache_pair(k_cache, v_cache, fn.endswith("_vt"))
         num_kv_heads, head_dim = shp[-3], shp[-1]
         num_pages = shp[-4]
     elif head_dim is None or num_pages is None:
@@ -321,7 +364,7 @@ def kv_compact(k_cache, v_cache, block_tables, context_lens, cu_q, accepted_path
     if new_context_lens is None:
         new_context_lens = torch.empty(B, dtype=torch.int32, device=k_cache.device)
     _dev(new_context_lens, torch.int32, "new_context_lens")
-    _check(lib.kv_compact(_ptr(k_cache), _ptr(v_cache), int(layer_stride_elems), int(num_layers),
+    _check(getattr(lib, fn)(_ptr(k_cache), _ptr(v_cache), int(layer_stride_elems), int(num_layers),
                           _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), _ptr(cu_q),
                           _ptr(accepted_path), _ptr(accept_len), _ptr(new_context_lens), B, T,
                           num_kv_heads, head_dim, 16, num_pages, _stream(stream)))
@@ -369,8 +412,25 @@ def spec_verify_attn_chunk_run(q, k_cache, v_cache, block_tables, context_lens, 
                                cu_chunk, tree_parent=None, *, total_q, out=None, softmax_scale=0.0,
                                workspace, num_pages=None, stream=None):
     """q [Tc,Hq,D] bf16 (the chunk's rows, packed by cu_chunk) -> out [Tc,Hq,D]; the plan must be
-    in `workspace` (spec_verify_attn_chunk_plan)."""
+    in `workspace` (spec_verify_attn_chunk_plan).  k_cache and v_cache [pages,Hkv,16,D]."""
+    return _chunk_run_call("spec_verify_attn_chunk_run", q, k_cache, v_cache, block_tables, context_lens, cu_q,
+                           chunk_begin, cu_chunk, tree_parent, total_q, out, softmax_scale, workspace, num_pages,
+                           stream)
+
+
+def spec_verify_attn_chunk_run_vt(q, k_cache, v_cache, block_tables, context_lens, cu_q, chunk_begin,
+                                  cu_chunk, tree_parent=None, *, total_q, out=None, softmax_scale=0.0,
+                                  workspace, num_pages=None, stream=None):
+    """spec_verify_attn_chunk_run with v_cache [pages,Hkv,D,16] (each page's V block transposed)."""
+    return _chunk_run_call("spec_verify_attn_chunk_run_vt", q, k_cache, v_cache, block_tables, context_lens,
+                           cu_q, chunk_begin, cu_chunk, tree_parent, total_q, out, softmax_scale, workspace,
+                           num_pages, stream)
+
+
+def _chunk_run_call(fn, q, k_cache, v_cache, block_tables, context_lens, cu_q, chunk_begin, cu_chunk,
+                    tree_parent, total_q, out, softmax_scale, workspace, num_pages, stream):
     lib = load_library()
+    vt = fn.endswith("_vt")
     _dev(q, torch.bfloat16, "q")
     _dev(k_cache, torch.bfloat16, "k_cache")
     _dev(v_cache, torch.bfloat16, "v_cache")
@@ -379,8 +439,9 @@ def spec_verify_attn_chunk_run(q, k_cache, v_cache, block_tables, context_lens, 
         _dev(t, torch.int32, nm)
     Tc, Hq, D = q.shape
     pages, Hkv, P, D2 = k_cache.shape
-    if D2 != D or tuple(v_cache.shape) != (pages, Hkv, D, P):
-        raise ValueError("caches must be K [pages, Hkv, 16, D] and V [pages, Hkv, D, 16] matching q")
+    if D2 != D or tuple(v_cache.shape) != _v_shape(k_cache.shape, vt):
+        raise ValueError("caches must be K [pages, Hkv, 16, D] and V [pages, Hkv, %s] matching q"
+                         % ("D, 16" if vt else "16, D"))
     B = context_lens.shape[0]
     if cu_q.numel() != B + 1 or cu_chunk.numel() != B + 1 or chunk_begin.numel() < B \
             or block_tables.dim() != 2 or block_tables.shape[0] != B:
@@ -394,7 +455,7 @@ def spec_verify_attn_chunk_run(q, k_cache, v_cache, block_tables, context_lens, 
     _dev(out, torch.bfloat16, "out")
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must have the shape of q")
-    _check(lib.spec_verify_attn_chunk_run(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+    _check(getattr(lib, fn)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                           block_tables.shape[1], _ptr(context_lens), _ptr(cu_q), int(total_q),
                                           _ptr(chunk_begin), _ptr(cu_chunk), Tc, _ptr(tree_parent), _ptr(out),
                                           B, Hq, Hkv, D, P, pages if num_pages is None else num_pages,
@@ -469,6 +530,24 @@ def spec_accept_compact(logits, draft_tokens, cu_q, tree_parent, k_cache, v_cach
     """spec_accept + kv_compact in one launch.  `workspace` (uint8, at least
     spec_accept_compact_workspace_size bytes) must be zero-filled before its first use.
     Returns (target_argmax, accept_len, accepted_path, out_tokens, new_context_lens)."""
+    return _accept_compact_call("spec_accept_compact", logits, draft_tokens, cu_q, tree_parent, k_cache, v_cache,
+                                block_tables, context_lens, workspace, num_layers, layer_stride_elems,
+                                target_argmax, accept_len, accepted_path, out_tokens, new_context_lens, stream)
+
+
+def spec_accept_compact_vt(logits, draft_tokens, cu_q, tree_parent, k_cache, v_cache, block_tables,
+                           context_lens, *, workspace, num_layers=1, layer_stride_elems=None,
+                           target_argmax=None, accept_len=None, accepted_path=None, out_tokens=None,
+                           new_context_lens=None, stream=None):
+    """spec_accept_compact with v_cache [(layers,) pages, Hkv, D, 16] (each page's V block transposed)."""
+    return _accept_compact_call("spec_accept_compact_vt", logits, draft_tokens, cu_q, tree_parent, k_cache,
+                                v_cache, block_tables, context_lens, workspace, num_layers, layer_stride_elems,
+                                target_argmax, accept_len, accepted_path, out_tokens, new_context_lens, stream)
+
+
+def _accept_compact_call(fn, logits, draft_tokens, cu_q, tree_parent, k_cache, v_cache, block_tables,
+                         context_lens, workspace, num_layers, layer_stride_elems, target_argmax, accept_len,
+                         accepted_path, out_tokens, new_context_lens, stream):
     lib = load_library()
     _dev(logits, torch.float32, "logits")
     _dev(k_cache, torch.bfloat16, "k_cache")
@@ -487,7 +566,7 @@ def spec_accept_compact(logits, draft_tokens, cu_q, tree_parent, k_cache, v_cach
     accepted_path = mk(T) if accepted_path is None else accepted_path
     out_tokens = mk(T) if out_tokens is None else out_tokens
     new_context_lens = mk(B) if new_context_lens is None else new_context_lens
-    _check_cache_pair(k_cache, v_cache)
+    _check_cache_pair(k_cache, v_cache, fn.endswith("_vt"))
     shp = k_cache.shape
     num_kv_heads, head_dim, num_pages = shp[-3], shp[-1], shp[-4]
     if layer_stride_elems is None:
@@ -498,7 +577,7 @@ def spec_accept_compact(logits, draft_tokens, cu_q, tree_parent, k_cache, v_cach
         raise ValueError(f"{num_layers} layers {layer_stride_elems} elements apart do not fit the caches")
     if context_lens.numel() != B or block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("context_lens and block_tables must match the batch of cu_q")
-    _check(lib.spec_accept_compact(_ptr(logits), V, _ptr(draft_tokens), _ptr(cu_q), _ptr(tree_parent), B, T,
+    _check(getattr(lib, fn)(_ptr(logits), V, _ptr(draft_tokens), _ptr(cu_q), _ptr(tree_parent), B, T,
                                    _ptr(target_argmax), _ptr(accept_len), _ptr(accepted_path), _ptr(out_tokens),
                                    _ptr(k_cache), _ptr(v_cache), int(layer_stride_elems), int(num_layers),
                                    _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),

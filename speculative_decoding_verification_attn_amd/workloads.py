@@ -11,9 +11,9 @@ What is drawn, per case, in a fixed order so a seed fixes every byte:
 2. draft-tree shapes (parent arrays, root = -1, parent[j] < j, BFS order);
 3. the physical page permutation of the paged KV pool;
 4. queries Q (bf16 bit patterns, [T, Hq, D], packed padding-free by cu_q);
-5. the K/V pool (bf16 bit patterns, [num_pages, Hkv, page_size, D]; the
-   library keeps V pages transposed, [num_pages, Hkv, D, page_size], and the
-   device-side generator below returns them that way);
+5. the K/V pool (bf16 bit patterns, [num_pages, Hkv, page_size, D], the
+   same token-major layout for K and V, on the host or drawn on the device;
+   a caller of the library's *_vt calls transposes each V page block);
 6. target logits (fp32, [T, V]);
 7. the planted greedy target token of every logits row: a uniformly drawn id
    whose logit is raised strictly above the row's maximum, so the row's
@@ -87,8 +87,8 @@ class VerifyCase:
     qkv_scale: float = 1.0
     logit_sigma: float = 1.0
     kv_device: Optional[str] = None
-    k_cache_dev: object = None        # torch tensors when the pool is drawn on device: K as
-    v_cache_dev: object = None        # k_cache, V with every (page, head) block transposed [.., D, P]
+    k_cache_dev: object = None        # torch tensors when the pool is drawn on device,
+    v_cache_dev: object = None        # both in the layout of k_cache / v_cache
     logits_dev: object = None
     extra: dict = field(default_factory=dict)
 
@@ -378,10 +378,8 @@ def _draw_kv_on_device(rng, shape, scale, device, poison_page, block_tables, con
                 s0 = used - (n - 1) * page_size
                 t[pg, :, s0:, :] = POISON_MAGNITUDE
         out.append(t)
-    # the library's V layout: every (page, head) block transposed, [pages, Hkv, D, P]
-    v = out[1].transpose(-1, -2).contiguous()
-    del out[1]
-    return out[0], v
+    # both [pages, Hkv, P, D] (token-major pages, as the host-drawn pools)
+    return out[0], out[1]
 
 
 def make_case(name: str, seed: Optional[int] = None, *, unit_scale: bool = False,

@@ -37,16 +37,44 @@ def bf16_dev_to_u16(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def v_to_dev(v):
+# The two V page layouts of the library: token-major [..., page_size, D] (the
+# generator's and the oracle's layout, taken by the plain calls) and transposed
+# [..., D, page_size] (the *_vt calls).
+LAYOUTS = [False, True]
+LAYOUT_IDS = ["v_token_major", "v_transposed"]
+
+
+def v_to_dev(v, vt):
     """V pages in the generator's (and the oracle's) layout, uint16 [..., page_size, D],
-    to the device in the library's layout: every (page, head) block transposed,
-    [..., D, page_size]."""
-    return u16_to_bf16_dev(np.ascontiguousarray(np.swapaxes(v, -1, -2)))
+    to the device in the layout of the calls used: as they are, or (vt) with every
+    (page, head) block transposed, [..., D, page_size]."""
+    return u16_to_bf16_dev(np.ascontiguousarray(np.swapaxes(v, -1, -2)) if vt else v)
 
 
-def v_from_dev(vd):
-    """The inverse of v_to_dev: device V [..., D, page_size] as uint16 [..., page_size, D]."""
-    return np.ascontiguousarray(np.swapaxes(bf16_dev_to_u16(vd), -1, -2))
+def v_from_dev(vd, vt):
+    """The inverse of v_to_dev: device V as uint16 [..., page_size, D]."""
+    u = bf16_dev_to_u16(vd)
+    return np.ascontiguousarray(np.swapaxes(u, -1, -2)) if vt else u
+
+
+def attn_fn(vt):
+    return ops.spec_verify_attn_vt if vt else ops.spec_verify_attn
+
+
+def attn_run_fn(vt):
+    return ops.spec_verify_attn_run_vt if vt else ops.spec_verify_attn_run
+
+
+def compact_fn(vt):
+    return ops.kv_compact_vt if vt else ops.kv_compact
+
+
+def accept_compact_fn(vt):
+    return ops.spec_accept_compact_vt if vt else ops.spec_accept_compact
+
+
+def chunk_run_fn(vt):
+    return ops.spec_verify_attn_chunk_run_vt if vt else ops.spec_verify_attn_chunk_run
 
 
 def i32(a):
@@ -54,17 +82,19 @@ def i32(a):
 
 
 class DevCase:
-    """Device copies of a case's arrays."""
+    """Device copies of a case's arrays, V in the layout of the calls used (vt:
+    the *_vt calls, V page blocks transposed)."""
 
-    def __init__(self, case):
+    def __init__(self, case, vt=False):
         self.case = case
+        self.vt = vt
         self.q = u16_to_bf16_dev(case.q)
         if case.k_cache_dev is not None:
             self.k = case.k_cache_dev
-            self.v = case.v_cache_dev
+            self.v = case.v_cache_dev.transpose(-1, -2).contiguous() if vt else case.v_cache_dev
         else:
             self.k = u16_to_bf16_dev(case.k_cache)
-            self.v = v_to_dev(case.v_cache)
+            self.v = v_to_dev(case.v_cache, vt)
         self.bt = i32(case.block_tables)
         self.ctx = i32(case.context_lens)
         self.cu = i32(case.cu_q)
@@ -77,12 +107,12 @@ class DevCase:
 
 
 def gpu_attn(dc, **kw):
-    note(f"[gpu] spec_verify_attn {dc.case.name} B={dc.case.batch} T={dc.case.total_q}")
+    note(f"[gpu] spec_verify_attn{'_vt' if dc.vt else ''} {dc.case.name} B={dc.case.batch} T={dc.case.total_q}")
     ws = torch.empty(ops.spec_verify_attn_workspace_size(dc.case.batch, dc.case.total_q,
                                                          dc.case.num_q_heads, dc.case.num_kv_heads,
                                                          dc.case.head_dim),
                      dtype=torch.uint8, device=DEV)
-    out = ops.spec_verify_attn(dc.q, dc.k, dc.v, dc.bt, dc.ctx, dc.cu, dc.par, workspace=ws, **kw)
+    out = attn_fn(dc.vt)(dc.q, dc.k, dc.v, dc.bt, dc.ctx, dc.cu, dc.par, workspace=ws, **kw)
     torch.cuda.synchronize()
     return out, ws
 
@@ -115,45 +145,6 @@ def assert_attn_close(got, ref, tag=""):
     assert err.max() <= MAX_ABS, (tag, err.max())
     assert err.mean() <= MEAN_ABS, (tag, err.mean())
     assert rel <= REL_L2, (tag, rel)
-
-
-def subcase_from_device(dc, reqs):
-    """Host copy of a few requests of a case whose K/V live on the device: their
-    pages are copied back byte for byte and the block tables renumbered."""
-    case = dc.case
-    P = case.page_size
-    reqs = list(reqs)
-    pages = []
-    bt_rows = []
-    for i in reqs:
-        n = (int(case.context_lens[i]) + int(case.q_lens[i]) + P - 1) // P
-        row = list(range(len(pages), len(pages) + n))
-        pages.extend(int(p) for p in case.block_tables[i, :n])
-        bt_rows.append(row)
-    idx = torch.tensor(pages, dtype=torch.long, device=DEV)
-    k = bf16_dev_to_u16(dc.k.index_select(0, idx))
-    v = v_from_dev(dc.v.index_select(0, idx))
-    mb = max(len(r) for r in bt_rows)
-    bt = np.zeros((len(reqs), mb), np.int32)
-    for r, row in enumerate(bt_rows):
-        bt[r, :len(row)] = row
-    q_lens = case.q_lens[reqs]
-    cu = np.zeros(len(reqs) + 1, np.int32)
-    cu[1:] = np.cumsum(q_lens)
-    rows = np.concatenate([np.arange(case.cu_q[i], case.cu_q[i + 1]) for i in reqs])
-    sub = dict(q=case.q[rows], k_cache=k, v_cache=v, block_tables=bt,
-               context_lens=case.context_lens[reqs], cu_q=cu,
-               tree_parent=None if case.tree_parent is None else case.tree_parent[rows],
-               num_pages=len(pages), rows=rows)
-    return sub
-
-
-def oracle_attn_sub(case, sub):
-    return oracle.verify_attn(sub["q"], sub["k_cache"], sub["v_cache"], sub["block_tables"],
-                              sub["context_lens"], sub["cu_q"], sub["tree_parent"],
-                              num_q_heads=case.num_q_heads, num_kv_heads=case.num_kv_heads,
-                              head_dim=case.head_dim, page_size=case.page_size,
-                              num_pages=sub["num_pages"])
 
 
 def bf16_out_to_f64(out):

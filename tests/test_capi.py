@@ -2,6 +2,7 @@
 declares, and rejects bad arguments with the documented status codes before
 any HIP call (so these run without a GPU; no kernel is launched)."""
 import ctypes
+import functools
 import os
 import re
 
@@ -48,17 +49,20 @@ NULL = None
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation rejects the call first
 
 
-def attn(lib, **kw):
+def attn(lib, fn="spec_verify_attn", **kw):
     args = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, mb=4, ctx=FAKE, cu=FAKE, par=NULL, out=ctypes.c_void_p(0x90000000),
                 B=2, T=8, Hq=8, Hkv=2, D=64, P=16, pages=10, scale=0.0, ws=ctypes.c_void_p(0x20000000),
                 wsb=1 << 40, stream=NULL)
     args.update(kw)
-    return lib.spec_verify_attn(args["q"], args["k"], args["v"], args["bt"], args["mb"], args["ctx"], args["cu"],
+    return getattr(lib, fn)(args["q"], args["k"], args["v"], args["bt"], args["mb"], args["ctx"], args["cu"],
                                 args["par"], args["out"], args["B"], args["T"], args["Hq"], args["Hkv"], args["D"],
                                 args["P"], args["pages"], args["scale"], args["ws"], args["wsb"], args["stream"])
 
 
-def test_verify_attn_validation(lib):
+@pytest.mark.parametrize("fn", ["spec_verify_attn", "spec_verify_attn_vt", "spec_verify_attn_run",
+                                "spec_verify_attn_run_vt"])
+def test_verify_attn_validation(lib, fn):
+    attn = functools.partial(globals()["attn"], fn=fn)
     assert attn(lib, D=96) == ops.SV_ERR_UNSUPPORTED
     assert attn(lib, P=32) == ops.SV_ERR_UNSUPPORTED
     assert attn(lib, Hq=6, Hkv=4) == ops.SV_ERR_SHAPE
@@ -103,14 +107,15 @@ def test_accept_validation(lib):
     assert lib.spec_accept_workspace_size(4, 20, 128256) > 0
 
 
-def test_compact_validation(lib):
+@pytest.mark.parametrize("fn", ["kv_compact", "kv_compact_vt"])
+def test_compact_validation(lib, fn):
     def call(**kw):
         a = dict(k=FAKE, v=FAKE, stride=10 * 2 * 16 * 64, L=1, bt=FAKE, mb=4, ctx=ctypes.c_void_p(0x100000),
                  cu=FAKE, path=FAKE, acc=FAKE, new=ctypes.c_void_p(0x200000), B=2, T=8, Hkv=2, D=64, P=16,
                  pages=10, stream=NULL)
         a.update(kw)
-        return lib.kv_compact(a["k"], a["v"], a["stride"], a["L"], a["bt"], a["mb"], a["ctx"], a["cu"], a["path"],
-                              a["acc"], a["new"], a["B"], a["T"], a["Hkv"], a["D"], a["P"], a["pages"], a["stream"])
+        return getattr(lib, fn)(a["k"], a["v"], a["stride"], a["L"], a["bt"], a["mb"], a["ctx"], a["cu"], a["path"],
+                                a["acc"], a["new"], a["B"], a["T"], a["Hkv"], a["D"], a["P"], a["pages"], a["stream"])
     assert call(D=80) == ops.SV_ERR_UNSUPPORTED
     assert call(P=8) == ops.SV_ERR_UNSUPPORTED
     assert call(new=ctypes.c_void_p(0x100000)) == ops.SV_ERR_ALIAS
@@ -201,15 +206,23 @@ def test_read_probe_validation(lib):
 
 
 def test_cache_pair_layout_check():
-    """The binding tells K pages [.., pages, Hkv, 16, D] from V pages
-    [.., pages, Hkv, D, 16]; a token-major V (same size) is refused."""
+    """The binding tells the two V page layouts apart: the plain calls take V
+    pages like K, [.., pages, Hkv, 16, D]; the *_vt calls take every page
+    block transposed, [.., pages, Hkv, D, 16].  A V of the other layout (same
+    size) is refused."""
     import torch
     k = torch.empty((3, 5, 2, 16, 64), dtype=torch.bfloat16)
-    ops._check_cache_pair(k, torch.empty((3, 5, 2, 64, 16), dtype=torch.bfloat16))
-    ops._check_cache_pair(k[0], torch.empty((5, 2, 64, 16), dtype=torch.bfloat16))
+    vt = torch.empty((3, 5, 2, 64, 16), dtype=torch.bfloat16)
+    ops._check_cache_pair(k, vt, True)
+    ops._check_cache_pair(k, k.clone(), False)
+    ops._check_cache_pair(k[0], torch.empty((5, 2, 64, 16), dtype=torch.bfloat16), True)
+    ops._check_cache_pair(k[0], torch.empty((5, 2, 16, 64), dtype=torch.bfloat16), False)
     for bad in ((3, 5, 2, 16, 64), (5, 2, 64, 16), (3, 5, 2, 64, 8)):
         with pytest.raises(ValueError):
-            ops._check_cache_pair(k, torch.empty(bad, dtype=torch.bfloat16))
+            ops._check_cache_pair(k, torch.empty(bad, dtype=torch.bfloat16), True)
+    for bad in ((3, 5, 2, 64, 16), (5, 2, 16, 64), (3, 5, 2, 16, 32)):
+        with pytest.raises(ValueError):
+            ops._check_cache_pair(k, torch.empty(bad, dtype=torch.bfloat16), False)
     with pytest.raises(ValueError):
         ops._check_cache_pair(torch.empty((2, 16, 64), dtype=torch.bfloat16),
-                              torch.empty((2, 64, 16), dtype=torch.bfloat16))
+                              torch.empty((2, 64, 16), dtype=torch.bfloat16), True)

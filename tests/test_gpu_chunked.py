@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import DEV, DevCase, assert_attn_close, i32, note, oracle_attn
+from gpu_util import DEV, LAYOUT_IDS, LAYOUTS, DevCase, assert_attn_close, chunk_run_fn, i32, note, oracle_attn
 from speculative_decoding_verification_attn_amd import ops
 from speculative_decoding_verification_attn_amd import workloads as W
 
@@ -52,17 +52,18 @@ def _chunk_attn(dc, begin, length):
                                     max_blocks_per_seq=case.block_tables.shape[1],
                                     num_q_heads=case.num_q_heads, num_kv_heads=case.num_kv_heads,
                                     head_dim=case.head_dim, num_pages=case.num_pages, workspace=ws)
-    out = ops.spec_verify_attn_chunk_run(qc, dc.k, dc.v, dc.bt, dc.ctx, dc.cu, b_dev, cu_dev, dc.par,
-                                         total_q=case.total_q, workspace=ws)
+    out = chunk_run_fn(dc.vt)(qc, dc.k, dc.v, dc.bt, dc.ctx, dc.cu, b_dev, cu_dev, dc.par,
+                              total_q=case.total_q, workspace=ws)
     torch.cuda.synchronize()
     return rows, out, ws
 
 
+@pytest.mark.parametrize("vt", LAYOUTS, ids=LAYOUT_IDS)
 @pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("name", list(CASES))
-def test_chunk_attention_rows_equal_full_verification(name, seed):
+def test_chunk_attention_rows_equal_full_verification(name, seed, vt):
     case = W.make_custom(300 + list(CASES).index(name), **CASES[name])
-    dc = DevCase(case)
+    dc = DevCase(case, vt)
     ref = oracle_attn(case)
     rng = np.random.default_rng(seed)
     q = np.diff(case.cu_q)

@@ -9,7 +9,8 @@ import torch
 
 import oracle
 import pins
-from gpu_util import DEV, DevCase, bf16_dev_to_u16, i32, note, u16_to_bf16_dev, v_from_dev, v_to_dev
+from gpu_util import (DEV, LAYOUT_IDS, LAYOUTS, DevCase, accept_compact_fn, bf16_dev_to_u16, i32, note,
+                      u16_to_bf16_dev, v_from_dev, v_to_dev)
 from speculative_decoding_verification_attn_amd import ops
 from speculative_decoding_verification_attn_amd import workloads as W
 
@@ -52,7 +53,7 @@ def _oracle(case, k_all, v_all):
     return dict(t=t_ref, acc=acc, path=path, toks=toks, new=new, k=k_ref, v=v_ref)
 
 
-def _check(ref, outs, kd, vd, tag):
+def _check(ref, outs, kd, vd, tag, vt):
     t, acc, path, toks, new = [x.cpu().numpy() for x in outs]
     assert np.array_equal(t, ref["t"]), tag
     assert np.array_equal(acc, ref["acc"]), tag
@@ -60,11 +61,12 @@ def _check(ref, outs, kd, vd, tag):
     assert np.array_equal(toks, ref["toks"]), tag
     assert np.array_equal(new, ref["new"]), tag
     assert np.array_equal(bf16_dev_to_u16(kd), ref["k"]), tag
-    assert np.array_equal(v_from_dev(vd), ref["v"]), tag
+    assert np.array_equal(v_from_dev(vd, vt), ref["v"]), tag
 
 
+@pytest.mark.parametrize("vt", LAYOUTS, ids=LAYOUT_IDS)
 @pytest.mark.parametrize("name", list(CASES))
-def test_fused_equals_oracle_on_repeated_calls(name):
+def test_fused_equals_oracle_on_repeated_calls(name, vt):
     case = W.make_custom(400 + list(CASES).index(name), **CASES[name])
     dc = DevCase(case)
     k_all, v_all = _caches(case)
@@ -74,23 +76,24 @@ def test_fused_equals_oracle_on_repeated_calls(name):
     ws = torch.zeros(ops.spec_accept_compact_workspace_size(case.batch, case.total_q, case.vocab),
                      dtype=torch.uint8, device=DEV)
     for rep in range(3):
-        note(f"[gpu] spec_accept_compact {name} call {rep}")
-        kd, vd = u16_to_bf16_dev(k_all), v_to_dev(v_all)
-        outs = ops.spec_accept_compact(dc.logits, dc.draft, dc.cu, dc.par, kd, vd, dc.bt, dc.ctx,
-                                       workspace=ws, num_layers=LAYERS)
+        note(f"[gpu] spec_accept_compact {name} vt={vt} call {rep}")
+        kd, vd = u16_to_bf16_dev(k_all), v_to_dev(v_all, vt)
+        outs = accept_compact_fn(vt)(dc.logits, dc.draft, dc.cu, dc.par, kd, vd, dc.bt, dc.ctx,
+                                     workspace=ws, num_layers=LAYERS)
         torch.cuda.synchronize()
         assert ops.spec_accept_device_status(ws) == 0
-        _check(ref, outs, kd, vd, f"{name} call {rep}")
+        _check(ref, outs, kd, vd, f"{name} call {rep}", vt)
 
 
-def test_fused_graph_replays():
+@pytest.mark.parametrize("vt", LAYOUTS, ids=LAYOUT_IDS)
+def test_fused_graph_replays(vt):
     """The fused call captured in a HIP graph, replayed with eager cache restores between."""
     name = "trees_d128"
     case = W.make_custom(400, **CASES[name])
     dc = DevCase(case)
     k_all, v_all = _caches(case)
     ref = _oracle(case, k_all, v_all)
-    k0, v0 = u16_to_bf16_dev(k_all), v_to_dev(v_all)
+    k0, v0 = u16_to_bf16_dev(k_all), v_to_dev(v_all, vt)
     kd, vd = k0.clone(), v0.clone()
     ws = torch.zeros(ops.spec_accept_compact_workspace_size(case.batch, case.total_q, case.vocab),
                      dtype=torch.uint8, device=DEV)
@@ -98,9 +101,9 @@ def test_fused_graph_replays():
     outs = [torch.empty(n, dtype=torch.int32, device=DEV) for n in (T, B, T, T, B)]
 
     def call():
-        ops.spec_accept_compact(dc.logits, dc.draft, dc.cu, dc.par, kd, vd, dc.bt, dc.ctx, workspace=ws,
-                                num_layers=LAYERS, target_argmax=outs[0], accept_len=outs[1],
-                                accepted_path=outs[2], out_tokens=outs[3], new_context_lens=outs[4])
+        accept_compact_fn(vt)(dc.logits, dc.draft, dc.cu, dc.par, kd, vd, dc.bt, dc.ctx, workspace=ws,
+                              num_layers=LAYERS, target_argmax=outs[0], accept_len=outs[1],
+                              accepted_path=outs[2], out_tokens=outs[3], new_context_lens=outs[4])
 
     g = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
@@ -116,7 +119,7 @@ def test_fused_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         assert ops.spec_accept_device_status(ws) == 0
-        _check(ref, outs, kd, vd, f"replay {rep}")
+        _check(ref, outs, kd, vd, f"replay {rep}", vt)
         note(f"[gpu] fused replay {rep} ok")
 
 
@@ -132,7 +135,7 @@ def _ragged_trees(seed, batch, total):
             sizes[b] += 1
     trees = []
     for k, n in enumerate(sizes):
-        depth = int(min(n - 1, rng.integers(1, 5)))
+        depth = int(min(n - 1, rng.integers(3, 6)))  # depth >= 3 holds 9 nodes whatever the root fan-out
         trees.append(np.array([-1], np.int32) if n == 1 else _tree(seed * 1000 + k, int(n), depth))
     ctx = rng.integers(0, 90, batch).tolist()
     return dict(context_lens=ctx, tree_parents=trees, hq=8, hkv=2, d=64, vocab=151936, tree_match=(0.8, 0.5))
@@ -154,12 +157,12 @@ def test_fused_workspace_shared_across_shapes():
         dc = DevCase(case)
         k_all, v_all = _caches(case)
         ref = _oracle(case, k_all, v_all)
-        kd, vd = u16_to_bf16_dev(k_all), v_to_dev(v_all)
+        kd, vd = u16_to_bf16_dev(k_all), v_to_dev(v_all, False)
         outs = ops.spec_accept_compact(dc.logits, dc.draft, dc.cu, dc.par, kd, vd, dc.bt, dc.ctx,
                                        workspace=ws, num_layers=LAYERS)
         torch.cuda.synchronize()
         assert ops.spec_accept_device_status(ws) == 0, k
-        _check(ref, outs, kd, vd, f"shared workspace call {k}")
+        _check(ref, outs, kd, vd, f"shared workspace call {k}", False)
         # everything the call wrote is zero again, apart from the status word
         rest = ws[4:].cpu().numpy()
         assert not rest.any(), (k, np.flatnonzero(rest)[:8])
@@ -181,7 +184,7 @@ def test_fused_waits_give_up_and_workspace_recovers():
     ws[8:12].view(torch.int32).fill_(1 << 30)  # header word 2: the ticket counter
     torch.cuda.synchronize()
     note("[gpu] spec_accept_compact with a preset ticket counter (bounded waits give up)")
-    kd, vd = u16_to_bf16_dev(k_all), v_to_dev(v_all)
+    kd, vd = u16_to_bf16_dev(k_all), v_to_dev(v_all, False)
     ops.spec_accept_compact(dc.logits, dc.draft, dc.cu, dc.par, kd, vd, dc.bt, dc.ctx, workspace=ws,
                             num_layers=LAYERS)
     torch.cuda.synchronize()
@@ -189,9 +192,9 @@ def test_fused_waits_give_up_and_workspace_recovers():
     assert st & ops.SV_DEV_SYNC_TIMEOUT, st
     assert not ws[4:].cpu().numpy().any()
     note("[gpu] next call on the same workspace")
-    kd, vd = u16_to_bf16_dev(k_all), v_to_dev(v_all)
+    kd, vd = u16_to_bf16_dev(k_all), v_to_dev(v_all, False)
     outs = ops.spec_accept_compact(dc.logits, dc.draft, dc.cu, dc.par, kd, vd, dc.bt, dc.ctx, workspace=ws,
                                    num_layers=LAYERS)
     torch.cuda.synchronize()
     assert ops.spec_accept_device_status(ws) == 0
-    _check(ref, outs, kd, vd, "after give-up")
+    _check(ref, outs, kd, vd, "after give-up", False)

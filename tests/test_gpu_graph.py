@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import DEV, DevCase, note, u16_to_bf16_dev, v_to_dev
+from gpu_util import (DEV, LAYOUT_IDS, LAYOUTS, DevCase, attn_run_fn, compact_fn, note, u16_to_bf16_dev,
+                      v_to_dev)
 from speculative_decoding_verification_attn_amd import ops
 from speculative_decoding_verification_attn_amd import workloads as W
 
@@ -20,22 +21,23 @@ def _tree(seed, nodes=64, depth=6):
     return W.draw_tree(np.random.Generator(np.random.PCG64(seed)), nodes, depth, 4, 4)
 
 
+@pytest.mark.parametrize("vt", LAYOUTS, ids=LAYOUT_IDS)
 @pytest.mark.parametrize("kind", ["chains", "trees"])
-def test_graph_replay_equals_eager(kind):
+def test_graph_replay_equals_eager(kind, vt):
     if kind == "chains":
         case = W.make_custom(21, context_lens=[300, 5, 1200, 64, 0], q_lens=[4, 9, 2, 6, 1], hq=32, hkv=8, d=128)
     else:
         case = W.make_custom(22, context_lens=[300, 0, 77], tree_parents=[_tree(1), _tree(2, 40, 9), _tree(3, 7, 3)],
                              hq=32, hkv=8, d=128, vocab=512)
     note(f"[gpu] graph replay {kind}: B={case.batch} T={case.total_q}")
-    dc = DevCase(case)
+    dc = DevCase(case, vt)
     B, T, layers = case.batch, case.total_q, 3
     rng = np.random.default_rng(7)
     # three layers: distinct K/V pools stacked so one compaction call covers them
     K = torch.stack([dc.k] + [u16_to_bf16_dev(W.f32_to_bf16_bits(
         rng.standard_normal(case.k_cache.shape).astype(np.float32))) for _ in range(layers - 1)])
     V = torch.stack([dc.v] + [v_to_dev(W.f32_to_bf16_bits(
-        rng.standard_normal(case.v_cache.shape).astype(np.float32))) for _ in range(layers - 1)])
+        rng.standard_normal(case.v_cache.shape).astype(np.float32)), vt) for _ in range(layers - 1)])
     K0, V0 = K.clone(), V.clone()
     ws = torch.empty(ops.spec_verify_attn_workspace_size(B, T, 32, 8, 128), dtype=torch.uint8, device=DEV)
     wsa = torch.empty(ops.spec_accept_workspace_size(B, T, case.vocab), dtype=torch.uint8, device=DEV)
@@ -50,11 +52,11 @@ def test_graph_replay_equals_eager(kind):
         ops.spec_verify_attn_plan(dc.ctx, dc.cu, max_blocks_per_seq=case.max_blocks, num_q_heads=32,
                                   num_kv_heads=8, head_dim=128, num_pages=case.num_pages, total_q=T, workspace=ws)
         for layer in range(layers):
-            ops.spec_verify_attn_run(dc.q, K[layer], V[layer], dc.bt, dc.ctx, dc.cu, dc.par, out=outs[layer],
-                                     workspace=ws)
+            attn_run_fn(vt)(dc.q, K[layer], V[layer], dc.bt, dc.ctx, dc.cu, dc.par, out=outs[layer],
+                            workspace=ws)
         ops.spec_accept(dc.logits, dc.draft, dc.cu, dc.par, target_argmax=t_arg, accept_len=acc,
                         accepted_path=path, out_tokens=toks, workspace=wsa)
-        ops.kv_compact(K, V, dc.bt, dc.ctx, dc.cu, path, acc, num_layers=layers, new_context_lens=new_len)
+        compact_fn(vt)(K, V, dc.bt, dc.ctx, dc.cu, path, acc, num_layers=layers, new_context_lens=new_len)
 
     def results():
         return [x.clone() for x in (outs, t_arg, acc, path, toks, new_len, K, V)]

@@ -6,8 +6,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (DEV, DevCase, assert_attn_close, bf16_out_to_f64, gpu_accept, gpu_attn, i32,
-                      note, oracle_attn)
+from gpu_util import (DEV, LAYOUT_IDS, LAYOUTS, DevCase, assert_attn_close, bf16_out_to_f64, gpu_accept,
+                      gpu_attn, i32, note, oracle_attn)
 from speculative_decoding_verification_attn_amd import ops
 from speculative_decoding_verification_attn_amd import workloads as W
 
@@ -48,18 +48,20 @@ def test_batch_beyond_plan_lds():
     note(f"  B={B}: mean accept_len {acc_ref.mean():.3f}")
 
 
-def test_long_context():
+@pytest.mark.parametrize("vt", LAYOUTS, ids=LAYOUT_IDS)
+def test_long_context(vt):
     """One request with a 131,072-token context beside a 40,001-token one
     (8,193 + 2,501 pages, permuted): every row against the oracle."""
     case = W.make_custom(42, context_lens=[131072, 40001], q_lens=[4, 2], hq=32, hkv=8, d=128,
                          vocab=256)
-    dc = DevCase(case)
+    dc = DevCase(case, vt)
     out, ws = gpu_attn(dc)
     assert ops.spec_verify_attn_device_status(ws) == 0
     assert_attn_close(bf16_out_to_f64(out), oracle_attn(case), "L=131072")
 
 
-def test_chain_of_64_tokens():
+@pytest.mark.parametrize("vt", LAYOUTS, ids=LAYOUT_IDS)
+def test_chain_of_64_tokens(vt):
     """Chains of 64 and 33 verify tokens with G = 8 (512 and 264 rows: 16 and 9
     row tiles of one KV head): attention and acceptance, including an
     all-correct 64-token draft that accepts 64."""
@@ -69,7 +71,7 @@ def test_chain_of_64_tokens():
     t_ref = oracle.argmax(case.logits)
     o = int(case.cu_q[0])
     case.draft_tokens[o + 1:o + 64] = t_ref[o:o + 63]
-    dc = DevCase(case)
+    dc = DevCase(case, vt)
     out, ws = gpu_attn(dc)
     assert ops.spec_verify_attn_device_status(ws) == 0
     assert_attn_close(bf16_out_to_f64(out), oracle_attn(case), "q=64")

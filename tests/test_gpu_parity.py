@@ -2,7 +2,9 @@
 
 Acceptance lengths, accepted paths, emitted tokens, argmaxes and the whole
 compacted KV pool must be bit-exact; attention must be within max-abs 2e-2,
-mean-abs 2e-3 (and relative L2 1e-2) of the fp64 oracle on unit-scale data."""
+mean-abs 2e-3 (and relative L2 1e-2) of the fp64 oracle on unit-scale data.
+Attention and compaction run with both V page layouts (token-major, and
+transposed through the *_vt calls)."""
 import itertools
 
 import numpy as np
@@ -11,13 +13,14 @@ import torch
 
 import oracle
 import pins
-from gpu_util import (DEV, DevCase, assert_attn_close, bf16_dev_to_u16, bf16_out_to_f64,
-                      gpu_accept, gpu_attn, i32, note, oracle_attn, oracle_attn_sub,
-                      subcase_from_device, u16_to_bf16_dev, v_from_dev, v_to_dev)
+from gpu_util import (DEV, LAYOUT_IDS, LAYOUTS, DevCase, assert_attn_close, attn_fn, attn_run_fn,
+                      bf16_dev_to_u16, bf16_out_to_f64, compact_fn, gpu_accept, gpu_attn, i32, note,
+                      oracle_attn, u16_to_bf16_dev, v_from_dev, v_to_dev)
 from speculative_decoding_verification_attn_amd import ops
 from speculative_decoding_verification_attn_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
+layouts = pytest.mark.parametrize("vt", LAYOUTS, ids=LAYOUT_IDS)
 
 
 def _tree(seed, nodes=64, depth=6):
@@ -47,20 +50,22 @@ SMALL = {
 }
 
 
+@layouts
 @pytest.mark.parametrize("name", list(SMALL))
-def test_attn_small_cases(name):
+def test_attn_small_cases(name, vt):
     case = W.make_custom(100 + list(SMALL).index(name), **SMALL[name])
-    dc = DevCase(case)
+    dc = DevCase(case, vt)
     out, ws = gpu_attn(dc)
     assert ops.spec_verify_attn_device_status(ws) == 0
     assert_attn_close(bf16_out_to_f64(out), oracle_attn(case), name)
 
 
+@layouts
 @pytest.mark.parametrize("name", ["tiny_chain", "llama31_8b_chain", "llama3_70b_tree"])
 @pytest.mark.parametrize("unit", [True, False], ids=["unit_scale", "config_scale"])
-def test_attn_config_full(name, unit):
+def test_attn_config_full(name, unit, vt):
     case = W.make_case(name, unit_scale=unit)
-    dc = DevCase(case)
+    dc = DevCase(case, vt)
     out, ws = gpu_attn(dc)
     assert ops.spec_verify_attn_device_status(ws) == 0
     got = bf16_out_to_f64(out)
@@ -73,18 +78,22 @@ def test_attn_config_full(name, unit):
         assert_attn_close(got / scale, ref / scale, name + " (normalised)")
 
 
+@layouts
 @pytest.mark.parametrize("name", ["qwen3_8b_ragged", "llama3_70b_b256"])
-def test_attn_config_full_size_all_requests(name):
+def test_attn_config_full_size_all_requests(name, vt):
     """Full-size batch in the launch configuration the benchmark times, every
     request against the oracle (which runs on all host cores).  The device-drawn
     K/V pool is copied back byte for byte."""
     case = W.make_case(name, unit_scale=True, kv_device=DEV)
-    dc = DevCase(case)
+    dc = DevCase(case, vt)
     out, ws = gpu_attn(dc)
     assert ops.spec_verify_attn_device_status(ws) == 0
     got = bf16_out_to_f64(out)
+    del out
     case.k_cache = bf16_dev_to_u16(dc.k)
-    case.v_cache = v_from_dev(dc.v)
+    case.v_cache = v_from_dev(dc.v, vt)
+    dc.k = dc.v = case.k_cache_dev = case.v_cache_dev = None
+    torch.cuda.empty_cache()
     note(f"  oracle on {case.batch} requests, {oracle.set_threads(0)} host threads")
     ref = oracle_attn(case)
     assert_attn_close(got, ref, f"{name} all {case.batch} requests")
@@ -95,12 +104,13 @@ def test_attn_config_full_size_all_requests(name):
         assert err.max() <= 2e-2 and err.mean() <= 2e-3, (name, i, err.max(), err.mean())
 
 
+@layouts
 @pytest.mark.parametrize("scale", [0.02, 0.3])
-def test_attn_explicit_softmax_scale(scale):
+def test_attn_explicit_softmax_scale(scale, vt):
     """A caller's softmax scale instead of 1/sqrt(D), on chains and a tree."""
     case = W.make_custom(9, context_lens=[300, 17], tree_parents=[_tree(4, nodes=30, depth=5), pins.SMALL_TREES[0]],
                          hq=32, hkv=8, d=128)
-    dc = DevCase(case)
+    dc = DevCase(case, vt)
     out, ws = gpu_attn(dc, softmax_scale=scale)
     assert ops.spec_verify_attn_device_status(ws) == 0
     ref = oracle.verify_attn(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens,
@@ -112,37 +122,52 @@ def test_attn_explicit_softmax_scale(scale):
     assert np.abs(ref - oracle_attn(case)).max() > 1e-2
 
 
-def test_attn_sharp_softmax():
+@layouts
+def test_attn_sharp_softmax(vt):
     """Queries scaled x4: attention concentrates on few keys, outputs are O(1)."""
     case = W.make_custom(7, context_lens=[700, 64, 5], q_lens=[4, 8, 2], hq=64, hkv=8, d=128,
                          qkv_scale=1.0)
     case.q = W.f32_to_bf16_bits(W.bf16_bits_to_f32(case.q) * 4.0)
-    dc = DevCase(case)
+    dc = DevCase(case, vt)
     out, _ = gpu_attn(dc)
     ref = oracle_attn(case)
     assert np.abs(ref).max() > 0.5
     assert_attn_close(bf16_out_to_f64(out), ref, "sharp")
 
 
-def test_attn_chain_equals_degenerate_tree_and_page_permutation():
+@layouts
+def test_attn_chain_equals_degenerate_tree_and_page_permutation(vt):
     """Bit-identical GPU outputs for a chain stated as a tree, and for the same
     logical cache laid out through a different page permutation."""
     case = W.make_custom(8, context_lens=[40, 600, 0], q_lens=[5, 3, 7], hq=32, hkv=8, d=128)
-    dc = DevCase(case)
+    dc = DevCase(case, vt)
     out1, _ = gpu_attn(dc)
     tp = np.concatenate([np.arange(-1, q - 1, dtype=np.int32) for q in case.q_lens])
-    out2 = ops.spec_verify_attn(dc.q, dc.k, dc.v, dc.bt, dc.ctx, dc.cu, i32(tp))
+    out2 = attn_fn(vt)(dc.q, dc.k, dc.v, dc.bt, dc.ctx, dc.cu, i32(tp))
     perm = np.random.default_rng(3).permutation(case.num_pages)
     k2 = np.empty_like(case.k_cache)
     v2 = np.empty_like(case.v_cache)
     k2[perm] = case.k_cache
     v2[perm] = case.v_cache
-    out3 = ops.spec_verify_attn(dc.q, u16_to_bf16_dev(k2), v_to_dev(v2),
-                                i32(perm[case.block_tables]), dc.ctx, dc.cu, None)
+    out3 = attn_fn(vt)(dc.q, u16_to_bf16_dev(k2), v_to_dev(v2, vt),
+                       i32(perm[case.block_tables]), dc.ctx, dc.cu, None)
     torch.cuda.synchronize()
     a, b, c = (bf16_dev_to_u16(x) for x in (out1, out2, out3))
     assert np.array_equal(a, b)
     assert np.array_equal(a, c)
+
+
+def test_attn_layouts_agree():
+    """The two V page layouts give the same attention: the P.V products sum the
+    same terms, only the order of the fp32 accumulation differs (8 keys per
+    MFMA k-step in either case), so the outputs agree to bf16 rounding."""
+    case = W.make_custom(11, context_lens=[77, 1000, 3], tree_parents=[_tree(12, nodes=40, depth=6),
+                                                                       pins.SMALL_TREES[1], np.array([-1], np.int32)],
+                         hq=32, hkv=8, d=128)
+    a, _ = gpu_attn(DevCase(case, False))
+    b, _ = gpu_attn(DevCase(case, True))
+    fa, fb = bf16_out_to_f64(a), bf16_out_to_f64(b)
+    assert np.abs(fa - fb).max() <= 2 * 2.0 ** -8 * max(np.abs(fa).max(), 1.0)
 
 
 # ---------------------------------------------------------------------------
@@ -238,7 +263,8 @@ def test_argmax_ties_and_signed_zero(vocab):
 # ---------------------------------------------------------------------------
 # compaction
 # ---------------------------------------------------------------------------
-def test_kv_compact_trees_multilayer():
+@layouts
+def test_kv_compact_trees_multilayer(vt):
     """Tree paths (including overlapping moves like [0,2,3]) over 3 layers: the
     whole pool after the GPU move equals the oracle's copy-based compaction."""
     trees = [pins.SMALL_TREES[0], pins.SMALL_TREES[1], np.array([-1, 0, 1, 1, 2], np.int32), _tree(5)]
@@ -261,8 +287,8 @@ def test_kv_compact_trees_multilayer():
                                        for _ in range(layers - 1)])
     v_all = np.stack([case.v_cache] + [W.f32_to_bf16_bits(rng.standard_normal(case.v_cache.shape).astype(np.float32))
                                        for _ in range(layers - 1)])
-    kd, vd = u16_to_bf16_dev(k_all), v_to_dev(v_all)
-    new = ops.kv_compact(kd, vd, i32(case.block_tables), i32(case.context_lens), i32(case.cu_q),
+    kd, vd = u16_to_bf16_dev(k_all), v_to_dev(v_all, vt)
+    new = compact_fn(vt)(kd, vd, i32(case.block_tables), i32(case.context_lens), i32(case.cu_q),
                          i32(ap), i32(acc), num_layers=layers)
     torch.cuda.synchronize()
     k_ref, v_ref = k_all.copy(), v_all.copy()
@@ -271,7 +297,7 @@ def test_kv_compact_trees_multilayer():
                              num_layers=layers)
     assert np.array_equal(new.cpu().numpy(), new_ref)
     assert np.array_equal(bf16_dev_to_u16(kd), k_ref)
-    assert np.array_equal(v_from_dev(vd), v_ref)
+    assert np.array_equal(v_from_dev(vd, vt), v_ref)
     assert not np.array_equal(k_ref, k_all)  # something really moved
 
 
@@ -299,7 +325,8 @@ def test_empty_inputs_are_noops():
     bt = torch.zeros((0, 1), dtype=torch.int32, device=DEV)
     ctx = torch.zeros(0, dtype=torch.int32, device=DEV)
     cu = torch.zeros(1, dtype=torch.int32, device=DEV)
-    ops.spec_verify_attn(q, k, v, bt, ctx, cu, None)
+    ops.spec_verify_attn_vt(q, k, v, bt, ctx, cu, None)
+    ops.spec_verify_attn(q, k, k, bt, ctx, cu, None)
     # requests with no verify tokens
     cu2 = i32([0, 0, 0])
     res = ops.spec_accept(torch.zeros((0, 16), device=DEV), torch.zeros(0, dtype=torch.int32, device=DEV),
@@ -308,10 +335,11 @@ def test_empty_inputs_are_noops():
     assert res[1].cpu().tolist() == [0, 0]
 
 
-def test_plan_once_run_per_layer():
+@layouts
+def test_plan_once_run_per_layer(vt):
     """One plan serves several layers: each run equals the one-shot call bit for bit."""
     case = W.make_custom(10, context_lens=[300, 5, 1200, 64], q_lens=[4, 9, 2, 6], hq=32, hkv=8, d=128)
-    dc = DevCase(case)
+    dc = DevCase(case, vt)
     ws = torch.empty(ops.spec_verify_attn_workspace_size(case.batch, case.total_q, 32, 8, 128),
                      dtype=torch.uint8, device=DEV)
     ops.spec_verify_attn_plan(dc.ctx, dc.cu, max_blocks_per_seq=case.max_blocks, num_q_heads=32,
@@ -321,9 +349,9 @@ def test_plan_once_run_per_layer():
     for layer in range(3):
         q = u16_to_bf16_dev(W.f32_to_bf16_bits(rng.standard_normal(case.q.shape).astype(np.float32)))
         k = u16_to_bf16_dev(W.f32_to_bf16_bits(rng.standard_normal(case.k_cache.shape).astype(np.float32)))
-        v = v_to_dev(W.f32_to_bf16_bits(rng.standard_normal(case.v_cache.shape).astype(np.float32)))
-        got = ops.spec_verify_attn_run(q, k, v, dc.bt, dc.ctx, dc.cu, None, workspace=ws)
-        ref = ops.spec_verify_attn(q, k, v, dc.bt, dc.ctx, dc.cu, None)
+        v = v_to_dev(W.f32_to_bf16_bits(rng.standard_normal(case.v_cache.shape).astype(np.float32)), vt)
+        got = attn_run_fn(vt)(q, k, v, dc.bt, dc.ctx, dc.cu, None, workspace=ws)
+        ref = attn_fn(vt)(q, k, v, dc.bt, dc.ctx, dc.cu, None)
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), layer
     assert ops.spec_verify_attn_device_status(ws) == 0
@@ -351,20 +379,27 @@ def test_binding_rejects_mismatched_shapes():
         ops.kv_compact(dc.k, dc.v, dc.bt, dc.ctx, dc.cu, path, acc, num_layers=2)
     with pytest.raises(ValueError):
         ops.spec_accept(dc.logits, dc.draft[:-1], dc.cu)
-    # V handed over in the token-major (K) layout: same size, wrong layout
-    v_tok = dc.v.transpose(-1, -2).contiguous()
+    # V handed over in the other layout: same size, wrong layout (D != 16 here)
+    v_t = dc.v.transpose(-1, -2).contiguous()
     with pytest.raises(ValueError):
-        ops.spec_verify_attn(dc.q, dc.k, v_tok, dc.bt, dc.ctx, dc.cu, None)
+        ops.spec_verify_attn(dc.q, dc.k, v_t, dc.bt, dc.ctx, dc.cu, None)
     with pytest.raises(ValueError):
-        ops.kv_compact(dc.k, v_tok, dc.bt, dc.ctx, dc.cu, path, acc)
+        ops.spec_verify_attn_vt(dc.q, dc.k, dc.v, dc.bt, dc.ctx, dc.cu, None)
+    with pytest.raises(ValueError):
+        ops.kv_compact(dc.k, v_t, dc.bt, dc.ctx, dc.cu, path, acc)
+    with pytest.raises(ValueError):
+        ops.kv_compact_vt(dc.k, dc.v, dc.bt, dc.ctx, dc.cu, path, acc)
     ws = torch.zeros(ops.spec_accept_compact_workspace_size(case.batch, case.total_q, case.vocab),
                      dtype=torch.uint8, device=dc.k.device)
     with pytest.raises(ValueError):
-        ops.spec_accept_compact(dc.logits, dc.draft, dc.cu, None, dc.k, v_tok, dc.bt, dc.ctx, workspace=ws)
+        ops.spec_accept_compact(dc.logits, dc.draft, dc.cu, None, dc.k, v_t, dc.bt, dc.ctx, workspace=ws)
+    with pytest.raises(ValueError):
+        ops.spec_accept_compact_vt(dc.logits, dc.draft, dc.cu, None, dc.k, dc.v, dc.bt, dc.ctx, workspace=ws)
 
 
+@layouts
 @pytest.mark.parametrize("seed", range(8))
-def test_random_shapes(seed):
+def test_random_shapes(seed, vt):
     """Seeded random batches: 1-8 requests, contexts 0-1500 (some 0), chains of
     1-64 tokens or trees of 1-64 nodes, 1-8 KV heads, GQA ratio 1-16, head_dim
     64 or 128; attention, argmax and acceptance against the oracle."""
@@ -388,9 +423,9 @@ def test_random_shapes(seed):
         else:
             ql = [int(x) for x in rng.integers(1, 65, B)]
             case = W.make_custom(cs, context_lens=ctx, q_lens=ql, hq=g * hkv, hkv=hkv, d=d, vocab=300)
-        tag = f"seed {seed} case {c}: B={B} hkv={hkv} G={g} D={d} T={case.total_q}"
+        tag = f"seed {seed} case {c}: B={B} hkv={hkv} G={g} D={d} T={case.total_q} vt={vt}"
         note(tag)
-        dc = DevCase(case)
+        dc = DevCase(case, vt)
         out, ws = gpu_attn(dc)
         assert ops.spec_verify_attn_device_status(ws) == 0, tag
         assert_attn_close(bf16_out_to_f64(out), oracle_attn(case), tag)
