@@ -181,6 +181,37 @@ int spec_verify_attn_run_vt(const void *q, const void *k_cache, const void *v_ca
  * pointer). */
 int spec_verify_attn_device_status(const void *workspace, uint32_t *flags, void *stream);
 
+/*
+ * For callers that cannot allocate device memory (code under stream or graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * spec_verify_attn with no workspace argument.  The arguments and the result
+ * are those of spec_verify_attn (token-major V pages); the workspace is a
+ * static device array inside the library of SV_NOALLOC_SCRATCH_BYTES, which
+ * each GPU the library runs on holds from the first call on it until the
+ * process ends.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine).  Its first call on a device looks the array's device
+ * address up once (hipGetSymbolAddress, with that device current).
+ *
+ *   device_status  DEVICE pointer to one uint32, or NULL: receives the call's
+ *                  device status bits (as spec_verify_attn_device_status
+ *                  would report them), stream-ordered.
+ * Errors: those of spec_verify_attn, and SV_ERR_WORKSPACE (before anything is
+ * enqueued) when these sizes need more workspace than the array holds
+ * (spec_verify_attn_workspace_size() > SV_NOALLOC_SCRATCH_BYTES).
+ * Every call on one GPU uses the same array: calls on one GPU must not
+ * overlap in time (two streams, two host threads), or they race.  Nothing in
+ * the array needs to start at any value: each call writes all it reads.
+ */
+#define SV_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
+
+int spec_verify_attn_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *block_tables, int max_blocks_per_seq,
+                             const int32_t *context_lens, const int32_t *cu_q,
+                             const int32_t *tree_parent, void *out, int batch, int total_q,
+                             int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                             int num_pages, float softmax_scale, uint32_t *device_status,
+                             void *stream);
+
 /* ------------------------------------------------------------------------- */
 /* Greedy acceptance                                                          */
 /* ------------------------------------------------------------------------- */

@@ -5,6 +5,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "sv_internal.h"
 #include "read_probe.h"
 
@@ -730,3 +733,86 @@ int spec_accept_compact_vt(const float *logits, int vocab, const int32_t *draft_
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// spec_verify_attn with no caller workspace and no allocation: for callers
+// that cannot allocate device memory (code under stream capture, tight
+// serving loops, harnesses that forbid it).  The attention workspace lives in
+// `scratch`, a file-scope device array that every GPU the library runs on
+// holds for the life of the process.  In host code `scratch` names a host
+// stand-in, not device memory: its device address is taken once per device
+// with hipGetSymbolAddress and only that address is handed to kernels.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = SV_NOALLOC_SCRATCH_BYTES;
+
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// device address of `scratch` on the current device (looked up on the first
+// call on that device, with that device current)
+int scratch_on_current_device(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SV_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr)
+        return fail(SV_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_attn_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *block_tables, int max_blocks_per_seq,
+                             const int32_t *context_lens, const int32_t *cu_q,
+                             const int32_t *tree_parent, void *out, int batch, int total_q,
+                             int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                             int num_pages, float softmax_scale, uint32_t *device_status,
+                             void *stream) {
+  const size_t need = spec_verify_attn_workspace_size(batch, total_q, num_q_heads, num_kv_heads, head_dim);
+  if (need > kScratchBytes)
+    return fail(SV_ERR_WORKSPACE,
+                "spec_verify_attn_noalloc: these sizes need %zu bytes of workspace, more than the %zu bytes "
+                "of its static scratch; use spec_verify_attn with a caller workspace",
+                need, kScratchBytes);
+  // every host-checkable argument error first, before any HIP call
+  sv::AttnArgs a;
+  bool empty;
+  int rc = attn_common(block_tables, max_blocks_per_seq, context_lens, cu_q, batch, total_q, num_q_heads,
+                       num_kv_heads, head_dim, page_size, num_pages, reinterpret_cast<void *>(uintptr_t(256)),
+                       kScratchBytes, true, &a, &empty);
+  if (rc != SV_OK || empty) return rc;
+  rc = attn_data(q, k_cache, v_cache, tree_parent, out, head_dim, page_size, softmax_scale, false, &a);
+  if (rc != SV_OK) return rc;
+  void *ws = nullptr;
+  if ((rc = scratch_on_current_device(&ws)) != SV_OK) return rc;
+  rc = attn_run(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, cu_q, tree_parent, out,
+                batch, total_q, num_q_heads, num_kv_heads, head_dim, page_size, num_pages, softmax_scale, ws,
+                kScratchBytes, stream, true, false, "spec_verify_attn_noalloc");
+  if (rc != SV_OK || device_status == nullptr) return rc;
+  // the status word is the first word of the workspace (written by the plan and run)
+  const hipError_t e = hipMemcpyAsync(device_status, ws, sizeof(uint32_t), hipMemcpyDeviceToDevice,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SV_ERR_HIP, "spec_verify_attn_noalloc status copy: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"
+

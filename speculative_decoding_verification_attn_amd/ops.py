@@ -50,7 +50,9 @@ EXPORTED = ["spec_verify_attn_workspace_size", "spec_verify_attn", "spec_verify_
             "spec_chunk_start", "spec_accept_chunk_workspace_size", "spec_accept_chunk", "spec_verify_budget",
             "spec_accept_compact_workspace_size", "spec_accept_compact", "spec_accept_compact_vt",
             "spec_accept_stochastic_workspace_size", "spec_accept_stochastic",
-            "spec_accept_stochastic_device_status", "spec_hbm_read_probe"]
+            "spec_accept_stochastic_device_status", "spec_hbm_read_probe", "spec_verify_attn_noalloc"]
+
+NOALLOC_SCRATCH_BYTES = 40 << 20  # SV_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -113,6 +115,8 @@ def load_library():
     lib.spec_accept_stochastic.restype = I
     lib.spec_accept_stochastic_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
     lib.spec_accept_stochastic_device_status.restype = I
+    lib.spec_verify_attn_noalloc.argtypes = [P, P, P, P, I, P, P, P, P, I, I, I, I, I, I, I, F, P, P]
+    lib.spec_verify_attn_noalloc.restype = I
     lib.spec_hbm_read_probe.argtypes = [P, P, P, I64, I, I64, P, I64, P]
     lib.spec_hbm_read_probe.restype = I
     lib.sv_status_string.argtypes = [I]
@@ -237,6 +241,39 @@ def spec_verify_attn_run_vt(q, k_cache, v_cache, block_tables, context_lens, cu_
         raise ValueError("spec_verify_attn_run_vt needs the workspace holding the plan")
     return _attn_call("spec_verify_attn_run_vt", q, k_cache, v_cache, block_tables, context_lens, cu_q,
                       tree_parent, out, softmax_scale, workspace, num_pages, stream)
+
+
+def spec_verify_attn_noalloc(q, k_cache, v_cache, block_tables, context_lens, cu_q, tree_parent=None, *,
+                             out, softmax_scale=0.0, device_status=None, num_pages=None, stream=None):
+    """spec_verify_attn on the library's static scratch: no workspace, nothing allocated
+    (out, and device_status if wanted, are the caller's).  Returns out."""
+    lib = load_library()
+    for t, dt, nm in ((q, torch.bfloat16, "q"), (k_cache, torch.bfloat16, "k_cache"),
+                      (v_cache, torch.bfloat16, "v_cache"), (out, torch.bfloat16, "out"),
+                      (block_tables, torch.int32, "block_tables"), (context_lens, torch.int32, "context_lens"),
+                      (cu_q, torch.int32, "cu_q"), (tree_parent, torch.int32, "tree_parent"),
+                      (device_status, torch.int32, "device_status")):
+        _dev(t, dt, nm)
+    T, Hq, D = q.shape
+    pages, Hkv, P, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != _v_shape(k_cache.shape, False):
+        raise ValueError("caches must be K and V [pages, Hkv, 16, D] matching q")
+    B = context_lens.shape[0]
+    if cu_q.numel() != B + 1 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("cu_q must hold batch+1 entries and block_tables batch rows")
+    if tree_parent is not None and tree_parent.numel() != T:
+        raise ValueError("tree_parent must hold one entry per verify token")
+    if num_pages is not None and not 0 < num_pages <= pages:
+        raise ValueError(f"num_pages {num_pages} exceeds the {pages} pages of the caches")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have the shape of q")
+    if device_status is not None and device_status.numel() < 1:
+        raise ValueError("device_status must hold one word")
+    _check(lib.spec_verify_attn_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                        block_tables.shape[1], _ptr(context_lens), _ptr(cu_q), _ptr(tree_parent),
+                                        _ptr(out), B, T, Hq, Hkv, D, P, pages if num_pages is None else num_pages,
+                                        float(softmax_scale), _ptr(device_status), _stream(stream)))
+    return out
 
 
 def spec_verify_attn_plan(context_lens, cu_q, *, max_blocks_per_seq, num_q_heads, num_kv_heads,

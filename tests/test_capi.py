@@ -226,3 +226,33 @@ def test_cache_pair_layout_check():
     with pytest.raises(ValueError):
         ops._check_cache_pair(torch.empty((2, 16, 64), dtype=torch.bfloat16),
                               torch.empty((2, 64, 16), dtype=torch.bfloat16), True)
+
+
+def test_noalloc_host_checks(lib):
+    """spec_verify_attn_noalloc checks its arguments like spec_verify_attn and
+    refuses sizes whose workspace exceeds its static scratch, all on the host
+    before any HIP call (so this runs without a GPU)."""
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, mb=4, ctx=FAKE, cu=FAKE, par=NULL, out=ctypes.c_void_p(0x90000000),
+                 B=2, T=8, Hq=8, Hkv=2, D=64, P=16, pages=10, scale=0.0, status=NULL, stream=NULL)
+        a.update(kw)
+        return lib.spec_verify_attn_noalloc(a["q"], a["k"], a["v"], a["bt"], a["mb"], a["ctx"], a["cu"], a["par"],
+                                            a["out"], a["B"], a["T"], a["Hq"], a["Hkv"], a["D"], a["P"], a["pages"],
+                                            a["scale"], a["status"], a["stream"])
+    assert call(D=96) == ops.SV_ERR_UNSUPPORTED
+    assert call(P=32) == ops.SV_ERR_UNSUPPORTED
+    assert call(Hq=6, Hkv=4) == ops.SV_ERR_SHAPE
+    assert call(q=NULL) == ops.SV_ERR_NULL
+    assert call(mb=0) == ops.SV_ERR_SHAPE
+    assert call(scale=-1.0) == ops.SV_ERR_SHAPE
+    assert call(B=0, T=0, q=NULL, out=NULL) == ops.SV_OK
+    big = dict(B=40000, T=40000 * 64, Hq=64, Hkv=8, D=128)
+    assert lib.spec_verify_attn_workspace_size(40000, 40000 * 64, 64, 8, 128) > ops.NOALLOC_SCRATCH_BYTES
+    assert call(**big) == ops.SV_ERR_WORKSPACE
+    assert b"static scratch" in lib.sv_last_error()
+    # the 70B batch-256 shape fits
+    assert lib.spec_verify_attn_workspace_size(256, 1024, 64, 8, 128) <= ops.NOALLOC_SCRATCH_BYTES
+    # the binding's constant is the header's
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                            "spec_verify.h")).read()
+    assert "#define SV_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)" in hdr and ops.NOALLOC_SCRATCH_BYTES == 40 << 20
