@@ -83,7 +83,13 @@ def main():
                     help="no GPU run: turn a rocprofv3 --pmc run of SQ_INSTS_MFMA, "
                          "SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE (among others) into "
                          "profiles/verify_attn_<config>_mfma.json")
+    ap.add_argument("--sps-summary", metavar="BENCH_JSON", default=None,
+                    help="no GPU run: turn the sps_table of a default run's JSON line into "
+                         "profiles/sps_table_llama3_70b.json (the verify-budget scheduler's cost table)")
     args = ap.parse_args()
+    if args.sps_summary:
+        write_sps_summary(args.sps_summary)
+        return
     if args.mfma_summary:
         write_mfma_summary(args.config, args.mfma_summary)
         return
@@ -618,6 +624,23 @@ def write_traffic_summary(name, fetch_dir, write_dir, copy_mb):
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
+
+
+def write_sps_summary(bench_json):
+    """The SPS(B) table of a default run (70B-shape batch sweep) as the cost table
+    the verify-budget scheduler reads: verify rows -> verify steps per second."""
+    line = [ln for ln in open(bench_json).read().splitlines() if ln.strip().startswith("{")][-1]
+    rec = json.loads(line)
+    t = rec["sps_table"]
+    out = {"workload": "Llama-3-70B attention geometry (64/8 heads, D=128), chains gamma=3, contexts U[2048,8192], "
+                       "batch 16..256",
+           "rows": t["rows"], "steps_per_s": t["steps_per_s"], "definition": t["definition"],
+           "points": rec["sweep"], "v_layout": rec.get("v_layout"),
+           "command": "python bench.py  (default run; this file: python bench.py --sps-summary <its JSON line>)"}
+    path = os.path.join(ROOT, "profiles", "sps_table_llama3_70b.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def write_mfma_summary(name, pmc_dir):

@@ -150,3 +150,44 @@ def test_library_rejects_bad_arguments():
         ops.spec_verify_budget(np.zeros(64, np.float32), np.array([0, 64], np.int32), rows, val)
     verify, brows, th = ops.spec_verify_budget(np.zeros(0, np.float32), np.array([0], np.int32), rows, val)
     assert len(verify) == 0 and brows == 0 and th == 0.0
+
+
+def _measured_sps():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles",
+                        "sps_table_llama3_70b.json")
+    t = json.load(open(path))
+    rows, sps = np.asarray(t["rows"], np.float32), np.asarray(t["steps_per_s"], np.float32)
+    assert len(rows) >= 3 and np.all(np.diff(rows) > 0) and np.all(sps > 0)
+    return rows, sps
+
+
+@pytest.mark.parametrize("shape", ["b256_p075_gamma3", "ragged_beta22", "b16_mixed"])
+def test_library_matches_oracle_on_measured_sps_table(shape):
+    """The verify path's measured SPS(B) table (verify rows -> verify steps per
+    second, 70B-shape sweep in profiles/) as the scheduler's cost table, with
+    survival probabilities shaped like the workloads' acceptance: the library
+    and the oracle choose the same verify lengths, and the chosen Theta is at
+    least that of verifying no draft and of verifying every draft."""
+    rows, sps = _measured_sps()
+    rng = np.random.default_rng({"b256_p075_gamma3": 1, "ragged_beta22": 2, "b16_mixed": 3}[shape])
+    if shape == "b256_p075_gamma3":
+        gam = [3] * 256
+        cond = [np.full(3, 0.75, np.float32) for _ in gam]
+    elif shape == "ragged_beta22":
+        gam = [int(g) for g in rng.integers(1, 9, 64)]
+        cond = [np.full(g, rng.beta(2, 2), np.float32) for g in gam]
+    else:
+        gam = [int(g) for g in rng.integers(0, 9, 16)]
+        cond = [rng.uniform(0.2, 1.0, g).astype(np.float32) for g in gam]
+    cu = np.zeros(len(gam) + 1, np.int32)
+    cu[1:] = np.cumsum(gam)
+    flat = np.concatenate(cond).astype(np.float32)
+    verify, brows, th = ops.spec_verify_budget(flat, cu, rows, sps)
+    ov, ob, oth = budget.verify_budget(cond, gam, rows, sps)
+    assert verify.tolist() == ov and brows == ob
+    assert th == pytest.approx(oth, rel=1e-9)
+    assert th >= _theta(cond, [0] * len(gam), rows, sps) * (1 - 1e-12)
+    assert th >= _theta(cond, gam, rows, sps) * (1 - 1e-12)
+    assert brows == len(gam) + int(verify.sum())
