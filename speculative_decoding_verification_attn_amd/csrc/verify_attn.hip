@@ -663,16 +663,11 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   // the 8 XCDs), so units that share K/V (tile groups of one head) meet in
   // one L2
   const int bx = blockIdx.x;
-  const int w = (a.grid % 8 == 0) ? (bx % 8) * (a.grid / 8) + bx / 8 : bx;
-  if (w >= P) return;
+  const int wg = (a.grid % 8 == 0) ? (bx % 8) * (a.grid / 8) + bx / 8 : bx;
+  if (wg >= P) return;
   const const_i32_ptr wg_start = (const_i32_ptr)(uintptr_t)(a.ws + a.lay.wg_start);
-  const int start = wg_start[w];
-  const int end = wg_start[w + 1];
   const const_unit_ptr units{(const_i32_ptr)(uintptr_t)(a.ws + a.lay.units)};
-  const int first_unit = ((const_i32_ptr)(uintptr_t)(a.ws + a.lay.wg_first))[w];
-  const UnitRec rec0 = const_unit_ptr{(const_i32_ptr)(uintptr_t)(a.ws + a.lay.wg_rec)}[w];
   const int n_units = hdr[3];
-  if (first_unit < 0 || first_unit >= n_units || start >= end) return;  // not for a consistent plan
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -681,223 +676,237 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   const size_t page_stride = (size_t)a.num_kv_heads * kPage * D;
   bool bad_page = false;
 
-  // Two walks over the same pieces: the consumer at the round being
-  // computed, the producer two rounds ahead (it fetches page ids for round
-  // g+2 and issues the K/V loads of round g+1 into the buffer freed by round
-  // g-1), so K/V streaming runs on across unit boundaries.
-  Walk Wc, Wp;
-  walk_enter(Wc, first_unit, rec0, start, end, 0, units, n_units);
-  Wp = Wc;
+  // The workgroup's block range w.  (Written as a function of w, whose
+  // record is read here rather than at kernel entry: the compiler then keeps
+  // far fewer scalars live through the round loop, and spills fewer of them
+  // to vector-register lanes.)
+  auto run_range = [&](const int w) {
+    const int start = wg_start[w];
+    const int end = wg_start[w + 1];
+    const int first_unit = ((const_i32_ptr)(uintptr_t)(a.ws + a.lay.wg_first))[w];
+    const UnitRec rec0 = const_unit_ptr{(const_i32_ptr)(uintptr_t)(a.ws + a.lay.wg_rec)}[w];
+    if (first_unit < 0 || first_unit >= n_units || start >= end) return;  // not for a consistent plan
 
-  // per-unit consumer context, one entry per query tile of the unit
-  int nt = 1;  // tiles of the consumer's unit
-  uint64_t anc[kUnitTiles];
-  int nk = 0;
-  float m[kUnitTiles], l[kUnitTiles];
-  floatx16 acc[kUnitTiles][DPL];
-  bf16x8 qpf[KQ];    // tile-0 Q chunks prefetched for unit qpf_u
-  int qpf_u = -1;
+    // Two walks over the same pieces: the consumer at the round being
+    // computed, the producer two rounds ahead (it fetches page ids for round
+    // g+2 and issues the K/V loads of round g+1 into the buffer freed by round
+    // g-1), so K/V streaming runs on across unit boundaries.
+    Walk Wc, Wp;
+    walk_enter(Wc, first_unit, rec0, start, end, 0, units, n_units);
+    Wp = Wc;
 
-  // enter the consumer's unit: ancestor masks of the lane's rows and Q in LDS
-  auto enter_unit = [&]() {
-    // masks of the verify tokens [0, s+q) (keys L .. L+s+q-1); row r of the
-    // unit's tiles is token s + r / G
-    bool parents_ok;
-    const uint64_t anc_all = ancestor_mask(a.tree_parent, Wc.ot, Wc.s + Wc.qn, lane, &parents_ok);
-    if (!parents_ok && threadIdx.x == 0 && Wc.ps == Wc.ub && Wc.h == 0 && Wc.rg == 0)
-      atomicOr(reinterpret_cast<unsigned *>(a.ws + a.lay.hdr), SV_DEV_BAD_PARENT);
-    nt = min(kUnitTiles, (G * Wc.qn + kTileRows - 1) / kTileRows - Wc.rg * kUnitTiles);
-#pragma unroll
-    for (int tt = 0; tt < kUnitTiles; ++tt) {
-      const int R = (Wc.rg * kUnitTiles + tt) * kTileRows + n;
-      const bool row_ok = R < G * Wc.qn;
-      const int tok = row_ok ? R / G : 0;
-      // the shuffle must run on every lane: a source lane whose own row is
-      // past the end would be inactive and read back as zero
-      const uint64_t anc_tok = __shfl(anc_all, Wc.s + tok);
-      anc[tt] = row_ok ? anc_tok : 0ull;
-      m[tt] = -INFINITY;
-      l[tt] = 0.f;
-#pragma unroll
-      for (int c = 0; c < DPL; ++c) acc[tt][c] = floatx16{};
-    }
-    nk = Wc.L + Wc.s + Wc.qn;
-    if (qpf_u != Wc.u) load_q_chunks<D>(a, Wc, 0, wave, n, hh, qpf);
-#pragma unroll
-    for (int j = 0; j < KQ; ++j) sm_q[0][wave * KQ + j][lane] = qpf[j];
-    qpf_u = -1;
-#pragma unroll
-    for (int tt = 1; tt < kUnitTiles; ++tt) {
-      if (tt >= nt) break;
-      bf16x8 qc[KQ];
-      load_q_chunks<D>(a, Wc, tt, wave, n, hh, qc);
-#pragma unroll
-      for (int j = 0; j < KQ; ++j) sm_q[tt][wave * KQ + j][lane] = qc[j];
-    }
-  };
+    // per-unit consumer context, one entry per query tile of the unit
+    int nt = 1;  // tiles of the consumer's unit
+    uint64_t anc[kUnitTiles];
+    int nk = 0;
+    float m[kUnitTiles], l[kUnitTiles];
+    floatx16 acc[kUnitTiles][DPL];
+    bf16x8 qpf[KQ];    // tile-0 Q chunks prefetched for unit qpf_u
+    int qpf_u = -1;
 
-  // The unit's Q^T operands stay in registers while it runs: read from LDS
-  // once per unit instead of once per block, the hot loop has no LDS reads
-  // to wait for before its MFMAs.
-  bf16x8 qop[kUnitTiles][KK];
-  auto load_qop = [&]() {
+    // enter the consumer's unit: ancestor masks of the lane's rows and Q in LDS
+    auto enter_unit = [&]() {
+      // masks of the verify tokens [0, s+q) (keys L .. L+s+q-1); row r of the
+      // unit's tiles is token s + r / G
+      bool parents_ok;
+      const uint64_t anc_all = ancestor_mask(a.tree_parent, Wc.ot, Wc.s + Wc.qn, lane, &parents_ok);
+      if (!parents_ok && threadIdx.x == 0 && Wc.ps == Wc.ub && Wc.h == 0 && Wc.rg == 0)
+        atomicOr(reinterpret_cast<unsigned *>(a.ws + a.lay.hdr), SV_DEV_BAD_PARENT);
+      nt = min(kUnitTiles, (G * Wc.qn + kTileRows - 1) / kTileRows - Wc.rg * kUnitTiles);
 #pragma unroll
-    for (int tt = 0; tt < kUnitTiles; ++tt) {
-      if (tt >= nt) break;
+      for (int tt = 0; tt < kUnitTiles; ++tt) {
+        const int R = (Wc.rg * kUnitTiles + tt) * kTileRows + n;
+        const bool row_ok = R < G * Wc.qn;
+        const int tok = row_ok ? R / G : 0;
+        // the shuffle must run on every lane: a source lane whose own row is
+        // past the end would be inactive and read back as zero
+        const uint64_t anc_tok = __shfl(anc_all, Wc.s + tok);
+        anc[tt] = row_ok ? anc_tok : 0ull;
+        m[tt] = -INFINITY;
+        l[tt] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) qop[tt][kk] = sm_q[tt][kk][lane];
-    }
-  };
-
-  // producer: page ids and head of the round it will load next
-  int2 pg_next = make_int2(0, 0);
-  int h_next = Wp.h;
-  auto fetch_pages = [&](int g) {
-    walk_to(Wp, g, start, end, units, n_units);
-    const int lbk = (Wp.ps - Wp.ub) + kAttnWaves * min(g - Wp.g0, Wp.nr - 1) + wave;
-    const int lmax = Wp.pe - Wp.ub - 1;  // a wave without a block re-reads the piece's last one
-    const const_i32_ptr bt = (const_i32_ptr)(uintptr_t)(a.block_tables + (size_t)Wp.i * a.max_blocks);
-    const int npages = (Wp.L + Wp.s + Wp.qn + kPage - 1) / kPage;
-    int safe = bt[0];
-    if (safe < 0 || safe >= a.num_pages) safe = 0;
-    pg_next = block_pages(bt, min(lbk, lmax), npages, a.num_pages, safe, &bad_page);
-    h_next = Wp.h;
-  };
-  auto produce = [&](KVBlock<D, VT> &buf) {
-    load_block<D, VT>(buf, a.k_cache + (size_t)h_next * kPage * D, a.v_cache + (size_t)h_next * kPage * D,
-                  pg_next, n, hh, page_stride);
-  };
-
-  // finish the consumer's unit: per tile, merge the waves through LDS and
-  // write the output or a partial
-  auto finish_unit = [&]() {
-    const bool whole = Wc.ps == Wc.ub && Wc.pe == Wc.ub + Wc.nblk;
-    const int side = Wc.u == first_unit ? 0 : 1;
-#pragma unroll
-    for (int tt = 0; tt < kUnitTiles; ++tt) {
-      if (tt >= nt) break;
-      if (tt > 0) __syncthreads();  // every wave has read the previous tile's sm_o
-      const float lt = l[tt] + __shfl_xor(l[tt], 32);  // both lane halves summed different keys of a row
-      if (hh == 0) {
-        sm_m[wave][n] = m[tt];
-        sm_l[wave][n] = lt;
+        for (int c = 0; c < DPL; ++c) acc[tt][c] = floatx16{};
       }
+      nk = Wc.L + Wc.s + Wc.qn;
+      if (qpf_u != Wc.u) load_q_chunks<D>(a, Wc, 0, wave, n, hh, qpf);
 #pragma unroll
-      for (int c = 0; c < DPL; ++c)
+      for (int j = 0; j < KQ; ++j) sm_q[0][wave * KQ + j][lane] = qpf[j];
+      qpf_u = -1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          sm_o[wave][c][j][lane] = float4v{acc[tt][c][4 * j], acc[tt][c][4 * j + 1], acc[tt][c][4 * j + 2],
-                                           acc[tt][c][4 * j + 3]};
-      __syncthreads();
-      float M = -INFINITY;
+      for (int tt = 1; tt < kUnitTiles; ++tt) {
+        if (tt >= nt) break;
+        bf16x8 qc[KQ];
+        load_q_chunks<D>(a, Wc, tt, wave, n, hh, qc);
 #pragma unroll
-      for (int ww = 0; ww < kAttnWaves; ++ww) M = fmaxf(M, sm_m[ww][n]);
-      const float Mref = M == -INFINITY ? 0.f : M;
-      float f[kAttnWaves];
-      float Lsum = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < kAttnWaves; ++ww) {
-        f[ww] = fast_exp2(sm_m[ww][n] - Mref);
-        Lsum += f[ww] * sm_l[ww][n];
+        for (int j = 0; j < KQ; ++j) sm_q[tt][wave * KQ + j][lane] = qc[j];
       }
-      // this wave finalises registers r = 4*wave .. 4*wave+3 of every tile c,
-      // O^T rows i = 8*wave + 4*hh + rr: with transposed V pages output
-      // d = 32*c + i (ov[4c + rr], four contiguous per c); with token-major
-      // pages d = DPL*i + c (ov[DPL*rr + c], 4*DPL contiguous)
-      float ov[4 * DPL];
+    };
+
+    // The unit's Q^T operands stay in registers while it runs: read from LDS
+    // once per unit instead of once per block, the hot loop has no LDS reads
+    // to wait for before its MFMAs.
+    bf16x8 qop[kUnitTiles][KK];
+    auto load_qop = [&]() {
 #pragma unroll
-      for (int i = 0; i < 4 * DPL; ++i) ov[i] = 0.f;
+      for (int tt = 0; tt < kUnitTiles; ++tt) {
+        if (tt >= nt) break;
 #pragma unroll
-      for (int c = 0; c < DPL; ++c)
+        for (int kk = 0; kk < KK; ++kk) qop[tt][kk] = sm_q[tt][kk][lane];
+      }
+    };
+
+    // producer: page ids and head of the round it will load next
+    int2 pg_next = make_int2(0, 0);
+    int h_next = Wp.h;
+    auto fetch_pages = [&](int g) {
+      walk_to(Wp, g, start, end, units, n_units);
+      const int lbk = (Wp.ps - Wp.ub) + kAttnWaves * min(g - Wp.g0, Wp.nr - 1) + wave;
+      const int lmax = Wp.pe - Wp.ub - 1;  // a wave without a block re-reads the piece's last one
+      const const_i32_ptr bt = (const_i32_ptr)(uintptr_t)(a.block_tables + (size_t)Wp.i * a.max_blocks);
+      const int npages = (Wp.L + Wp.s + Wp.qn + kPage - 1) / kPage;
+      int safe = bt[0];
+      if (safe < 0 || safe >= a.num_pages) safe = 0;
+      pg_next = block_pages(bt, min(lbk, lmax), npages, a.num_pages, safe, &bad_page);
+      h_next = Wp.h;
+    };
+    auto produce = [&](KVBlock<D, VT> &buf) {
+      load_block<D, VT>(buf, a.k_cache + (size_t)h_next * kPage * D, a.v_cache + (size_t)h_next * kPage * D,
+                    pg_next, n, hh, page_stride);
+    };
+
+    // finish the consumer's unit: per tile, merge the waves through LDS and
+    // write the output or a partial
+    auto finish_unit = [&]() {
+      const bool whole = Wc.ps == Wc.ub && Wc.pe == Wc.ub + Wc.nblk;
+      const int side = Wc.u == first_unit ? 0 : 1;
+#pragma unroll
+      for (int tt = 0; tt < kUnitTiles; ++tt) {
+        if (tt >= nt) break;
+        if (tt > 0) __syncthreads();  // every wave has read the previous tile's sm_o
+        const float lt = l[tt] + __shfl_xor(l[tt], 32);  // both lane halves summed different keys of a row
+        if (hh == 0) {
+          sm_m[wave][n] = m[tt];
+          sm_l[wave][n] = lt;
+        }
+#pragma unroll
+        for (int c = 0; c < DPL; ++c)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            sm_o[wave][c][j][lane] = float4v{acc[tt][c][4 * j], acc[tt][c][4 * j + 1], acc[tt][c][4 * j + 2],
+                                             acc[tt][c][4 * j + 3]};
+        __syncthreads();
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < kAttnWaves; ++ww) M = fmaxf(M, sm_m[ww][n]);
+        const float Mref = M == -INFINITY ? 0.f : M;
+        float f[kAttnWaves];
+        float Lsum = 0.f;
 #pragma unroll
         for (int ww = 0; ww < kAttnWaves; ++ww) {
-          const float4v x = sm_o[ww][c][wave][lane];
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) ov[VT ? 4 * c + rr : DPL * rr + c] += f[ww] * x[rr];
+          f[ww] = fast_exp2(sm_m[ww][n] - Mref);
+          Lsum += f[ww] * sm_l[ww][n];
         }
-      const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
-      const int d0 = VT ? 8 * wave + 4 * hh : DPL * (8 * wave + 4 * hh);
-      const int R = (Wc.rg * kUnitTiles + tt) * kTileRows + n;
-      if (R < G * Wc.qn) {
-        const int tok = R / G, gq = R - tok * G;
-        if (whole) {
-          uint16_t *orow = a.out + ((size_t)(Wc.o + tok) * a.num_q_heads + (size_t)Wc.h * G + gq) * D + d0;
-          if constexpr (VT) {
+        // this wave finalises registers r = 4*wave .. 4*wave+3 of every tile c,
+        // O^T rows i = 8*wave + 4*hh + rr: with transposed V pages output
+        // d = 32*c + i (ov[4c + rr], four contiguous per c); with token-major
+        // pages d = DPL*i + c (ov[DPL*rr + c], 4*DPL contiguous)
+        float ov[4 * DPL];
 #pragma unroll
-            for (int c = 0; c < DPL; ++c)
-              *reinterpret_cast<uint2 *>(orow + 32 * c) =
-                  make_uint2(pack_bf16x2(ov[4 * c] * inv, ov[4 * c + 1] * inv),
-                             pack_bf16x2(ov[4 * c + 2] * inv, ov[4 * c + 3] * inv));
-          } else {
+        for (int i = 0; i < 4 * DPL; ++i) ov[i] = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4 * DPL; j += 8)
-              *reinterpret_cast<uint4 *>(orow + j) =
-                  make_uint4(pack_bf16x2(ov[j] * inv, ov[j + 1] * inv), pack_bf16x2(ov[j + 2] * inv, ov[j + 3] * inv),
-                             pack_bf16x2(ov[j + 4] * inv, ov[j + 5] * inv), pack_bf16x2(ov[j + 6] * inv, ov[j + 7] * inv));
+        for (int c = 0; c < DPL; ++c)
+#pragma unroll
+          for (int ww = 0; ww < kAttnWaves; ++ww) {
+            const float4v x = sm_o[ww][c][wave][lane];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) ov[VT ? 4 * c + rr : DPL * rr + c] += f[ww] * x[rr];
           }
-        } else {
-          const size_t slot = (2 * (size_t)w + side) * kUnitTiles + tt;
-          float *po = reinterpret_cast<float *>(a.ws + a.lay.part_o) + (slot * kTileRows + n) * D + d0;
-          if constexpr (VT) {
+        const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
+        const int d0 = VT ? 8 * wave + 4 * hh : DPL * (8 * wave + 4 * hh);
+        const int R = (Wc.rg * kUnitTiles + tt) * kTileRows + n;
+        if (R < G * Wc.qn) {
+          const int tok = R / G, gq = R - tok * G;
+          if (whole) {
+            uint16_t *orow = a.out + ((size_t)(Wc.o + tok) * a.num_q_heads + (size_t)Wc.h * G + gq) * D + d0;
+            if constexpr (VT) {
 #pragma unroll
-            for (int c = 0; c < DPL; ++c)
-              *reinterpret_cast<float4 *>(po + 32 * c) =
-                  make_float4(ov[4 * c] * inv, ov[4 * c + 1] * inv, ov[4 * c + 2] * inv, ov[4 * c + 3] * inv);
+              for (int c = 0; c < DPL; ++c)
+                *reinterpret_cast<uint2 *>(orow + 32 * c) =
+                    make_uint2(pack_bf16x2(ov[4 * c] * inv, ov[4 * c + 1] * inv),
+                               pack_bf16x2(ov[4 * c + 2] * inv, ov[4 * c + 3] * inv));
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4 * DPL; j += 8)
+                *reinterpret_cast<uint4 *>(orow + j) =
+                    make_uint4(pack_bf16x2(ov[j] * inv, ov[j + 1] * inv), pack_bf16x2(ov[j + 2] * inv, ov[j + 3] * inv),
+                               pack_bf16x2(ov[j + 4] * inv, ov[j + 5] * inv), pack_bf16x2(ov[j + 6] * inv, ov[j + 7] * inv));
+            }
           } else {
+            const size_t slot = (2 * (size_t)w + side) * kUnitTiles + tt;
+            float *po = reinterpret_cast<float *>(a.ws + a.lay.part_o) + (slot * kTileRows + n) * D + d0;
+            if constexpr (VT) {
 #pragma unroll
-            for (int j = 0; j < 4 * DPL; j += 4)
-              *reinterpret_cast<float4 *>(po + j) =
-                  make_float4(ov[j] * inv, ov[j + 1] * inv, ov[j + 2] * inv, ov[j + 3] * inv);
-          }
-          if (wave == 0 && hh == 0) {
-            float *pl = reinterpret_cast<float *>(a.ws + a.lay.part_lse);
-            pl[slot * kTileRows + n] = Lsum > 0.f ? Mref + fast_log2(Lsum) : -INFINITY;
+              for (int c = 0; c < DPL; ++c)
+                *reinterpret_cast<float4 *>(po + 32 * c) =
+                    make_float4(ov[4 * c] * inv, ov[4 * c + 1] * inv, ov[4 * c + 2] * inv, ov[4 * c + 3] * inv);
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4 * DPL; j += 4)
+                *reinterpret_cast<float4 *>(po + j) =
+                    make_float4(ov[j] * inv, ov[j + 1] * inv, ov[j + 2] * inv, ov[j + 3] * inv);
+            }
+            if (wave == 0 && hh == 0) {
+              float *pl = reinterpret_cast<float *>(a.ws + a.lay.part_lse);
+              pl[slot * kTileRows + n] = Lsum > 0.f ? Mref + fast_log2(Lsum) : -INFINITY;
+            }
           }
         }
       }
+    };
+
+    // one round g: issue the loads of round g+1 into `into` (freed by round
+    // g-1), compute round g from `cur`; true once the last unit is finished
+    auto round = [&](int g, KVBlock<D, VT> &cur, KVBlock<D, VT> &into) -> bool {
+      produce(into);
+      fetch_pages(g + 2);
+      // prefetch the next unit's first Q tile once this unit is under way
+      if (Wc.has_next && qpf_u != Wc.u + 1 && g == Wc.g0 + 1) {
+        Walk Wn;
+        walk_enter(Wn, Wc.u + 1, Wc.next, start, end, 0, units, 0);
+        load_q_chunks<D>(a, Wn, 0, wave, n, hh, qpf);
+        qpf_u = Wc.u + 1;
+      }
+      const int gb = Wc.ps + kAttnWaves * (g - Wc.g0) + wave;  // this wave's global block
+      if (gb < Wc.pe)
+        compute_block<D, VT>(cur, qop, nt, (gb - Wc.ub) * kBlockKeys, Wc.L, nk, anc, hh,
+                         a.scale_log2, m, l, acc);
+      if (g + 1 == Wc.g0 + Wc.nr) {
+        finish_unit();
+        if (!Wc.has_next) return true;
+        walk_to(Wc, g + 1, start, end, units, n_units);
+        enter_unit();
+        __syncthreads();  // the next unit's Q is in LDS; sm_o may be reused
+        load_qop();
+      }
+      return false;
+    };
+
+    // the first K/V loads go out before the Q operands are staged, so the
+    // two memory round trips overlap
+    KVBlock<D, VT> A, Bb;
+    fetch_pages(0);
+    produce(A);
+    fetch_pages(1);
+    enter_unit();
+    __syncthreads();
+    load_qop();
+    for (int g = 0;; g += 2) {
+      if (round(g, A, Bb)) break;
+      if (round(g + 1, Bb, A)) break;
     }
   };
 
-  // one round g: issue the loads of round g+1 into `into` (freed by round
-  // g-1), compute round g from `cur`; true once the last unit is finished
-  auto round = [&](int g, KVBlock<D, VT> &cur, KVBlock<D, VT> &into) -> bool {
-    produce(into);
-    fetch_pages(g + 2);
-    // prefetch the next unit's first Q tile once this unit is under way
-    if (Wc.has_next && qpf_u != Wc.u + 1 && g == Wc.g0 + 1) {
-      Walk Wn;
-      walk_enter(Wn, Wc.u + 1, Wc.next, start, end, 0, units, 0);
-      load_q_chunks<D>(a, Wn, 0, wave, n, hh, qpf);
-      qpf_u = Wc.u + 1;
-    }
-    const int gb = Wc.ps + kAttnWaves * (g - Wc.g0) + wave;  // this wave's global block
-    if (gb < Wc.pe)
-      compute_block<D, VT>(cur, qop, nt, (gb - Wc.ub) * kBlockKeys, Wc.L, nk, anc, hh,
-                       a.scale_log2, m, l, acc);
-    if (g + 1 == Wc.g0 + Wc.nr) {
-      finish_unit();
-      if (!Wc.has_next) return true;
-      walk_to(Wc, g + 1, start, end, units, n_units);
-      enter_unit();
-      __syncthreads();  // the next unit's Q is in LDS; sm_o may be reused
-      load_qop();
-    }
-    return false;
-  };
-
-  // the first K/V loads go out before the Q operands are staged, so the
-  // two memory round trips overlap
-  KVBlock<D, VT> A, Bb;
-  fetch_pages(0);
-  produce(A);
-  fetch_pages(1);
-  enter_unit();
-  __syncthreads();
-  load_qop();
-  for (int g = 0;; g += 2) {
-    if (round(g, A, Bb)) break;
-    if (round(g + 1, Bb, A)) break;
-  }
+  run_range(wg);
   if (bad_page) atomicOr(reinterpret_cast<unsigned *>(a.ws + a.lay.hdr), SV_DEV_BAD_PAGE);
 }
 
