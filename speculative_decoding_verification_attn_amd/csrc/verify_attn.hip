@@ -494,25 +494,21 @@ __global__ __launch_bounds__(64 * kMergeRows) void attn_merge_kernel(AttnArgs a)
   const int G = a.group;
   const float *pl = reinterpret_cast<const float *>(a.ws + a.lay.part_lse);
   const float *po = reinterpret_cast<const float *>(a.ws + a.lay.part_o);
-  for (int tt = 0; tt < kUnitTiles; ++tt) {
-  const int R = (rowgroup * kUnitTiles + tt) * kTileRows + n;
-  if (R >= G * qn) return;
-  const int tok = R / G, gq = R - tok * G;
   // range w0 holds the unit's first block (its first or second partial
   // slot); every later range starts inside the unit (first slot).  No range
   // between w0 and w1 is empty: distinct cost targets inside one unit map to
   // distinct blocks, so an empty range can only begin at a unit start.
   const int np = w1 - w0 + 1;
-  auto slot_of = [&](int k) {
+  auto slot_of = [&](int k, int tt) {
     const int w = w0 + k;
     return (2 * (size_t)w + (k == 0 ? side0 : 0)) * kUnitTiles + tt;
   };
-  // rows of pieces k0 + j0 .. k0 + j0 + 7 (past the last piece: the last one
-  // again, weighted 0 by the caller)
-  auto load8 = [&](int k0, int j0, int kn, float (&x)[8][DPT]) {
+  // rows of pieces k0 + j0 .. k0 + j0 + 7 of tile tt (past the last piece:
+  // the last one again, weighted 0 by the caller)
+  auto load8 = [&](int tt, int k0, int j0, int kn, float (&x)[8][DPT]) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const size_t row = (slot_of(k0 + min(j0 + u, kn - 1)) * kTileRows + n) * D;
+      const size_t row = (slot_of(k0 + min(j0 + u, kn - 1), tt) * kTileRows + n) * D;
       if constexpr (DPT == 2) {
         const float2 xv = reinterpret_cast<const float2 *>(po + row)[lane];
         x[u][0] = xv.x;
@@ -522,49 +518,65 @@ __global__ __launch_bounds__(64 * kMergeRows) void attn_merge_kernel(AttnArgs a)
       }
     }
   };
-  float acc[DPT];
+  // The first loads of every tile go out together: each piece's
+  // log-sum-exp (lane k holds piece k) and the first eight pieces' rows, so
+  // a unit cut into a few pieces costs one memory round trip for all of its
+  // tiles rather than one per tile.
+  bool valid[kUnitTiles];
+  float ls0[kUnitTiles];
+  float x0[kUnitTiles][8][DPT];
 #pragma unroll
-  for (int t = 0; t < DPT; ++t) acc[t] = 0.f;
-  auto add8 = [&](int j0, int kn, float wl, const float (&x)[8][DPT]) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = min(j0 + u, kn - 1);
-      const float wt = j0 + u < kn ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wl), j)) : 0.f;
-#pragma unroll
-      for (int t = 0; t < DPT; ++t) acc[t] += wt * x[u][t];
-    }
-  };
-  // the common maximum over the pieces' log-sum-exps, 64 pieces per load
-  // (lane k holds piece k0 + k); with at most 64 pieces the first eight
-  // rows are loaded alongside, so a few pieces cost one memory round trip
-  float M = -INFINITY, den = 0.f;
-  float x[8][DPT];
-  float ls0 = -INFINITY;
-  for (int k0 = 0; k0 < np; k0 += 64) {
-    const float ls = k0 + lane < np ? pl[slot_of(k0 + lane) * kTileRows + n] : -INFINITY;
-    if (k0 == 0) {
-      ls0 = ls;
-      load8(0, 0, min(64, np), x);
-    }
-    M = fmaxf(M, wave_max(ls));
-  }
-  const float Mref = M == -INFINITY ? 0.f : M;
-  for (int k0 = 0; k0 < np; k0 += 64) {
-    const float ls = k0 == 0 ? ls0 : (k0 + lane < np ? pl[slot_of(k0 + lane) * kTileRows + n] : -INFINITY);
-    const float wl = ls == -INFINITY ? 0.f : fast_exp2(ls - Mref);  // piece k0+lane's weight
-    den += wave_sum(wl);
-    const int kn = min(64, np - k0);
-    for (int j0 = 0; j0 < kn; j0 += 8) {
-      if (k0 > 0 || j0 > 0) load8(k0, j0, kn, x);
-      add8(j0, kn, wl, x);
+  for (int tt = 0; tt < kUnitTiles; ++tt) {
+    valid[tt] = (rowgroup * kUnitTiles + tt) * kTileRows + n < G * qn;
+    if (valid[tt]) {
+      ls0[tt] = lane < np ? pl[slot_of(lane, tt) * kTileRows + n] : -INFINITY;
+      load8(tt, 0, 0, min(64, np), x0[tt]);
     }
   }
-  const float inv = den > 0.f ? 1.0f / den : 0.f;
-  uint16_t *orow = a.out + ((size_t)(o + tok) * a.num_q_heads + (size_t)h * G + gq) * D;
-  if constexpr (DPT == 2)
-    reinterpret_cast<uint32_t *>(orow)[lane] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  else
-    orow[lane] = (uint16_t)bf16_bits(acc[0] * inv);
+#pragma unroll
+  for (int tt = 0; tt < kUnitTiles; ++tt) {
+    if (!valid[tt]) break;  // rows of a unit are a prefix of its tiles
+    const int R = (rowgroup * kUnitTiles + tt) * kTileRows + n;
+    const int tok = R / G, gq = R - tok * G;
+    float acc[DPT];
+#pragma unroll
+    for (int t = 0; t < DPT; ++t) acc[t] = 0.f;
+    auto add8 = [&](int j0, int kn, float wl, const float (&x)[8][DPT]) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = min(j0 + u, kn - 1);
+        const float wt = j0 + u < kn ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wl), j)) : 0.f;
+#pragma unroll
+        for (int t = 0; t < DPT; ++t) acc[t] += wt * x[u][t];
+      }
+    };
+    // the common maximum over the pieces' log-sum-exps, 64 pieces per load
+    float M = wave_max(ls0[tt]);
+    for (int k0 = 64; k0 < np; k0 += 64)
+      M = fmaxf(M, wave_max(k0 + lane < np ? pl[slot_of(k0 + lane, tt) * kTileRows + n] : -INFINITY));
+    const float Mref = M == -INFINITY ? 0.f : M;
+    float den = 0.f;
+    for (int k0 = 0; k0 < np; k0 += 64) {
+      const float ls = k0 == 0 ? ls0[tt] : (k0 + lane < np ? pl[slot_of(k0 + lane, tt) * kTileRows + n] : -INFINITY);
+      const float wl = ls == -INFINITY ? 0.f : fast_exp2(ls - Mref);  // piece k0+lane's weight
+      den += wave_sum(wl);
+      const int kn = min(64, np - k0);
+      for (int j0 = 0; j0 < kn; j0 += 8) {
+        if (k0 == 0 && j0 == 0) {
+          add8(0, kn, wl, x0[tt]);
+        } else {
+          float x[8][DPT];
+          load8(tt, k0, j0, kn, x);
+          add8(j0, kn, wl, x);
+        }
+      }
+    }
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    uint16_t *orow = a.out + ((size_t)(o + tok) * a.num_q_heads + (size_t)h * G + gq) * D;
+    if constexpr (DPT == 2)
+      reinterpret_cast<uint32_t *>(orow)[lane] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    else
+      orow[lane] = (uint16_t)bf16_bits(acc[0] * inv);
   }
 }
 
