@@ -91,10 +91,11 @@ def main():
         write_sps_summary(args.sps_summary)
         return
     if args.mfma_summary:
-        write_mfma_summary(args.config, args.mfma_summary)
+        write_mfma_summary(args.config, args.mfma_summary, vt=args.v_layout == "transposed")
         return
     if args.pmc_summary:
-        write_traffic_summary(args.config, *args.pmc_summary, copy_mb=args.calibrate_copy_mb or 1024)
+        write_traffic_summary(args.config, *args.pmc_summary, copy_mb=args.calibrate_copy_mb or 1024,
+                              vt=args.v_layout == "transposed")
         return
 
     if args.gpus != 1:
@@ -371,8 +372,8 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, kv_for_cpu, logits, args.cpu_sample_requests, layers)
 
-    traffic = measured_traffic(name)
-    mfma = measured_mfma(name)
+    traffic = measured_traffic(name, vt)
+    mfma = measured_mfma(name, vt)
     if mfma_bound:
         roof = {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": PEAK_MFMA_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4),
@@ -594,7 +595,16 @@ def _pmc_per_kernel(run_dir, counter):
     return out, last[1]
 
 
-def write_traffic_summary(name, fetch_dir, write_dir, copy_mb):
+def _timed_attention_kernel(per_kernel, vt):
+    """The attention kernel instantiation of the timed V layout (template
+    argument true: transposed V page blocks); the run also launches the other
+    layout's instantiation for its side-by-side timing."""
+    tag = "true>" if vt else "false>"
+    names = [k for k in per_kernel if "verify_attn_kernel" in k and tag in k]
+    return names[0] if names else None
+
+
+def write_traffic_summary(name, fetch_dir, write_dir, copy_mb, vt=True):
     """HBM traffic per launch of the attention kernel: FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch) scaled by what the same counters read for
     the plain device copy of copy_mb MiB that the profiled run ends with."""
@@ -604,11 +614,13 @@ def write_traffic_summary(name, fetch_dir, write_dir, copy_mb):
     copy_bytes = copy_mb * (1 << 20)
     fetch_scale = copy_bytes / (fetch_copy * 1024.0)
     write_scale = copy_bytes / (write_copy * 1024.0)
-    kname = next(k for k in fetch if "verify_attn_kernel" in k)
+    kname = _timed_attention_kernel(fetch, vt)
+    if kname is None:
+        raise SystemExit(f"{fetch_dir}: no attention kernel of the {'transposed' if vt else 'token-major'} layout")
     f_kib = float(np.mean(fetch[kname]))
     w_kib = float(np.mean(write[kname]))
     rec = {
-        "kernel": kname, "workload": name,
+        "kernel": kname, "workload": name, "v_transposed": vt,
         "source_sha256": _sources_sha256(TRAFFIC_SOURCES), "sources": TRAFFIC_SOURCES,
         "fetch_kib_per_launch": round(f_kib, 1), "write_kib_per_launch": round(w_kib, 1),
         "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
@@ -643,7 +655,7 @@ def write_sps_summary(bench_json):
     print(json.dumps(out))
 
 
-def write_mfma_summary(name, pmc_dir):
+def write_mfma_summary(name, pmc_dir, vt=True):
     """MFMA use of the attention kernel from one rocprofv3 --pmc run.
     SQ_VALU_MFMA_BUSY_CYCLES is summed over the SIMDs (a 32x32x16 bf16 MFMA
     counts 32 cycles, so 1024 SIMDs busy all the time is the 2.5 PFLOP/s
@@ -661,7 +673,7 @@ def write_mfma_summary(name, pmc_dir):
             per, _ = _pmc_per_kernel(pmc_dir, c)
         except SystemExit:
             continue
-        k = next((k for k in per if "verify_attn_kernel" in k), None)
+        k = _timed_attention_kernel(per, vt)
         if k is None:
             continue
         kname = k
@@ -670,7 +682,7 @@ def write_mfma_summary(name, pmc_dir):
     if kname is None or any(c not in got for c in need):
         raise SystemExit(f"{pmc_dir}: needs {need} for the attention kernel")
     busy = got["SQ_VALU_MFMA_BUSY_CYCLES"] / (got["GRBM_GUI_ACTIVE"] / MI355X_XCDS * MI355X_SIMDS)
-    rec = {"kernel": kname, "workload": name,
+    rec = {"kernel": kname, "workload": name, "v_transposed": vt,
            "source_sha256": _sources_sha256(TRAFFIC_SOURCES), "sources": TRAFFIC_SOURCES,
            "counters_per_launch": {c: round(v, 1) for c, v in got.items()},
            "simds": MI355X_SIMDS, "xcds": MI355X_XCDS,
@@ -689,14 +701,15 @@ def write_mfma_summary(name, pmc_dir):
     print(json.dumps(rec))
 
 
-def measured_mfma(name):
+def measured_mfma(name, vt):
     """MFMA busy fraction of the attention kernel from the committed counter
-    summary, if taken on this workload and the current kernel sources."""
+    summary, if taken on this workload, V layout and the current kernel
+    sources."""
     path = os.path.join(ROOT, "profiles", f"verify_attn_{name}_mfma.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if _sources_sha256(rec["sources"]) != rec["source_sha256"]:
+    if _sources_sha256(rec["sources"]) != rec["source_sha256"] or rec.get("v_transposed") != vt:
         return None
     return {"busy_frac": rec["mfma_busy_frac"],
             "busy_frac_of_resident_wave_cycles": rec.get("mfma_busy_frac_of_resident_wave_cycles"),
@@ -704,15 +717,15 @@ def measured_mfma(name):
                       % (rec["xcds"], rec["simds"])}
 
 
-def measured_traffic(name):
+def measured_traffic(name, vt):
     """HBM bytes per launch of the attention kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on this
-    workload and on the current kernel sources; else None."""
+    workload, V layout and the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", f"verify_attn_{name}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if _sources_sha256(rec["sources"]) != rec["source_sha256"]:
+    if _sources_sha256(rec["sources"]) != rec["source_sha256"] or rec.get("v_transposed") != vt:
         return None
     return {"read_bytes": rec["read_bytes_per_launch"], "write_bytes": rec["write_bytes_per_launch"],
             "total_bytes": rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"],

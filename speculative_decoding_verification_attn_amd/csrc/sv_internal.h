@@ -53,19 +53,34 @@ struct UnitRec {
 
 struct AttnLayout {
   size_t hdr;        // int32[8]: 0 status bits, 1 active workgroups P, 2 total blocks, 3 units
-  size_t req_meta;   // int32[4][B]: unit base, block base, row tiles, blocks per unit (large batches)
-  size_t units;      // UnitRec[unit_bound]
   size_t wg_start;   // int32[kMaxGrid + 1]: first global block of each workgroup's range
   size_t wg_first;   // int32[kMaxGrid]: first unit of each workgroup's range
   size_t wg_rec;     // UnitRec[kMaxGrid]: a copy of that first unit's record
   size_t merge_rec;  // UnitRec[kMaxGrid]: {cut unit merged here or -1, w0, w1, side of w0}, {o, q, head, tile}
   size_t part_lse;   // float[2*kMaxGrid][kUnitTiles][32] log2-sum-exp of partial rows
   size_t part_o;     // float[2*kMaxGrid][kUnitTiles][32][D] normalised partial outputs
+  size_t units;      // UnitRec[unit_bound]
+  size_t req_meta;   // int32[4][B]: unit base, block base, row tiles, blocks per unit (large batches)
   size_t total;
   int unit_bound;
 };
 
-__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+__host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Every array up to part_o has a fixed size, so its offset is a constant
+// (units follows part_o, whose size depends on head_dim only): the attention
+// kernels address them from the workspace base alone, with no per-array
+// kernel argument held in registers.
+constexpr size_t kWsHdr = 0;
+constexpr size_t kWsWgStart = align256(kWsHdr + 8 * sizeof(int32_t));
+constexpr size_t kWsWgFirst = align256(kWsWgStart + size_t(kMaxGrid + 1) * sizeof(int32_t));
+constexpr size_t kWsWgRec = align256(kWsWgFirst + size_t(kMaxGrid) * sizeof(int32_t));
+constexpr size_t kWsMergeRec = align256(kWsWgRec + size_t(kMaxGrid) * sizeof(UnitRec));
+constexpr size_t kWsPartLse = align256(kWsMergeRec + size_t(kMaxGrid) * sizeof(UnitRec));
+constexpr size_t kWsPartO = align256(kWsPartLse + size_t(2 * kMaxGrid) * kUnitTiles * kTileRows * sizeof(float));
+__host__ __device__ constexpr size_t ws_units_offset(int head_dim) {
+  return align256(kWsPartO + size_t(2 * kMaxGrid) * kUnitTiles * kTileRows * head_dim * sizeof(float));
+}
 
 __host__ __device__ inline AttnLayout attn_layout(int batch, int total_q, int num_q_heads,
                                                   int num_kv_heads, int head_dim) {
@@ -75,16 +90,16 @@ __host__ __device__ inline AttnLayout attn_layout(int batch, int total_q, int nu
   // sum_i ceil(G*q_i/32) <= B + ceil(G*T/32)
   const long long tiles = (long long)batch + ((long long)G * total_q + kTileRows - 1) / kTileRows;
   l.unit_bound = (int)(tiles * num_kv_heads);
-  size_t off = 0;
-  l.hdr = off;        off = align256(off + 8 * sizeof(int32_t));
-  l.req_meta = off;   off = align256(off + size_t(batch) * 16);
+  l.hdr = kWsHdr;
+  l.wg_start = kWsWgStart;
+  l.wg_first = kWsWgFirst;
+  l.wg_rec = kWsWgRec;
+  l.merge_rec = kWsMergeRec;
+  l.part_lse = kWsPartLse;
+  l.part_o = kWsPartO;
+  size_t off = ws_units_offset(head_dim);
   l.units = off;      off = align256(off + size_t(l.unit_bound) * sizeof(UnitRec));
-  l.wg_start = off;   off = align256(off + size_t(kMaxGrid + 1) * sizeof(int32_t));
-  l.wg_first = off;   off = align256(off + size_t(kMaxGrid) * sizeof(int32_t));
-  l.wg_rec = off;     off = align256(off + size_t(kMaxGrid) * sizeof(UnitRec));
-  l.merge_rec = off;  off = align256(off + size_t(kMaxGrid) * sizeof(UnitRec));
-  l.part_lse = off;   off = align256(off + size_t(2 * kMaxGrid) * kUnitTiles * kTileRows * sizeof(float));
-  l.part_o = off;     off = align256(off + size_t(2 * kMaxGrid) * kUnitTiles * kTileRows * head_dim * sizeof(float));
+  l.req_meta = off;   off = align256(off + size_t(batch) * 16);
   l.total = off;
   return l;
 }

@@ -482,18 +482,18 @@ constexpr int kMergeRows = 4;
 template <int D>
 __global__ __launch_bounds__(64 * kMergeRows) void attn_merge_kernel(AttnArgs a) {
   constexpr int DPT = D / 64;
-  const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + a.lay.hdr);
+  const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws + kWsHdr);
   constexpr int kChunks = kTileRows / kMergeRows;
   const int wm = blockIdx.x / kChunks;
-  const UnitRec mr = reinterpret_cast<const UnitRec *>(a.ws + a.lay.merge_rec)[wm];
+  const UnitRec mr = reinterpret_cast<const UnitRec *>(a.ws + kWsMergeRec)[wm];
   if (wm >= hdr[1] || mr.a.x < 0) return;  // no cut unit to merge here
   const int w0 = mr.a.y, w1 = mr.a.z, side0 = mr.a.w;
   const int o = mr.b.x, qn = mr.b.y, h = mr.b.z, rowgroup = mr.b.w;
   const int n = (blockIdx.x - wm * kChunks) * kMergeRows + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int G = a.group;
-  const float *pl = reinterpret_cast<const float *>(a.ws + a.lay.part_lse);
-  const float *po = reinterpret_cast<const float *>(a.ws + a.lay.part_o);
+  const float *pl = reinterpret_cast<const float *>(a.ws + kWsPartLse);
+  const float *po = reinterpret_cast<const float *>(a.ws + kWsPartO);
   // range w0 holds the unit's first block (its first or second partial
   // slot); every later range starts inside the unit (first slot).  No range
   // between w0 and w1 is empty: distinct cost targets inside one unit map to
@@ -669,7 +669,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   __shared__ bf16x8 sm_q[kUnitTiles][KK][64];  // Q^T operands, [tile][kk][lane], shared by the waves
 
   // header words 1..3 are not written by this launch (word 0 only, by atomics)
-  const const_i32_ptr hdr = (const_i32_ptr)(uintptr_t)(a.ws + a.lay.hdr);
+  const const_i32_ptr hdr = (const_i32_ptr)(uintptr_t)(a.ws + kWsHdr);
   const int P = hdr[1];
   // consecutive ranges on the same XCD (workgroups are dealt round-robin to
   // the 8 XCDs), so units that share K/V (tile groups of one head) meet in
@@ -677,8 +677,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   const int bx = blockIdx.x;
   const int wg = (a.grid % 8 == 0) ? (bx % 8) * (a.grid / 8) + bx / 8 : bx;
   if (wg >= P) return;
-  const const_i32_ptr wg_start = (const_i32_ptr)(uintptr_t)(a.ws + a.lay.wg_start);
-  const const_unit_ptr units{(const_i32_ptr)(uintptr_t)(a.ws + a.lay.units)};
+  const const_i32_ptr wg_start = (const_i32_ptr)(uintptr_t)(a.ws + kWsWgStart);
+  const const_unit_ptr units{(const_i32_ptr)(uintptr_t)(a.ws + ws_units_offset(D))};
   const int n_units = hdr[3];
 
   const int lane = threadIdx.x & 63;
@@ -695,8 +695,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   auto run_range = [&](const int w) {
     const int start = wg_start[w];
     const int end = wg_start[w + 1];
-    const int first_unit = ((const_i32_ptr)(uintptr_t)(a.ws + a.lay.wg_first))[w];
-    const UnitRec rec0 = const_unit_ptr{(const_i32_ptr)(uintptr_t)(a.ws + a.lay.wg_rec)}[w];
+    const int first_unit = ((const_i32_ptr)(uintptr_t)(a.ws + kWsWgFirst))[w];
+    const UnitRec rec0 = const_unit_ptr{(const_i32_ptr)(uintptr_t)(a.ws + kWsWgRec)}[w];
     if (first_unit < 0 || first_unit >= n_units || start >= end) return;  // not for a consistent plan
 
     // Two walks over the same pieces: the consumer at the round being
@@ -723,7 +723,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
       bool parents_ok;
       const uint64_t anc_all = ancestor_mask(a.tree_parent, Wc.ot, Wc.s + Wc.qn, lane, &parents_ok);
       if (!parents_ok && threadIdx.x == 0 && Wc.ps == Wc.ub && Wc.h == 0 && Wc.rg == 0)
-        atomicOr(reinterpret_cast<unsigned *>(a.ws + a.lay.hdr), SV_DEV_BAD_PARENT);
+        atomicOr(reinterpret_cast<unsigned *>(a.ws + kWsHdr), SV_DEV_BAD_PARENT);
       nt = min(kUnitTiles, (G * Wc.qn + kTileRows - 1) / kTileRows - Wc.rg * kUnitTiles);
 #pragma unroll
       for (int tt = 0; tt < kUnitTiles; ++tt) {
@@ -855,7 +855,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
             }
           } else {
             const size_t slot = (2 * (size_t)w + side) * kUnitTiles + tt;
-            float *po = reinterpret_cast<float *>(a.ws + a.lay.part_o) + (slot * kTileRows + n) * D + d0;
+            float *po = reinterpret_cast<float *>(a.ws + kWsPartO) + (slot * kTileRows + n) * D + d0;
             if constexpr (VT) {
 #pragma unroll
               for (int c = 0; c < DPL; ++c)
@@ -868,7 +868,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
                     make_float4(ov[j] * inv, ov[j + 1] * inv, ov[j + 2] * inv, ov[j + 3] * inv);
             }
             if (wave == 0 && hh == 0) {
-              float *pl = reinterpret_cast<float *>(a.ws + a.lay.part_lse);
+              float *pl = reinterpret_cast<float *>(a.ws + kWsPartLse);
               pl[slot * kTileRows + n] = Lsum > 0.f ? Mref + fast_log2(Lsum) : -INFINITY;
             }
           }
@@ -919,7 +919,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   };
 
   run_range(wg);
-  if (bad_page) atomicOr(reinterpret_cast<unsigned *>(a.ws + a.lay.hdr), SV_DEV_BAD_PAGE);
+  if (bad_page) atomicOr(reinterpret_cast<unsigned *>(a.ws + kWsHdr), SV_DEV_BAD_PAGE);
 }
 
 }  // namespace
