@@ -286,11 +286,13 @@ typedef const __attribute__((address_space(4))) int32_t *const_i32_ptr;
 // (the block index is wave-uniform).  Pages past the request's last page, and
 // ids outside [0, num_pages), are replaced by `safe` (a valid page) so every
 // load below stays in bounds; *bad records the latter.
-__device__ inline int2 block_pages(const_i32_ptr bt, int b, int npages, int num_pages, int safe,
-                                   bool *bad) {
+__device__ inline int2 block_pages(const_i32_ptr bt, int b, int npages, int num_pages, bool *bad) {
   const int lp = 2 * b;
   const int i0 = min(lp, npages - 1), i1 = min(lp + 1, npages - 1);
+  // the three entries are read together: one round trip
   int p0 = bt[i0], p1 = bt[i1];
+  int safe = bt[0];
+  if (safe < 0 || safe >= num_pages) safe = 0;
   const bool bad0 = p0 < 0 || p0 >= num_pages, bad1 = p1 < 0 || p1 >= num_pages;
   *bad = *bad || (lp < npages && bad0) || (lp + 1 < npages && bad1);
   if (lp >= npages || bad0) p0 = safe;
@@ -608,7 +610,7 @@ struct Walk {
   int ps, pe;  // global blocks [ps, pe) of the unit processed by this workgroup
   int g0, nr;  // its rounds [g0, g0 + nr)
   bool has_next;
-  UnitRec next;  // record of unit u+1 (fetched on entry, needed at the next advance)
+  UnitRec next;  // record of unit u+1 (fetched after entry, needed at the next advance)
 };
 
 __device__ inline void walk_enter(Walk &W, int u, const UnitRec &r, int start, int end, int g0,
@@ -622,17 +624,18 @@ __device__ inline void walk_enter(Walk &W, int u, const UnitRec &r, int start, i
   W.g0 = g0;
   W.nr = (W.pe - W.ps + kAttnWaves - 1) / kAttnWaves;
   W.has_next = W.pe < end && u + 1 < n_units;
-  if (W.has_next) W.next = units[u + 1];
 }
 
 // Moves the walk forward until round g lies in its piece; false if g is past
-// the workgroup's last piece (the walk then stays on the last piece).
+// the workgroup's last piece (the walk then stays on the last piece).  Each
+// unit entered fetches the record of the unit after it.
 __device__ inline bool walk_to(Walk &W, int g, int start, int end, const_unit_ptr units,
                                int n_units) {
   while (g >= W.g0 + W.nr) {
     if (!W.has_next) return false;
     const UnitRec r = W.next;
     walk_enter(W, W.u + 1, r, start, end, W.g0 + W.nr, units, n_units);
+    if (W.has_next) W.next = units[W.u + 1];
   }
   return true;
 }
@@ -676,10 +679,22 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   // one L2
   const int bx = blockIdx.x;
   const int wg = (a.grid % 8 == 0) ? (bx % 8) * (a.grid / 8) + bx / 8 : bx;
-  if (wg >= P) return;
   const const_i32_ptr wg_start = (const_i32_ptr)(uintptr_t)(a.ws + kWsWgStart);
   const const_unit_ptr units{(const_i32_ptr)(uintptr_t)(a.ws + ws_units_offset(D))};
+  // Everything the range needs first is read in one round trip, before the
+  // range count is checked: the per-workgroup arrays have kMaxGrid (+1)
+  // entries and wg < grid <= kMaxGrid, so these reads stay in bounds.
   const int n_units = hdr[3];
+  const int start0 = wg_start[wg];
+  const int end0 = wg_start[wg + 1];
+  const int first0 = ((const_i32_ptr)(uintptr_t)(a.ws + kWsWgFirst))[wg];
+  const UnitRec rec0 = const_unit_ptr{(const_i32_ptr)(uintptr_t)(a.ws + kWsWgRec)}[wg];
+  // one test of all of them (a consistent plan gives every range that holds
+  // blocks a first unit of a request i >= 0 with at least one block, whose
+  // rows start at a verify token s >= 0)
+  if ((wg >= P) | (first0 < 0) | (first0 >= n_units) | (start0 >= end0) | (rec0.a.x < 0) | (rec0.b.w < 1) |
+      (rec0.c.x < 0))
+    return;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -688,16 +703,11 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   const size_t page_stride = (size_t)a.num_kv_heads * kPage * D;
   bool bad_page = false;
 
-  // The workgroup's block range w.  (Written as a function of w, whose
-  // record is read here rather than at kernel entry: the compiler then keeps
-  // far fewer scalars live through the round loop, and spills fewer of them
-  // to vector-register lanes.)
-  auto run_range = [&](const int w) {
-    const int start = wg_start[w];
-    const int end = wg_start[w + 1];
-    const int first_unit = ((const_i32_ptr)(uintptr_t)(a.ws + kWsWgFirst))[w];
-    const UnitRec rec0 = const_unit_ptr{(const_i32_ptr)(uintptr_t)(a.ws + kWsWgRec)}[w];
-    if (first_unit < 0 || first_unit >= n_units || start >= end) return;  // not for a consistent plan
+  // The workgroup's block range w, [start, end), whose first unit and its
+  // record are given.  (Written as a function: the compiler then keeps far
+  // fewer scalars live through the round loop, and spills fewer of them to
+  // vector-register lanes.)
+  auto run_range = [&](const int w, const int start, const int end, const int first_unit, const UnitRec &rec0) {
 
     // Two walks over the same pieces: the consumer at the round being
     // computed, the producer two rounds ahead (it fetches page ids for round
@@ -776,9 +786,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
       const int lmax = Wp.pe - Wp.ub - 1;  // a wave without a block re-reads the piece's last one
       const const_i32_ptr bt = (const_i32_ptr)(uintptr_t)(a.block_tables + (size_t)Wp.i * a.max_blocks);
       const int npages = (Wp.L + Wp.s + Wp.qn + kPage - 1) / kPage;
-      int safe = bt[0];
-      if (safe < 0 || safe >= a.num_pages) safe = 0;
-      pg_next = block_pages(bt, min(lbk, lmax), npages, a.num_pages, safe, &bad_page);
+      pg_next = block_pages(bt, min(lbk, lmax), npages, a.num_pages, &bad_page);
       h_next = Wp.h;
     };
     auto produce = [&](KVBlock<D, VT> &buf) {
@@ -908,6 +916,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
     KVBlock<D, VT> A, Bb;
     fetch_pages(0);
     produce(A);
+    if (Wc.has_next) {  // the first unit's successor, read once the first K/V loads are out
+      Wc.next = units[Wc.u + 1];
+      Wp.next = Wc.next;
+    }
     fetch_pages(1);
     enter_unit();
     __syncthreads();
@@ -918,7 +930,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
     }
   };
 
-  run_range(wg);
+  run_range(wg, start0, end0, first0, rec0);
   if (bad_page) atomicOr(reinterpret_cast<unsigned *>(a.ws + kWsHdr), SV_DEV_BAD_PAGE);
 }
 
