@@ -131,3 +131,45 @@ def test_compaction_leaves_a_broken_request_untouched(vt):
     new = new.cpu().numpy()
     assert new[1] == -1 and new[0] == new_ref[0] and new[2] == new_ref[2]
     assert np.array_equal(bf16_dev_to_u16(kd), k_ref) and np.array_equal(v_from_dev(vd, vt), v_ref)
+
+
+def test_acceptance_with_a_broken_request():
+    """spec_accept: a parent after its child in one tree request, then a request of
+    65 rows: the status bit is set and every other request's argmax, acceptance,
+    path and tokens equal the oracle's."""
+    trees = [W.draw_tree(np.random.Generator(np.random.PCG64(930 + i)), n, min(n - 1, 6), 4, 4)
+             for i, n in enumerate([11, 16, 8])]
+    case = W.make_custom(931, context_lens=[10, 20, 30], tree_parents=trees, hq=4, hkv=2, d=64, vocab=3000,
+                         tree_match=(0.8, 0.3))
+    dc = DevCase(case, False)
+    t_ref = oracle.argmax(case.logits)
+    acc_ref, path_ref, tok_ref = oracle.accept(case.draft_tokens, t_ref, case.cu_q, case.tree_parent)
+    par = case.tree_parent.copy()
+    o1 = int(case.cu_q[1])
+    par[o1 + 4] = 9
+    ws = torch.empty(ops.spec_accept_workspace_size(case.batch, case.total_q, case.vocab), dtype=torch.uint8,
+                     device=dc.logits.device)
+    note("[gpu] spec_accept with a parent after its child in request 1")
+    t, acc, path, tok = [x.cpu().numpy() for x in ops.spec_accept(dc.logits, dc.draft, dc.cu, i32(par),
+                                                                  workspace=ws)]
+    assert ops.spec_accept_device_status(ws) & ops.DEV_BAD_PARENT
+    assert np.array_equal(t, t_ref)  # the argmax of every row is still exact
+    rows = _rows(case, [0, 2])
+    assert acc[0] == acc_ref[0] and acc[2] == acc_ref[2]
+    assert np.array_equal(path[rows], path_ref[rows]) and np.array_equal(tok[rows], tok_ref[rows])
+    # a chain batch whose middle request claims 65 rows
+    case = _chain_case(q_lens=(4, 64, 1), ctx=(30, 50, 20))
+    dc = DevCase(case, False)
+    t_ref = oracle.argmax(case.logits)
+    acc_ref, path_ref, tok_ref = oracle.accept(case.draft_tokens, t_ref, case.cu_q, None)
+    cu = case.cu_q.copy()
+    cu[2] += 1
+    ws = torch.empty(ops.spec_accept_workspace_size(case.batch, case.total_q, case.vocab), dtype=torch.uint8,
+                     device=dc.logits.device)
+    note("[gpu] spec_accept with 65 rows in request 1")
+    t, acc, path, tok = [x.cpu().numpy() for x in ops.spec_accept(dc.logits, dc.draft, i32(cu), None,
+                                                                  workspace=ws)]
+    assert ops.spec_accept_device_status(ws) & ops.DEV_TOO_MANY_TOKENS
+    rows = _rows(case, [0])
+    assert acc[0] == acc_ref[0]
+    assert np.array_equal(path[rows], path_ref[rows]) and np.array_equal(tok[rows], tok_ref[rows])
