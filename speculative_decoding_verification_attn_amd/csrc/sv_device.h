@@ -85,14 +85,20 @@ __device__ inline uint32_t pack_hi16(uint32_t x0, uint32_t x1) {
 // the whole wave; lanes >= q return 0.  *ok is false if the parent array
 // breaks root = -1, 0 <= parent[j] < j.  Pointer jumping: after round r a
 // lane knows its ancestors closer than 2^r, so 6 rounds cover depth <= 63.
-__device__ inline uint64_t ancestor_mask(const int32_t *tree_parent, int o, int q, int lane,
-                                         bool *ok) {
-  if (tree_parent == nullptr) {
+//
+// The one memory read, the lane's parent entry, is a function of its own so
+// that a caller can issue it early and pass the value to ancestor_mask_of.
+__device__ inline int tree_parent_of(const int32_t *tree_parent, int o, int q, int lane) {
+  return (tree_parent != nullptr && lane < q) ? tree_parent[o + lane] : -1;
+}
+
+__device__ inline uint64_t ancestor_mask_of(bool is_tree, int par, int q, int lane, bool *ok) {
+  if (!is_tree) {
     *ok = true;
     if (lane >= q) return 0ull;
     return lane == 63 ? ~0ull : ((2ull << lane) - 1ull);
   }
-  int par = lane < q ? tree_parent[o + lane] : -1;
+  if (lane >= q) par = -1;
   bool good = lane >= q || (lane == 0 ? par == -1 : (par >= 0 && par < lane));
   if (!good) par = -1;
   *ok = __all(good);
@@ -109,6 +115,10 @@ __device__ inline uint64_t ancestor_mask(const int32_t *tree_parent, int o, int 
     }
   }
   return anc;
+}
+
+__device__ inline uint64_t ancestor_mask(const int32_t *tree_parent, int o, int q, int lane, bool *ok) {
+  return ancestor_mask_of(tree_parent != nullptr, tree_parent_of(tree_parent, o, q, lane), q, lane, ok);
 }
 
 // Exclusive prefix sum over a 1024-thread block; *total receives the sum.

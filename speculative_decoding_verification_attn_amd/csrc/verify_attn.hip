@@ -50,6 +50,7 @@
 //                                               consecutive keys).
 // Both accumulators keep a query row per lane, so the softmax statistics of a
 // row live in one lane pair (lanes n and n+32) and never need a transpose.
+#include <type_traits>
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -727,11 +728,18 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
     int qpf_u = -1;
 
     // enter the consumer's unit: ancestor masks of the lane's rows and Q in LDS
-    auto enter_unit = [&]() {
+    // The range's first unit has its parent entries and the Q chunks of its
+    // further tiles read at kernel entry (pre_*), so those round trips overlap
+    // the page-id reads; later units read them at entry.
+    int pre_par = -1;
+    bf16x8 pre_q[kUnitTiles - 1][KQ];
+    auto enter_unit = [&](auto first) {
+      constexpr bool kFirst = decltype(first)::value;
       // masks of the verify tokens [0, s+q) (keys L .. L+s+q-1); row r of the
       // unit's tiles is token s + r / G
       bool parents_ok;
-      const uint64_t anc_all = ancestor_mask(a.tree_parent, Wc.ot, Wc.s + Wc.qn, lane, &parents_ok);
+      const int par = kFirst ? pre_par : tree_parent_of(a.tree_parent, Wc.ot, Wc.s + Wc.qn, lane);
+      const uint64_t anc_all = ancestor_mask_of(a.tree_parent != nullptr, par, Wc.s + Wc.qn, lane, &parents_ok);
       if (!parents_ok && threadIdx.x == 0 && Wc.ps == Wc.ub && Wc.h == 0 && Wc.rg == 0)
         atomicOr(reinterpret_cast<unsigned *>(a.ws + kWsHdr), SV_DEV_BAD_PARENT);
       nt = min(kUnitTiles, (G * Wc.qn + kTileRows - 1) / kTileRows - Wc.rg * kUnitTiles);
@@ -758,7 +766,12 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
       for (int tt = 1; tt < kUnitTiles; ++tt) {
         if (tt >= nt) break;
         bf16x8 qc[KQ];
-        load_q_chunks<D>(a, Wc, tt, wave, n, hh, qc);
+        if constexpr (kFirst) {
+#pragma unroll
+          for (int j = 0; j < KQ; ++j) qc[j] = pre_q[tt - 1][j];
+        } else {
+          load_q_chunks<D>(a, Wc, tt, wave, n, hh, qc);
+        }
 #pragma unroll
         for (int j = 0; j < KQ; ++j) sm_q[tt][wave * KQ + j][lane] = qc[j];
       }
@@ -904,7 +917,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
         finish_unit();
         if (!Wc.has_next) return true;
         walk_to(Wc, g + 1, start, end, units, n_units);
-        enter_unit();
+        enter_unit(std::false_type{});
         __syncthreads();  // the next unit's Q is in LDS; sm_o may be reused
         load_qop();
       }
@@ -914,6 +927,13 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
     // the first K/V loads go out before the Q operands are staged, so the
     // two memory round trips overlap
     KVBlock<D, VT> A, Bb;
+    // the first unit's parent entries and Q chunks (tiles with no rows load
+    // nothing) go out before the page ids are requested
+    pre_par = tree_parent_of(a.tree_parent, Wc.ot, Wc.s + Wc.qn, lane);
+    load_q_chunks<D>(a, Wc, 0, wave, n, hh, qpf);
+    qpf_u = Wc.u;
+#pragma unroll
+    for (int tt = 1; tt < kUnitTiles; ++tt) load_q_chunks<D>(a, Wc, tt, wave, n, hh, pre_q[tt - 1]);
     fetch_pages(0);
     produce(A);
     if (Wc.has_next) {  // the first unit's successor, read once the first K/V loads are out
@@ -921,7 +941,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
       Wp.next = Wc.next;
     }
     fetch_pages(1);
-    enter_unit();
+    enter_unit(std::true_type{});
     __syncthreads();
     load_qop();
     for (int g = 0;; g += 2) {
