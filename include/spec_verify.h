@@ -182,6 +182,23 @@ int spec_verify_attn_run_vt(const void *q, const void *k_cache, const void *v_ca
 int spec_verify_attn_device_status(const void *workspace, uint32_t *flags, void *stream);
 
 /*
+ * Diagnostic: the attention kernel's phase timeline.  Only the trace build of
+ * the library (libspecverify_trace.so, compiled with SV_PHASE_TRACE) records
+ * one; in it, every wave of every workgroup range stores up to 2048 64-bit
+ * words (shader-clock time << 8 | phase code) into a static device array of
+ * the library, overwriting it on each attention launch.  Waits for the
+ * device, then copies min(bytes, *total_bytes) of that array into host_dst
+ * (host pointer; may be NULL with bytes = 0) and, if clear != 0, zeroes it.
+ * *total_bytes (may be NULL) receives the array's size.  Layout and codes:
+ * word (w * 4 + wave) * 2048 + i is event i of that wave of range w (w < 512); codes are
+ * 1 range header read, 2 first unit ready, 3 round start, 4 next loads
+ * issued, 5 round data in, 6 block computed, 7 unit written, 8 next unit
+ * entered, 9 range done.  Errors: SV_ERR_UNSUPPORTED in the production build,
+ * SV_ERR_HIP.
+ */
+int spec_verify_attn_phase_trace(void *host_dst, size_t bytes, int clear, size_t *total_bytes);
+
+/*
  * For callers that cannot allocate device memory (code under stream or graph
  * capture, tight serving loops, harnesses that forbid allocation):
  * spec_verify_attn with no workspace argument.  The arguments and the result

@@ -456,6 +456,15 @@ int spec_verify_attn_device_status(const void *workspace, uint32_t *flags, void 
   return read_status(workspace, 0, flags, stream);
 }
 
+int spec_verify_attn_phase_trace(void *host_dst, size_t bytes, int clear, size_t *total_bytes) {
+  size_t total = 0;
+  const hipError_t e = sv::verify_attn_phase_trace(host_dst, bytes, clear != 0, &total);
+  if (total_bytes) *total_bytes = total;
+  if (e == hipErrorNotSupported) return fail(SV_ERR_UNSUPPORTED, "not a phase-trace build");
+  if (e != hipSuccess) return fail(SV_ERR_HIP, "phase trace: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t spec_accept_workspace_size(int batch, int total_q, int vocab) {
   if (batch < 0 || total_q < 0 || vocab <= 0) return 0;
   return sv::accept_layout(batch, total_q, vocab).total;

@@ -126,6 +126,10 @@ struct AttnArgs {
 
 void launch_verify_attn_plan(const AttnArgs &a, hipStream_t stream);
 void launch_verify_attn_run(const AttnArgs &a, int head_dim, hipStream_t stream);
+// Phase timeline of the attention kernel (diagnostic builds only): copies up
+// to `bytes` of it to host memory and/or clears it.  Returns hipErrorNotSupported
+// in the production build.
+hipError_t verify_attn_phase_trace(void *host_dst, size_t bytes, bool clear, size_t *total);
 
 // ---------------------------------------------------------------------------
 // Acceptance

@@ -659,6 +659,39 @@ __device__ inline void load_q_chunks(const AttnArgs &a, const Walk &W, int tt, i
     qc[j] = row_ok ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * (wave * KQ + j)) : bf16x8{};
 }
 
+// --------------------------------------------------------------------------
+// Phase timeline, compiled in diagnostic builds only (SV_PHASE_TRACE; the
+// library is then libspecverify_trace.so).  Lane 0 of every wave of range w
+// stores up to kPhaseEvents words (time << 8 | code) at
+// g_phase_trace[(w * kAttnWaves + wave) * kPhaseEvents + i], time read with
+// s_memtime (shader clock, counted per XCD, so only differences within one
+// wave are meaningful).  Codes:
+//   1 range header read      2 first unit's Q operands in registers
+//   3 round start            4 next round's K/V loads issued
+//   5 this round's K/V in    6 block computed (or skipped)
+//   7 unit merged and written  8 next unit entered      9 range done
+// To tell the wait for data from the arithmetic, a trace build waits for the
+// whole of a round's K/V before its block (the production build waits load by
+// load), and requests the page ids of round g+2 after the block, since every
+// timestamp read would otherwise wait for them; both shift the schedule
+// slightly.
+#ifdef SV_PHASE_TRACE
+constexpr int kPhaseEvents = 2048;
+__device__ uint64_t g_phase_trace[(size_t)kMaxGrid * kAttnWaves * kPhaseEvents];
+#define SV_MARK(code)                                                                              \
+  do {                                                                                             \
+    const uint64_t sv_t = __builtin_amdgcn_s_memtime();                                            \
+    if (lane == 0 && sv_ev < kPhaseEvents)                                                         \
+      g_phase_trace[((size_t)wg * kAttnWaves + wave) * kPhaseEvents + sv_ev] = (sv_t << 8) | (code); \
+    ++sv_ev;                                                                                       \
+  } while (0)
+#else
+#define SV_MARK(code) ((void)0)
+#endif
+
+// s_waitcnt operand for vmcnt(n) with the other counters unconstrained
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 template <int D, bool VT>
 __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu(1, 1))) void verify_attn_kernel(AttnArgs a) {
   constexpr int DPL = D / 32;  // contiguous d per lane of a V row; O^T tiles
@@ -700,6 +733,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, hh = lane >> 5;
+#ifdef SV_PHASE_TRACE
+  int sv_ev = 0;
+#endif
+  SV_MARK(1);
   const int G = a.group;
   const size_t page_stride = (size_t)a.num_kv_heads * kPage * D;
   bool bad_page = false;
@@ -900,8 +937,11 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
     // one round g: issue the loads of round g+1 into `into` (freed by round
     // g-1), compute round g from `cur`; true once the last unit is finished
     auto round = [&](int g, KVBlock<D, VT> &cur, KVBlock<D, VT> &into) -> bool {
+      SV_MARK(3);
       produce(into);
+#ifndef SV_PHASE_TRACE
       fetch_pages(g + 2);
+#endif
       // prefetch the next unit's first Q tile once this unit is under way
       if (Wc.has_next && qpf_u != Wc.u + 1 && g == Wc.g0 + 1) {
         Walk Wn;
@@ -910,16 +950,29 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
         qpf_u = Wc.u + 1;
       }
       const int gb = Wc.ps + kAttnWaves * (g - Wc.g0) + wave;  // this wave's global block
+      SV_MARK(4);
+#ifdef SV_PHASE_TRACE
+      // this round's K/V (the loads before the next round's); a Q prefetch
+      // issued this round makes it wait for two of the next round's loads too
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(KK + (VT ? D / 16 : 16)));
+#endif
+      SV_MARK(5);
       if (gb < Wc.pe)
         compute_block<D, VT>(cur, qop, nt, (gb - Wc.ub) * kBlockKeys, Wc.L, nk, anc, hh,
                          a.scale_log2, m, l, acc);
+      SV_MARK(6);
+#ifdef SV_PHASE_TRACE
+      fetch_pages(g + 2);
+#endif
       if (g + 1 == Wc.g0 + Wc.nr) {
         finish_unit();
+        SV_MARK(7);
         if (!Wc.has_next) return true;
         walk_to(Wc, g + 1, start, end, units, n_units);
         enter_unit(std::false_type{});
         __syncthreads();  // the next unit's Q is in LDS; sm_o may be reused
         load_qop();
+        SV_MARK(8);
       }
       return false;
     };
@@ -944,6 +997,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
     enter_unit(std::true_type{});
     __syncthreads();
     load_qop();
+    SV_MARK(2);
     for (int g = 0;; g += 2) {
       if (round(g, A, Bb)) break;
       if (round(g + 1, Bb, A)) break;
@@ -951,10 +1005,34 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
   };
 
   run_range(wg, start0, end0, first0, rec0);
+  SV_MARK(9);
   if (bad_page) atomicOr(reinterpret_cast<unsigned *>(a.ws + kWsHdr), SV_DEV_BAD_PAGE);
 }
 
 }  // namespace
+
+hipError_t verify_attn_phase_trace(void *host_dst, size_t bytes, bool clear, size_t *total) {
+#ifdef SV_PHASE_TRACE
+  *total = sizeof(g_phase_trace);
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess && host_dst != nullptr && bytes > 0)
+    e = hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(g_phase_trace), bytes < *total ? bytes : *total, 0,
+                            hipMemcpyDeviceToHost);
+  if (e == hipSuccess && clear) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_phase_trace));
+    if (e == hipSuccess) e = hipMemset(p, 0, *total);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+  }
+  return e;
+#else
+  (void)host_dst;
+  (void)bytes;
+  (void)clear;
+  *total = 0;
+  return hipErrorNotSupported;
+#endif
+}
 
 void launch_verify_attn_plan(const AttnArgs &a, hipStream_t stream) {
   attn_plan_kernel<<<1, kPlanThreads, 0, stream>>>(a);

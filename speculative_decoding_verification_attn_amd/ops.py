@@ -50,7 +50,8 @@ EXPORTED = ["spec_verify_attn_workspace_size", "spec_verify_attn", "spec_verify_
             "spec_chunk_start", "spec_accept_chunk_workspace_size", "spec_accept_chunk", "spec_verify_budget",
             "spec_accept_compact_workspace_size", "spec_accept_compact", "spec_accept_compact_vt",
             "spec_accept_stochastic_workspace_size", "spec_accept_stochastic",
-            "spec_accept_stochastic_device_status", "spec_hbm_read_probe", "spec_verify_attn_noalloc"]
+            "spec_accept_stochastic_device_status", "spec_hbm_read_probe", "spec_verify_attn_noalloc",
+            "spec_verify_attn_phase_trace"]
 
 NOALLOC_SCRATCH_BYTES = 40 << 20  # SV_NOALLOC_SCRATCH_BYTES
 
@@ -82,6 +83,8 @@ def load_library():
     lib.spec_verify_attn_plan.restype = I
     lib.spec_verify_attn_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
     lib.spec_verify_attn_device_status.restype = I
+    lib.spec_verify_attn_phase_trace.argtypes = [P, SZ, I, ctypes.POINTER(ctypes.c_size_t)]
+    lib.spec_verify_attn_phase_trace.restype = I
     lib.spec_accept_workspace_size.argtypes = [I, I, I]
     lib.spec_accept_workspace_size.restype = SZ
     lib.spec_accept.argtypes = [P, I, P, P, P, I, I, P, P, P, P, P, SZ, P]
@@ -294,6 +297,20 @@ def spec_verify_attn_device_status(workspace, stream=None) -> int:
     _check(load_library().spec_verify_attn_device_status(_ptr(workspace), ctypes.byref(flags),
                                                          _stream(stream)))
     return int(flags.value)
+
+
+def spec_verify_attn_phase_trace(clear: bool = True):
+    """The attention kernel's phase timeline from the trace build of the
+    library (libspecverify_trace.so): a uint64 numpy array of
+    [512 ranges, 4 waves, 2048 events], each event (shader-clock time << 8 | code);
+    zeroed afterwards if `clear`.  SV_ERR_UNSUPPORTED from the production build."""
+    import numpy as np
+    lib = load_library()
+    total = ctypes.c_size_t(0)
+    _check(lib.spec_verify_attn_phase_trace(None, 0, 0, ctypes.byref(total)))
+    buf = np.zeros(total.value // 8, dtype=np.uint64)
+    _check(lib.spec_verify_attn_phase_trace(buf.ctypes.data, total.value, int(clear), ctypes.byref(total)))
+    return buf.reshape(-1, 4, 2048)
 
 
 def spec_accept_workspace_size(batch, total_q, vocab) -> int:

@@ -256,3 +256,17 @@ def test_noalloc_host_checks(lib):
     hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
                             "spec_verify.h")).read()
     assert "#define SV_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)" in hdr and ops.NOALLOC_SCRATCH_BYTES == 40 << 20
+
+
+def test_phase_trace_only_in_the_trace_build(lib):
+    """The production library answers the phase-trace call with
+    SV_ERR_UNSUPPORTED (no HIP call is made); the trace build, when present,
+    exports every declared function too."""
+    total = ctypes.c_size_t(123)
+    assert lib.spec_verify_attn_phase_trace(None, 0, 0, ctypes.byref(total)) == 3  # SV_ERR_UNSUPPORTED
+    assert total.value == 0
+    from speculative_decoding_verification_attn_amd import build
+    if os.path.exists(build.TRACE_LIB):
+        tlib = ctypes.CDLL(build.TRACE_LIB)
+        for n in declared_functions():
+            assert hasattr(tlib, n), n
