@@ -285,8 +285,9 @@ typedef const __attribute__((address_space(4))) int32_t *const_i32_ptr;
 
 // Physical pages of the two logical pages of block b, read with scalar loads
 // (the block index is wave-uniform).  Pages past the request's last page, and
-// ids outside [0, num_pages), are replaced by `safe` (a valid page) so every
-// load below stays in bounds; *bad records the latter.
+// ids outside [0, num_pages), are replaced by a valid page (the request's
+// first page if its id is valid, else page 0) so every load below stays in
+// bounds; *bad records the latter.
 __device__ inline int2 block_pages(const_i32_ptr bt, int b, int npages, int num_pages, bool *bad) {
   const int lp = 2 * b;
   const int i0 = min(lp, npages - 1), i1 = min(lp + 1, npages - 1);
@@ -977,11 +978,11 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
       return false;
     };
 
-    // the first K/V loads go out before the Q operands are staged, so the
-    // two memory round trips overlap
+    // The first unit's parent entries and Q chunks (tiles with no rows load
+    // nothing) go out first, then the page ids are requested and the first
+    // K/V loads issued; the Q operands are staged through LDS after that, so
+    // the memory round trips overlap.
     KVBlock<D, VT> A, Bb;
-    // the first unit's parent entries and Q chunks (tiles with no rows load
-    // nothing) go out before the page ids are requested
     pre_par = tree_parent_of(a.tree_parent, Wc.ot, Wc.s + Wc.qn, lane);
     load_q_chunks<D>(a, Wc, 0, wave, n, hh, qpf);
     qpf_u = Wc.u;
