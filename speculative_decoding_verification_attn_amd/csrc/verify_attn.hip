@@ -762,21 +762,31 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
     int nk = 0;
     float m[kUnitTiles], l[kUnitTiles];
     floatx16 acc[kUnitTiles][DPL];
-    bf16x8 qpf[KQ];    // tile-0 Q chunks prefetched for unit qpf_u
+    bf16x8 qpf[kUnitTiles][KQ];  // this wave's Q chunks of every tile of unit qpf_u, read ahead
+    int par_pf = -1;             // and the lane's parent entry of that unit
     int qpf_u = -1;
 
     // enter the consumer's unit: ancestor masks of the lane's rows and Q in LDS
-    // The range's first unit has its parent entries and the Q chunks of its
-    // further tiles read at kernel entry (pre_*), so those round trips overlap
-    // the page-id reads; later units read them at entry.
-    int pre_par = -1;
-    bf16x8 pre_q[kUnitTiles - 1][KQ];
-    auto enter_unit = [&](auto first) {
-      constexpr bool kFirst = decltype(first)::value;
+    // A unit's parent entries and Q chunks are read ahead: the range's first
+    // unit's at kernel entry, so those round trips overlap the page-id reads,
+    // a later unit's in the second round of the unit before it, ahead of that
+    // round's K/V loads.  Loads retire in order, so a value read at entry
+    // itself would make the wave wait for the next round's K/V loads too (a
+    // whole memory round trip per unit); only a unit of one round reads them
+    // at entry.
+    auto enter_unit = [&]() {
+      if (qpf_u != Wc.u) {
+        // a unit of one round: read now, and waited for here, so that the
+        // path below (and its registers) is the same as after a prefetch
+        par_pf = tree_parent_of(a.tree_parent, Wc.ot, Wc.s + Wc.qn, lane);
+#pragma unroll
+        for (int tt = 0; tt < kUnitTiles; ++tt) load_q_chunks<D>(a, Wc, tt, wave, n, hh, qpf[tt]);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      }
       // masks of the verify tokens [0, s+q) (keys L .. L+s+q-1); row r of the
       // unit's tiles is token s + r / G
       bool parents_ok;
-      const int par = kFirst ? pre_par : tree_parent_of(a.tree_parent, Wc.ot, Wc.s + Wc.qn, lane);
+      const int par = par_pf;
       const uint64_t anc_all = ancestor_mask_of(a.tree_parent != nullptr, par, Wc.s + Wc.qn, lane, &parents_ok);
       if (!parents_ok && threadIdx.x == 0 && Wc.ps == Wc.ub && Wc.h == 0 && Wc.rg == 0)
         atomicOr(reinterpret_cast<unsigned *>(a.ws + kWsHdr), SV_DEV_BAD_PARENT);
@@ -796,23 +806,13 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
         for (int c = 0; c < DPL; ++c) acc[tt][c] = floatx16{};
       }
       nk = Wc.L + Wc.s + Wc.qn;
-      if (qpf_u != Wc.u) load_q_chunks<D>(a, Wc, 0, wave, n, hh, qpf);
 #pragma unroll
-      for (int j = 0; j < KQ; ++j) sm_q[0][wave * KQ + j][lane] = qpf[j];
-      qpf_u = -1;
-#pragma unroll
-      for (int tt = 1; tt < kUnitTiles; ++tt) {
+      for (int tt = 0; tt < kUnitTiles; ++tt) {
         if (tt >= nt) break;
-        bf16x8 qc[KQ];
-        if constexpr (kFirst) {
 #pragma unroll
-          for (int j = 0; j < KQ; ++j) qc[j] = pre_q[tt - 1][j];
-        } else {
-          load_q_chunks<D>(a, Wc, tt, wave, n, hh, qc);
-        }
-#pragma unroll
-        for (int j = 0; j < KQ; ++j) sm_q[tt][wave * KQ + j][lane] = qc[j];
+        for (int j = 0; j < KQ; ++j) sm_q[tt][wave * KQ + j][lane] = qpf[tt][j];
       }
+      qpf_u = -1;
     };
 
     // The unit's Q^T operands stay in registers while it runs: read from LDS
@@ -939,17 +939,20 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
     // g-1), compute round g from `cur`; true once the last unit is finished
     auto round = [&](int g, KVBlock<D, VT> &cur, KVBlock<D, VT> &into) -> bool {
       SV_MARK(3);
+      // read ahead the next unit's parent entries and Q chunks once this unit
+      // is under way, before this round's K/V loads (see enter_unit)
+      if (Wc.has_next && qpf_u != Wc.u + 1 && g == Wc.g0 + 1) {
+        Walk Wn;
+        walk_enter(Wn, Wc.u + 1, Wc.next, start, end, 0, units, 0);
+        par_pf = tree_parent_of(a.tree_parent, Wn.ot, Wn.s + Wn.qn, lane);
+#pragma unroll
+        for (int tt = 0; tt < kUnitTiles; ++tt) load_q_chunks<D>(a, Wn, tt, wave, n, hh, qpf[tt]);
+        qpf_u = Wc.u + 1;
+      }
       produce(into);
 #ifndef SV_PHASE_TRACE
       fetch_pages(g + 2);
 #endif
-      // prefetch the next unit's first Q tile once this unit is under way
-      if (Wc.has_next && qpf_u != Wc.u + 1 && g == Wc.g0 + 1) {
-        Walk Wn;
-        walk_enter(Wn, Wc.u + 1, Wc.next, start, end, 0, units, 0);
-        load_q_chunks<D>(a, Wn, 0, wave, n, hh, qpf);
-        qpf_u = Wc.u + 1;
-      }
       const int gb = Wc.ps + kAttnWaves * (g - Wc.g0) + wave;  // this wave's global block
       SV_MARK(4);
 #ifdef SV_PHASE_TRACE
@@ -970,7 +973,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
         SV_MARK(7);
         if (!Wc.has_next) return true;
         walk_to(Wc, g + 1, start, end, units, n_units);
-        enter_unit(std::false_type{});
+        enter_unit();
         __syncthreads();  // the next unit's Q is in LDS; sm_o may be reused
         load_qop();
         SV_MARK(8);
@@ -983,11 +986,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
     // K/V loads issued; the Q operands are staged through LDS after that, so
     // the memory round trips overlap.
     KVBlock<D, VT> A, Bb;
-    pre_par = tree_parent_of(a.tree_parent, Wc.ot, Wc.s + Wc.qn, lane);
-    load_q_chunks<D>(a, Wc, 0, wave, n, hh, qpf);
-    qpf_u = Wc.u;
+    par_pf = tree_parent_of(a.tree_parent, Wc.ot, Wc.s + Wc.qn, lane);
 #pragma unroll
-    for (int tt = 1; tt < kUnitTiles; ++tt) load_q_chunks<D>(a, Wc, tt, wave, n, hh, pre_q[tt - 1]);
+    for (int tt = 0; tt < kUnitTiles; ++tt) load_q_chunks<D>(a, Wc, tt, wave, n, hh, qpf[tt]);
+    qpf_u = Wc.u;
     fetch_pages(0);
     produce(A);
     if (Wc.has_next) {  // the first unit's successor, read once the first K/V loads are out
@@ -995,7 +997,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu
       Wp.next = Wc.next;
     }
     fetch_pages(1);
-    enter_unit(std::true_type{});
+    enter_unit();
     __syncthreads();
     load_qop();
     SV_MARK(2);
