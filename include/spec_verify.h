@@ -392,23 +392,28 @@ int spec_accept_compact_vt(const float *logits, int vocab, const int32_t *draft_
  * FASER, "Early Token Pruning": verification runs over chunks of each
  * request's verify tokens, and at every chunk boundary the tokens behind an
  * already rejected prefix are dropped, so no work is spent on them.  A verify
- * step becomes a loop:
+ * step becomes a loop that runs on the device from start to end:
  *
  *   spec_chunk_start(cu_q, ...)                -> chunk_begin, cu_chunk
- *   while cu_chunk[batch] > 0:
+ *   repeat ceil(max_i q_i / chunk_size) times (the host knows the draft lengths):
  *     (every layer) spec_verify_attn_chunk_plan / _run over the chunk's rows
- *     spec_accept_chunk(logits of the chunk's rows, ...) -> next_begin, next_cu
+ *     spec_accept_chunk(logits, ...)           -> next_begin, next_cu
  *     swap (chunk_begin, cu_chunk) with (next_begin, next_cu)
  *
  * and ends with the same accept_len / accepted_path / out_tokens as
  * spec_accept over all verify tokens (the tokens dropped are never accepted).
  * Request i's rows in a chunk are its verify tokens
  * [chunk_begin[i], chunk_begin[i] + c_i), c_i = cu_chunk[i+1] - cu_chunk[i]
- * (c_i = 0: not in this chunk).  cu_q, tree_parent, draft_tokens and the
- * target_argmax / accepted_path / out_tokens arrays keep the packing of all
- * verify tokens (total_q of them); q, out and logits hold the chunk's rows
- * only (total_chunk = cu_chunk[batch] of them).  The verify tokens' K/V are
- * in the cache from the start, as for spec_verify_attn.
+ * (c_i = 0: not in this chunk).  No host call needs a chunk's row count: the
+ * kernels read cu_chunk[batch] on the device, so no call waits for the
+ * device and the whole loop can be captured in one graph; once every
+ * request has ended, cu_chunk[batch] = 0 and the remaining calls do
+ * nothing.  All arrays keep the packing of all verify tokens (total_q of
+ * them): cu_q, tree_parent, draft_tokens, target_argmax, accepted_path,
+ * out_tokens, and also q, out and logits, whose row cu_q[i] + j is verify
+ * token j of request i; a chunk reads and writes its own rows in place.  The
+ * verify tokens' K/V are in the cache from the start, as for
+ * spec_verify_attn.
  */
 
 /* First chunk: chunk_begin[i] = 0 and cu_chunk = prefix sums of
@@ -418,43 +423,41 @@ int spec_chunk_start(const int32_t *cu_q, int batch, int total_q, int chunk_size
                      int32_t *chunk_begin, int32_t *cu_chunk, void *stream);
 
 /*
- * Verify attention of one chunk's rows: row cu_chunk[i]+r is verify token
- * j = chunk_begin[i]+r of request i and attends, as in spec_verify_attn, to
- * slots p < L_i and p = L_i + k for k = j or k an ancestor of j (chain:
- * k <= j).  The workspace is sized with spec_verify_attn_workspace_size for
- * total_chunk rows; the plan/run contract is that of spec_verify_attn_plan
- * and spec_verify_attn_run.  Device status: SV_DEV_BAD_CU_Q also covers a
- * chunk that does not lie inside its request.
+ * Verify attention of one chunk's rows: verify token j = chunk_begin[i]+r of
+ * request i (row cu_q[i] + j of q and out) attends, as in spec_verify_attn,
+ * to slots p < L_i and p = L_i + k for k = j or k an ancestor of j (chain:
+ * k <= j); rows of other tokens are neither read nor written.  The workspace
+ * is sized with spec_verify_attn_workspace_size for total_q rows; the
+ * plan/run contract is that of spec_verify_attn_plan and spec_verify_attn_run.
+ * Device status: SV_DEV_BAD_CU_Q also covers a chunk that does not lie inside
+ * its request, or cu_chunk[batch] > total_q.
  *
- *   q, out       bf16 [total_chunk, num_q_heads, head_dim]
+ *   q, out       bf16 [total_q, num_q_heads, head_dim], one row per verify token
  *   cu_q         int32 [batch+1] packing of all verify tokens, total_q of them
  *   chunk_begin  int32 [batch];  cu_chunk int32 [batch+1]
  *   tree_parent  int32 [total_q] or NULL for chains
  *   other arguments as for spec_verify_attn
  */
 int spec_verify_attn_chunk_plan(const int32_t *context_lens, const int32_t *cu_q, int total_q,
-                                const int32_t *chunk_begin, const int32_t *cu_chunk, int total_chunk,
-                                int max_blocks_per_seq, int batch, int num_q_heads, int num_kv_heads,
-                                int head_dim, int num_pages, void *workspace, size_t workspace_bytes,
-                                void *stream);
+                                const int32_t *chunk_begin, const int32_t *cu_chunk, int max_blocks_per_seq,
+                                int batch, int num_q_heads, int num_kv_heads, int head_dim, int num_pages,
+                                void *workspace, size_t workspace_bytes, void *stream);
 
 int spec_verify_attn_chunk_run(const void *q, const void *k_cache, const void *v_cache,
                                const int32_t *block_tables, int max_blocks_per_seq,
                                const int32_t *context_lens, const int32_t *cu_q, int total_q,
-                               const int32_t *chunk_begin, const int32_t *cu_chunk, int total_chunk,
-                               const int32_t *tree_parent, void *out, int batch, int num_q_heads,
-                               int num_kv_heads, int head_dim, int page_size, int num_pages,
-                               float softmax_scale, void *workspace, size_t workspace_bytes,
-                               void *stream);
+                               const int32_t *chunk_begin, const int32_t *cu_chunk, const int32_t *tree_parent,
+                               void *out, int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                               int page_size, int num_pages, float softmax_scale, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
 int spec_verify_attn_chunk_run_vt(const void *q, const void *k_cache, const void *v_cache,
                                   const int32_t *block_tables, int max_blocks_per_seq,
                                   const int32_t *context_lens, const int32_t *cu_q, int total_q,
-                                  const int32_t *chunk_begin, const int32_t *cu_chunk, int total_chunk,
-                                  const int32_t *tree_parent, void *out, int batch, int num_q_heads,
-                                  int num_kv_heads, int head_dim, int page_size, int num_pages,
-                                  float softmax_scale, void *workspace, size_t workspace_bytes,
-                                  void *stream);
+                                  const int32_t *chunk_begin, const int32_t *cu_chunk, const int32_t *tree_parent,
+                                  void *out, int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                  int page_size, int num_pages, float softmax_scale, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 /* Workspace bytes spec_accept_chunk needs for any chunk of a step with
  * total_q verify tokens (host function). */
@@ -462,20 +465,22 @@ size_t spec_accept_chunk_workspace_size(int batch, int total_q, int vocab);
 
 /*
  * Acceptance after one chunk.  target_argmax[o + j] (o = cu_q[i]) is computed
- * for the chunk's tokens from logits row cu_chunk[i] + (j - chunk_begin[i]);
- * the entries of earlier tokens must hold what earlier chunks of the same
- * step wrote.  With e = chunk_begin[i] + c_i, the edge into node j (chain:
- * parent j-1) is decided once its parent is < e; a node is alive while no
- * decided edge on its root path mismatches.  If some node in [e, q_i) is
- * alive, the request continues: next_begin[i] = e and it gets
- * min(chunk_size, q_i - e) rows in the next chunk.  Otherwise it ends here:
- * accept_len[i], accepted_path[o..o+q_i) and out_tokens[o..o+q_i) are written
- * exactly as spec_accept would write them, and it gets 0 rows next.
- * Requests with c_i = 0 are left unchanged.  next_cu int32 [batch+1] = prefix
- * sums of the next chunk's rows (next_cu[batch] = 0 once every request has
- * ended).  next_begin / next_cu must not overlap chunk_begin / cu_chunk.
+ * for the chunk's tokens from logits row o + j; the entries of earlier tokens
+ * must hold what earlier chunks of the same step wrote.  With
+ * e = chunk_begin[i] + c_i, the edge into node j (chain: parent j-1) is
+ * decided once its parent is < e; a node is alive while no decided edge on
+ * its root path mismatches.  If some node in [e, q_i) is alive, the request
+ * continues: next_begin[i] = e and it gets min(chunk_size, q_i - e) rows in
+ * the next chunk.  Otherwise it ends here: accept_len[i],
+ * accepted_path[o..o+q_i) and out_tokens[o..o+q_i) are written exactly as
+ * spec_accept would write them, and it gets 0 rows next.  Requests with
+ * c_i = 0 are left unchanged.  next_cu int32 [batch+1] = prefix sums of the
+ * next chunk's rows (next_cu[batch] = 0 once every request has ended).
+ * next_begin / next_cu must not overlap chunk_begin / cu_chunk.  chunk_size
+ * is the one given to spec_chunk_start (it bounds a chunk's rows).
  *
- *   logits       fp32 [total_chunk, vocab], the chunk's rows
+ *   logits       fp32 [total_q, vocab], one row per verify token (only the
+ *                chunk's rows are read)
  *   draft_tokens int32 [total_q]; cu_q, tree_parent as for spec_accept
  *   workspace    at least spec_accept_chunk_workspace_size(batch, total_q, vocab) bytes
  * Device status (spec_accept_device_status): as spec_accept, plus
@@ -483,10 +488,10 @@ size_t spec_accept_chunk_workspace_size(int batch, int total_q, int vocab);
  */
 int spec_accept_chunk(const float *logits, int vocab, const int32_t *draft_tokens,
                       const int32_t *cu_q, const int32_t *tree_parent, const int32_t *chunk_begin,
-                      const int32_t *cu_chunk, int batch, int total_q, int total_chunk,
-                      int chunk_size, int32_t *target_argmax, int32_t *accept_len,
-                      int32_t *accepted_path, int32_t *out_tokens, int32_t *next_begin,
-                      int32_t *next_cu, void *workspace, size_t workspace_bytes, void *stream);
+                      const int32_t *cu_chunk, int batch, int total_q, int chunk_size,
+                      int32_t *target_argmax, int32_t *accept_len, int32_t *accepted_path,
+                      int32_t *out_tokens, int32_t *next_begin, int32_t *next_cu, void *workspace,
+                      size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------- */
 /* Verify-budget scheduling (host)                                            */

@@ -120,7 +120,13 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_partial_kernel(AcceptAr
   if (split == 0 && row == 0 && threadIdx.x == 0)
     reinterpret_cast<int32_t *>(a.ws + a.lay.hdr)[0] = 0;
   if (row >= a.rows) return;  // the grid has one row even when there are none
-  const Best r = argmax_slice(a.logits, a.vocab, row, split, splits);
+  int lrow = row;
+  if (a.chunk_begin) {  // a chunk's rows, as many as cu_rows says, each a verify token's logits row
+    if (row >= a.cu_rows[a.batch]) return;
+    lrow = reinterpret_cast<const int32_t *>(a.ws + a.lay.row_map)[row];
+    if (lrow < 0 || lrow >= a.total_q) return;  // a malformed chunk: flagged by accept_chunk_kernel
+  }
+  const Best r = argmax_slice(a.logits, a.vocab, lrow, split, splits);
   if (threadIdx.x == 0) {
     float2 *part = reinterpret_cast<float2 *>(a.ws + a.lay.part);
     part[(size_t)row * splits + split] = make_float2(r.v, __int_as_float(r.i));
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(256) void accept_chunk_kernel(AcceptArgs a) {
     return;
   }
   if (i == 0 && tid == 0 &&
-      (a.cu_q[0] != 0 || a.cu_q[a.batch] != a.total_q || a.cu_rows[0] != 0 || a.cu_rows[a.batch] != a.rows))
+      (a.cu_q[0] != 0 || a.cu_q[a.batch] != a.total_q || a.cu_rows[0] != 0 || a.cu_rows[a.batch] > a.rows))
     atomicOr(status, SV_DEV_BAD_CU_Q);
   if (c == 0) {  // not in this chunk: finished earlier (or q == 0)
     if (tid == 0) {
@@ -327,6 +333,20 @@ __global__ __launch_bounds__(256) void accept_chunk_kernel(AcceptArgs a) {
     a.accept_len[i] = n + 1;
     next_len[i] = 0;
     a.next_begin[i] = e;
+  }
+}
+
+// The verify token (logits row) of each of a chunk's rows, cu_q[i] +
+// chunk_begin[i] + r for row cu_rows[i] + r (one workgroup); rows of a
+// malformed chunk get -1 (accept_chunk_kernel reports it).
+__global__ __launch_bounds__(kPlanThreads) void chunk_rows_kernel(AcceptArgs a) {
+  int32_t *map = reinterpret_cast<int32_t *>(a.ws + a.lay.row_map);
+  for (int i = threadIdx.x; i < a.batch; i += kPlanThreads) {
+    const int r0 = a.cu_rows[i], r1 = a.cu_rows[i + 1];
+    const int o = a.cu_q[i], q = a.cu_q[i + 1] - o, s0 = a.chunk_begin[i];
+    if (r0 < 0 || r1 < r0 || r1 > a.rows) continue;
+    const bool ok = o >= 0 && q >= 0 && o + q <= a.total_q && s0 >= 0 && s0 + (r1 - r0) <= q;
+    for (int r = r0; r < r1; ++r) map[r] = ok ? o + s0 + (r - r0) : -1;
   }
 }
 
@@ -600,6 +620,7 @@ void launch_accept(const AcceptArgs &a, hipStream_t stream) {
 }
 
 void launch_accept_chunk(const AcceptArgs &a, hipStream_t stream) {
+  chunk_rows_kernel<<<1, kPlanThreads, 0, stream>>>(a);
   dim3 grid(a.lay.splits, a.rows > 0 ? a.rows : 1);
   argmax_partial_kernel<<<grid, kArgmaxThreads, 0, stream>>>(a);
   accept_chunk_kernel<<<a.batch, 256, 0, stream>>>(a);

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -301,15 +302,18 @@ int attn_run(const void *q, const void *k_cache, const void *v_cache, const int3
   return check_launch(what);
 }
 
+// A chunk's rows are read and written in place in q and out, which hold one
+// row per verify token (total_q); their count, cu_chunk[batch], is read on
+// the device, with total_q as its bound.
 int attn_chunk_run(const void *q, const void *k_cache, const void *v_cache, const int32_t *block_tables,
                    int max_blocks_per_seq, const int32_t *context_lens, const int32_t *cu_q, int total_q,
-                   const int32_t *chunk_begin, const int32_t *cu_chunk, int total_chunk,
-                   const int32_t *tree_parent, void *out, int batch, int num_q_heads, int num_kv_heads,
-                   int head_dim, int page_size, int num_pages, float softmax_scale, void *workspace,
-                   size_t workspace_bytes, void *stream, bool v_transposed, const char *what) {
+                   const int32_t *chunk_begin, const int32_t *cu_chunk, const int32_t *tree_parent, void *out,
+                   int batch, int num_q_heads, int num_kv_heads, int head_dim, int page_size, int num_pages,
+                   float softmax_scale, void *workspace, size_t workspace_bytes, void *stream, bool v_transposed,
+                   const char *what) {
   sv::AttnArgs a;
   bool empty;
-  int rc = attn_common(block_tables, max_blocks_per_seq, context_lens, cu_chunk, batch, total_chunk,
+  int rc = attn_common(block_tables, max_blocks_per_seq, context_lens, cu_chunk, batch, total_q,
                        num_q_heads, num_kv_heads, head_dim, page_size, num_pages, workspace,
                        workspace_bytes, true, &a, &empty);
   if (rc != SV_OK || empty) return rc;
@@ -386,13 +390,12 @@ int spec_verify_attn_vt(const void *q, const void *k_cache, const void *v_cache,
 }
 
 int spec_verify_attn_chunk_plan(const int32_t *context_lens, const int32_t *cu_q, int total_q,
-                                const int32_t *chunk_begin, const int32_t *cu_chunk, int total_chunk,
-                                int max_blocks_per_seq, int batch, int num_q_heads, int num_kv_heads,
-                                int head_dim, int num_pages, void *workspace, size_t workspace_bytes,
-                                void *stream) {
+                                const int32_t *chunk_begin, const int32_t *cu_chunk, int max_blocks_per_seq,
+                                int batch, int num_q_heads, int num_kv_heads, int head_dim, int num_pages,
+                                void *workspace, size_t workspace_bytes, void *stream) {
   sv::AttnArgs a;
   bool empty;
-  int rc = attn_common(nullptr, max_blocks_per_seq, context_lens, cu_chunk, batch, total_chunk,
+  int rc = attn_common(nullptr, max_blocks_per_seq, context_lens, cu_chunk, batch, total_q,
                        num_q_heads, num_kv_heads, head_dim, sv::kPage, num_pages, workspace,
                        workspace_bytes, false, &a, &empty);
   if (rc != SV_OK || empty) return rc;
@@ -405,28 +408,26 @@ int spec_verify_attn_chunk_plan(const int32_t *context_lens, const int32_t *cu_q
 int spec_verify_attn_chunk_run(const void *q, const void *k_cache, const void *v_cache,
                                const int32_t *block_tables, int max_blocks_per_seq,
                                const int32_t *context_lens, const int32_t *cu_q, int total_q,
-                               const int32_t *chunk_begin, const int32_t *cu_chunk, int total_chunk,
-                               const int32_t *tree_parent, void *out, int batch, int num_q_heads,
-                               int num_kv_heads, int head_dim, int page_size, int num_pages,
-                               float softmax_scale, void *workspace, size_t workspace_bytes,
-                               void *stream) {
+                               const int32_t *chunk_begin, const int32_t *cu_chunk, const int32_t *tree_parent,
+                               void *out, int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                               int page_size, int num_pages, float softmax_scale, void *workspace,
+                               size_t workspace_bytes, void *stream) {
   return attn_chunk_run(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, cu_q, total_q,
-                        chunk_begin, cu_chunk, total_chunk, tree_parent, out, batch, num_q_heads, num_kv_heads,
-                        head_dim, page_size, num_pages, softmax_scale, workspace, workspace_bytes, stream, false,
+                        chunk_begin, cu_chunk, tree_parent, out, batch, num_q_heads, num_kv_heads, head_dim,
+                        page_size, num_pages, softmax_scale, workspace, workspace_bytes, stream, false,
                         "spec_verify_attn_chunk_run");
 }
 
 int spec_verify_attn_chunk_run_vt(const void *q, const void *k_cache, const void *v_cache,
                                   const int32_t *block_tables, int max_blocks_per_seq,
                                   const int32_t *context_lens, const int32_t *cu_q, int total_q,
-                                  const int32_t *chunk_begin, const int32_t *cu_chunk, int total_chunk,
-                                  const int32_t *tree_parent, void *out, int batch, int num_q_heads,
-                                  int num_kv_heads, int head_dim, int page_size, int num_pages,
-                                  float softmax_scale, void *workspace, size_t workspace_bytes,
-                                  void *stream) {
+                                  const int32_t *chunk_begin, const int32_t *cu_chunk, const int32_t *tree_parent,
+                                  void *out, int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                  int page_size, int num_pages, float softmax_scale, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
   return attn_chunk_run(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, cu_q, total_q,
-                        chunk_begin, cu_chunk, total_chunk, tree_parent, out, batch, num_q_heads, num_kv_heads,
-                        head_dim, page_size, num_pages, softmax_scale, workspace, workspace_bytes, stream, true,
+                        chunk_begin, cu_chunk, tree_parent, out, batch, num_q_heads, num_kv_heads, head_dim,
+                        page_size, num_pages, softmax_scale, workspace, workspace_bytes, stream, true,
                         "spec_verify_attn_chunk_run_vt");
 }
 
@@ -485,9 +486,9 @@ int spec_accept(const float *logits, int vocab, const int32_t *draft_tokens, con
 
 size_t spec_accept_chunk_workspace_size(int batch, int total_q, int vocab) {
   if (batch < 0 || total_q < 0 || vocab <= 0) return 0;
-  size_t m = sv::accept_layout(batch, 0, vocab).total;
+  size_t m = sv::chunk_layout(batch, 0, vocab).total;
   for (int rows = 1; rows <= total_q; ++rows) {
-    const size_t t = sv::accept_layout(batch, rows, vocab).total;
+    const size_t t = sv::chunk_layout(batch, rows, vocab).total;
     if (t > m) m = t;
   }
   return m;
@@ -517,13 +518,12 @@ int spec_chunk_start(const int32_t *cu_q, int batch, int total_q, int chunk_size
 
 int spec_accept_chunk(const float *logits, int vocab, const int32_t *draft_tokens,
                       const int32_t *cu_q, const int32_t *tree_parent, const int32_t *chunk_begin,
-                      const int32_t *cu_chunk, int batch, int total_q, int total_chunk,
-                      int chunk_size, int32_t *target_argmax, int32_t *accept_len,
-                      int32_t *accepted_path, int32_t *out_tokens, int32_t *next_begin,
-                      int32_t *next_cu, void *workspace, size_t workspace_bytes, void *stream) {
-  if (batch < 0 || total_q < 0 || total_chunk < 0 || total_chunk > total_q)
-    return fail(SV_ERR_SHAPE, "batch (%d), total_q (%d), total_chunk (%d) out of range", batch,
-                total_q, total_chunk);
+                      const int32_t *cu_chunk, int batch, int total_q, int chunk_size,
+                      int32_t *target_argmax, int32_t *accept_len, int32_t *accepted_path,
+                      int32_t *out_tokens, int32_t *next_begin, int32_t *next_cu, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  if (batch < 0 || total_q < 0)
+    return fail(SV_ERR_SHAPE, "batch (%d) and total_q (%d) must be >= 0", batch, total_q);
   if (vocab <= 0) return fail(SV_ERR_SHAPE, "vocab %d must be > 0", vocab);
   if (chunk_size <= 0) return fail(SV_ERR_SHAPE, "chunk_size %d must be > 0", chunk_size);
   if (total_q > (long long)batch * sv::kMaxTokens)
@@ -533,8 +533,10 @@ int spec_accept_chunk(const float *logits, int vocab, const int32_t *draft_token
     return fail(SV_ERR_NULL, "spec_accept_chunk: a required pointer is NULL");
   if (total_q > 0 && (!draft_tokens || !target_argmax || !accepted_path || !out_tokens))
     return fail(SV_ERR_NULL, "spec_accept_chunk: a required pointer is NULL");
-  if (total_chunk > 0 && !logits) return fail(SV_ERR_NULL, "spec_accept_chunk: logits is NULL");
-  const sv::AcceptLayout lay = sv::accept_layout(batch, total_chunk, vocab);
+  if (total_q > 0 && !logits) return fail(SV_ERR_NULL, "spec_accept_chunk: logits is NULL");
+  // the most rows a chunk can have; the chunk's own count, cu_chunk[batch], is read on the device
+  const int rows = (int)std::min<long long>(total_q, (long long)batch * std::min(chunk_size, sv::kMaxTokens));
+  const sv::AcceptLayout lay = sv::chunk_layout(batch, rows, vocab);
   if (workspace_bytes < lay.total)
     return fail(SV_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, lay.total);
   const size_t tb = (size_t)total_q * 4, bb = (size_t)batch * 4, cb = (size_t)(batch + 1) * 4;
@@ -560,7 +562,7 @@ int spec_accept_chunk(const float *logits, int vocab, const int32_t *draft_token
   a.batch = batch;
   a.total_q = total_q;
   a.vocab = vocab;
-  a.rows = total_chunk;
+  a.rows = rows;
   a.cu_rows = cu_chunk;
   a.chunk_begin = chunk_begin;
   a.chunk_size = chunk_size;

@@ -43,8 +43,10 @@ constexpr int kPlanLdsRequests = 4096;  // per-request plan data kept in LDS up 
 // A unit record: {request, kv head, tile group, first global block},
 // {first row o, rows q, context L, blocks per unit} and {first verify token s
 // of the rows, the request's first entry in the tree parent array, -, -}.
-// Row r of the unit's request is verify token s + r; its keys are the
-// L + s + q slots [0, L + s + q).  s = 0 except for chunked verification.
+// Row r of the unit's request is verify token s + r, in row o + r of q and
+// out (o = the request's first verify token's row + s: a chunk's rows are
+// read and written in place); its keys are the L + s + q slots
+// [0, L + s + q).  s = 0 except for chunked verification.
 struct UnitRec {
   int4 a;
   int4 b;
@@ -143,6 +145,7 @@ struct AcceptLayout {
   size_t hdr;       // int32[8]: 0 status bits; fused launch: 2 ticket, 3 finished, 4 status cleared, 5 abort
   size_t part;      // {float value, int index}[rows][splits]
   size_t next_len;  // int32[batch]: rows of each request in the next chunk (chunked acceptance)
+  size_t row_map;   // int32[rows]: chunked acceptance, the verify token (logits row) of each chunk row
   // fused acceptance + compaction only (0 otherwise)
   size_t arrive;    // int32[rows]: slices of each row done
   size_t done;      // int32[batch]: request walked, moves listed
@@ -169,7 +172,16 @@ __host__ __device__ inline AcceptLayout accept_layout(int batch, int rows, int v
   l.hdr = off;       off = align256(off + 8 * sizeof(int32_t));
   l.part = off;      off = align256(off + size_t(rows) * l.splits * 8);
   l.next_len = off;  off = align256(off + size_t(batch) * sizeof(int32_t));
-  l.arrive = l.done = l.moves = 0;
+  l.arrive = l.done = l.moves = l.row_map = 0;
+  l.total = off;
+  return l;
+}
+
+// chunked acceptance: rows = the most rows a chunk can have
+__host__ __device__ inline AcceptLayout chunk_layout(int batch, int rows, int vocab) {
+  AcceptLayout l = accept_layout(batch, rows, vocab);
+  size_t off = l.total;
+  l.row_map = off;  off = align256(off + size_t(rows) * sizeof(int32_t));
   l.total = off;
   return l;
 }
@@ -185,7 +197,7 @@ __host__ __device__ inline AcceptLayout fused_layout(int batch, int rows, int vo
 }
 
 struct AcceptArgs {
-  const float *logits;          // [rows, vocab]
+  const float *logits;          // [rows, vocab]; chunked: [total_q, vocab], one row per verify token
   const int32_t *draft;
   const int32_t *cu_q;
   const int32_t *tree_parent;
@@ -196,10 +208,11 @@ struct AcceptArgs {
   char *ws;
   AcceptLayout lay;
   int batch, total_q, vocab;
-  int rows;                     // logits rows (== total_q unless chunked)
-  // chunked acceptance (FASER early pruning): the logits rows are the chunk's
-  // rows, packed by cu_rows; request i's rows are its verify tokens
-  // [chunk_begin[i], chunk_begin[i] + rows_i)
+  int rows;                     // logits rows (== total_q); chunked: the most rows a chunk can have
+  // chunked acceptance (FASER early pruning): the chunk's rows are packed by
+  // cu_rows (cu_rows[batch] of them, read on the device); request i's rows
+  // are its verify tokens [chunk_begin[i], chunk_begin[i] + rows_i), whose
+  // logits rows are cu_q[i] + chunk_begin[i] + r
   const int32_t *cu_rows;
   const int32_t *chunk_begin;
   int chunk_size;

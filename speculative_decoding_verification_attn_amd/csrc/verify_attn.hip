@@ -96,7 +96,8 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a) {
   unsigned flags = 0;
   if (tid == 0) {
     hdr[0] = 0;
-    if (a.cu_q[0] != 0 || a.cu_q[B] != a.total_q) flags |= SV_DEV_BAD_CU_Q;
+    // a chunk's row count is read here (total_q bounds it)
+    if (a.cu_q[0] != 0 || (a.chunk_begin ? a.cu_q[B] > a.total_q : a.cu_q[B] != a.total_q)) flags |= SV_DEV_BAD_CU_Q;
   }
 
   // pass 1: per request row tiles and blocks; unit and block bases
@@ -160,8 +161,9 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a) {
     for (int i = tid; i < B; i += kPlanThreads) {
       const int rg = rgs[i], nblk = nblks[i], u0 = ubase[i], b0 = bbase[i];
       if (rg == 0) continue;
-      const int o = a.cu_q[i], qn = a.cu_q[i + 1] - o, L = a.context_lens[i];
-      const int s0 = a.chunk_begin ? a.chunk_begin[i] : 0, ot = a.chunk_begin ? a.cu_full[i] : o;
+      const int qn = a.cu_q[i + 1] - a.cu_q[i], L = a.context_lens[i];
+      const int s0 = a.chunk_begin ? a.chunk_begin[i] : 0, ot = a.chunk_begin ? a.cu_full[i] : a.cu_q[i];
+      const int o = ot + s0;  // q and out rows: one per verify token (a chunk's rows in place)
       for (int k = 0; k < rg * Hkv; ++k) {
         const int h = k / rg, r = k - h * rg;
         units[u0 + k] = UnitRec{make_int4(i, h, r, b0 + k * nblk), make_int4(o, qn, L, nblk),
@@ -217,8 +219,9 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a) {
       const int u = ubase[lo] + k;
       const int h = k / rg, r = k - h * rg;
       const int ub = bbase[lo] + k * nblk;
-      const int o = a.cu_q[lo], qn = a.cu_q[lo + 1] - o, L = a.context_lens[lo];
-      const int s0 = a.chunk_begin ? a.chunk_begin[lo] : 0, ot = a.chunk_begin ? a.cu_full[lo] : o;
+      const int qn = a.cu_q[lo + 1] - a.cu_q[lo], L = a.context_lens[lo];
+      const int s0 = a.chunk_begin ? a.chunk_begin[lo] : 0, ot = a.chunk_begin ? a.cu_full[lo] : a.cu_q[lo];
+      const int o = ot + s0;
       wg_first[w] = u;
       wg_rec[w] = UnitRec{make_int4(lo, h, r, ub), make_int4(o, qn, L, nblk), make_int4(s0, ot, 0, 0)};
       const int w0 = wg_of_block(wg_start, P, ub);

@@ -94,16 +94,16 @@ def load_library():
     for fn in ("kv_compact", "kv_compact_vt"):
         getattr(lib, fn).argtypes = [P, P, I64, I, P, I, P, P, P, P, P, I, I, I, I, I, I, P]
         getattr(lib, fn).restype = I
-    lib.spec_verify_attn_chunk_plan.argtypes = [P, P, I, P, P, I, I, I, I, I, I, I, P, SZ, P]
+    lib.spec_verify_attn_chunk_plan.argtypes = [P, P, I, P, P, I, I, I, I, I, I, P, SZ, P]
     lib.spec_verify_attn_chunk_plan.restype = I
     for fn in ("spec_verify_attn_chunk_run", "spec_verify_attn_chunk_run_vt"):
-        getattr(lib, fn).argtypes = [P, P, P, P, I, P, P, I, P, P, I, P, P, I, I, I, I, I, I, F, P, SZ, P]
+        getattr(lib, fn).argtypes = [P, P, P, P, I, P, P, I, P, P, P, P, I, I, I, I, I, I, F, P, SZ, P]
         getattr(lib, fn).restype = I
     lib.spec_chunk_start.argtypes = [P, I, I, I, P, P, P]
     lib.spec_chunk_start.restype = I
     lib.spec_accept_chunk_workspace_size.argtypes = [I, I, I]
     lib.spec_accept_chunk_workspace_size.restype = SZ
-    lib.spec_accept_chunk.argtypes = [P, I, P, P, P, P, P, I, I, I, I, P, P, P, P, P, P, P, SZ, P]
+    lib.spec_accept_chunk.argtypes = [P, I, P, P, P, P, P, I, I, I, P, P, P, P, P, P, P, SZ, P]
     lib.spec_accept_chunk.restype = I
     lib.spec_verify_budget.argtypes = [P, P, I, P, P, I, P, P, ctypes.POINTER(ctypes.c_double)]
     lib.spec_verify_budget.restype = I
@@ -445,17 +445,18 @@ def spec_chunk_start(cu_q, chunk_size, *, total_q, chunk_begin=None, cu_chunk=No
     return chunk_begin, cu_chunk
 
 
-def spec_verify_attn_chunk_plan(context_lens, cu_q, chunk_begin, cu_chunk, *, total_q, total_chunk,
+def spec_verify_attn_chunk_plan(context_lens, cu_q, chunk_begin, cu_chunk, *, total_q,
                                 max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, num_pages,
                                 workspace, stream=None):
-    """Plan of verify attention over one chunk's rows into `workspace`."""
+    """Plan of verify attention over one chunk's rows into `workspace` (sized for total_q rows);
+    the chunk's row count is read on the device."""
     lib = load_library()
     for t, nm in ((context_lens, "context_lens"), (cu_q, "cu_q"), (chunk_begin, "chunk_begin"),
                   (cu_chunk, "cu_chunk")):
         _dev(t, torch.int32, nm)
     B = context_lens.shape[0]
     _check(lib.spec_verify_attn_chunk_plan(_ptr(context_lens), _ptr(cu_q), int(total_q), _ptr(chunk_begin),
-                                           _ptr(cu_chunk), int(total_chunk), int(max_blocks_per_seq), B,
+                                           _ptr(cu_chunk), int(max_blocks_per_seq), B,
                                            int(num_q_heads), int(num_kv_heads), int(head_dim),
                                            int(num_pages), _ptr(workspace), workspace.numel(),
                                            _stream(stream)))
@@ -465,8 +466,9 @@ def spec_verify_attn_chunk_plan(context_lens, cu_q, chunk_begin, cu_chunk, *, to
 def spec_verify_attn_chunk_run(q, k_cache, v_cache, block_tables, context_lens, cu_q, chunk_begin,
                                cu_chunk, tree_parent=None, *, total_q, out=None, softmax_scale=0.0,
                                workspace, num_pages=None, stream=None):
-    """q [Tc,Hq,D] bf16 (the chunk's rows, packed by cu_chunk) -> out [Tc,Hq,D]; the plan must be
-    in `workspace` (spec_verify_attn_chunk_plan).  k_cache and v_cache [pages,Hkv,16,D]."""
+    """q, out [T,Hq,D] bf16, one row per verify token of the step: the chunk's rows are read and
+    written in place; the plan must be in `workspace` (spec_verify_attn_chunk_plan).  k_cache and
+    v_cache [pages,Hkv,16,D]."""
     return _chunk_run_call("spec_verify_attn_chunk_run", q, k_cache, v_cache, block_tables, context_lens, cu_q,
                            chunk_begin, cu_chunk, tree_parent, total_q, out, softmax_scale, workspace, num_pages,
                            stream)
@@ -491,7 +493,9 @@ def _chunk_run_call(fn, q, k_cache, v_cache, block_tables, context_lens, cu_q, c
     for t, nm in ((block_tables, "block_tables"), (context_lens, "context_lens"), (cu_q, "cu_q"),
                   (chunk_begin, "chunk_begin"), (cu_chunk, "cu_chunk"), (tree_parent, "tree_parent")):
         _dev(t, torch.int32, nm)
-    Tc, Hq, D = q.shape
+    T, Hq, D = q.shape
+    if T != total_q:
+        raise ValueError("q and out hold one row per verify token of the step (total_q rows)")
     pages, Hkv, P, D2 = k_cache.shape
     if D2 != D or tuple(v_cache.shape) != _v_shape(k_cache.shape, vt):
         raise ValueError("caches must be K [pages, Hkv, 16, D] and V [pages, Hkv, %s] matching q"
@@ -511,7 +515,7 @@ def _chunk_run_call(fn, q, k_cache, v_cache, block_tables, context_lens, cu_q, c
         raise ValueError("out must have the shape of q")
     _check(getattr(lib, fn)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                           block_tables.shape[1], _ptr(context_lens), _ptr(cu_q), int(total_q),
-                                          _ptr(chunk_begin), _ptr(cu_chunk), Tc, _ptr(tree_parent), _ptr(out),
+                                          _ptr(chunk_begin), _ptr(cu_chunk), _ptr(tree_parent), _ptr(out),
                                           B, Hq, Hkv, D, P, pages if num_pages is None else num_pages,
                                           float(softmax_scale), _ptr(workspace), workspace.numel(),
                                           _stream(stream)))
@@ -525,9 +529,10 @@ def spec_accept_chunk_workspace_size(batch, total_q, vocab) -> int:
 def spec_accept_chunk(logits, draft_tokens, cu_q, chunk_begin, cu_chunk, tree_parent=None, *,
                       chunk_size, target_argmax, accept_len, accepted_path, out_tokens, next_begin,
                       next_cu, workspace, stream=None):
-    """Acceptance after one chunk: logits [Tc,V] fp32 are the chunk's rows.  Fills the chunk's
-    entries of target_argmax [T]; requests that end here get accept_len / accepted_path /
-    out_tokens; next_begin [B] and next_cu [B+1] describe the next chunk (next_cu[B] = its rows)."""
+    """Acceptance after one chunk: logits [T,V] fp32, one row per verify token (the chunk's rows are
+    read).  Fills the chunk's entries of target_argmax [T]; requests that end here get accept_len /
+    accepted_path / out_tokens; next_begin [B] and next_cu [B+1] describe the next chunk (next_cu[B] =
+    its rows, 0 once every request has ended)."""
     lib = load_library()
     _dev(logits, torch.float32, "logits")
     for t, nm in ((draft_tokens, "draft_tokens"), (cu_q, "cu_q"), (chunk_begin, "chunk_begin"),
@@ -535,16 +540,16 @@ def spec_accept_chunk(logits, draft_tokens, cu_q, chunk_begin, cu_chunk, tree_pa
                   (accept_len, "accept_len"), (accepted_path, "accepted_path"), (out_tokens, "out_tokens"),
                   (next_begin, "next_begin"), (next_cu, "next_cu")):
         _dev(t, torch.int32, nm)
-    Tc, V = logits.shape
+    TL, V = logits.shape
     B = cu_q.shape[0] - 1
     T = draft_tokens.shape[0]
-    if any(t.numel() != T for t in (target_argmax, accepted_path, out_tokens)) or \
+    if TL != T or any(t.numel() != T for t in (target_argmax, accepted_path, out_tokens)) or \
             (tree_parent is not None and tree_parent.numel() != T) or accept_len.numel() != B or \
             next_cu.numel() != B + 1 or cu_chunk.numel() != B + 1 or chunk_begin.numel() < B or \
             next_begin.numel() < B:
         raise ValueError("chunk acceptance arrays do not match the batch or the step's verify tokens")
     _check(lib.spec_accept_chunk(_ptr(logits), V, _ptr(draft_tokens), _ptr(cu_q), _ptr(tree_parent),
-                                 _ptr(chunk_begin), _ptr(cu_chunk), B, T, Tc, int(chunk_size),
+                                 _ptr(chunk_begin), _ptr(cu_chunk), B, T, int(chunk_size),
                                  _ptr(target_argmax), _ptr(accept_len), _ptr(accepted_path),
                                  _ptr(out_tokens), _ptr(next_begin), _ptr(next_cu), _ptr(workspace),
                                  workspace.numel(), _stream(stream)))

@@ -137,14 +137,15 @@ def test_chunk_validation(lib):
 
     def acc(**kw):
         a = dict(logits=FAKE, V=100, dr=FAKE, cu=FAKE, par=NULL, cb=ctypes.c_void_p(0x500000),
-                 cuc=ctypes.c_void_p(0x600000), B=2, T=8, Tc=4, c=2, t=ctypes.c_void_p(0x100000),
+                 cuc=ctypes.c_void_p(0x600000), B=2, T=8, c=2, t=ctypes.c_void_p(0x100000),
                  acc=ctypes.c_void_p(0x200000), path=ctypes.c_void_p(0x300000), toks=ctypes.c_void_p(0x400000),
                  nb=ctypes.c_void_p(0x700000), ncu=ctypes.c_void_p(0x800000), ws=FAKE, wsb=1 << 30, stream=NULL)
         a.update(kw)
         return lib.spec_accept_chunk(a["logits"], a["V"], a["dr"], a["cu"], a["par"], a["cb"], a["cuc"], a["B"],
-                                     a["T"], a["Tc"], a["c"], a["t"], a["acc"], a["path"], a["toks"], a["nb"],
+                                     a["T"], a["c"], a["t"], a["acc"], a["path"], a["toks"], a["nb"],
                                      a["ncu"], a["ws"], a["wsb"], a["stream"])
-    assert acc(Tc=9) == ops.SV_ERR_SHAPE
+    assert acc(T=-1) == ops.SV_ERR_SHAPE
+    assert acc(T=200) == ops.SV_ERR_SHAPE
     assert acc(c=0) == ops.SV_ERR_SHAPE
     assert acc(V=0) == ops.SV_ERR_SHAPE
     assert acc(nb=NULL) == ops.SV_ERR_NULL
@@ -152,21 +153,21 @@ def test_chunk_validation(lib):
     assert acc(wsb=8) == ops.SV_ERR_WORKSPACE
     assert acc(nb=ctypes.c_void_p(0x500000)) == ops.SV_ERR_ALIAS   # next_begin over chunk_begin
     assert acc(ncu=ctypes.c_void_p(0x600004)) == ops.SV_ERR_ALIAS  # next_cu over cu_chunk
-    assert acc(B=0, T=0, Tc=0) == ops.SV_OK
+    assert acc(B=0, T=0) == ops.SV_OK
     assert lib.spec_accept_chunk_workspace_size(4, 20, 128256) >= lib.spec_accept_workspace_size(4, 20, 128256)
 
     def plan(**kw):
-        a = dict(ctx=FAKE, cu=FAKE, T=8, cb=FAKE, cuc=FAKE, Tc=4, mb=4, B=2, Hq=8, Hkv=2, D=64, pages=10,
+        a = dict(ctx=FAKE, cu=FAKE, T=8, cb=FAKE, cuc=FAKE, mb=4, B=2, Hq=8, Hkv=2, D=64, pages=10,
                  ws=FAKE, wsb=1 << 30, stream=NULL)
         a.update(kw)
-        return lib.spec_verify_attn_chunk_plan(a["ctx"], a["cu"], a["T"], a["cb"], a["cuc"], a["Tc"], a["mb"],
+        return lib.spec_verify_attn_chunk_plan(a["ctx"], a["cu"], a["T"], a["cb"], a["cuc"], a["mb"],
                                                a["B"], a["Hq"], a["Hkv"], a["D"], a["pages"], a["ws"], a["wsb"],
                                                a["stream"])
     assert plan(cb=NULL) == ops.SV_ERR_NULL
     assert plan(T=200) == ops.SV_ERR_SHAPE
     assert plan(D=96) == ops.SV_ERR_UNSUPPORTED
     assert plan(wsb=8) == ops.SV_ERR_WORKSPACE
-    assert plan(Tc=0) == ops.SV_OK
+    assert plan(T=0) == ops.SV_OK
 
 
 def test_fused_validation(lib):
