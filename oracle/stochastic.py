@@ -76,3 +76,72 @@ def accept_stochastic(logits, draft_probs, draft_tokens, u, w, cu_q, temperature
         toks[o:o + n] = np.asarray(draft_tokens[o + 1:o + n + 1])
         toks[o + n] = y
     return acc, path, toks
+
+
+# ---------------------------------------------------------------------------
+# Draft trees (SwiftSpec, "Tree-aware KV cache management": the verify tokens of
+# a request form a tree; DSpark's glossary: the rule must keep the target's
+# distribution).  The pages give no rule for trees; the plainest lossless one is
+# speculative sampling applied to the siblings of a node one after another, each
+# test against the target distribution left over by the siblings rejected before
+# it (multi-draft rejection sampling).  For request i, node 0 = root, parent[o+k]
+# in [0, k) for k >= 1:
+#   at the current node c (c = 0 first) the distribution is p = softmax(row c / T);
+#   its children are tested in index order; child k (draft x_k drawn from q_k =
+#   draft_probs[o+k]) is accepted iff u[o+k] * q_k(x_k) < p'(x_k), p' being the
+#   distribution in force (p at first);
+#   on acceptance the walk moves to k (p' starts again from k's own row);
+#   on rejection p' becomes max(0, p' - q_k) normalised, unless that has no mass
+#   (then p' stays);
+#   when no child of c is accepted, y is drawn with w[i] by inverse CDF from the
+#   last residual max(0, p' - q_k) that had mass, or from p if none did.
+# A chain is the special case of one child per node.  Outputs as for chains,
+# except that accepted_path lists the node indices of the accepted path.
+def accept_request_tree(logits, draft_probs, draft, parent, u, w, o, q, temperature):
+    """One request of a tree.  Returns (path, y, weights, tests): path = node
+    indices from the root, weights = the (unnormalised) draw weights, tests =
+    (u*q(x), p'(x)) of every acceptance test made, in order."""
+    c, path, tests = 0, [0], []
+    while True:
+        p = target_probs(logits[o + c], temperature)
+        cur, last, moved = p, None, False
+        for k in range(c + 1, q):
+            if int(parent[o + k]) != c:
+                continue
+            x = int(draft[o + k])
+            qk = np.asarray(draft_probs[o + k], np.float64)
+            lhs = float(u[o + k]) * float(qk[x])
+            tests.append((lhs, float(cur[x])))
+            if lhs < cur[x]:
+                path.append(k)
+                c, moved = k, True
+                break
+            r = np.maximum(0.0, cur - qk)
+            if r.sum() > 0.0:
+                last = r
+                cur = r / r.sum()
+        if not moved:
+            weights = p if last is None else last
+            return path, inverse_cdf(weights, w), weights, tests
+
+
+def accept_stochastic_tree(logits, draft_probs, draft_tokens, tree_parent, u, w, cu_q, temperature=1.0):
+    """Returns (accept_len [B], accepted_path [T], out_tokens [T]); -1 past the path."""
+    cu_q = np.asarray(cu_q, np.int64)
+    B = len(cu_q) - 1
+    T = int(cu_q[-1])
+    acc = np.zeros(B, np.int32)
+    path = np.full(T, -1, np.int32)
+    toks = np.full(T, -1, np.int32)
+    for i in range(B):
+        o, q = int(cu_q[i]), int(cu_q[i + 1] - cu_q[i])
+        if q == 0:
+            continue
+        pth, y, _, _ = accept_request_tree(logits, draft_probs, draft_tokens, tree_parent, u, w[i], o, q,
+                                           temperature)
+        n = len(pth) - 1
+        acc[i] = n + 1
+        path[o:o + n + 1] = pth
+        toks[o:o + n] = [int(draft_tokens[o + k]) for k in pth[1:]]
+        toks[o + n] = y
+    return acc, path, toks

@@ -2,6 +2,8 @@
 torch's softmax and the two-logit logistic closed form; the rejection rule
 keeps the target's distribution (the defining property the pages state), plus
 special cases and the inverse CDF against brute force."""
+import itertools
+
 import numpy as np
 import pytest
 
@@ -184,6 +186,204 @@ def test_pins_catch_planted_mistake(tmp_path, monkeypatch, name, old, new):
                   test_target_probs_neg_inf_logit_and_shift,
                   lambda: test_lossless_first_token(0), lambda: test_lossless_first_token(1),
                   test_all_accepted_bonus_from_last_row, test_zero_target_probability_is_never_accepted):
+        try:
+            check()
+        except AssertionError:
+            failed = True
+            break
+    assert failed, f"no pin caught {name}"
+
+
+# ---------------------------------------------------------------------------
+# Draft trees: multi-draft rejection sampling over the siblings of each node.
+# The defining property is again that the emitted token keeps the target's
+# distribution.  The pins integrate the oracle's decisions exactly: a test is
+# a threshold in its uniform and a draw is monotone in w, so bisection on the
+# oracle as a black box gives each branch's probability to ~1e-15.
+def _bisect(pred, iters=64):
+    """Measure of {t in [0, 1): pred(t)} for a predicate true on [0, a) only."""
+    if not pred(0.0):
+        return 0.0
+    lo, hi = 0.0, 1.0
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        if pred(mid):
+            lo = mid
+        else:
+            hi = mid
+    return lo
+
+
+def _draw_law(y_of_w, V):
+    """Law of y(w) for w uniform in [0, 1), y non-decreasing in w."""
+    bounds = [0.0] + [_bisect(lambda w, v=v: y_of_w(w) < v) for v in range(1, V)] + [1.0]
+    return np.diff(np.array(bounds))
+
+
+def _token_law_at(node, logits, dprobs, parent, draft, u, temp):
+    """Law of the token emitted right after `node` (an accepted child's draft
+    or the draw at `node`), given that the walk reaches `node`, integrated over
+    the children's drafts and uniforms and the draw's w."""
+    V = logits.shape[1]
+    q = len(parent)
+    kids = [k for k in range(node + 1, q) if parent[k] == node]
+    depth = 0
+    a = node
+    while a != 0:
+        a = parent[a]
+        depth += 1
+    law = np.zeros(V)
+    for xs in itertools.product(range(V), repeat=len(kids)):
+        pr = float(np.prod([dprobs[k][x] for k, x in zip(kids, xs)]))
+        if pr == 0.0:
+            continue
+        d = draft.copy()
+        d[kids] = xs
+        uu = u.copy()
+
+        def run(w=0.5):
+            return S.accept_request_tree(logits, dprobs, d, parent, uu, w, 0, q, temp)
+        reach = pr
+        for k, x in zip(kids, xs):
+            def accepted(t, k=k):
+                uu[k] = t
+                pth = run()[0]
+                return len(pth) > depth + 1 and pth[depth + 1] == k
+            acc = _bisect(accepted)
+            law[x] += reach * acc
+            reach *= 1.0 - acc
+            if reach == 0.0:
+                break
+            uu[k] = 0.5 * (acc + 1.0)  # inside the rejection region
+        if reach > 0.0:
+            law += reach * _draw_law(lambda w: run(w)[1], V)
+    return law
+
+
+def _tree_case(seed, V, parent):
+    """Each draft row a perturbed copy of its parent's target row, so that the
+    residuals left by rejections keep mass on several tokens."""
+    rng = np.random.default_rng(seed)
+    q = len(parent)
+    logits = rng.standard_normal((q, V)) * 1.5
+    dprobs = np.zeros((q, V))
+    for k in range(1, q):
+        dprobs[k] = S.target_probs(logits[parent[k]] + rng.standard_normal(V) * 0.8, 1.0)
+    return logits, dprobs, np.zeros(q, np.int64), np.full(q, 0.5)
+
+
+@pytest.mark.parametrize("seed,temp", [(0, 1.0), (1, 0.7), (2, 1.3)])
+def test_tree_lossless_first_token(seed, temp):
+    """Root with three children whose drafts come from three different q rows."""
+    V = 4
+    parent = np.array([-1, 0, 0, 0])
+    logits, dprobs, draft, u = _tree_case(100 + seed, V, parent)
+    got = _token_law_at(0, logits, dprobs, parent, draft, u, temp)
+    want = S.target_probs(logits[0], temp)
+    assert np.abs(got - want).max() < 1e-9, (got, want)
+
+
+def test_tree_lossless_after_a_rejected_sibling():
+    """parent = [-1, 0, 0, 2, 2]: node 1 rejected, node 2 accepted, then node
+    2's children; the token after node 2 must follow node 2's own row (the
+    residual left at the root does not carry over), for every draft of nodes 1
+    and 2 that can reach node 2 this way."""
+    V = 3
+    parent = np.array([-1, 0, 0, 2, 2])
+    logits, dprobs, draft, u = _tree_case(7, V, parent)
+    dprobs[1] = [0.9, 0.05, 0.05]
+    checked = 0
+    for x1 in range(V):
+        for x2 in range(V):
+            draft[1], draft[2] = x1, x2
+            uu = u.copy()
+            uu[1] = 1.0 - 1e-12
+            uu[2] = 0.0
+            pth = S.accept_request_tree(logits, dprobs, draft, parent, uu, 0.5, 0, 5, 1.0)[0]
+            if pth[:2] != [0, 2]:
+                continue
+            got = _token_law_at(2, logits, dprobs, parent, draft, uu, 1.0)
+            assert np.abs(got - S.target_probs(logits[2], 1.0)).max() < 1e-9, (x1, x2, got)
+            checked += 1
+    assert checked >= 2
+
+
+def test_tree_chain_equals_chain_rule():
+    """A tree with one child per node is a chain: same path, same draw."""
+    rng = np.random.default_rng(21)
+    for _ in range(300):
+        q = int(rng.integers(1, 8))
+        V = int(rng.integers(2, 12))
+        logits = rng.standard_normal((q, V)) * 2.0
+        dprobs = rng.dirichlet(np.ones(V) * 0.5, q)
+        draft = rng.integers(0, V, q)
+        u, w = rng.random(q), rng.random()
+        n, y, _ = S.accept_request(logits, dprobs, draft, u, w, 0, q, 0.9)
+        pth, yt, _, _ = S.accept_request_tree(logits, dprobs, draft, np.arange(-1, q - 1), u, w, 0, q, 0.9)
+        assert pth == list(range(n + 1)) and yt == y
+
+
+def test_tree_siblings_in_index_order():
+    """Two children that would both be accepted: the lower index wins."""
+    V = 4
+    parent = np.array([-1, 0, 0])
+    logits = np.zeros((3, V))
+    dprobs = np.full((3, V), 0.25)  # q == p: every test with u < 1 accepts
+    draft = np.array([0, 2, 1])
+    pth = S.accept_request_tree(logits, dprobs, draft, parent, np.array([0.0, 0.3, 0.3]), 0.5, 0, 3, 1.0)[0]
+    assert pth == [0, 1]
+
+
+def test_tree_outputs_layout():
+    rng = np.random.default_rng(8)
+    V = 20
+    parent = np.array([-1, 0, 0, 1, 1, 3, -1, -1, 0, 1])  # requests of 6, 1 and 3 tokens
+    cu = np.array([0, 6, 7, 7, 10])
+    T = 10
+    logits = rng.standard_normal((T, V))
+    dprobs = np.tile(S.target_probs(np.zeros(V), 1.0), (T, 1))
+    draft = rng.integers(0, V, T)
+    for _ in range(20):
+        acc, path, toks = S.accept_stochastic_tree(logits, dprobs, draft, parent, rng.random(T), rng.random(4), cu)
+        assert acc[1] == 1 and acc[2] == 0 and path[6] == 0
+        for i in (0, 1, 3):
+            o, q = cu[i], cu[i + 1] - cu[i]
+            n = acc[i] - 1
+            pth = path[o:o + n + 1]
+            assert pth[0] == 0 and all(parent[o + pth[t + 1]] == pth[t] for t in range(n))
+            assert np.all(path[o + n + 1:o + q] == -1) and np.all(toks[o + n + 1:o + q] == -1)
+            assert toks[o:o + n].tolist() == [draft[o + k] for k in pth[1:]] and 0 <= toks[o + n] < V
+
+
+TREE_MUTANTS = [
+    ("tree_test_against_target_not_residual", "if lhs < cur[x]:", "if lhs < p[x]:"),
+    ("tree_residual_unnormalised", "cur = r / r.sum()", "cur = r"),
+    ("tree_residual_from_target", "r = np.maximum(0.0, cur - qk)", "r = np.maximum(0.0, p - qk)"),
+    ("tree_draw_ignores_residual", "weights = p if last is None else last", "weights = p"),
+    ("tree_row_by_depth", "p = target_probs(logits[o + c], temperature)",
+     "p = target_probs(logits[o + len(path) - 1], temperature)"),
+    ("tree_first_sibling_draft_row", "qk = np.asarray(draft_probs[o + k], np.float64)",
+     "qk = np.asarray(draft_probs[o + c + 1], np.float64)"),
+    ("tree_siblings_reversed", "for k in range(c + 1, q):", "for k in reversed(range(c + 1, q)):"),
+    ("tree_residual_kept_after_move", "cur, last, moved = p, None, False",
+     "cur, last, moved = (p if c == 0 else cur), (None if c == 0 else last), False"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", TREE_MUTANTS, ids=[m[0] for m in TREE_MUTANTS])
+def test_tree_pins_catch_planted_mistake(tmp_path, monkeypatch, name, old, new):
+    import importlib.util
+    src = open(S.__file__).read()
+    assert src.count(old) == 1, name
+    path = tmp_path / f"stochastic_{name}.py"
+    path.write_text(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location(f"stochastic_{name}", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    monkeypatch.setattr(S, "accept_request_tree", mod.accept_request_tree)
+    failed = False
+    for check in (lambda: test_tree_lossless_first_token(0, 1.0), test_tree_lossless_after_a_rejected_sibling,
+                  test_tree_chain_equals_chain_rule, test_tree_siblings_in_index_order):
         try:
             check()
         except AssertionError:
