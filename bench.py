@@ -169,10 +169,16 @@ def main():
     toks = torch.empty(T, dtype=torch.int32, device=dev)
     new_len = torch.empty(B, dtype=torch.int32, device=dev)
     if args.stochastic:
-        if case.tree_parent is not None:
-            raise SystemExit("--stochastic covers chains only")
         g = torch.Generator(device=dev).manual_seed(1234)
-        dprobs = torch.softmax(logits + 0.3 * torch.randn(logits.shape, device=dev, generator=g), dim=-1)
+        # each draft row a perturbed copy of the target row that predicts its token
+        # (the previous token's row; in a tree, the parent's)
+        src = np.arange(T, dtype=np.int64)
+        for i in range(B):
+            o, o1 = int(case.cu_q[i]), int(case.cu_q[i + 1])
+            ks = np.arange(1, o1 - o)
+            src[o + ks] = o + (ks - 1 if case.tree_parent is None else case.tree_parent[o + ks])
+        src_rows = torch.from_numpy(src).to(dev)
+        dprobs = torch.softmax(logits[src_rows] + 0.3 * torch.randn(logits.shape, device=dev, generator=g), dim=-1)
         u_acc = torch.rand(T, device=dev, generator=g)
         w_smp = torch.rand(B, device=dev, generator=g)
         ws_sto = torch.empty(ops.spec_accept_stochastic_workspace_size(B, T, case.vocab), dtype=torch.uint8,
@@ -203,8 +209,12 @@ def main():
 
     def phase_accept(st):
         if args.stochastic:
-            ops.spec_accept_stochastic(logits, dprobs, draft, u_acc, w_smp, cu, workspace=ws_sto, accept_len=acc,
-                                       accepted_path=path, out_tokens=toks, stream=st)
+            if par is None:
+                ops.spec_accept_stochastic(logits, dprobs, draft, u_acc, w_smp, cu, workspace=ws_sto,
+                                           accept_len=acc, accepted_path=path, out_tokens=toks, stream=st)
+            else:
+                ops.spec_accept_stochastic_tree(logits, dprobs, draft, par, u_acc, w_smp, cu, workspace=ws_sto,
+                                                accept_len=acc, accepted_path=path, out_tokens=toks, stream=st)
             return
         if args.fused:  # acceptance and compaction in one launch; the compact phase is then empty
             accept_compact(logits, draft, cu, par, K, V, bt, ctx, workspace=ws_fused, num_layers=copies,

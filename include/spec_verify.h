@@ -299,7 +299,7 @@ int kv_compact_vt(void *k_cache, void *v_cache, int64_t layer_stride_elems, int 
                   int page_size, int num_pages, void *stream);
 
 /* ------------------------------------------------------------------------- */
-/* Lossless stochastic acceptance (chains)                                    */
+/* Lossless stochastic acceptance (chains and trees)                         */
 /* ------------------------------------------------------------------------- */
 /*
  * DSpark, glossary "Speculative Decoding": the verification rule keeps the
@@ -320,7 +320,7 @@ int kv_compact_vt(void *k_cache, void *v_cache, int64_t layer_stride_elems, int 
  *   logits, draft_probs  fp32 [total_q, vocab] (draft_probs row o, the root, unused;
  *                        each draft row sums to 1)
  *   draft_tokens int32 [total_q]; uniform_accept fp32 [total_q]; uniform_sample fp32 [batch]
- *   temperature  > 0;  chains only (no tree_parent)
+ *   temperature  > 0;  chains (trees: spec_accept_stochastic_tree below)
  *   workspace    at least spec_accept_stochastic_workspace_size() bytes (no initialisation)
  * Device status (spec_accept_stochastic_device_status): SV_DEV_BAD_CU_Q,
  * SV_DEV_BAD_TOKEN.
@@ -333,6 +333,34 @@ int spec_accept_stochastic(const float *logits, const float *draft_probs, int vo
                            const int32_t *cu_q, int batch, int total_q, int32_t *accept_len,
                            int32_t *accepted_path, int32_t *out_tokens, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/*
+ * Draft trees.  SwiftSpec ("Tree-aware KV cache management") verifies a tree of
+ * draft tokens per request; DSpark's glossary asks the rule to keep the target's
+ * distribution, and the pages give no rule for trees.  This call takes multi-draft
+ * rejection sampling: with tree_parent as for spec_accept (parent[o] = -1,
+ * 0 <= parent[o+k] < k), the walk starts at the root c = 0 with p' = p_c =
+ * softmax(logits[o+c] / temperature); the children k of c are tested in index
+ * order, child k accepted iff u[o+k] * q_k(x_k) < p'(x_k) (q_k = draft_probs[o+k],
+ * the distribution x_k was drawn from); an accepted child becomes c (p' restarts
+ * from its row); a rejection replaces p' by max(0, p' - q_k) normalised when that
+ * has mass (else p' stays); when no child of c is accepted, y is drawn with w[i]
+ * by inverse CDF from the last residual with mass (unnormalised), or from p_c.
+ * Outputs: accept_len[i] = n + 1 (n accepted drafts); accepted_path[o+t] = node
+ * index of the t-th path node (0 = root) for t <= n, -1 after; out_tokens[o+t] =
+ * draft token of path node t+1 for t < n, y at t = n, -1 after.  A tree with one
+ * child per node gives spec_accept_stochastic's results.  Each rejection costs one
+ * pass over the vocabulary (its residual's mass), inside one workgroup per request.
+ * Arguments, workspace (spec_accept_stochastic_workspace_size) and precision as for
+ * spec_accept_stochastic; tree_parent int32 [total_q].  Device status: also
+ * SV_DEV_BAD_PARENT (that request: accept_len 0, its path and tokens -1).
+ */
+int spec_accept_stochastic_tree(const float *logits, const float *draft_probs, int vocab,
+                                float temperature, const int32_t *draft_tokens, const int32_t *tree_parent,
+                                const float *uniform_accept, const float *uniform_sample,
+                                const int32_t *cu_q, int batch, int total_q, int32_t *accept_len,
+                                int32_t *accepted_path, int32_t *out_tokens, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 int spec_accept_stochastic_device_status(const void *workspace, uint32_t *flags, void *stream);
 

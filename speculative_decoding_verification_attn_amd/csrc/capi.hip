@@ -625,35 +625,39 @@ size_t spec_accept_stochastic_workspace_size(int batch, int total_q, int vocab) 
   return sv::stoch_layout(batch, total_q, vocab).total;
 }
 
-int spec_accept_stochastic(const float *logits, const float *draft_probs, int vocab,
-                           float temperature, const int32_t *draft_tokens,
-                           const float *uniform_accept, const float *uniform_sample,
-                           const int32_t *cu_q, int batch, int total_q, int32_t *accept_len,
-                           int32_t *accepted_path, int32_t *out_tokens, void *workspace,
-                           size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int stochastic_call(const float *logits, const float *draft_probs, int vocab, float temperature,
+                    const int32_t *draft_tokens, const int32_t *tree_parent, const float *uniform_accept,
+                    const float *uniform_sample, const int32_t *cu_q, int batch, int total_q, int32_t *accept_len,
+                    int32_t *accepted_path, int32_t *out_tokens, void *workspace, size_t workspace_bytes,
+                    void *stream, const char *name) {
   if (batch < 0 || total_q < 0 || total_q > (long long)batch * sv::kMaxTokens)
-    return fail(SV_ERR_SHAPE, "batch (%d) and total_q (%d) out of range", batch, total_q);
-  if (vocab <= 0) return fail(SV_ERR_SHAPE, "vocab %d must be > 0", vocab);
+    return fail(SV_ERR_SHAPE, "%s: batch (%d) and total_q (%d) out of range", name, batch, total_q);
+  if (vocab <= 0) return fail(SV_ERR_SHAPE, "%s: vocab %d must be > 0", name, vocab);
   if (!(temperature > 0.0f) || !isfinite(temperature))
-    return fail(SV_ERR_SHAPE, "temperature must be finite and > 0");
+    return fail(SV_ERR_SHAPE, "%s: temperature must be finite and > 0", name);
   if (batch == 0) return ok();
   if (!cu_q || !accept_len || !uniform_sample || !workspace)
-    return fail(SV_ERR_NULL, "spec_accept_stochastic: a required pointer is NULL");
+    return fail(SV_ERR_NULL, "%s: a required pointer is NULL", name);
   if (total_q > 0 && (!logits || !draft_probs || !draft_tokens || !uniform_accept || !accepted_path ||
                       !out_tokens))
-    return fail(SV_ERR_NULL, "spec_accept_stochastic: a required pointer is NULL");
+    return fail(SV_ERR_NULL, "%s: a required pointer is NULL", name);
   const sv::StochLayout lay = sv::stoch_layout(batch, total_q, vocab);
   if (workspace_bytes < lay.total)
-    return fail(SV_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, lay.total);
+    return fail(SV_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", name, workspace_bytes, lay.total);
   const size_t tb = (size_t)total_q * 4, bb = (size_t)batch * 4;
   if (overlaps(accepted_path, tb, out_tokens, tb) || overlaps(accept_len, bb, accepted_path, tb) ||
       overlaps(accept_len, bb, out_tokens, tb))
-    return fail(SV_ERR_ALIAS, "spec_accept_stochastic outputs overlap");
+    return fail(SV_ERR_ALIAS, "%s outputs overlap", name);
   sv::StochArgs a;
   memset(&a, 0, sizeof a);
   a.logits = logits;
   a.draft_probs = draft_probs;
   a.draft = draft_tokens;
+  a.parent = tree_parent;
   a.u = uniform_accept;
   a.w = uniform_sample;
   a.cu_q = cu_q;
@@ -667,7 +671,35 @@ int spec_accept_stochastic(const float *logits, const float *draft_probs, int vo
   a.vocab = vocab;
   a.c = 1.4426950408889634f / temperature;
   sv::launch_stochastic(a, static_cast<hipStream_t>(stream));
-  return check_launch("spec_accept_stochastic");
+  return check_launch(name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_accept_stochastic(const float *logits, const float *draft_probs, int vocab,
+                           float temperature, const int32_t *draft_tokens,
+                           const float *uniform_accept, const float *uniform_sample,
+                           const int32_t *cu_q, int batch, int total_q, int32_t *accept_len,
+                           int32_t *accepted_path, int32_t *out_tokens, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  return stochastic_call(logits, draft_probs, vocab, temperature, draft_tokens, nullptr, uniform_accept,
+                         uniform_sample, cu_q, batch, total_q, accept_len, accepted_path, out_tokens, workspace,
+                         workspace_bytes, stream, "spec_accept_stochastic");
+}
+
+int spec_accept_stochastic_tree(const float *logits, const float *draft_probs, int vocab,
+                                float temperature, const int32_t *draft_tokens, const int32_t *tree_parent,
+                                const float *uniform_accept, const float *uniform_sample,
+                                const int32_t *cu_q, int batch, int total_q, int32_t *accept_len,
+                                int32_t *accepted_path, int32_t *out_tokens, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  if (batch > 0 && total_q > 0 && !tree_parent)
+    return fail(SV_ERR_NULL, "spec_accept_stochastic_tree: tree_parent is NULL");
+  return stochastic_call(logits, draft_probs, vocab, temperature, draft_tokens, tree_parent, uniform_accept,
+                         uniform_sample, cu_q, batch, total_q, accept_len, accepted_path, out_tokens, workspace,
+                         workspace_bytes, stream, "spec_accept_stochastic_tree");
 }
 
 int spec_accept_stochastic_device_status(const void *workspace, uint32_t *flags, void *stream) {

@@ -12,13 +12,23 @@
 //   the next token y is drawn with w[i] by inverse CDF from max(0, p - q) at
 //   position n+1 (a rejection), or from p_{gamma+1} (all accepted); a residual
 //   without mass falls back to p_{n+1}.
+// Draft trees (SwiftSpec, "Tree-aware KV cache management"; the pages give no
+// rule for them): the siblings of the current node are tested in index order,
+// each against the target distribution left over by the siblings rejected before
+// it (max(0, p' - q) normalised, kept only when it has mass); an accepted child
+// becomes the current node with its own row's p; when no child is accepted the
+// draw takes the last residual with mass, or p.  A chain is the case of one
+// child per node and gives the same results.
 //
 // Four launches, all but the walk streaming over the vocabulary:
 //   softmax_stats_kernel  grid (splits, rows): per slice of a logits row the
 //                         running (max, sum of 2^(x - max)) of x = logit*log2(e)/T;
 //   stochastic_walk_kernel  one wave per request: merges the slices' stats,
 //                         tests every draft, writes the accepted prefix and the
-//                         sampling job (target row, draft row or none, w);
+//                         sampling job (target row, rejections in force, w);
+//   stochastic_tree_walk_kernel  (trees, in its place) one workgroup per request:
+//                         walks the tree, summing each rejection's residual mass
+//                         over the vocabulary with all its threads;
 //   sample_mass_kernel    grid (sub-slices of 2048 entries, batch): mass of the
 //                         draw's weights per sub-slice;
 //   sample_pick_kernel    one workgroup per request: finds the sub-slice holding
@@ -177,7 +187,8 @@ __global__ __launch_bounds__(64) void stochastic_walk_kernel(StochArgs a) {
     a.accept_len[i] = n + 1;
     StochJob jb;
     jb.tr = o + n;
-    jb.dr = n < q - 1 ? o + n + 1 : -1;
+    jb.nrej = n < q - 1 ? 1 : 0;
+    if (jb.nrej) reinterpret_cast<StochRej *>(a.ws + a.lay.rej)[(size_t)i * kMaxTokens] = StochRej{o + n + 1, 0.f};
     jb.m = sn.m;
     jb.s = sn.s;
     jb.w = a.w[i];
@@ -186,11 +197,27 @@ __global__ __launch_bounds__(64) void stochastic_walk_kernel(StochArgs a) {
   }
 }
 
-// weight of vocabulary entry v for a job
-__device__ inline float job_weight(const StochArgs &a, const StochJob &jb, int v, bool residual) {
-  const float p = fast_exp2(a.logits[(size_t)jb.tr * a.vocab + v] * a.c - jb.m) / jb.s;
-  if (!residual) return p;
-  return fmaxf(0.f, p - a.draft_probs[(size_t)jb.dr * a.vocab + v]);
+// p'(v) at a node whose logits row is lrow (softmax stats m, s) after the
+// first cnt rejections of rl: p(v), then each rejection's residual
+// max(0, p' - q) divided by its mass
+__device__ inline float resid_norm(const StochArgs &a, const float *lrow, float m, float s, const StochRej *rl,
+                                   int cnt, int v) {
+  float val = fast_exp2(lrow[v] * a.c - m) / s;
+  for (int t = 0; t < cnt; ++t) val = fmaxf(0.f, val - a.draft_probs[(size_t)rl[t].row * a.vocab + v]) / rl[t].mass;
+  return val;
+}
+
+// the draw's weight of entry v: p(v) without rejections, else the last
+// rejection's residual, unnormalised
+__device__ inline float draw_weight(const StochArgs &a, const StochJob &jb, const StochRej *rl, int nrej, int v) {
+  const float *lrow = a.logits + (size_t)jb.tr * a.vocab;
+  if (nrej == 0) return fast_exp2(lrow[v] * a.c - jb.m) / jb.s;
+  const float pv = resid_norm(a, lrow, jb.m, jb.s, rl, nrej - 1, v);
+  return fmaxf(0.f, pv - a.draft_probs[(size_t)rl[nrej - 1].row * a.vocab + v]);
+}
+
+__device__ inline const StochRej *rej_list(const StochArgs &a, int i) {
+  return reinterpret_cast<const StochRej *>(a.ws + a.lay.rej) + (size_t)i * kMaxTokens;
 }
 
 // the draw's weights are summed per sub-slice of kSub entries: thread t of
@@ -198,40 +225,46 @@ __device__ inline float job_weight(const StochArgs &a, const StochJob &jb, int v
 constexpr int kSub = 2048;
 constexpr int kPerThread = kSub / 256;
 
-__device__ inline float thread_weights(const StochArgs &a, const StochJob &jb, int base, bool residual,
-                                       float (&wv)[kPerThread]) {
+__device__ inline float thread_weights(const StochArgs &a, const StochJob &jb, const StochRej *rl, int nrej,
+                                       int base, float (&wv)[kPerThread]) {
   const int v0 = base + kPerThread * (int)threadIdx.x;
-  float l[kPerThread], d[kPerThread];
+  float val[kPerThread];
   if (v0 + kPerThread <= a.vocab && (a.vocab & 3) == 0) {
-    // two 16-byte loads per array (v0 is a multiple of 8 and rows start 16-byte aligned)
+    // two 16-byte loads per row (v0 is a multiple of 8 and rows start 16-byte aligned)
     const float4v *lp = reinterpret_cast<const float4v *>(a.logits + (size_t)jb.tr * a.vocab + v0);
+    float l[kPerThread];
 #pragma unroll
     for (int h = 0; h < kPerThread / 4; ++h) {
       const float4v x = lp[h];
       l[4 * h] = x.x; l[4 * h + 1] = x.y; l[4 * h + 2] = x.z; l[4 * h + 3] = x.w;
     }
-    if (residual) {
-      const float4v *dp = reinterpret_cast<const float4v *>(a.draft_probs + (size_t)jb.dr * a.vocab + v0);
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) val[e] = fast_exp2(l[e] * a.c - jb.m) / jb.s;
+    for (int t = 0; t < nrej; ++t) {
+      const float4v *dp = reinterpret_cast<const float4v *>(a.draft_probs + (size_t)rl[t].row * a.vocab + v0);
+      float d[kPerThread];
 #pragma unroll
       for (int h = 0; h < kPerThread / 4; ++h) {
         const float4v x = dp[h];
         d[4 * h] = x.x; d[4 * h + 1] = x.y; d[4 * h + 2] = x.z; d[4 * h + 3] = x.w;
       }
+      if (t + 1 < nrej) {
+        const float M = rl[t].mass;
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) val[e] = fmaxf(0.f, val[e] - d[e]) / M;
+      } else {
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) val[e] = fmaxf(0.f, val[e] - d[e]);
+      }
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      const int v = min(v0 + e, a.vocab - 1);
-      l[e] = a.logits[(size_t)jb.tr * a.vocab + v];
-      d[e] = residual ? a.draft_probs[(size_t)jb.dr * a.vocab + v] : 0.f;
-    }
+    for (int e = 0; e < kPerThread; ++e) val[e] = draw_weight(a, jb, rl, nrej, min(v0 + e, a.vocab - 1));
   }
   float own = 0.f;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
-    float p = fast_exp2(l[e] * a.c - jb.m) / jb.s;
-    if (residual) p = fmaxf(0.f, p - d[e]);
-    wv[e] = v0 + e < a.vocab ? p : 0.f;
+    wv[e] = v0 + e < a.vocab ? val[e] : 0.f;
     own += wv[e];
   }
   return own;
@@ -247,13 +280,167 @@ __device__ inline float block_sum_256(float x, float *scratch) {
   return r;
 }
 
+// one workgroup per request of a tree: the children of a node all have larger
+// indices than the node, so one scan over the verify tokens in index order
+// meets every test of the walk in the rule's order.  A rejection's residual mass
+// is a pass over the vocabulary whose entries each walk the rejection list with
+// dependent loads, so the pass runs 16 waves, each thread four entries at a time.
+constexpr int kTreeThreads = 1024;
+constexpr int kTreeIlp = 4;
+
+__device__ inline float block_sum_tree(float x, float *scratch) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float r = 0.f;
+#pragma unroll
+  for (int w = 0; w < kTreeThreads / 64; ++w) r += scratch[w];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kTreeThreads) void stochastic_tree_walk_kernel(StochArgs a) {
+  __shared__ float s_m[kMaxTokens], s_s[kMaxTokens];
+  __shared__ int s_par[kMaxTokens], s_path[kMaxTokens];
+  __shared__ StochRej s_rej[kMaxTokens];
+  __shared__ float s_red[kTreeThreads / 64];
+  __shared__ int s_dec;
+  const int i = blockIdx.x, tid = threadIdx.x;
+  unsigned *status = reinterpret_cast<unsigned *>(a.ws + a.lay.hdr);
+  StochJob *jobs = reinterpret_cast<StochJob *>(a.ws + a.lay.jobs);
+  const int o = a.cu_q[i], c1 = a.cu_q[i + 1], q = c1 - o;
+  if (o < 0 || c1 < o || c1 > a.total_q || q > kMaxTokens) {
+    if (tid == 0) {
+      atomicOr(status, SV_DEV_BAD_CU_Q);
+      a.accept_len[i] = 0;
+      jobs[i].tr = -1;
+    }
+    return;
+  }
+  if (i == 0 && tid == 0 && (a.cu_q[0] != 0 || a.cu_q[a.batch] != a.total_q)) atomicOr(status, SV_DEV_BAD_CU_Q);
+  if (q == 0) {
+    if (tid == 0) {
+      a.accept_len[i] = 0;
+      jobs[i].tr = -1;
+    }
+    return;
+  }
+  int bad = 0;
+  if (tid < q) {
+    const int pk = a.parent[o + tid];
+    bad = tid == 0 ? pk != -1 : (pk < 0 || pk >= tid);
+    s_par[tid] = pk;
+    Stat st{-INFINITY, 0.f};
+    const float2 *ps = reinterpret_cast<const float2 *>(a.ws + a.lay.stats) + (size_t)(o + tid) * a.lay.splits;
+    for (int k = 0; k < a.lay.splits; ++k) {
+      const float2 v = ps[k];
+      st = merge(st, Stat{v.x, v.y});
+    }
+    s_m[tid] = st.m;
+    s_s[tid] = st.s;
+  }
+  if (tid == 0) s_path[0] = 0;
+  if (__syncthreads_or(bad)) {
+    if (tid == 0) {
+      atomicOr(status, SV_DEV_BAD_PARENT);
+      a.accept_len[i] = 0;
+      jobs[i].tr = -1;
+    }
+    if (tid < q) {
+      a.accepted_path[o + tid] = -1;
+      a.out_tokens[o + tid] = -1;
+    }
+    return;
+  }
+  int c = 0, n = 0, cnt = 0;  // current node, accepted drafts, rejections in force at c
+  const float *lrow = a.logits + (size_t)o * a.vocab;
+  for (int k = 1; k < q; ++k) {
+    if (s_par[k] != c) continue;
+    if (tid == 0) {
+      const int x = a.draft[o + k];
+      int acc = 0;
+      if (x < 0 || x >= a.vocab) {
+        atomicOr(status, SV_DEV_BAD_TOKEN);
+      } else {
+        const float px = resid_norm(a, lrow, s_m[c], s_s[c], s_rej, cnt, x);
+        const float qx = a.draft_probs[(size_t)(o + k) * a.vocab + x];
+        acc = a.u[o + k] * qx < px;
+      }
+      s_dec = acc;
+    }
+    __syncthreads();
+    const int acc = s_dec;
+    __syncthreads();
+    if (acc) {
+      c = k;
+      ++n;
+      if (tid == 0) s_path[n] = k;
+      cnt = 0;
+      lrow = a.logits + (size_t)(o + k) * a.vocab;
+      continue;
+    }
+    // rejected: the mass of max(0, p' - q_k), kept as the next residual if positive
+    const float *qrow = a.draft_probs + (size_t)(o + k) * a.vocab;
+    const float mc = s_m[c], sc = s_s[c];
+    float part = 0.f;
+    for (int v0 = tid; v0 < a.vocab; v0 += kTreeIlp * kTreeThreads) {
+      float val[kTreeIlp];
+#pragma unroll
+      for (int e = 0; e < kTreeIlp; ++e) {
+        const int v = min(v0 + e * kTreeThreads, a.vocab - 1);
+        val[e] = fast_exp2(lrow[v] * a.c - mc) / sc;
+      }
+      for (int t = 0; t < cnt; ++t) {
+        const float *qt = a.draft_probs + (size_t)s_rej[t].row * a.vocab;
+        const float M = s_rej[t].mass;
+#pragma unroll
+        for (int e = 0; e < kTreeIlp; ++e) {
+          const int v = min(v0 + e * kTreeThreads, a.vocab - 1);
+          val[e] = fmaxf(0.f, val[e] - qt[v]) / M;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < kTreeIlp; ++e) {
+        const int v = v0 + e * kTreeThreads;
+        if (v < a.vocab) part += fmaxf(0.f, val[e] - qrow[v]);
+      }
+    }
+    const float M = block_sum_tree(part, s_red);
+    if (M > 0.f) {
+      if (tid == 0) s_rej[cnt] = StochRej{o + k, M};
+      ++cnt;
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  StochRej *rej = reinterpret_cast<StochRej *>(a.ws + a.lay.rej) + (size_t)i * kMaxTokens;
+  if (tid < cnt) rej[tid] = s_rej[tid];
+  if (tid < q) {
+    a.accepted_path[o + tid] = tid <= n ? s_path[tid] : -1;
+    if (tid < n) a.out_tokens[o + tid] = a.draft[o + s_path[tid + 1]];
+    if (tid > n) a.out_tokens[o + tid] = -1;
+  }
+  if (tid == 0) {
+    a.accept_len[i] = n + 1;
+    StochJob jb;
+    jb.tr = o + c;
+    jb.nrej = cnt;
+    jb.m = s_m[c];
+    jb.s = s_s[c];
+    jb.w = a.w[i];
+    jb.out = o + n;
+    jobs[i] = jb;
+  }
+}
+
 __global__ __launch_bounds__(256) void sample_mass_kernel(StochArgs a) {
   __shared__ float s_r[4];
   const int sb = blockIdx.x, i = blockIdx.y;
   const StochJob jb = reinterpret_cast<const StochJob *>(a.ws + a.lay.jobs)[i];
   if (jb.tr < 0) return;
   float wv[kPerThread];
-  const float own = thread_weights(a, jb, sb * kSub, jb.dr >= 0, wv);
+  const float own = thread_weights(a, jb, rej_list(a, i), jb.nrej, sb * kSub, wv);
   const float tot = block_sum_256(own, s_r);
   if (threadIdx.x == 0) reinterpret_cast<float *>(a.ws + a.lay.mass)[(size_t)i * a.lay.nsub + sb] = tot;
 }
@@ -272,16 +459,17 @@ __global__ __launch_bounds__(kPickThreads) void sample_pick_kernel(StochArgs a) 
   if (tid == 0) {
     float tot = 0.f;
     for (int k = 0; k < nsub; ++k) tot += mass[k];
-    s_residual = jb.dr >= 0 && tot > 0.f;
+    s_residual = jb.nrej > 0 && tot > 0.f;
   }
   __syncthreads();
-  const bool residual = s_residual;
-  if (jb.dr >= 0 && !residual) {
-    // a residual without mass: draw from p instead (rare); this workgroup
-    // recomputes the sub-slice masses of p
+  const StochRej *rl = rej_list(a, i);
+  const int nrej = s_residual ? jb.nrej : 0;
+  if (jb.nrej > 0 && nrej == 0) {
+    // a residual without mass: draw from p instead (rare; a tree's recorded
+    // residuals all have mass); this workgroup recomputes the sub-slice masses of p
     for (int k = 0; k < nsub; ++k) {
       float wv[kPerThread];
-      const float tot = block_sum_256(thread_weights(a, jb, k * kSub, false, wv), s_r);
+      const float tot = block_sum_256(thread_weights(a, jb, rl, 0, k * kSub, wv), s_r);
       if (tid == 0) mass[k] = tot;
     }
     __syncthreads();
@@ -310,7 +498,7 @@ __global__ __launch_bounds__(kPickThreads) void sample_pick_kernel(StochArgs a) 
   __syncthreads();
   const int base = s_k * kSub;
   float wv[kPerThread];
-  s_seg[tid] = thread_weights(a, jb, base, residual, wv);
+  s_seg[tid] = thread_weights(a, jb, rl, nrej, base, wv);
   __syncthreads();
   if (tid == 0) {  // exclusive prefix of the thread sums, in index order
     float run = 0.f;
@@ -343,7 +531,7 @@ __global__ __launch_bounds__(kPickThreads) void sample_pick_kernel(StochArgs a) 
     int y = s_pick;
     if (y < 0) {  // rounding left the target past the sub-slice: its last entry with weight
       for (int v = min(a.vocab, base + kSub) - 1; v >= base; --v)
-        if (job_weight(a, jb, v, residual) > 0.f) {
+        if (draw_weight(a, jb, rl, nrej, v) > 0.f) {
           y = v;
           break;
         }
@@ -357,7 +545,10 @@ __global__ __launch_bounds__(kPickThreads) void sample_pick_kernel(StochArgs a) 
 void launch_stochastic(const StochArgs &a, hipStream_t stream) {
   const int rows = a.total_q > 0 ? a.total_q : 1;
   softmax_stats_kernel<<<dim3(a.lay.splits, rows), 256, 0, stream>>>(a);
-  stochastic_walk_kernel<<<a.batch, 64, 0, stream>>>(a);
+  if (a.parent)
+    stochastic_tree_walk_kernel<<<a.batch, kTreeThreads, 0, stream>>>(a);
+  else
+    stochastic_walk_kernel<<<a.batch, 64, 0, stream>>>(a);
   sample_mass_kernel<<<dim3(a.lay.nsub, a.batch), 256, 0, stream>>>(a);
   sample_pick_kernel<<<a.batch, kPickThreads, 0, stream>>>(a);
 }

@@ -231,7 +231,7 @@ void launch_chunk_start(const AcceptArgs &a, hipStream_t stream);
 // ---------------------------------------------------------------------------
 struct StochJob {
   int tr;    // target row whose distribution the next token is drawn from (-1: none)
-  int dr;    // draft row subtracted for the residual, or -1 (draw from p itself)
+  int nrej;  // rejections whose residual the draw takes (0: the target row's p itself)
   int out;   // out_tokens entry of the drawn token
   int pad;
   float m, s;  // the target row's softmax stats (log2 domain)
@@ -239,11 +239,20 @@ struct StochJob {
   float pad2;
 };
 
+// One rejection in force at the node the draw is made at: the rejected draft's
+// row and the mass of the residual it left (the normaliser of that residual,
+// unused for the last one, whose unnormalised residual is the draw's weights).
+struct StochRej {
+  int row;
+  float mass;
+};
+
 struct StochLayout {
   size_t hdr;    // int32[8]: 0 status bits
   size_t stats;  // float2 [total_q][splits]: (max, sum) of each slice of each logits row
   size_t jobs;   // StochJob [batch]
   size_t mass;   // float [batch][nsub]: weight of each 2048-entry sub-slice of the draw
+  size_t rej;    // StochRej [batch][kMaxTokens]: the rejections of each request's draw
   size_t total;
   int splits;
   int nsub;
@@ -258,6 +267,7 @@ __host__ __device__ inline StochLayout stoch_layout(int batch, int total_q, int 
   l.jobs = off;   off = align256(off + size_t(batch) * sizeof(StochJob));
   l.nsub = (vocab + 2047) / 2048;
   l.mass = off;   off = align256(off + size_t(batch) * l.nsub * sizeof(float));
+  l.rej = off;    off = align256(off + size_t(batch) * kMaxTokens * sizeof(StochRej));
   l.total = off;
   return l;
 }
@@ -266,6 +276,7 @@ struct StochArgs {
   const float *logits;       // [total_q, vocab]
   const float *draft_probs;  // [total_q, vocab]
   const int32_t *draft;
+  const int32_t *parent;     // [total_q] per-request tree parents, or null for chains
   const float *u;            // [total_q]
   const float *w;            // [batch]
   const int32_t *cu_q;

@@ -49,7 +49,7 @@ EXPORTED = ["spec_verify_attn_workspace_size", "spec_verify_attn", "spec_verify_
             "spec_verify_attn_chunk_plan", "spec_verify_attn_chunk_run", "spec_verify_attn_chunk_run_vt",
             "spec_chunk_start", "spec_accept_chunk_workspace_size", "spec_accept_chunk", "spec_verify_budget",
             "spec_accept_compact_workspace_size", "spec_accept_compact", "spec_accept_compact_vt",
-            "spec_accept_stochastic_workspace_size", "spec_accept_stochastic",
+            "spec_accept_stochastic_workspace_size", "spec_accept_stochastic", "spec_accept_stochastic_tree",
             "spec_accept_stochastic_device_status", "spec_hbm_read_probe", "spec_verify_attn_noalloc",
             "spec_verify_attn_phase_trace"]
 
@@ -116,6 +116,8 @@ def load_library():
     lib.spec_accept_stochastic_workspace_size.restype = SZ
     lib.spec_accept_stochastic.argtypes = [P, P, I, F, P, P, P, P, I, I, P, P, P, P, SZ, P]
     lib.spec_accept_stochastic.restype = I
+    lib.spec_accept_stochastic_tree.argtypes = [P, P, I, F, P, P, P, P, P, I, I, P, P, P, P, SZ, P]
+    lib.spec_accept_stochastic_tree.restype = I
     lib.spec_accept_stochastic_device_status.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
     lib.spec_accept_stochastic_device_status.restype = I
     lib.spec_verify_attn_noalloc.argtypes = [P, P, P, P, I, P, P, P, P, I, I, I, I, I, I, I, F, P, P]
@@ -646,7 +648,7 @@ def _accept_compact_call(fn, logits, draft_tokens, cu_q, tree_parent, k_cache, v
 
 
 # ----------------------------------------------------------------------------
-# Lossless stochastic acceptance (chains)
+# Lossless stochastic acceptance (chains and trees)
 def spec_accept_stochastic_workspace_size(batch, total_q, vocab) -> int:
     return int(load_library().spec_accept_stochastic_workspace_size(batch, total_q, vocab))
 
@@ -679,6 +681,41 @@ def spec_accept_stochastic(logits, draft_probs, draft_tokens, uniform_accept, un
                                       _ptr(uniform_accept), _ptr(uniform_sample), _ptr(cu_q), B, T,
                                       _ptr(accept_len), _ptr(accepted_path), _ptr(out_tokens), _ptr(workspace),
                                       workspace.numel(), _stream(stream)))
+    return accept_len, accepted_path, out_tokens
+
+
+def spec_accept_stochastic_tree(logits, draft_probs, draft_tokens, tree_parent, uniform_accept, uniform_sample,
+                                cu_q, *, temperature=1.0, workspace=None, accept_len=None, accepted_path=None,
+                                out_tokens=None, stream=None):
+    """Multi-draft speculative sampling over draft trees (tree_parent int32 [T],
+    per request: root -1, else the parent's index within the request); returns
+    (accept_len [B], accepted_path [T] node indices, out_tokens [T])."""
+    lib = load_library()
+    _dev(logits, torch.float32, "logits")
+    _dev(draft_probs, torch.float32, "draft_probs")
+    _dev(uniform_accept, torch.float32, "uniform_accept")
+    _dev(uniform_sample, torch.float32, "uniform_sample")
+    _dev(draft_tokens, torch.int32, "draft_tokens")
+    _dev(tree_parent, torch.int32, "tree_parent")
+    _dev(cu_q, torch.int32, "cu_q")
+    T, V = logits.shape
+    B = cu_q.shape[0] - 1
+    dev = logits.device
+    if draft_tokens.numel() != T or tree_parent.numel() != T or uniform_accept.numel() != T \
+            or uniform_sample.numel() != B or tuple(draft_probs.shape) != (T, V):
+        raise ValueError("draft_tokens, tree_parent, uniform_accept and draft_probs must match the logits rows, "
+                         "uniform_sample the batch")
+    mk = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
+    accept_len = mk(B) if accept_len is None else accept_len
+    accepted_path = mk(T) if accepted_path is None else accepted_path
+    out_tokens = mk(T) if out_tokens is None else out_tokens
+    if workspace is None:
+        workspace = torch.empty(spec_accept_stochastic_workspace_size(B, T, V), dtype=torch.uint8, device=dev)
+    _check(lib.spec_accept_stochastic_tree(_ptr(logits), _ptr(draft_probs), V, float(temperature),
+                                           _ptr(draft_tokens), _ptr(tree_parent), _ptr(uniform_accept),
+                                           _ptr(uniform_sample), _ptr(cu_q), B, T, _ptr(accept_len),
+                                           _ptr(accepted_path), _ptr(out_tokens), _ptr(workspace),
+                                           workspace.numel(), _stream(stream)))
     return accept_len, accepted_path, out_tokens
 
 

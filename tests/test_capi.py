@@ -192,6 +192,33 @@ def test_fused_validation(lib):
     assert lib.spec_accept_compact_workspace_size(4, 20, 128256) > lib.spec_accept_workspace_size(4, 20, 128256)
 
 
+@pytest.mark.parametrize("fn", ["spec_accept_stochastic", "spec_accept_stochastic_tree"])
+def test_stochastic_validation(lib, fn):
+    def call(**kw):
+        a = dict(logits=FAKE, dp=FAKE, V=100, temp=1.0, dr=FAKE, par=FAKE, u=FAKE, w=FAKE, cu=FAKE, B=2, T=8,
+                 acc=ctypes.c_void_p(0x200000), path=ctypes.c_void_p(0x300000), toks=ctypes.c_void_p(0x400000),
+                 ws=FAKE, wsb=1 << 30, stream=NULL)
+        a.update(kw)
+        head = (a["logits"], a["dp"], a["V"], ctypes.c_float(a["temp"]), a["dr"])
+        tail = (a["u"], a["w"], a["cu"], a["B"], a["T"], a["acc"], a["path"], a["toks"], a["ws"], a["wsb"],
+                a["stream"])
+        if fn == "spec_accept_stochastic_tree":
+            return lib.spec_accept_stochastic_tree(*head, a["par"], *tail)
+        return lib.spec_accept_stochastic(*head, *tail)
+    assert call(V=0) == ops.SV_ERR_SHAPE
+    assert call(temp=0.0) == ops.SV_ERR_SHAPE
+    assert call(temp=float("inf")) == ops.SV_ERR_SHAPE
+    assert call(T=2 * 64 + 1) == ops.SV_ERR_SHAPE
+    assert call(dp=NULL) == ops.SV_ERR_NULL
+    assert call(w=NULL) == ops.SV_ERR_NULL
+    assert call(wsb=8) == ops.SV_ERR_WORKSPACE
+    assert call(toks=ctypes.c_void_p(0x300010)) == ops.SV_ERR_ALIAS
+    assert call(B=0, T=0) == ops.SV_OK
+    if fn == "spec_accept_stochastic_tree":
+        assert call(par=NULL) == ops.SV_ERR_NULL
+    assert lib.spec_accept_stochastic_workspace_size(4, 20, 1000) >= 4 * 64 * 8
+
+
 def test_read_probe_validation(lib):
     def call(**kw):
         a = dict(k=FAKE, v=FAKE, ch=FAKE, n=10, cb=4096, nb=100, sink=FAKE, sw=ops.PROBE_SINK_WORDS, stream=NULL)

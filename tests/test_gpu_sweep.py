@@ -1,7 +1,8 @@
 """Randomised sweeps of the whole path against the oracle, stopping at the first
 mismatch: verify attention with argmax and acceptance, compaction (plain and
 fused with acceptance) with the chunked acceptance loop, and stochastic
-acceptance, over seeded random batches and both V page layouts.
+acceptance of chains and of draft trees, over seeded random batches and both V
+page layouts.
 
 The default run is short (SV_SWEEP_BATCHES batches per sweep, default 3, in one
 part); longer sweeps run the same tests with more parts and batches:
@@ -180,4 +181,27 @@ def test_sweep_stochastic_acceptance(part):
         note(f"  draws equal to the oracle's {exact}/{B}, borderline acceptances {borderline}")
         # every draw was checked against the oracle's weights inside _compare; an
         # index may differ only where the draw point lies within 1e-4 of a boundary
+        assert borderline <= 1 and exact >= B - 2, (tag, exact, borderline)
+
+
+@parts
+def test_sweep_stochastic_tree_acceptance(part):
+    """Random batches of 1-16 draft trees (random, wide, bushy and chain shapes,
+    up to 24 nodes), vocabularies 2-32,000, temperatures 0.5-2.0: walks and draws
+    against the oracle (a decision within fp32 rounding of its threshold is not
+    counted)."""
+    rng = np.random.default_rng(50_000 + part)
+    for c in range(BATCHES):
+        B = int(rng.integers(1, 17))
+        V = int(rng.choice([2, 7, 100, 1000, 4099, 32000]))
+        qmax = int(rng.integers(1, 25))
+        temp = float(rng.choice([0.5, 0.7, 1.0, 1.3, 2.0]))
+        shape = str(rng.choice(["random", "wide", "bushy", "chain"]))
+        case = TS._stoch_tree_case(51_000 + 1000 * part + c, B, V, qmax, temp, shape)
+        tag = f"part {part} batch {c}: B={B} V={V} qmax={qmax} temperature={temp} shape={shape} T={int(case[0][-1])}"
+        note(tag)
+        (acc, path, toks), st = TS._run_tree(*case, temp)
+        assert st == 0, tag
+        exact, borderline = TS._compare_tree(*case, temp, acc, path, toks)
+        note(f"  draws equal to the oracle's {exact}/{B}, borderline walks {borderline}")
         assert borderline <= 1 and exact >= B - 2, (tag, exact, borderline)
