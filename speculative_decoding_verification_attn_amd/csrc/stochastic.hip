@@ -284,7 +284,8 @@ __device__ inline float block_sum_256(float x, float *scratch) {
 // indices than the node, so one scan over the verify tokens in index order
 // meets every test of the walk in the rule's order.  A rejection's residual mass
 // is a pass over the vocabulary whose entries each walk the rejection list with
-// dependent loads, so the pass runs 16 waves, each thread four entries at a time.
+// dependent loads, so the pass runs 16 waves, each thread taking kTreeIlp groups
+// of entries at a time (four consecutive entries per group with 16-byte loads).
 constexpr int kTreeThreads = 1024;
 constexpr int kTreeIlp = 4;
 
@@ -384,26 +385,67 @@ __global__ __launch_bounds__(kTreeThreads) void stochastic_tree_walk_kernel(Stoc
     const float *qrow = a.draft_probs + (size_t)(o + k) * a.vocab;
     const float mc = s_m[c], sc = s_s[c];
     float part = 0.f;
-    for (int v0 = tid; v0 < a.vocab; v0 += kTreeIlp * kTreeThreads) {
-      float val[kTreeIlp];
+    if ((a.vocab & 3) == 0) {
+      // 16-byte loads (rows start 16-byte aligned): each thread takes four
+      // consecutive entries from each of kTreeIlp groups per iteration
+      const int nv4 = a.vocab >> 2;
+      const float4v *l4 = reinterpret_cast<const float4v *>(lrow);
+      const float4v *q4 = reinterpret_cast<const float4v *>(qrow);
+      for (int b0 = tid; b0 < nv4; b0 += kTreeIlp * kTreeThreads) {
+        float val[kTreeIlp][4];
 #pragma unroll
-      for (int e = 0; e < kTreeIlp; ++e) {
-        const int v = min(v0 + e * kTreeThreads, a.vocab - 1);
-        val[e] = fast_exp2(lrow[v] * a.c - mc) / sc;
+        for (int g = 0; g < kTreeIlp; ++g) {
+          const float4v x = l4[min(b0 + g * kTreeThreads, nv4 - 1)];
+          val[g][0] = fast_exp2(x.x * a.c - mc) / sc;
+          val[g][1] = fast_exp2(x.y * a.c - mc) / sc;
+          val[g][2] = fast_exp2(x.z * a.c - mc) / sc;
+          val[g][3] = fast_exp2(x.w * a.c - mc) / sc;
+        }
+        for (int t = 0; t < cnt; ++t) {
+          const float4v *qt = reinterpret_cast<const float4v *>(a.draft_probs + (size_t)s_rej[t].row * a.vocab);
+          const float M = s_rej[t].mass;
+#pragma unroll
+          for (int g = 0; g < kTreeIlp; ++g) {
+            const float4v d = qt[min(b0 + g * kTreeThreads, nv4 - 1)];
+            val[g][0] = fmaxf(0.f, val[g][0] - d.x) / M;
+            val[g][1] = fmaxf(0.f, val[g][1] - d.y) / M;
+            val[g][2] = fmaxf(0.f, val[g][2] - d.z) / M;
+            val[g][3] = fmaxf(0.f, val[g][3] - d.w) / M;
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < kTreeIlp; ++g) {
+          if (b0 + g * kTreeThreads < nv4) {
+            const float4v d = q4[b0 + g * kTreeThreads];
+            part += fmaxf(0.f, val[g][0] - d.x);
+            part += fmaxf(0.f, val[g][1] - d.y);
+            part += fmaxf(0.f, val[g][2] - d.z);
+            part += fmaxf(0.f, val[g][3] - d.w);
+          }
+        }
       }
-      for (int t = 0; t < cnt; ++t) {
-        const float *qt = a.draft_probs + (size_t)s_rej[t].row * a.vocab;
-        const float M = s_rej[t].mass;
+    } else {
+      for (int v0 = tid; v0 < a.vocab; v0 += kTreeIlp * kTreeThreads) {
+        float val[kTreeIlp];
 #pragma unroll
         for (int e = 0; e < kTreeIlp; ++e) {
           const int v = min(v0 + e * kTreeThreads, a.vocab - 1);
-          val[e] = fmaxf(0.f, val[e] - qt[v]) / M;
+          val[e] = fast_exp2(lrow[v] * a.c - mc) / sc;
         }
-      }
+        for (int t = 0; t < cnt; ++t) {
+          const float *qt = a.draft_probs + (size_t)s_rej[t].row * a.vocab;
+          const float M = s_rej[t].mass;
 #pragma unroll
-      for (int e = 0; e < kTreeIlp; ++e) {
-        const int v = v0 + e * kTreeThreads;
-        if (v < a.vocab) part += fmaxf(0.f, val[e] - qrow[v]);
+          for (int e = 0; e < kTreeIlp; ++e) {
+            const int v = min(v0 + e * kTreeThreads, a.vocab - 1);
+            val[e] = fmaxf(0.f, val[e] - qt[v]) / M;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < kTreeIlp; ++e) {
+          const int v = v0 + e * kTreeThreads;
+          if (v < a.vocab) part += fmaxf(0.f, val[e] - qrow[v]);
+        }
       }
     }
     const float M = block_sum_tree(part, s_red);
