@@ -230,3 +230,49 @@ def test_stochastic_tree_bad_parent_sets_status():
         o2, q2 = int(cu[i]), int(cu[i + 1] - cu[i])
         pth, _, _, _ = S.accept_request_tree(logits, dprobs, draft, parent, u, w[i], o2, q2, 1.0)
         assert path[o2:o2 + len(pth)].tolist() == pth
+
+
+@pytest.mark.parametrize("shape", ["chain", "random"])
+def test_stochastic_in_captured_graph(shape):
+    """Both stochastic calls captured in one HIP graph: three replays, with eager
+    work and synchronisation between them, each equal bit for bit to an eager
+    call on the same inputs."""
+    cu, logits, dprobs, draft, parent, u, w = _stoch_tree_case(18, 12, 3000, 10, 1.0, shape)
+    B, T, V = len(cu) - 1, int(cu[-1]), 3000
+    d = lambda x: torch.from_numpy(x).to(DEV)
+    L, Q, U, W = d(logits), d(dprobs), d(u), d(w)
+    dr, par, cq = i32(draft), i32(parent), i32(cu)
+    ws = [torch.empty(ops.spec_accept_stochastic_workspace_size(B, T, V), dtype=torch.uint8, device=DEV)
+          for _ in range(2)]
+    outs = [[torch.full((n,), -7, dtype=torch.int32, device=DEV) for n in (B, T, T)] for _ in range(2)]
+
+    def calls(stream=None):
+        if shape == "chain":
+            ops.spec_accept_stochastic(L, Q, dr, U, W, cq, workspace=ws[0], accept_len=outs[0][0],
+                                       accepted_path=outs[0][1], out_tokens=outs[0][2], stream=stream)
+        ops.spec_accept_stochastic_tree(L, Q, dr, par, U, W, cq, workspace=ws[1], accept_len=outs[1][0],
+                                        accepted_path=outs[1][1], out_tokens=outs[1][2], stream=stream)
+    calls()
+    torch.cuda.synchronize()
+    eager = [[x.clone() for x in o] for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        calls(side)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        calls(side)
+    for rep in range(3):
+        for o in outs:
+            for x in o:
+                x.fill_(-7)
+        noise = torch.randn(1 << 16, device=DEV).sum()  # eager work between the replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(noise)
+        for k in (0, 1) if shape == "chain" else (1,):
+            for x, y in zip(outs[k], eager[k]):
+                assert torch.equal(x, y), (rep, k)
+    assert ops.spec_accept_stochastic_device_status(ws[1]) == 0
