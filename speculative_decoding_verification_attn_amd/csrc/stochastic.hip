@@ -307,6 +307,9 @@ __global__ __launch_bounds__(kTreeThreads) void stochastic_tree_walk_kernel(Stoc
   __shared__ StochRej s_rej[kMaxTokens];
   __shared__ float s_red[kTreeThreads / 64];
   __shared__ int s_dec;
+  __shared__ int s_x[kMaxTokens];         // the request's draft tokens
+  __shared__ float s_u[kMaxTokens];       // and acceptance uniforms
+  __shared__ float s_val[kMaxTokens + 2];  // a test's operands, loaded side by side
   const int i = blockIdx.x, tid = threadIdx.x;
   unsigned *status = reinterpret_cast<unsigned *>(a.ws + a.lay.hdr);
   StochJob *jobs = reinterpret_cast<StochJob *>(a.ws + a.lay.jobs);
@@ -340,6 +343,8 @@ __global__ __launch_bounds__(kTreeThreads) void stochastic_tree_walk_kernel(Stoc
     }
     s_m[tid] = st.m;
     s_s[tid] = st.s;
+    s_x[tid] = a.draft[o + tid];
+    s_u[tid] = a.u[o + tid];
   }
   if (tid == 0) s_path[0] = 0;
   if (__syncthreads_or(bad)) {
@@ -358,15 +363,24 @@ __global__ __launch_bounds__(kTreeThreads) void stochastic_tree_walk_kernel(Stoc
   const float *lrow = a.logits + (size_t)o * a.vocab;
   for (int k = 1; k < q; ++k) {
     if (s_par[k] != c) continue;
+    // the test's operands in one round trip: the logit of x at c, q_k(x), and
+    // q(x) of every rejection in force; then thread 0 evaluates p'(x) from them
+    // in resid_norm's order
+    const int x = s_x[k];
+    const bool x_ok = x >= 0 && x < a.vocab;
+    if (x_ok && tid < cnt + 2) {
+      const size_t row = tid == 0 ? (size_t)(o + c) : tid == 1 ? (size_t)(o + k) : (size_t)s_rej[tid - 2].row;
+      s_val[tid] = (tid == 0 ? a.logits : a.draft_probs)[row * a.vocab + x];
+    }
+    __syncthreads();
     if (tid == 0) {
-      const int x = a.draft[o + k];
       int acc = 0;
-      if (x < 0 || x >= a.vocab) {
+      if (!x_ok) {
         atomicOr(status, SV_DEV_BAD_TOKEN);
       } else {
-        const float px = resid_norm(a, lrow, s_m[c], s_s[c], s_rej, cnt, x);
-        const float qx = a.draft_probs[(size_t)(o + k) * a.vocab + x];
-        acc = a.u[o + k] * qx < px;
+        float px = fast_exp2(s_val[0] * a.c - s_m[c]) / s_s[c];
+        for (int t = 0; t < cnt; ++t) px = fmaxf(0.f, px - s_val[2 + t]) / s_rej[t].mass;
+        acc = s_u[k] * s_val[1] < px;
       }
       s_dec = acc;
     }
