@@ -11,6 +11,12 @@
  *                     matching prefix (chain) or deepest accepted root path (tree);
  *   kv_compact        moves the accepted path's K/V into consecutive slots of
  *                     the request's cache, in place, for every layer.
+ * Further calls, each described where it is declared: spec_accept_compact
+ * (acceptance and compaction in one launch), the chunked-verification calls
+ * (spec_chunk_start, spec_verify_attn_chunk_plan/_run, spec_accept_chunk),
+ * stochastic acceptance (spec_accept_stochastic for chains,
+ * spec_accept_stochastic_tree for draft trees), the verify-budget scheduler
+ * (spec_verify_budget, host memory), and spec_verify_attn_noalloc.
  *
  * Sources (page titles; sections as the pages name them):
  *   SwiftSpec (ASPLOS 2026), "Fused Latency-Optimized Kernels": padding-free
